@@ -1,0 +1,52 @@
+"""Parity metrics between a GPU result and the fp64 oracle (test infrastructure).
+
+err_raw    = max |y - o| / rms(o)
+err_excess = max( |y - o| - ulp_dtype(max(|y|, |o|)) / 2 , 0 ) / rms(o)
+
+y is the GPU output widened to float64, o the oracle output, rms over the whole
+output tensor of one call.  err_excess removes the half-ulp that rounding the
+exact result to the output dtype costs by itself; for bfloat16 outputs that
+rounding alone exceeds 1e-2 of rms on the benchmark's data, so the bfloat16
+gate is on err_excess (fp32 and fp16 are gated on err_raw).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# (mantissa bits, smallest normal exponent) of each I/O dtype
+_FMT = {"f32": (23, -126), "f16": (10, -14), "bf16": (7, -126)}
+
+# Tolerances: max |err| / rms(out) <= 1e-4 for fp32 I/O and <= 1e-2 for 16-bit I/O.
+TOLERANCE = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}
+GATED_ON = {"f32": "err_raw", "f16": "err_raw", "bf16": "err_excess"}
+
+
+def ulp(x, dtype: str) -> np.ndarray:
+    mant, emin = _FMT[dtype]
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.where(ax > 0, np.floor(np.log2(np.where(ax > 0, ax, 1.0))), emin)
+    e = np.maximum(e, emin)
+    return np.exp2(e - mant)
+
+
+def parity_errors(y, o, dtype: str) -> dict:
+    y = np.asarray(y, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    if y.shape != o.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {o.shape}")
+    rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
+    if rms == 0.0:
+        rms = 1.0
+    d = np.abs(y - o)
+    finite = bool(np.all(np.isfinite(y)))
+    half = 0.5 * ulp(np.maximum(np.abs(y), np.abs(o)), dtype)
+    raw = float(np.max(d)) / rms if d.size else 0.0
+    excess = float(np.max(np.maximum(d - half, 0.0))) / rms if d.size else 0.0
+    floor = float(np.max(0.5 * ulp(o, dtype))) / rms if d.size else 0.0
+    if not finite:
+        raw = excess = float("inf")
+    res = {"err_raw": raw, "err_excess": excess, "rounding_floor": floor, "rms": rms,
+           "tol": TOLERANCE[dtype], "gated_on": GATED_ON[dtype]}
+    res["ok"] = res[GATED_ON[dtype]] <= TOLERANCE[dtype]
+    return res
