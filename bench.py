@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the GTR gated-linear-attention forward pass on one MI355X.
+
+One step = every call of the chosen workload (e.g. the four scan directions of
+a 4-layer round), each on its own seeded inputs already resident in HBM.
+Steps are captured once in a HIP graph and replayed; the timed region is K
+replays bracketed by device synchronisation, timed with HIP events on the
+replay stream.  Prints one JSON line.
+
+  value        tokens/s = sum over the step's calls of B*H*N, per second
+  roofline     the dominant kernel's algorithmic bytes per launch over its
+               average duration (HIP events around each launch, eager, on the
+               launch stream), against 8 TB/s HBM
+  cpu_baseline the fp64 oracle on the host cores, on the same step's inputs
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1..5; default 2 = 40x40 grid, fp16, B1 H6, four directions")
+    ap.add_argument("--chunks-per-segment", type=int, default=0)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--profile-steps", type=int, default=50)
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_vision_backbone_chunkwise_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rows = json.load(f)
+    for r in rows:
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("source") == digest:
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this operator is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gla_inputs
+    import recurrent_vision_backbone_chunkwise_amd as gla
+
+    if not os.path.exists(gla.LIB_PATH):
+        from recurrent_vision_backbone_chunkwise_amd import build as hip_build
+        hip_build.build()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible")
+    dev = torch.device("cuda:0")
+    w = gla_inputs.workload(args.workload)
+    cps = args.chunks_per_segment
+
+    cpu_inputs = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
+    inputs = [[x.to(dev) for x in ins] for ins in cpu_inputs]
+    outs = [torch.empty_like(ins[2]) for ins in inputs]
+    tokens_per_call = w.B * w.H * w.n_tok
+    tokens_per_step = tokens_per_call * len(w.directions)
+    elt = 4 if w.dtype == "f32" else 2
+
+    stream = torch.cuda.Stream()
+
+    def step():
+        for (q, k, v, g), d, o in zip(inputs, w.directions, outs):
+            gla.gtr_gla_fwd_ex(q, k, v, g, o, d, chunks_per_segment=cps, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = start.elapsed_time(stop)
+    ms_per_step = ev_ms / args.steps
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    # per-kernel durations: HIP events around every launch, eager, same stream
+    gla.gtr_gla_profile_begin()
+    with torch.cuda.stream(stream):
+        for _ in range(args.profile_steps):
+            step()
+    prof = gla.gtr_gla_profile_end()
+    torch.cuda.synchronize()
+    kern = {name: {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.profile_steps}
+            for name, (ms, n) in prof.items() if n > 0}
+    dominant = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches_per_step"])
+    seg_len = cps if cps > 0 else gla.gtr_gla_auto_chunks_per_segment(w.B, w.H, w.grid_h, w.grid_w)
+    n_chunk = -(-w.n_tok // 64)
+    n_seg = -(-n_chunk // seg_len)
+    # algorithmic bytes per launch of each kernel (what it must move at minimum)
+    alg_bytes = {
+        "gla_seg_out": tokens_per_call * (3 * w.d_k + 2 * w.d_v) * elt,
+        "gla_seg_state": w.B * w.H * min(w.n_tok, (n_seg - 1) * seg_len * 64) * (2 * w.d_k + w.d_v) * elt,
+        "gla_seg_scan": w.B * w.H * n_seg * w.d_k * w.d_v * 4 * 2,
+    }
+    avg_s = kern[dominant]["avg_us"] * 1e-6
+    achieved = alg_bytes[dominant] / avg_s / 1e9
+    digest = kernel_sources_digest()
+    traffic = measured_traffic(dominant, w.name, digest)
+    path_gbs = value * (3 * w.d_k + 2 * w.d_v) * elt / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "alg_bytes_per_launch": alg_bytes[dominant], "avg_launch_us": round(kern[dominant]["avg_us"], 3),
+        "path_achieved": round(path_gbs, 1), "path_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+        "kernels": {n: {"avg_us": round(v["avg_us"], 3), "per_step": v["launches_per_step"]}
+                    for n, v in kern.items()},
+        "source": digest,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, cpu_inputs, args.cpu_seconds)
+
+    line = {
+        "metric": "GLA fwd tokens/sec (B*H*N), one MI355X",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "n_tok": w.n_tok,
+            "d_k": w.d_k, "d_v": w.d_v, "io_dtype": w.dtype, "gate": w.gate,
+            "directions": [gla_inputs.DIR_NAMES[d] for d in w.directions],
+            "tokens_per_step": tokens_per_step, "chunks_per_segment": seg_len,
+            "timing": "eager" if args.eager else "hip graph replay", "wall_ms": round(wall_ms, 3),
+            "accumulate": "f32",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, cpu_inputs, budget_s):
+    """The fp64 oracle, as it is, on the step's own inputs; repeats until ~budget_s."""
+    import oracle
+
+    t_total = 0.0
+    tokens = 0
+    reps = 0
+    threads = 1
+    while True:
+        for (q, k, v, g), d in zip(cpu_inputs, w.directions):
+            t0 = time.perf_counter()
+            _, threads = oracle.gla_forward(q, k, v, g, d, return_threads=True)
+            t_total += time.perf_counter() - t0
+            tokens += w.B * w.H * w.n_tok
+        reps += 1
+        if t_total >= budget_s or reps >= 1000:
+            break
+    return {"value": round(tokens / t_total, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full step ({len(w.directions)} calls, {w.name}) x {reps} repetitions, "
+                      f"{t_total:.1f} s of oracle time, fp64 token-by-token recurrence"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * gtr_gla.h - C ABI of the MI355X (gfx950) chunkwise forward pass of
+ * key-only-gated linear attention (GLA), the token mixer of GTR (Gated Token
+ * Recurrence).
+ *
+ * What every entry point computes
+ * -------------------------------
+ * Source: x-techcon article on GTR ("视觉AI看得越细，还能又快又准吗？..."),
+ * section 架构 (Architecture), and the abstract of "GTR: Gated Token
+ * Recurrence for Efficient Dense Prediction" (goodpapers.org listing).
+ * For each sequence (b, h) the patch grid of grid_h x grid_w tokens is visited
+ * in one of four scan orders.  A d_k x d_v state S starts at zero (or at a
+ * caller-supplied S_0) and, at each scan position t,
+ *     S_t = diag(alpha_t) S_{t-1} + k_t^T v_t ,  alpha_t = exp(log_gate_t),
+ *     o_t = q_t S_t ,
+ * i.e. the state first decays per KEY dimension by an input-generated gate
+ * (the value-side decay is 1), then takes the current key/value outer
+ * product, and the query reads the UPDATED state.  The article's printed
+ * formula did not survive extraction; the sentences around it fix the
+ * reading above.  No q.k scale and no softmax are applied.
+ *
+ * Scan orders (same section; the article names them, the index formulas are
+ * this library's reading): with grid cells numbered row-major n = r*grid_w + c
+ * and N = grid_h*grid_w,
+ *   GTR_DIR_L2R = 0  n(t) = t                         (row-major)
+ *   GTR_DIR_R2L = 1  n(t) = N-1-t                     (L->R reversed)
+ *   GTR_DIR_T2B = 2  n(t) = (t % grid_h)*grid_w + t / grid_h   (column-major)
+ *   GTR_DIR_B2T = 3  n(t) = n_T2B(N-1-t)              (T->B reversed)
+ * Every output is written at its own grid position ("the grid arrangement is
+ * restored after each scan"), so out has the layout of the inputs.
+ *
+ * How: the operator section of the same article splits the scan into
+ * 64-token chunks, computes each chunk's state contribution in parallel,
+ * passes chunk-boundary states along, then forms each chunk's outputs in
+ * parallel.  This library does the same with hand-written gfx950 kernels
+ * (MFMA contractions, scores kept in LDS); the result does not depend on the
+ * chunking beyond floating-point rounding.
+ *
+ * Layout (all tensors dense, row-major, one element type per call):
+ *   q, k, log_gate : [B][H][grid_h][grid_w][d_k]
+ *   v, out         : [B][H][grid_h][grid_w][d_v]
+ *   s0, s_final    : [B][H][d_k][d_v] float32 (entry point _ex only)
+ * log_gate holds natural-log alpha; finite values <= 0 are the domain
+ * (log-sigmoid outputs).  Outside it the output is unspecified.
+ *
+ * Ownership and execution:
+ *   - All tensor pointers are caller-owned memory of the current HIP device.
+ *     The library never frees them.  out must not overlap any input.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  The library
+ *     keeps one internal workspace per (device, stream); it is allocated on
+ *     first use and grown when a larger call arrives.  Growing it is refused
+ *     while `stream` is being captured into a graph (GTR_ERR_CAPTURE): make
+ *     one call of the largest shape before capturing.  Calls on one stream
+ *     are ordered by that stream; calls on different streams use different
+ *     workspaces.
+ *   - Every argument is validated on the host before the first HIP call;
+ *     a call that returns an error has launched nothing.  Outside stream
+ *     capture each pointer is also checked to be device memory of the
+ *     current device with room for its tensor (GTR_ERR_POINTER); while the
+ *     stream is being captured that query is skipped, so capture a call only
+ *     after the same call has run eagerly.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *
+ * Supported sizes (first build): d_k = d_v = 64; 1 <= grid_h*grid_w <= 2^28;
+ * 1 <= B*H <= 2^20.  Pointers must be 16-byte aligned.
+ */
+#ifndef GTR_GLA_H
+#define GTR_GLA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* scan directions */
+#define GTR_DIR_L2R 0
+#define GTR_DIR_R2L 1
+#define GTR_DIR_T2B 2
+#define GTR_DIR_B2T 3
+
+/* element types of q, k, v, log_gate and out */
+#define GTR_DTYPE_F32 0
+#define GTR_DTYPE_F16 1
+#define GTR_DTYPE_BF16 2
+
+/* return codes: 0 on success, negative on error */
+#define GTR_OK 0
+#define GTR_ERR_INVALID_ARG (-1)  /* null pointer, size <= 0 or too large, bad direction/dtype */
+#define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v other than 64 */
+#define GTR_ERR_ALIGNMENT (-3)    /* a pointer is not 16-byte aligned */
+#define GTR_ERR_ALIAS (-4)        /* out (or s_final) overlaps an input */
+#define GTR_ERR_NO_DEVICE (-5)    /* no usable HIP device */
+#define GTR_ERR_POINTER (-6)      /* a pointer is not device memory of the current device,
+                                     or its allocation is smaller than the tensor */
+#define GTR_ERR_ALLOC (-7)        /* workspace allocation failed */
+#define GTR_ERR_CAPTURE (-8)      /* workspace would have to grow during stream capture */
+#define GTR_ERR_LAUNCH (-9)       /* a kernel launch failed */
+
+/*
+ * Generic entry point: dtype selects the element type (GTR_DTYPE_*).
+ * Arguments: q, k, v, log_gate (inputs), out (output), B batch, H heads,
+ * grid_h x grid_w patch grid, d_k key width, d_v value width, direction
+ * (GTR_DIR_*), stream.
+ */
+int gtr_gla_fwd(const void *q, const void *k, const void *v, const void *log_gate,
+                void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                int direction, int dtype, hipStream_t stream);
+
+/* Typed entry points with the plain argument list; the element type is in the name. */
+int gtr_gla_fwd_f32(const void *q, const void *k, const void *v, const void *log_gate,
+                    void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                    int direction, hipStream_t stream);
+int gtr_gla_fwd_f16(const void *q, const void *k, const void *v, const void *log_gate,
+                    void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                    int direction, hipStream_t stream);
+int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *log_gate,
+                     void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                     int direction, hipStream_t stream);
+
+/*
+ * Extended entry point.  Same recurrence, plus:
+ *   s0       (nullable) float32 [B][H][d_k][d_v], the state before the first
+ *            scan position (NULL = zero state);
+ *   s_final  (nullable) float32 [B][H][d_k][d_v], receives the state after the
+ *            last scan position (NULL = not wanted);
+ *   chunks_per_segment  how many consecutive 64-token chunks one workgroup
+ *            walks with its state held in registers (<= 0 = chosen by the
+ *            library from the shape).  Any value gives the same result up to
+ *            rounding.
+ * The initial state makes a long scan splittable: running the two halves of
+ * a sequence with the first half's s_final as the second half's s0 equals one
+ * call on the whole sequence.
+ */
+int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_gate,
+                   void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                   int direction, int dtype, const float *s0, float *s_final,
+                   int chunks_per_segment, hipStream_t stream);
+
+/*
+ * Runs every check gtr_gla_fwd_ex would run on these arguments (sizes,
+ * alignment, overlap, device presence, and that each pointer is device memory
+ * of the current device with room for its tensor) and returns the code the
+ * call would return before launching anything.  Launches nothing.
+ */
+int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_gate,
+                  void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                  int direction, int dtype, const float *s0, float *s_final,
+                  int chunks_per_segment);
+
+/* Workspace bytes a call of this shape uses (0 on invalid arguments). */
+size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                               int dtype, int chunks_per_segment);
+
+/* Chunks per segment the library picks for this shape when given <= 0. */
+int gtr_gla_auto_chunks_per_segment(int B, int H, int grid_h, int grid_w);
+
+/* Message for the last error returned on this thread ("" if none).  The string
+ * is owned by the library and stays valid until the next call on this thread. */
+const char *gtr_gla_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gtr_gla_version(void);
+
+/* Frees every cached workspace (synchronises each device that has one). */
+void gtr_gla_release_workspaces(void);
+
+/*
+ * Per-kernel timing (measurement aid).  Between gtr_gla_profile_begin() and
+ * gtr_gla_profile_end() every kernel the library launches outside graph
+ * capture is bracketed by two HIP events recorded on the call's stream.
+ * gtr_gla_profile_end() waits for those events and fills, for kernel ids
+ * 0..max_kernels-1, the summed elapsed milliseconds and the launch counts
+ * (either array may be NULL).  Returns the number of kernel ids (3), or
+ * GTR_ERR_LAUNCH if an event could not be read.  Kernel ids: 0 gla_seg_state
+ * (segment state contributions), 1 gla_seg_scan (boundary-state scan),
+ * 2 gla_seg_out (outputs); gtr_gla_kernel_name() returns those names.
+ */
+void gtr_gla_profile_begin(void);
+int gtr_gla_profile_end(double *total_ms, int *launches, int max_kernels);
+const char *gtr_gla_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GTR_GLA_H */

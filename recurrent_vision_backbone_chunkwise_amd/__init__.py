@@ -1,0 +1,202 @@
+"""MI355X (gfx950) chunkwise forward pass of key-only-gated linear attention.
+
+Thin ctypes binding over ``libgtr_gla.so`` (built from ``csrc/`` by
+``build.py``).  The functions below carry the C names of ``include/gtr_gla.h``
+and only marshal arguments: every step of the computation runs in the HIP
+kernels of the library.  PyTorch is used for device memory and streams.
+
+There is no fallback: if the library is not built, or no GPU is present, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgtr_gla.so")
+
+GTR_DIR_L2R, GTR_DIR_R2L, GTR_DIR_T2B, GTR_DIR_B2T = 0, 1, 2, 3
+GTR_DTYPE_F32, GTR_DTYPE_F16, GTR_DTYPE_BF16 = 0, 1, 2
+ERRORS = {
+    0: "GTR_OK", -1: "GTR_ERR_INVALID_ARG", -2: "GTR_ERR_UNSUPPORTED", -3: "GTR_ERR_ALIGNMENT",
+    -4: "GTR_ERR_ALIAS", -5: "GTR_ERR_NO_DEVICE", -6: "GTR_ERR_POINTER", -7: "GTR_ERR_ALLOC",
+    -8: "GTR_ERR_CAPTURE", -9: "GTR_ERR_LAUNCH",
+}
+DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
+               torch.bfloat16: GTR_DTYPE_BF16}
+
+# Every symbol include/gtr_gla.h declares.
+EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
+           "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_auto_chunks_per_segment",
+           "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
+           "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name")
+
+
+class GlaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        self.code = code
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m recurrent_vision_backbone_chunkwise_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    fp = ctypes.c_void_p
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
+    L.gtr_gla_fwd.argtypes = sig + [i, st]
+    for name in ("gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16"):
+        getattr(L, name).argtypes = sig + [st]
+    L.gtr_gla_fwd_ex.argtypes = sig + [i, fp, fp, i, st]
+    L.gtr_gla_check.argtypes = sig + [i, fp, fp, i]
+    for name in ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
+                 "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version",
+                 "gtr_gla_auto_chunks_per_segment"):
+        getattr(L, name).restype = ctypes.c_int
+    L.gtr_gla_workspace_bytes.argtypes = [i] * 8
+    L.gtr_gla_workspace_bytes.restype = ctypes.c_size_t
+    L.gtr_gla_auto_chunks_per_segment.argtypes = [i] * 4
+    L.gtr_gla_last_error.argtypes = []
+    L.gtr_gla_last_error.restype = ctypes.c_char_p
+    L.gtr_gla_release_workspaces.argtypes = []
+    L.gtr_gla_release_workspaces.restype = None
+    L.gtr_gla_profile_begin.argtypes = []
+    L.gtr_gla_profile_begin.restype = None
+    L.gtr_gla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), i]
+    L.gtr_gla_profile_end.restype = ctypes.c_int
+    L.gtr_gla_kernel_name.argtypes = [i]
+    L.gtr_gla_kernel_name.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Paths of every HIP runtime mapped into this process (must be exactly one)."""
+    with open("/proc/self/maps") as f:
+        return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+
+
+def gtr_gla_last_error() -> str:
+    return lib().gtr_gla_last_error().decode()
+
+
+def gtr_gla_version() -> int:
+    return lib().gtr_gla_version()
+
+
+def gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYPE_F16,
+                            chunks_per_segment=0) -> int:
+    return lib().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, dtype, chunks_per_segment)
+
+
+def gtr_gla_auto_chunks_per_segment(B, H, grid_h, grid_w) -> int:
+    return lib().gtr_gla_auto_chunks_per_segment(B, H, grid_h, grid_w)
+
+
+def gtr_gla_release_workspaces() -> None:
+    lib().gtr_gla_release_workspaces()
+
+
+def gtr_gla_profile_begin() -> None:
+    lib().gtr_gla_profile_begin()
+
+
+def gtr_gla_profile_end() -> dict:
+    """{kernel name: (total ms, launches)} for the kernels launched since profile_begin."""
+    n = 8
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    rc = lib().gtr_gla_profile_end(ms, cnt, n)
+    if rc < 0:
+        raise GlaError(rc, "profiling events could not be read")
+    return {lib().gtr_gla_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(rc)}
+
+
+def gtr_gla_kernel_name(kernel: int) -> str:
+    return lib().gtr_gla_kernel_name(kernel).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise GlaError(rc, gtr_gla_last_error())
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _shapes(q, k, v, log_gate, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate), ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 5:
+            raise ValueError(f"{name} must be [B, H, grid_h, grid_w, d], got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, gh, gw, dk = q.shape
+    dv = v.shape[4]
+    if k.shape != q.shape or log_gate.shape != q.shape or v.shape[:4] != q.shape[:4] \
+            or out.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v, log_gate and out")
+    return B, H, gh, gw, dk, dv
+
+
+def gtr_gla_fwd(q, k, v, log_gate, out, direction: int, stream=None) -> None:
+    """out <- GLA forward of (q, k, v, log_gate) along `direction` (asynchronous)."""
+    B, H, gh, gw, dk, dv = _shapes(q, k, v, log_gate, out)
+    _check(lib().gtr_gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(),
+                             out.data_ptr(), B, H, gh, gw, dk, dv, int(direction),
+                             DTYPE_CODES[q.dtype], _stream_handle(stream)))
+
+
+def gtr_gla_fwd_ex(q, k, v, log_gate, out, direction: int, s0=None, s_final=None,
+                   chunks_per_segment: int = 0, stream=None) -> None:
+    """Extended call: optional initial state s0 / final state s_final (float32 [B,H,d_k,d_v])."""
+    B, H, gh, gw, dk, dv = _shapes(q, k, v, log_gate, out)
+    for name, t in (("s0", s0), ("s_final", s_final)):
+        if t is None:
+            continue
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() \
+                or tuple(t.shape) != (B, H, dk, dv):
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [B, H, d_k, d_v]")
+    _check(lib().gtr_gla_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(),
+                                out.data_ptr(), B, H, gh, gw, dk, dv, int(direction),
+                                DTYPE_CODES[q.dtype],
+                                s0.data_ptr() if s0 is not None else None,
+                                s_final.data_ptr() if s_final is not None else None,
+                                int(chunks_per_segment), _stream_handle(stream)))
+
+
+def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = False,
+                chunks_per_segment: int = 0, stream=None):
+    """Allocating convenience wrapper: returns out (and the final state when asked)."""
+    out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    s_final = None
+    if want_state:
+        s_final = torch.empty(q.shape[0], q.shape[1], q.shape[4], v.shape[4],
+                              dtype=torch.float32, device=q.device)
+    gtr_gla_fwd_ex(q, k, v, log_gate, out, direction, s0=s0, s_final=s_final,
+                   chunks_per_segment=chunks_per_segment, stream=stream)
+    return (out, s_final) if want_state else out

@@ -1,0 +1,366 @@
+// Host entry points of the GLA forward library: argument validation (before
+// any HIP call), a per-(device, stream) workspace cache, and dispatch to the
+// kernel launchers.  See include/gtr_gla.h for the contract.
+
+#include "gtr_gla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "gla_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr long long kMaxTokens = 1LL << 28;
+constexpr long long kMaxSeqs = 1LL << 20;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int elem_size(int dtype) { return dtype == GTR_DTYPE_F32 ? 4 : 2; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+struct Shape {
+  long long bh, n_tok;
+  int n_chunk, seg_len, n_seg;
+};
+
+int auto_seg_len(long long bh, int n_chunk) {
+  // Aim at about two resident workgroups per CU (256 CUs) for the output kernel;
+  // longer segments cut boundary-state traffic, shorter ones add parallelism.
+  const long long total = bh * n_chunk;
+  long long len = total / 512;
+  if (len < 1) len = 1;
+  if (len > 16) len = 16;
+  if (len > n_chunk) len = n_chunk;
+  return (int)len;
+}
+
+// Shape, direction and dtype checks; fills `shape`.
+int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                   int dtype, int chunks_per_segment, Shape *shape) {
+  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(GTR_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d grid=%dx%d d_k=%d d_v=%d)", B,
+                H, grid_h, grid_w, d_k, d_v);
+  if (direction < 0 || direction > 3)
+    return fail(GTR_ERR_INVALID_ARG, "direction %d not in 0..3", direction);
+  if (dtype < 0 || dtype > 2) return fail(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
+  const long long n_tok = (long long)grid_h * grid_w;
+  const long long bh = (long long)B * H;
+  if (n_tok > kMaxTokens)
+    return fail(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^28 tokens", grid_h, grid_w);
+  if (bh > kMaxSeqs) return fail(GTR_ERR_INVALID_ARG, "B*H = %lld exceeds 2^20", bh);
+  if (d_k != gtr::kHead || d_v != gtr::kHead)
+    return fail(GTR_ERR_UNSUPPORTED, "d_k=%d d_v=%d: this build supports d_k = d_v = 64", d_k, d_v);
+  shape->bh = bh;
+  shape->n_tok = n_tok;
+  shape->n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
+  int len = chunks_per_segment > 0 ? chunks_per_segment : auto_seg_len(bh, shape->n_chunk);
+  if (len > shape->n_chunk) len = shape->n_chunk;
+  shape->seg_len = len;
+  shape->n_seg = (shape->n_chunk + len - 1) / len;
+  if (bh * shape->n_seg > 0x7fffffffLL)
+    return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", bh * shape->n_seg);
+  return GTR_OK;
+}
+
+// Everything that can be checked without touching the HIP runtime.
+int validate(const void *q, const void *k, const void *v, const void *g, const void *out, int B,
+             int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
+             const float *s0, const float *s_final, int chunks_per_segment, Shape *shape) {
+  if (!q || !k || !v || !g || !out)
+    return fail(GTR_ERR_INVALID_ARG, "null tensor pointer (q=%p k=%p v=%p log_gate=%p out=%p)", q, k,
+                v, g, out);
+  int rc = validate_shape(B, H, grid_h, grid_w, d_k, d_v, direction, dtype, chunks_per_segment,
+                          shape);
+  if (rc != GTR_OK) return rc;
+  const void *ptrs[7] = {q, k, v, g, out, s0, s_final};
+  const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
+  for (int i = 0; i < 7; ++i)
+    if (ptrs[i] && (reinterpret_cast<uintptr_t>(ptrs[i]) & 15u))
+      return fail(GTR_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+  const size_t nb = (size_t)(shape->bh * shape->n_tok * gtr::kHead) * elem_size(dtype);
+  const size_t sb = (size_t)shape->bh * gtr::kStateElems * sizeof(float);
+  const void *ins[5] = {q, k, v, g, s0};
+  const size_t in_bytes[5] = {nb, nb, nb, nb, sb};
+  for (int i = 0; i < 5; ++i) {
+    if (!ins[i]) continue;
+    if (overlaps(out, nb, ins[i], in_bytes[i]))
+      return fail(GTR_ERR_ALIAS, "out overlaps %s", names[i]);
+    if (s_final && overlaps(s_final, sb, ins[i], in_bytes[i]))
+      return fail(GTR_ERR_ALIAS, "s_final overlaps %s", names[i]);
+  }
+  if (s_final && overlaps(s_final, sb, out, nb)) return fail(GTR_ERR_ALIAS, "s_final overlaps out");
+  return GTR_OK;
+}
+
+// Device memory of the current device, at least `bytes` long from `p`.
+int check_device_range(const void *p, size_t bytes, int device, const char *name) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GTR_ERR_POINTER, "%s=%p is not memory known to the HIP runtime", name, p);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(GTR_ERR_POINTER, "%s=%p is not device memory (type %d)", name, p, (int)attr.type);
+  if (attr.device != device)
+    return fail(GTR_ERR_POINTER, "%s=%p lives on device %d, current device is %d", name, p,
+                attr.device, device);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) == hipSuccess && base) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), x = reinterpret_cast<uintptr_t>(p);
+    if (x + bytes > b + size)
+      return fail(GTR_ERR_POINTER, "%s=%p: allocation ends %zu bytes short of the tensor", name, p,
+                  (size_t)(x + bytes - (b + size)));
+  } else {
+    (void)hipGetLastError();
+  }
+  return GTR_OK;
+}
+
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(int device, hipStream_t stream, size_t bytes, void **out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace &ws = g_ws[{device, stream}];
+  if (ws.bytes >= bytes) {
+    *out = ws.ptr;
+    return GTR_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    cs = hipStreamCaptureStatusNone;
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(GTR_ERR_CAPTURE,
+                "workspace must grow from %zu to %zu bytes while the stream is being captured; "
+                "make one call of this shape before capturing",
+                ws.bytes, bytes);
+  if (ws.ptr) {
+    // Kernels queued earlier on this stream may still read the old buffer.
+    if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
+    (void)hipFree(ws.ptr);
+    ws.ptr = nullptr;
+    ws.bytes = 0;
+  }
+  size_t want = bytes + bytes / 4;  // some headroom for slightly larger calls
+  if (hipMalloc(&ws.ptr, want) != hipSuccess) {
+    (void)hipGetLastError();
+    ws.ptr = nullptr;
+    return fail(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", want);
+  }
+  ws.bytes = want;
+  *out = ws.ptr;
+  return GTR_OK;
+}
+
+bool skip_pointer_checks() {
+  static const bool skip = [] {
+    const char *s = std::getenv("GTR_GLA_SKIP_POINTER_CHECKS");
+    return s && s[0] == '1';
+  }();
+  return skip;
+}
+
+}  // namespace
+
+extern "C" {
+
+}  // extern "C"
+
+namespace {
+
+// All host-side checks of one call, including the device-pointer queries.
+int check_call(const void *q, const void *k, const void *v, const void *log_gate, void *out, int B,
+               int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
+               const float *s0, float *s_final, int chunks_per_segment, Shape *sh, int *device,
+               hipStream_t stream, bool check_stream) {
+  g_last_error.clear();
+  int rc = validate(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
+                    s_final, chunks_per_segment, sh);
+  if (rc != GTR_OK) return rc;
+  int n_dev = 0;
+  if (hipGetDeviceCount(&n_dev) != hipSuccess || n_dev <= 0) {
+    (void)hipGetLastError();
+    return fail(GTR_ERR_NO_DEVICE, "no HIP device available");
+  }
+  if (hipGetDevice(device) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GTR_ERR_NO_DEVICE, "hipGetDevice failed");
+  }
+  bool capturing = false;
+  if (check_stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+    } else {
+      capturing = cs != hipStreamCaptureStatusNone;
+    }
+  }
+  // Pointer queries are not capture-safe on every runtime; calls being captured
+  // rely on the same checks having passed for an eager call before capture.
+  if (!capturing && !skip_pointer_checks()) {
+    const size_t nb = (size_t)(sh->bh * sh->n_tok * gtr::kHead) * elem_size(dtype);
+    const size_t sb = (size_t)sh->bh * gtr::kStateElems * sizeof(float);
+    const void *ptrs[7] = {q, k, v, log_gate, out, s0, s_final};
+    const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
+    const size_t sizes[7] = {nb, nb, nb, nb, nb, sb, sb};
+    for (int i = 0; i < 7; ++i) {
+      if (!ptrs[i]) continue;
+      rc = check_device_range(ptrs[i], sizes[i], *device, names[i]);
+      if (rc != GTR_OK) return rc;
+    }
+  }
+  return GTR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_gate, void *out,
+                  int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
+                  const float *s0, float *s_final, int chunks_per_segment) {
+  Shape sh;
+  int device = 0;
+  return check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
+                    s_final, chunks_per_segment, &sh, &device, nullptr, false);
+}
+
+int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_gate, void *out,
+                   int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                   int dtype, const float *s0, float *s_final, int chunks_per_segment,
+                   hipStream_t stream) {
+  Shape sh;
+  int device = 0;
+  int rc = check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
+                      s_final, chunks_per_segment, &sh, &device, stream, true);
+  if (rc != GTR_OK) return rc;
+
+  gtr::LaunchArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_gate;
+  a.out = out;
+  a.bh = (int)sh.bh;
+  a.grid_h = grid_h;
+  a.grid_w = grid_w;
+  a.n_tok = (int)sh.n_tok;
+  a.direction = direction;
+  a.dtype = dtype;
+  a.n_chunk = sh.n_chunk;
+  a.seg_len = sh.seg_len;
+  a.n_seg = sh.n_seg;
+  a.s0 = s0;
+  a.s_final = s_final;
+  a.stream = stream;
+  const bool need_ws = sh.n_seg > 1 || s0 || s_final;
+  if (need_ws) {
+    void *ws = nullptr;
+    rc = get_workspace(device, stream, gtr::workspace_floats(sh.bh, sh.n_seg) * sizeof(float), &ws);
+    if (rc != GTR_OK) return rc;
+    float *f = static_cast<float *>(ws);
+    const size_t st = (size_t)sh.bh * sh.n_seg * gtr::kStateElems;
+    a.agg = f;
+    a.prev = f + st;
+    a.agg_log2 = f + 2 * st;
+  }
+  const int err = gtr::launch_gla(a);
+  if (err != (int)hipSuccess)
+    return fail(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  return GTR_OK;
+}
+
+int gtr_gla_fwd(const void *q, const void *k, const void *v, const void *log_gate, void *out, int B,
+                int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
+                hipStream_t stream) {
+  return gtr_gla_fwd_ex(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype,
+                        nullptr, nullptr, 0, stream);
+}
+
+int gtr_gla_fwd_f32(const void *q, const void *k, const void *v, const void *log_gate, void *out,
+                    int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                    hipStream_t stream) {
+  return gtr_gla_fwd(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction,
+                     GTR_DTYPE_F32, stream);
+}
+
+int gtr_gla_fwd_f16(const void *q, const void *k, const void *v, const void *log_gate, void *out,
+                    int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                    hipStream_t stream) {
+  return gtr_gla_fwd(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction,
+                     GTR_DTYPE_F16, stream);
+}
+
+int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *log_gate, void *out,
+                     int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                     hipStream_t stream) {
+  return gtr_gla_fwd(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction,
+                     GTR_DTYPE_BF16, stream);
+}
+
+size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dtype,
+                               int chunks_per_segment) {
+  Shape sh;
+  if (validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, dtype, chunks_per_segment, &sh) != GTR_OK)
+    return 0;
+  return gtr::workspace_floats(sh.bh, sh.n_seg) * sizeof(float);
+}
+
+int gtr_gla_auto_chunks_per_segment(int B, int H, int grid_h, int grid_w) {
+  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0) return fail(GTR_ERR_INVALID_ARG, "bad shape");
+  const long long n_tok = (long long)grid_h * grid_w;
+  return auto_seg_len((long long)B * H, (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk));
+}
+
+const char *gtr_gla_last_error(void) { return g_last_error.c_str(); }
+
+int gtr_gla_version(void) { return kVersion; }
+
+void gtr_gla_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  for (auto &kv : g_ws) {
+    if (kv.second.ptr) {
+      int cur = 0;
+      if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(kv.second.ptr);
+        (void)hipSetDevice(cur);
+      }
+    }
+  }
+  g_ws.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal interface between the host entry points (gla_api.cpp) and the
+// kernel launchers (gla_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace gtr {
+
+constexpr int kChunk = 64;   // tokens per chunk (the pages' operator uses 64)
+constexpr int kHead = 64;    // d_k = d_v handled by this build
+constexpr int kStateElems = kHead * kHead;
+
+struct LaunchArgs {
+  const void *q, *k, *v, *g;
+  void *out;
+  int bh;            // B*H sequences
+  int grid_h, grid_w;
+  int n_tok;         // grid_h*grid_w
+  int direction;
+  int dtype;         // GTR_DTYPE_*
+  int n_chunk;       // ceil(n_tok / 64)
+  int seg_len;       // chunks per segment
+  int n_seg;         // ceil(n_chunk / seg_len)
+  // workspace (float32), all in the register-order state layout
+  float *agg;        // [bh][n_seg][4096] segment state contributions
+  float *agg_log2;   // [bh][n_seg][64]   segment log2 decay per key dim
+  float *prev;       // [bh][n_seg][4096] state entering each segment
+  const float *s0;   // user initial state, row-major [bh][64][64], nullable
+  float *s_final;    // user final state, row-major [bh][64][64], nullable
+  hipStream_t stream;
+};
+
+// Workspace floats needed for (bh, n_seg).
+inline size_t workspace_floats(size_t bh, size_t n_seg) {
+  return bh * n_seg * (2 * (size_t)kStateElems + kHead);
+}
+
+// Enqueues the kernels for one call.  Returns a hipError_t value.
+int launch_gla(const LaunchArgs &a);
+
+}  // namespace gtr

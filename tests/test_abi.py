@@ -1,0 +1,103 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented codes before touching the HIP
+runtime.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import recurrent_vision_backbone_chunkwise_amd as gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gtr_gla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gtr_gla_\w+)\s*\(", text)))
+
+
+def declared_constants():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(GTR_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_library_exports_every_declared_symbol():
+    L = gla.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(gla.EXPORTS) == names
+
+
+def test_binding_constants_match_header():
+    c = declared_constants()
+    assert c["GTR_DIR_L2R"] == gla.GTR_DIR_L2R and c["GTR_DIR_B2T"] == gla.GTR_DIR_B2T
+    assert c["GTR_DTYPE_BF16"] == gla.GTR_DTYPE_BF16
+    for code, name in gla.ERRORS.items():
+        assert c[name] == code
+
+
+def test_version_and_sizes():
+    assert gla.gtr_gla_version() == 10000
+    # one segment, no state: no workspace needed in practice, but the size query is still defined
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1) == 6 * 25 * (2 * 4096 + 64) * 4
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 0) == 0
+    assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0) == 0
+    assert gla.gtr_gla_auto_chunks_per_segment(1, 16, 128, 128) == 8
+    assert gla.gtr_gla_auto_chunks_per_segment(1, 6, 40, 40) == 1
+
+
+A = 0x10000  # fake, 16-byte aligned, never dereferenced
+
+
+def call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, out=A + 0x400000, B=1, H=1, gh=4,
+         gw=4, dk=64, dv=64, d=0, dt=1, s0=None, sf=None, seg=0):
+    return gla.lib().gtr_gla_fwd_ex(q, k, v, g, out, B, H, gh, gw, dk, dv, d, dt, s0, sf, seg, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(B=0), -1), (dict(H=-1), -1), (dict(gh=0), -1),
+    (dict(d=4), -1), (dict(d=-1), -1), (dict(dt=3), -1), (dict(gh=1 << 15, gw=1 << 14), -1),
+    (dict(B=1 << 11, H=1 << 10), -1),
+    (dict(dk=32), -2), (dict(dv=128), -2),
+    (dict(k=A + 0x100008), -3), (dict(out=A + 0x400004), -3), (dict(s0=A + 0x500002), -3),
+    (dict(out=A + 0x200000), -4), (dict(out=A + 0x300000 + 0x400), -4),
+    (dict(sf=A + 0x400000), -4), (dict(s0=A + 0x500000, sf=A + 0x500000), -4),
+])
+def test_argument_errors_before_any_hip_call(kw, code):
+    assert call(**kw) == code
+    assert gla.gtr_gla_last_error() != ""
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
+                    reason="a GPU is visible")
+def test_valid_call_without_gpu_reports_no_device():
+    assert call() == -5
+    assert "device" in gla.gtr_gla_last_error()
+    assert call(q=None) == -1  # argument errors still come first
+
+
+def test_typed_entry_points_validate_too():
+    L = gla.lib()
+    for fn in (L.gtr_gla_fwd_f32, L.gtr_gla_fwd_f16, L.gtr_gla_fwd_bf16):
+        assert fn(A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, 1, 1, 4, 4, 64, 64, 7,
+                  None) == -1
+    assert L.gtr_gla_fwd(A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, 1, 1, 4, 4, 64,
+                         64, 0, 5, None) == -1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 2, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        gla.gtr_gla_fwd(x, x, x, x, x.clone(), 0)
+
+
+def test_single_hip_runtime_mapped():
+    gla.lib()
+    assert len(gla.hip_runtimes_mapped()) == 1

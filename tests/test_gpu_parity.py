@@ -1,0 +1,231 @@
+"""HIP path vs the fp64 oracle, element by element (needs an MI355X).
+
+Every call goes through the C ABI (libgtr_gla.so) via the thin binding; the
+oracle runs on the host on the same seeded inputs.  Gate: max|y - o| / rms(o)
+<= 1e-4 for fp32 I/O and <= 1e-2 for fp16 I/O; bf16 I/O is gated on the same
+bound after removing the half-ulp that rounding the exact result to bf16
+costs by itself (see oracle/compare.py).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gla_inputs
+import oracle
+import recurrent_vision_backbone_chunkwise_amd as gla
+from oracle.compare import parity_errors
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = ("f32", "f16", "bf16")
+
+
+def note(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def gpu_run(q, k, v, g, direction, **kw):
+    args = [x.to(DEV) for x in (q, k, v, g)]
+    res = gla.gla_forward(*args, direction, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def check(q, k, v, g, direction, dtype, label, **kw):
+    note(f"{label} dir={direction} dtype={dtype} shape={tuple(q.shape)} {kw}")
+    y = gpu_run(q, k, v, g, direction, **kw)
+    ref = oracle.gla_forward(q, k, v, g, direction)
+    e = parity_errors(y.double().cpu().numpy(), ref, dtype)
+    assert e["ok"], f"{label}: {e}"
+    return e
+
+
+# ---- small grids: several tiles, ragged tails, degenerate shapes ---------------------
+
+SMALL_GRIDS = [(1, 1), (1, 63), (1, 65), (8, 8), (7, 9), (5, 13), (9, 17), (13, 11), (3, 100),
+               (100, 3), (16, 16)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+@pytest.mark.parametrize("grid", SMALL_GRIDS, ids=lambda g: f"{g[0]}x{g[1]}")
+def test_small_grids(grid, direction, dtype):
+    gh, gw = grid
+    q, k, v, g = gla_inputs.make_inputs(2, 3, gh, gw, 64, 64, dtype, "light",
+                                        seed=gh * 1000 + gw * 10 + direction)
+    check(q, k, v, g, direction, dtype, f"small {gh}x{gw}")
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 6, 7, 0])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_segment_lengths(seg, dtype):
+    q, k, v, g = gla_inputs.make_inputs(1, 4, 17, 19, 64, 64, dtype, "heavy", seed=77 + seg)
+    check(q, k, v, g, 3, dtype, f"seg_len={seg}", chunks_per_segment=seg)
+
+
+# ---- the five benchmark workloads at full size, every listed direction ----------------
+
+@pytest.mark.parametrize("widx", [1, 2, 3, 4, 5])
+def test_workloads_full_size(widx):
+    w = gla_inputs.workload(widx)
+    for layer, d in enumerate(w.directions):
+        q, k, v, g = gla_inputs.workload_inputs(w, layer)
+        e = check(q, k, v, g, d, w.dtype, w.name)
+        note(f"  {w.name} dir={d}: err_raw={e['err_raw']:.3g} err_excess={e['err_excess']:.3g}")
+
+
+# ---- gates that stress the exponent range ------------------------------------------------
+
+@pytest.mark.parametrize("gate", ["ones", "scale:4", "const:-30", "const:-1000", "mixed_extreme",
+                                  "const:-0.7"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gate_extremes(gate, dtype):
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 19, 23, 64, 64, dtype, gate, seed=5)
+    for d in (0, 2):
+        check(q, k, v, g, d, dtype, f"gate={gate}")
+
+
+def test_unit_gate_long_sequence():
+    """alpha = 1 over 16,384 tokens: the state only grows."""
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 128, 128, 64, 64, "f16", "ones", seed=6)
+    check(q, k, v, g, 1, "f16", "ones 128x128")
+
+
+# ---- initial / final state -----------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_initial_and_final_state(dtype):
+    B, H, gh, gw = 1, 3, 11, 13
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, dtype, "light", seed=8)
+    s0 = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(9)) * 0.5
+    for d in range(4):
+        note(f"state dir={d} dtype={dtype}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1)
+        ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
+        es = parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")
+        assert es["ok"], es
+
+
+def test_split_sequence_equals_whole():
+    """Top rows then bottom rows with the state carried equals one L->R call."""
+    B, H, gh, gw, r = 1, 2, 40, 40, 17
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, "f32", "light", seed=10)
+    whole = gpu_run(q, k, v, g, 0)
+    top, s_mid = gpu_run(q[:, :, :r].contiguous(), k[:, :, :r].contiguous(),
+                         v[:, :, :r].contiguous(), g[:, :, :r].contiguous(), 0, want_state=True)
+    bot = gpu_run(q[:, :, r:].contiguous(), k[:, :, r:].contiguous(), v[:, :, r:].contiguous(),
+                  g[:, :, r:].contiguous(), 0, s0=s_mid)
+    joined = torch.cat([top, bot], dim=2)
+    ref = oracle.gla_forward(q, k, v, g, 0)
+    assert parity_errors(joined.double().cpu().numpy(), ref, "f32")["ok"]
+    assert parity_errors(whole.double().cpu().numpy(), ref, "f32")["ok"]
+
+
+# ---- execution properties ------------------------------------------------------------------
+
+def test_deterministic_bitwise():
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 4, 40, 40, 64, 64, "f16", "light",
+                                                              seed=11))
+    outs = [gla.gla_forward(q, k, v, g, 2) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_non_default_stream_and_graph_replay():
+    w = gla_inputs.workload(2)
+    ins = [[x.to(DEV) for x in gla_inputs.workload_inputs(w, l)] for l in range(4)]
+    outs = [torch.empty_like(i[2]) for i in ins]
+    s = torch.cuda.Stream()
+    eager = []
+    with torch.cuda.stream(s):
+        for (q, k, v, g), d in zip(ins, w.directions):
+            eager.append(gla.gla_forward(q, k, v, g, d, stream=s))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):  # warm the capture stream's workspace first
+        for (q, k, v, g), d, o in zip(ins, w.directions, outs):
+            gla.gtr_gla_fwd(q, k, v, g, o, d, stream=cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        for (q, k, v, g), d, o in zip(ins, w.directions, outs):
+            gla.gtr_gla_fwd(q, k, v, g, o, d, stream=cap)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from eager"
+        # unrelated eager work between replays
+        gla.gla_forward(*ins[0], 0)
+        torch.cuda.synchronize()
+
+
+def test_capture_refuses_workspace_growth():
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 2, 30, 31, 64, 64, "f16", "light",
+                                                              seed=12))
+    out = torch.empty_like(v)
+    fresh = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(graph, stream=fresh):
+        try:
+            gla.gtr_gla_fwd_ex(q, k, v, g, out, 0, chunks_per_segment=1, stream=fresh)
+        except gla.GlaError as ex:
+            err = ex
+    assert err is not None and err.code == -8
+
+
+def test_pointer_checks_on_gpu():
+    """Host-side pointer checks, exercised through gtr_gla_check, which launches nothing."""
+    L = gla.lib()
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 1, 8, 8, 64, 64, "f16", "light",
+                                                              seed=13))
+    out = torch.empty_like(v)
+    pinned = torch.empty_like(v, device="cpu").pin_memory()
+    plain_host = np.zeros(8 * 8 * 64 + 16, dtype=np.float16)
+    host_ptr = (plain_host.ctypes.data + 15) // 16 * 16
+
+    def chk(o, gh=8, gw=8):
+        return L.gtr_gla_check(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), o, 1, 1, gh,
+                               gw, 64, 64, 0, 1, None, None, 0)
+
+    assert chk(out.data_ptr()) == 0
+    assert chk(host_ptr) == -6
+    assert chk(pinned.data_ptr()) == -6
+    # an output allocation half the size the tensor needs (a raw hipMalloc, so that
+    # no caching-allocator segment around it hides the shortfall)
+    import ctypes
+    hip = ctypes.CDLL(gla.hip_runtimes_mapped()[0])
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), ctypes.c_size_t(4096)) == 0
+    try:
+        assert chk(raw.value) == -6
+    finally:
+        hip.hipFree(raw)
+    torch.cuda.synchronize()
+
+
+def test_profiling_counts_launches():
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 2, 40, 40, 64, 64, "f16", "light",
+                                                              seed=14))
+    gla.gtr_gla_profile_begin()
+    for _ in range(3):
+        gla.gla_forward(q, k, v, g, 0, chunks_per_segment=5)
+    prof = gla.gtr_gla_profile_end()
+    assert prof["gla_seg_out"][1] == 3 and prof["gla_seg_state"][1] == 3
+    assert prof["gla_seg_scan"][1] == 3
+    assert all(ms > 0 for ms, n in prof.values())
+
+
+def test_single_runtime_and_library_loaded():
+    gla.lib()
+    assert len(gla.hip_runtimes_mapped()) == 1
+    with open("/proc/self/maps") as f:
+        assert any("libgtr_gla.so" in ln for ln in f)
