@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=2,
                     help="1..5; default 2 = 40x40 grid, fp16, B1 H6, four directions")
     ap.add_argument("--chunks-per-segment", type=int, default=0)
+    ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -88,6 +89,8 @@ def main():
     dev = torch.device("cuda:0")
     w = gla_inputs.workload(args.workload)
     cps = args.chunks_per_segment
+    path = {"auto": 0, "fused": 1, "split": 2}[args.path]
+    plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, cps, path)
 
     cpu_inputs = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
     inputs = [[x.to(dev) for x in ins] for ins in cpu_inputs]
@@ -100,7 +103,7 @@ def main():
 
     def step():
         for (q, k, v, g), d, o in zip(inputs, w.directions, outs):
-            gla.gtr_gla_fwd_ex(q, k, v, g, o, d, chunks_per_segment=cps, stream=stream)
+            gla.gtr_gla_fwd_ex(q, k, v, g, o, d, chunks_per_segment=cps, path=path, stream=stream)
 
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.warmup)):
@@ -144,11 +147,10 @@ def main():
     kern = {name: {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.profile_steps}
             for name, (ms, n) in prof.items() if n > 0}
     dominant = max(kern, key=lambda n: kern[n]["avg_us"] * kern[n]["launches_per_step"])
-    seg_len = cps if cps > 0 else gla.gtr_gla_auto_chunks_per_segment(w.B, w.H, w.grid_h, w.grid_w)
-    n_chunk = -(-w.n_tok // 64)
-    n_seg = -(-n_chunk // seg_len)
+    seg_len, n_seg = plan["seg_len"], plan["n_seg"]
     # algorithmic bytes per launch of each kernel (what it must move at minimum)
     alg_bytes = {
+        "gla_fused": tokens_per_call * (3 * w.d_k + 2 * w.d_v) * elt,
         "gla_seg_out": tokens_per_call * (3 * w.d_k + 2 * w.d_v) * elt,
         "gla_seg_state": w.B * w.H * min(w.n_tok, (n_seg - 1) * seg_len * 64) * (2 * w.d_k + w.d_v) * elt,
         "gla_seg_scan": w.B * w.H * n_seg * w.d_k * w.d_v * 4 * 2,
@@ -190,6 +192,7 @@ def main():
             "d_k": w.d_k, "d_v": w.d_v, "io_dtype": w.dtype, "gate": w.gate,
             "directions": [gla_inputs.DIR_NAMES[d] for d in w.directions],
             "tokens_per_step": tokens_per_step, "chunks_per_segment": seg_len,
+            "segments_per_sequence": n_seg, "kernels": "fused" if plan["fused"] else "split",
             "timing": "eager" if args.eager else "hip graph replay", "wall_ms": round(wall_ms, 3),
             "accumulate": "f32",
         },

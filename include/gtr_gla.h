@@ -26,8 +26,9 @@
  *   GTR_DIR_R2L = 1  n(t) = N-1-t                     (L->R reversed)
  *   GTR_DIR_T2B = 2  n(t) = (t % grid_h)*grid_w + t / grid_h   (column-major)
  *   GTR_DIR_B2T = 3  n(t) = n_T2B(N-1-t)              (T->B reversed)
- * Every output is written at its own grid position ("the grid arrangement is
- * restored after each scan"), so out has the layout of the inputs.
+ * Every output is written back at the grid position of its own token (the
+ * scan order only decides which tokens precede it), so out has the layout of
+ * the inputs.
  *
  * How: the operator section of the same article splits the scan into
  * 64-token chunks, computes each chunk's state contribution in parallel,
@@ -61,7 +62,7 @@
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
  *
- * Supported sizes (first build): d_k = d_v = 64; 1 <= grid_h*grid_w <= 2^28;
+ * Supported sizes (first build): d_k = d_v = 64; 1 <= grid_h*grid_w <= 2^23;
  * 1 <= B*H <= 2^20.  Pointers must be 16-byte aligned.
  */
 #ifndef GTR_GLA_H
@@ -85,9 +86,14 @@ extern "C" {
 #define GTR_DTYPE_F16 1
 #define GTR_DTYPE_BF16 2
 
+/* launch structure (entry points _ex, _check, _workspace_bytes, _plan) */
+#define GTR_PATH_AUTO 0   /* chosen by the library */
+#define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, flag-ordered combine, outputs */
+#define GTR_PATH_SPLIT 2  /* three kernels: segment aggregates, boundary scan, outputs */
+
 /* return codes: 0 on success, negative on error */
 #define GTR_OK 0
-#define GTR_ERR_INVALID_ARG (-1)  /* null pointer, size <= 0 or too large, bad direction/dtype */
+#define GTR_ERR_INVALID_ARG (-1)  /* null pointer, size <= 0 or too large, bad direction/dtype/path */
 #define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v other than 64 */
 #define GTR_ERR_ALIGNMENT (-3)    /* a pointer is not 16-byte aligned */
 #define GTR_ERR_ALIAS (-4)        /* out (or s_final) overlaps an input */
@@ -127,8 +133,9 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
  *            last scan position (NULL = not wanted);
  *   chunks_per_segment  how many consecutive 64-token chunks one workgroup
  *            walks with its state held in registers (<= 0 = chosen by the
- *            library from the shape).  Any value gives the same result up to
- *            rounding.
+ *            library from the shape);
+ *   path     GTR_PATH_AUTO, GTR_PATH_FUSED or GTR_PATH_SPLIT.
+ * Any segment length and path give the same result up to rounding.
  * The initial state makes a long scan splittable: running the two halves of
  * a sequence with the first half's s_final as the second half's s0 equals one
  * call on the whole sequence.
@@ -136,7 +143,7 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
 int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_gate,
                    void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                    int direction, int dtype, const float *s0, float *s_final,
-                   int chunks_per_segment, hipStream_t stream);
+                   int chunks_per_segment, int path, hipStream_t stream);
 
 /*
  * Runs every check gtr_gla_fwd_ex would run on these arguments (sizes,
@@ -147,14 +154,17 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
 int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_gate,
                   void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                   int direction, int dtype, const float *s0, float *s_final,
-                  int chunks_per_segment);
+                  int chunks_per_segment, int path);
 
 /* Workspace bytes a call of this shape uses (0 on invalid arguments). */
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
-                               int dtype, int chunks_per_segment);
+                               int dtype, int chunks_per_segment, int path);
 
-/* Chunks per segment the library picks for this shape when given <= 0. */
-int gtr_gla_auto_chunks_per_segment(int B, int H, int grid_h, int grid_w);
+/* The plan the library uses for a shape (d_k = d_v = 64): chunks per segment,
+ * segments per sequence, and 1 if one fused kernel runs (0: three kernels).
+ * Any output pointer may be NULL.  Returns 0 or an argument error. */
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int chunks_per_segment, int path,
+                 int *seg_len, int *n_seg, int *fused);
 
 /* Message for the last error returned on this thread ("" if none).  The string
  * is owned by the library and stays valid until the next call on this thread. */
@@ -172,10 +182,12 @@ void gtr_gla_release_workspaces(void);
  * capture is bracketed by two HIP events recorded on the call's stream.
  * gtr_gla_profile_end() waits for those events and fills, for kernel ids
  * 0..max_kernels-1, the summed elapsed milliseconds and the launch counts
- * (either array may be NULL).  Returns the number of kernel ids (3), or
+ * (either array may be NULL).  Returns the number of kernel ids (4), or
  * GTR_ERR_LAUNCH if an event could not be read.  Kernel ids: 0 gla_seg_state
  * (segment state contributions), 1 gla_seg_scan (boundary-state scan),
- * 2 gla_seg_out (outputs); gtr_gla_kernel_name() returns those names.
+ * 2 gla_seg_out (outputs), 3 gla_fused (the one-kernel path);
+ * gtr_gla_kernel_name() returns those names.  The events are taken by the
+ * dispatch itself, so they measure kernel execution, not launch overhead.
  */
 void gtr_gla_profile_begin(void);
 int gtr_gla_profile_end(double *total_ms, int *launches, int max_kernels);

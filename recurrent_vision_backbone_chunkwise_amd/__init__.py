@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libgtr_gla.so")
 
 GTR_DIR_L2R, GTR_DIR_R2L, GTR_DIR_T2B, GTR_DIR_B2T = 0, 1, 2, 3
 GTR_DTYPE_F32, GTR_DTYPE_F16, GTR_DTYPE_BF16 = 0, 1, 2
+GTR_PATH_AUTO, GTR_PATH_FUSED, GTR_PATH_SPLIT = 0, 1, 2
 ERRORS = {
     0: "GTR_OK", -1: "GTR_ERR_INVALID_ARG", -2: "GTR_ERR_UNSUPPORTED", -3: "GTR_ERR_ALIGNMENT",
     -4: "GTR_ERR_ALIAS", -5: "GTR_ERR_NO_DEVICE", -6: "GTR_ERR_POINTER", -7: "GTR_ERR_ALLOC",
@@ -30,7 +31,7 @@ DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
 
 # Every symbol include/gtr_gla.h declares.
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
-           "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_auto_chunks_per_segment",
+           "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
            "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name")
 
@@ -59,15 +60,15 @@ def lib() -> ctypes.CDLL:
     L.gtr_gla_fwd.argtypes = sig + [i, st]
     for name in ("gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16"):
         getattr(L, name).argtypes = sig + [st]
-    L.gtr_gla_fwd_ex.argtypes = sig + [i, fp, fp, i, st]
-    L.gtr_gla_check.argtypes = sig + [i, fp, fp, i]
+    L.gtr_gla_fwd_ex.argtypes = sig + [i, fp, fp, i, i, st]
+    L.gtr_gla_check.argtypes = sig + [i, fp, fp, i, i]
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.gtr_gla_plan.argtypes = [i] * 6 + [ip, ip, ip]
     for name in ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
-                 "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version",
-                 "gtr_gla_auto_chunks_per_segment"):
+                 "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version", "gtr_gla_plan"):
         getattr(L, name).restype = ctypes.c_int
-    L.gtr_gla_workspace_bytes.argtypes = [i] * 8
+    L.gtr_gla_workspace_bytes.argtypes = [i] * 9
     L.gtr_gla_workspace_bytes.restype = ctypes.c_size_t
-    L.gtr_gla_auto_chunks_per_segment.argtypes = [i] * 4
     L.gtr_gla_last_error.argtypes = []
     L.gtr_gla_last_error.restype = ctypes.c_char_p
     L.gtr_gla_release_workspaces.argtypes = []
@@ -97,12 +98,17 @@ def gtr_gla_version() -> int:
 
 
 def gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYPE_F16,
-                            chunks_per_segment=0) -> int:
-    return lib().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, dtype, chunks_per_segment)
+                            chunks_per_segment=0, path=GTR_PATH_AUTO) -> int:
+    return lib().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, dtype, chunks_per_segment,
+                                         path)
 
 
-def gtr_gla_auto_chunks_per_segment(B, H, grid_h, grid_w) -> int:
-    return lib().gtr_gla_auto_chunks_per_segment(B, H, grid_h, grid_w)
+def gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment=0, path=GTR_PATH_AUTO) -> dict:
+    """{"seg_len", "n_seg", "fused"} the library uses for this shape."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment, path, ctypes.byref(a),
+                              ctypes.byref(b), ctypes.byref(c)))
+    return {"seg_len": a.value, "n_seg": b.value, "fused": bool(c.value)}
 
 
 def gtr_gla_release_workspaces() -> None:
@@ -172,7 +178,7 @@ def gtr_gla_fwd(q, k, v, log_gate, out, direction: int, stream=None) -> None:
 
 
 def gtr_gla_fwd_ex(q, k, v, log_gate, out, direction: int, s0=None, s_final=None,
-                   chunks_per_segment: int = 0, stream=None) -> None:
+                   chunks_per_segment: int = 0, path: int = GTR_PATH_AUTO, stream=None) -> None:
     """Extended call: optional initial state s0 / final state s_final (float32 [B,H,d_k,d_v])."""
     B, H, gh, gw, dk, dv = _shapes(q, k, v, log_gate, out)
     for name, t in (("s0", s0), ("s_final", s_final)):
@@ -186,11 +192,11 @@ def gtr_gla_fwd_ex(q, k, v, log_gate, out, direction: int, s0=None, s_final=None
                                 DTYPE_CODES[q.dtype],
                                 s0.data_ptr() if s0 is not None else None,
                                 s_final.data_ptr() if s_final is not None else None,
-                                int(chunks_per_segment), _stream_handle(stream)))
+                                int(chunks_per_segment), int(path), _stream_handle(stream)))
 
 
 def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = False,
-                chunks_per_segment: int = 0, stream=None):
+                chunks_per_segment: int = 0, path: int = GTR_PATH_AUTO, stream=None):
     """Allocating convenience wrapper: returns out (and the final state when asked)."""
     out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     s_final = None
@@ -198,5 +204,5 @@ def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = F
         s_final = torch.empty(q.shape[0], q.shape[1], q.shape[4], v.shape[4],
                               dtype=torch.float32, device=q.device)
     gtr_gla_fwd_ex(q, k, v, log_gate, out, direction, s0=s0, s_final=s_final,
-                   chunks_per_segment=chunks_per_segment, stream=stream)
+                   chunks_per_segment=chunks_per_segment, path=path, stream=stream)
     return (out, s_final) if want_state else out

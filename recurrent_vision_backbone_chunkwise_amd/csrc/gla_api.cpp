@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -20,7 +21,7 @@
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
-constexpr long long kMaxTokens = 1LL << 28;
+constexpr long long kMaxTokens = 1LL << 23;  // element offsets inside a sequence fit in 32 bits
 constexpr long long kMaxSeqs = 1LL << 20;
 
 thread_local std::string g_last_error;
@@ -45,42 +46,50 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 struct Shape {
   long long bh, n_tok;
   int n_chunk, seg_len, n_seg;
+  bool fused;
 };
 
-int auto_seg_len(long long bh, int n_chunk) {
-  // Aim at about two resident workgroups per CU (256 CUs) for the output kernel;
-  // longer segments cut boundary-state traffic, shorter ones add parallelism.
+constexpr int kMaxFusedSegments = 24;  // longest aggregate chain one fused workgroup combines
+
+// Chunks per segment and launch structure for a shape.  The fused launch reads
+// the aggregates of all earlier segments of its sequence, so it caps the
+// segment count; the three-launch path scans segments in a separate kernel.
+void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
   const long long total = bh * n_chunk;
-  long long len = total / 512;
-  if (len < 1) len = 1;
-  if (len > 16) len = 16;
+  sh->fused = path != GTR_PATH_SPLIT;
+  long long len = chunks_per_segment;
+  if (len <= 0) {
+    // about three resident workgroups per CU on 256 CUs
+    len = (total + 767) / 768;
+    if (sh->fused) len = std::max<long long>(len, (n_chunk + kMaxFusedSegments - 1) / kMaxFusedSegments);
+    len = std::max<long long>(1, std::min<long long>(len, 32));
+  }
   if (len > n_chunk) len = n_chunk;
-  return (int)len;
+  sh->seg_len = (int)len;
+  sh->n_seg = (int)((n_chunk + len - 1) / len);
 }
 
 // Shape, direction and dtype checks; fills `shape`.
 int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
-                   int dtype, int chunks_per_segment, Shape *shape) {
+                   int dtype, int chunks_per_segment, int path, Shape *shape) {
   if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || d_k <= 0 || d_v <= 0)
     return fail(GTR_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d grid=%dx%d d_k=%d d_v=%d)", B,
                 H, grid_h, grid_w, d_k, d_v);
   if (direction < 0 || direction > 3)
     return fail(GTR_ERR_INVALID_ARG, "direction %d not in 0..3", direction);
   if (dtype < 0 || dtype > 2) return fail(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
+  if (path < 0 || path > 2) return fail(GTR_ERR_INVALID_ARG, "path %d not in 0..2", path);
   const long long n_tok = (long long)grid_h * grid_w;
   const long long bh = (long long)B * H;
   if (n_tok > kMaxTokens)
-    return fail(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^28 tokens", grid_h, grid_w);
+    return fail(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^23 tokens", grid_h, grid_w);
   if (bh > kMaxSeqs) return fail(GTR_ERR_INVALID_ARG, "B*H = %lld exceeds 2^20", bh);
   if (d_k != gtr::kHead || d_v != gtr::kHead)
     return fail(GTR_ERR_UNSUPPORTED, "d_k=%d d_v=%d: this build supports d_k = d_v = 64", d_k, d_v);
   shape->bh = bh;
   shape->n_tok = n_tok;
   shape->n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  int len = chunks_per_segment > 0 ? chunks_per_segment : auto_seg_len(bh, shape->n_chunk);
-  if (len > shape->n_chunk) len = shape->n_chunk;
-  shape->seg_len = len;
-  shape->n_seg = (shape->n_chunk + len - 1) / len;
+  plan(bh, shape->n_chunk, path, chunks_per_segment, shape);
   if (bh * shape->n_seg > 0x7fffffffLL)
     return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", bh * shape->n_seg);
   return GTR_OK;
@@ -89,12 +98,13 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
 // Everything that can be checked without touching the HIP runtime.
 int validate(const void *q, const void *k, const void *v, const void *g, const void *out, int B,
              int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
-             const float *s0, const float *s_final, int chunks_per_segment, Shape *shape) {
+             const float *s0, const float *s_final, int chunks_per_segment, int path,
+             Shape *shape) {
   if (!q || !k || !v || !g || !out)
     return fail(GTR_ERR_INVALID_ARG, "null tensor pointer (q=%p k=%p v=%p log_gate=%p out=%p)", q, k,
                 v, g, out);
   int rc = validate_shape(B, H, grid_h, grid_w, d_k, d_v, direction, dtype, chunks_per_segment,
-                          shape);
+                          path, shape);
   if (rc != GTR_OK) return rc;
   const void *ptrs[7] = {q, k, v, g, out, s0, s_final};
   const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
@@ -142,18 +152,22 @@ int check_device_range(const void *p, size_t bytes, int device, const char *name
 }
 
 struct Workspace {
-  void *ptr = nullptr;
-  size_t bytes = 0;
+  void *data = nullptr;  // float32 aggregates and boundary states
+  size_t data_bytes = 0;
+  int *sync = nullptr;   // fused-path control words and flags, zero-initialised
+  size_t sync_words = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(int device, hipStream_t stream, size_t bytes, void **out) {
+int get_workspace(int device, hipStream_t stream, size_t bytes, size_t words, void **data,
+                  int **sync) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace &ws = g_ws[{device, stream}];
-  if (ws.bytes >= bytes) {
-    *out = ws.ptr;
+  if (ws.data_bytes >= bytes && ws.sync_words >= words) {
+    *data = ws.data;
+    *sync = ws.sync;
     return GTR_OK;
   }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -163,24 +177,44 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, void **out) {
   }
   if (cs != hipStreamCaptureStatusNone)
     return fail(GTR_ERR_CAPTURE,
-                "workspace must grow from %zu to %zu bytes while the stream is being captured; "
-                "make one call of this shape before capturing",
-                ws.bytes, bytes);
-  if (ws.ptr) {
-    // Kernels queued earlier on this stream may still read the old buffer.
-    if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
-    (void)hipFree(ws.ptr);
-    ws.ptr = nullptr;
-    ws.bytes = 0;
+                "workspace must grow (%zu -> %zu bytes, %zu -> %zu sync words) while the stream "
+                "is being captured; make one call of this shape before capturing",
+                ws.data_bytes, bytes, ws.sync_words, words);
+  // Kernels queued earlier on this stream may still use the old buffers.
+  if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
+  if (ws.data_bytes < bytes) {
+    if (ws.data) (void)hipFree(ws.data);
+    ws.data = nullptr;
+    ws.data_bytes = 0;
+    const size_t want = bytes + bytes / 4;  // headroom for slightly larger calls
+    if (hipMalloc(&ws.data, want) != hipSuccess) {
+      (void)hipGetLastError();
+      ws.data = nullptr;
+      return fail(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", want);
+    }
+    ws.data_bytes = want;
   }
-  size_t want = bytes + bytes / 4;  // some headroom for slightly larger calls
-  if (hipMalloc(&ws.ptr, want) != hipSuccess) {
-    (void)hipGetLastError();
-    ws.ptr = nullptr;
-    return fail(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", want);
+  if (ws.sync_words < words) {
+    if (ws.sync) (void)hipFree(ws.sync);
+    ws.sync = nullptr;
+    ws.sync_words = 0;
+    const size_t want = words + words / 4;
+    if (hipMalloc(&ws.sync, want * sizeof(int)) != hipSuccess) {
+      (void)hipGetLastError();
+      ws.sync = nullptr;
+      return fail(GTR_ERR_ALLOC, "hipMalloc of %zu sync words failed", want);
+    }
+    // synchronous clear, so that kernels on any stream see zeros
+    if (hipMemset(ws.sync, 0, want * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(ws.sync);
+      ws.sync = nullptr;
+      return fail(GTR_ERR_ALLOC, "clearing %zu sync words failed", want);
+    }
+    ws.sync_words = want;
   }
-  ws.bytes = want;
-  *out = ws.ptr;
+  *data = ws.data;
+  *sync = ws.sync;
   return GTR_OK;
 }
 
@@ -203,11 +237,11 @@ namespace {
 // All host-side checks of one call, including the device-pointer queries.
 int check_call(const void *q, const void *k, const void *v, const void *log_gate, void *out, int B,
                int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
-               const float *s0, float *s_final, int chunks_per_segment, Shape *sh, int *device,
-               hipStream_t stream, bool check_stream) {
+               const float *s0, float *s_final, int chunks_per_segment, int path, Shape *sh,
+               int *device, hipStream_t stream, bool check_stream) {
   g_last_error.clear();
   int rc = validate(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
-                    s_final, chunks_per_segment, sh);
+                    s_final, chunks_per_segment, path, sh);
   if (rc != GTR_OK) return rc;
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess || n_dev <= 0) {
@@ -250,21 +284,21 @@ extern "C" {
 
 int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_gate, void *out,
                   int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
-                  const float *s0, float *s_final, int chunks_per_segment) {
+                  const float *s0, float *s_final, int chunks_per_segment, int path) {
   Shape sh;
   int device = 0;
   return check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
-                    s_final, chunks_per_segment, &sh, &device, nullptr, false);
+                    s_final, chunks_per_segment, path, &sh, &device, nullptr, false);
 }
 
 int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_gate, void *out,
                    int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
-                   int dtype, const float *s0, float *s_final, int chunks_per_segment,
+                   int dtype, const float *s0, float *s_final, int chunks_per_segment, int path,
                    hipStream_t stream) {
   Shape sh;
   int device = 0;
   int rc = check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
-                      s_final, chunks_per_segment, &sh, &device, stream, true);
+                      s_final, chunks_per_segment, path, &sh, &device, stream, true);
   if (rc != GTR_OK) return rc;
 
   gtr::LaunchArgs a{};
@@ -285,16 +319,23 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   a.s0 = s0;
   a.s_final = s_final;
   a.stream = stream;
-  const bool need_ws = sh.n_seg > 1 || s0 || s_final;
+  // A single fused segment needs no state passing: the fused kernel covers it
+  // with an empty wait list; the split path needs its scan only for n_seg > 1 or a state.
+  a.fused = sh.fused;
+  const bool need_ws = sh.fused || sh.n_seg > 1 || s0 || s_final;
   if (need_ws) {
     void *ws = nullptr;
-    rc = get_workspace(device, stream, gtr::workspace_floats(sh.bh, sh.n_seg) * sizeof(float), &ws);
+    int *sync = nullptr;
+    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.bh, sh.n_seg),
+                       sh.fused ? gtr::sync_words(sh.bh, sh.n_seg) : 0, &ws, &sync);
     if (rc != GTR_OK) return rc;
     float *f = static_cast<float *>(ws);
     const size_t st = (size_t)sh.bh * sh.n_seg * gtr::kStateElems;
     a.agg = f;
     a.prev = f + st;
-    a.agg_log2 = f + 2 * st;
+    a.agg_dec = f + 2 * st;
+    a.ctl = sync;
+    a.flags = sync ? sync + gtr::kCtlWords : nullptr;
   }
   const int err = gtr::launch_gla(a);
   if (err != (int)hipSuccess)
@@ -306,7 +347,7 @@ int gtr_gla_fwd(const void *q, const void *k, const void *v, const void *log_gat
                 int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
                 hipStream_t stream) {
   return gtr_gla_fwd_ex(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype,
-                        nullptr, nullptr, 0, stream);
+                        nullptr, nullptr, 0, GTR_PATH_AUTO, stream);
 }
 
 int gtr_gla_fwd_f32(const void *q, const void *k, const void *v, const void *log_gate, void *out,
@@ -331,17 +372,25 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
 }
 
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dtype,
-                               int chunks_per_segment) {
+                               int chunks_per_segment, int path) {
   Shape sh;
-  if (validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, dtype, chunks_per_segment, &sh) != GTR_OK)
+  if (validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, dtype, chunks_per_segment, path, &sh) !=
+      GTR_OK)
     return 0;
-  return gtr::workspace_floats(sh.bh, sh.n_seg) * sizeof(float);
+  return gtr::workspace_bytes(sh.bh, sh.n_seg) +
+         (sh.fused ? gtr::sync_words(sh.bh, sh.n_seg) * sizeof(int) : 0);
 }
 
-int gtr_gla_auto_chunks_per_segment(int B, int H, int grid_h, int grid_w) {
-  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0) return fail(GTR_ERR_INVALID_ARG, "bad shape");
-  const long long n_tok = (long long)grid_h * grid_w;
-  return auto_seg_len((long long)B * H, (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk));
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int chunks_per_segment, int path,
+                 int *seg_len, int *n_seg, int *fused) {
+  Shape sh;
+  const int rc = validate_shape(B, H, grid_h, grid_w, gtr::kHead, gtr::kHead, 0, GTR_DTYPE_F16,
+                                chunks_per_segment, path, &sh);
+  if (rc != GTR_OK) return rc;
+  if (seg_len) *seg_len = sh.seg_len;
+  if (n_seg) *n_seg = sh.n_seg;
+  if (fused) *fused = sh.fused ? 1 : 0;
+  return GTR_OK;
 }
 
 const char *gtr_gla_last_error(void) { return g_last_error.c_str(); }
@@ -351,13 +400,12 @@ int gtr_gla_version(void) { return kVersion; }
 void gtr_gla_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   for (auto &kv : g_ws) {
-    if (kv.second.ptr) {
-      int cur = 0;
-      if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
-        (void)hipDeviceSynchronize();
-        (void)hipFree(kv.second.ptr);
-        (void)hipSetDevice(cur);
-      }
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      if (kv.second.data) (void)hipFree(kv.second.data);
+      if (kv.second.sync) (void)hipFree(kv.second.sync);
+      (void)hipSetDevice(cur);
     }
   }
   g_ws.clear();

@@ -24,17 +24,26 @@ struct LaunchArgs {
   int n_seg;         // ceil(n_chunk / seg_len)
   // workspace (float32), all in the register-order state layout
   float *agg;        // [bh][n_seg][4096] segment state contributions
-  float *agg_log2;   // [bh][n_seg][64]   segment log2 decay per key dim
+  float *agg_dec;   // [bh][n_seg][64]   segment decay factor per key dim
   float *prev;       // [bh][n_seg][4096] state entering each segment
+  int *flags;        // [bh][n_seg] fused path: aggregate-published flags (zeroed at allocation)
+  int *ctl;          // fused path: ticket, done, epoch, error words (zeroed at allocation)
   const float *s0;   // user initial state, row-major [bh][64][64], nullable
   float *s_final;    // user final state, row-major [bh][64][64], nullable
+  bool fused;        // one launch (gla_fused) instead of three
   hipStream_t stream;
 };
 
-// Workspace floats needed for (bh, n_seg).
-inline size_t workspace_floats(size_t bh, size_t n_seg) {
-  return bh * n_seg * (2 * (size_t)kStateElems + kHead);
+constexpr int kCtlWords = 64;  // control block (only the first 4 words are used)
+
+// Float workspace bytes for (bh, n_seg): agg, prev and agg_dec.
+inline size_t workspace_bytes(size_t bh, size_t n_seg) {
+  return bh * n_seg * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
+// Synchronisation words for the fused path: control block + one flag per segment.
+// They live in their own zero-initialised allocation and only ever hold epoch
+// numbers, so a flag can never be confused with left-over data.
+inline size_t sync_words(size_t bh, size_t n_seg) { return kCtlWords + bh * n_seg; }
 
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);

@@ -7,27 +7,32 @@
 // per-chunk state contributions, a pass over chunk-boundary states, per-chunk
 // outputs).  With E = log2(e) * (inclusive cumulative log-gate from the chunk
 // start) and S_prev the state entering the chunk:
-//   o_tau  = (q_tau * 2^E_tau) S_prev + sum_{sigma<=tau} (sum_i q_tau,i k_sigma,i 2^(E_tau,i - E_sigma,i)) v_sigma
-//   S_next = diag(2^E_last) S_prev + (k * 2^(E_last - E))^T V
+//   o_tau  = (q_tau 2^E_tau) S_prev + sum_{sigma<=tau} (sum_i q_tau,i k_sigma,i 2^(E_tau,i - E_sigma,i)) v_sigma
+//   S_next = diag(2^E_last) S_prev + (k 2^(E_last - E))^T V
 //
-// Work split.  A "segment" is `seg_len` consecutive chunks of one sequence.
-//   gla_seg_state : one workgroup per segment walks its chunks and sums their
-//                   state contributions (the segment's own aggregate).
-//   gla_seg_scan  : one thread per (sequence, state element) runs the
-//                   boundary recurrence over segments -> state entering each.
-//   gla_seg_out   : one workgroup per segment starts from that state, walks
-//                   its chunks, writes outputs and carries the state in MFMA
-//                   accumulator registers from chunk to chunk.
+// Work split.  A "segment" is `seg_len` consecutive chunks of one sequence; one
+// workgroup owns a segment and walks its chunks with the state held in MFMA
+// accumulator registers.  The state entering a segment comes either from
+//   * gla_seg_state + gla_seg_scan (separate launches: segment aggregates, then
+//     one thread per state element runs the boundary recurrence over segments),
+//     followed by gla_seg_out; or
+//   * gla_fused (one launch): each workgroup first forms its segment's
+//     aggregate and publishes it, then combines the aggregates of the segments
+//     before it in scan order (waiting on per-segment flags), then writes its
+//     outputs.  Workgroups take segments in the order they start (an atomic
+//     ticket), so every segment a workgroup waits for belongs to a workgroup
+//     that is already running.
 //
-// Inside a chunk (256 threads = 4 waves, 16-token sub-blocks = MFMA tiles):
-//   * the four input tiles are read once from HBM, rows addressed through the
-//     scan-direction map (no permuted copy);
-//   * the gate is prefix-summed in LDS;
+// Inside a chunk (256 threads = 4 waves; wave w owns tokens [16w, 16w+16), a
+// 16-token sub-block; lane l owns dims [4(l%16), +4) of tokens 16w+4(l/16)+r):
+//   * inputs are read once from HBM, rows addressed through the scan-direction
+//     map (no permuted copy);
+//   * the gate prefix runs in registers plus one cross-lane scan per wave;
 //   * every exponential factor that reaches an MFMA operand is <= 1, except on
 //     the four diagonal 16x16 score tiles, which are referenced at the
 //     sub-block midpoint (factors <= 2^8); when a sub-block's gate range is too
-//     wide for that, the tile is formed exactly in fp32 on the VALU instead;
-//   * scores are transposed tiles P^T = K Q^T written to LDS only;
+//     wide for that, the tile is formed exactly in fp32 on the VALU;
+//   * scores are transposed tiles P^T = K Q^T held in LDS only;
 //   * wave w owns value columns [16w, 16w+16): it forms O^T = V^T P^T +
 //     S^T (q 2^E)^T for those columns and carries S[:, 16w:16w+16].
 //
@@ -36,8 +41,12 @@
 // 16x16 fp32 result holds column l%16, rows 4*(l/16)+r.  Operands here use the
 // logical k of slot (g = l/16, e) = (e < 4 ? 4g+e : 16+4g+e-4) inside each
 // 32-wide k block, so a result tile pair feeds straight back in as an operand.
-// The fp32 path issues eight v_mfma_f32_16x16x4_f32 over the same fragments.
+// Transposed 16-bit operands are read with ds_read_b64_tr_b16: inside each
+// 16-lane group, lane 4a+b receives element b of the 8-byte rows that lanes
+// a, a+4, a+8, a+12 address.  The fp32 path issues eight
+// v_mfma_f32_16x16x4_f32 over the same fragments.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,7 +58,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdE = 68;  // padded row length of the fp32 cumulative-gate tile
+constexpr int kSpinLimit = 1 << 22;  // ~seconds of polling before a wait gives up
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -57,6 +66,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s4 lds_s4;
+typedef __attribute__((address_space(3))) _Float16 lds_h;
 
 // LDS-only barrier: waits for this wave's LDS traffic, not for its global loads,
 // so prefetched global loads stay in flight across it.
@@ -65,44 +78,39 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ f4 exp2v(f4 x) {
+  return f4{fast_exp2(x.x), fast_exp2(x.y), fast_exp2(x.z), fast_exp2(x.w)};
+}
 
 // ---------------------------------------------------------------- element I/O
+// Each thread moves 4 consecutive elements of a token row per access.
 struct IoF32 {
   using T = float;
-  static constexpr int V = 4;  // elements per 16-byte access
-  __device__ static void cvt(u4 r, float *x) {
-    x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
-    x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
-  }
+  using Raw = u4;  // 16 bytes
+  __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
   __device__ static float load1(const T *p) { return *p; }
   __device__ static void store4(T *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
 };
 
 struct IoF16 {
   using T = _Float16;
-  static constexpr int V = 8;
-  __device__ static void cvt(u4 r, float *x) {
-    h8 h = __builtin_bit_cast(h8, r);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
-  }
+  using Raw = u2;  // 8 bytes
+  __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
+  __device__ static f4 to_f4(Raw r) { return __builtin_convertvector(to_h4(r), f4); }
   __device__ static float load1(const T *p) { return (float)*p; }
   __device__ static void store4(T *p, f4 v) {
-    h4 h = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-    *reinterpret_cast<h4 *>(p) = h;
+    *reinterpret_cast<h4 *>(p) = __builtin_convertvector(v, h4);
   }
 };
 
 struct IoBF16 {
   using T = uint16_t;  // raw bfloat16 bits
-  static constexpr int V = 8;
-  __device__ static void cvt(u4 r, float *x) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      x[2 * w] = __uint_as_float(r[w] << 16);
-      x[2 * w + 1] = __uint_as_float(r[w] & 0xffff0000u);
-    }
+  using Raw = u2;
+  __device__ static f4 to_f4(Raw r) {
+    return f4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+              __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
   }
+  __device__ static h4 to_h4(Raw r) { return __builtin_convertvector(to_f4(r), h4); }
   __device__ static float load1(const T *p) { return __uint_as_float((uint32_t)*p << 16); }
   __device__ static uint32_t rne(float f) {  // round to nearest even, quiet NaN kept
     uint32_t u = __float_as_uint(f);
@@ -116,539 +124,716 @@ struct IoBF16 {
 };
 
 // ------------------------------------------------------------ MFMA operands
-template <typename Op> struct Frag;
-template <> struct Frag<_Float16> { h8 v; };
-template <> struct Frag<float> { f8 v; };
+template <typename Op> struct OpT;
+// LD: row stride (elements) of tiles read as row fragments (16 consecutive rows
+// at 136 B spread one 8-byte read per lane over all 32 banks); LDT: of tiles
+// read transposed (4 rows x 4 column groups at 160 B per row hit distinct banks).
+// kDiagMin: smallest gate product over a 16-token sub-block (per key dim) that
+// midpoint scaling handles (2^-16 keeps every scaled fp16 operand within 2^+-8).
+template <> struct OpT<_Float16> {
+  using V4 = h4;
+  using V8 = h8;
+  static constexpr int LD = 68;
+  static constexpr int LDT = 80;
+  static constexpr float kDiagMin = 1.52587890625e-05f;  // 2^-16
+};
+template <> struct OpT<float> {
+  using V4 = f4;
+  using V8 = f8;
+  static constexpr int LD = 68;
+  static constexpr int LDT = 68;
+  static constexpr float kDiagMin = 7.888609052210118e-31f;  // 2^-100
+};
 
-__device__ __forceinline__ f4 mma(const Frag<_Float16> &a, const Frag<_Float16> &b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
+template <typename Op> using op4 = typename OpT<Op>::V4;
+template <typename Op> using op8 = typename OpT<Op>::V8;
+
+__device__ __forceinline__ f4 mma(const h8 &a, const h8 &b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f4 mma(const Frag<float> &a, const Frag<float> &b, f4 c) {
+__device__ __forceinline__ f4 mma(const f8 &a, const f8 &b, f4 c) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
   return c;
 }
 
-template <typename Op> struct OpTraits;
-template <> struct OpTraits<_Float16> {
-  static constexpr int LD = 72;          // padded LDS row (elements): 144 B
-  static constexpr float kDiagRange = 16.f;  // widest log2 gate range of a 16-token
-                                             // sub-block handled by midpoint scaling
-};
-template <> struct OpTraits<float> {
-  static constexpr int LD = 68;          // 272 B
-  static constexpr float kDiagRange = 100.f;
-};
-
-// Fragment rows from a row-major LDS tile: elements [k0, k0+4) and [k0+16, k0+20).
-__device__ __forceinline__ Frag<_Float16> ld_frag(const _Float16 *row_k0) {
-  h4 lo = *reinterpret_cast<const h4 *>(row_k0);
-  h4 hi = *reinterpret_cast<const h4 *>(row_k0 + 16);
-  Frag<_Float16> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-__device__ __forceinline__ Frag<float> ld_frag(const float *row_k0) {
-  f4 lo = *reinterpret_cast<const f4 *>(row_k0);
-  f4 hi = *reinterpret_cast<const f4 *>(row_k0 + 16);
-  Frag<float> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-// Per-k factors (fp32 vector in LDS) for the same slots.
-__device__ __forceinline__ f8 ld_factors(const float *vec_k0) {
-  f4 lo = *reinterpret_cast<const f4 *>(vec_k0);
-  f4 hi = *reinterpret_cast<const f4 *>(vec_k0 + 16);
+__device__ __forceinline__ h8 cat(const h4 &lo, const h4 &hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ void scale(Frag<_Float16> &f, f8 s) {
-  h8 hs = __builtin_convertvector(s, h8);
-  f.v = f.v * hs;
+__device__ __forceinline__ f8 cat(const f4 &lo, const f4 &hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ void scale(Frag<float> &f, f8 s) { f.v = f.v * s; }
 
-__device__ __forceinline__ void to_op(const f4 &lo, const f4 &hi, Frag<_Float16> &f) {
-  f8 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  f.v = __builtin_convertvector(x, h8);
+// Row fragment: elements [k0, k0+4) and [k0+16, k0+20) of one LDS row.
+template <typename Op> __device__ __forceinline__ op8<Op> frag_row(const Op *row_k0) {
+  return cat(*reinterpret_cast<const op4<Op> *>(row_k0),
+             *reinterpret_cast<const op4<Op> *>(row_k0 + 16));
 }
-__device__ __forceinline__ void to_op(const f4 &lo, const f4 &hi, Frag<float> &f) {
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+
+// Transposed fragment of a row-major [token][dim] LDS tile: lane l gets
+// tile[r0 + 4(l/16) + e][c0 + l%16] for e = 0..3 and tile[r0 + 16 + 4(l/16) + e][...].
+__device__ __forceinline__ h4 tr4(const _Float16 *tile, int row, int col) {
+  lds_h *base = (lds_h *)(tile);
+  lds_s4 *ptr = (lds_s4 *)(base + row * OpT<_Float16>::LDT + col);
+  return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ptr));
+}
+__device__ __forceinline__ h8 frag_tr(const _Float16 *tile, int r0, int c0, int lane) {
+  const int src = lane & 15, g = lane >> 4;
+  const int row = r0 + 4 * g + (src >> 2), col = c0 + 4 * (src & 3);
+  return cat(tr4(tile, row, col), tr4(tile, row + 16, col));
+}
+__device__ __forceinline__ f8 frag_tr(const float *tile, int r0, int c0, int lane) {
+  constexpr int LD = OpT<float>::LDT;
+  const int g = lane >> 4, col = c0 + (lane & 15);
+  f8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = tile[(r0 + 4 * g + e) * LD + col];
+    f[4 + e] = tile[(r0 + 16 + 4 * g + e) * LD + col];
+  }
+  return f;
+}
+
+template <typename Op, class Io> struct ToOp;
+template <> struct ToOp<_Float16, IoF16> {
+  __device__ static h4 cvt(u2 r) { return IoF16::to_h4(r); }
+};
+template <> struct ToOp<_Float16, IoBF16> {
+  __device__ static h4 cvt(u2 r) { return IoBF16::to_h4(r); }
+};
+template <> struct ToOp<float, IoF32> {
+  __device__ static f4 cvt(u4 r) { return IoF32::to_f4(r); }
+};
+
+__device__ __forceinline__ void cvt4(f4 x, h4 &y) { y = __builtin_convertvector(x, h4); }
+__device__ __forceinline__ void cvt4(f4 x, f4 &y) { y = x; }
+template <typename Op> __device__ __forceinline__ op4<Op> to4(f4 x) {
+  op4<Op> y;
+  cvt4(x, y);
+  return y;
 }
 
 // score-tile slots: (query sub-block a, key sub-block b), b <= a, slot = a(a+1)/2 + b
 __device__ __forceinline__ int tile_a(int s) { return s >= 6 ? 3 : (s >= 3 ? 2 : (s >= 1 ? 1 : 0)); }
 __device__ __forceinline__ int tile_slot(int a, int b) { return (a * (a + 1)) / 2 + b; }
 
-// per-dim vectors (64 floats each) of one chunk, in LDS
-enum : int {
-  kR0 = 0, kR1, kR2, kR3,   // E at the end of sub-block 0..3 (kR3 = E_last)
-  kDec,                     // 2^E_last: decay of the state across the chunk
-  kH0, kH1, kH2, kH3,       // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
-  kP2R1, kP2R2, kP2R3,      // 2^E_end(a-1): query factor from sub-block start to chunk start
-  kP2L0, kP2L1, kP2L2,      // 2^(E_last - E_end(b)): key factor from sub-block end to chunk end
-  kC20, kC30, kC31,         // 2^(E_end(a-1) - E_end(b)), b < a-1: between-sub-block factor
-  kNumVec
-};
-
 // ----------------------------------------------------------- scan direction
-// Grid index of scan position t (see gtr_gla.h for the four orders).
-__device__ __forceinline__ int grid_index(int t, int n_tok, int gh, int gw, int dir) {
+// Grid index of scan position t (see gtr_gla.h for the four orders).  The
+// column-major orders divide by grid_h with a float reciprocal and one exact
+// correction step (t < 2^23, so float(t) is exact and the estimate is off by
+// at most one).
+__device__ __forceinline__ int grid_index(int t, int n_tok, int gh, int gw, int dir, float rcp_gh) {
   if (dir & 1) t = n_tok - 1 - t;
   if (dir & 2) {
-    int col = t / gh;
+    int col = (int)((float)t * rcp_gh);
     int row = t - col * gh;
+    if (row < 0) {
+      --col;
+      row += gh;
+    } else if (row >= gh) {
+      ++col;
+      row -= gh;
+    }
     return row * gw + col;
   }
   (void)gw;
   return t;
 }
 
+// One sequence: element offsets inside it fit in 32 bits (n_tok <= 2^23 is
+// checked on the host), so loads use a uniform 64-bit base plus a 32-bit offset.
 struct Seq {
   int n_tok, gh, gw, dir;
+  float rcp_gh;
   size_t base;  // element offset of this sequence: bh * n_tok * 64
-  __device__ size_t row(int t) const {
-    return base + (size_t)grid_index(t, n_tok, gh, gw, dir) * kHead;
+  __device__ uint32_t row(int t) const {
+    return (uint32_t)grid_index(t, n_tok, gh, gw, dir, rcp_gh) * kHead;
   }
+  template <typename T> __device__ const T *in(const void *p) const {
+    return static_cast<const T *>(p) + base;
+  }
+  template <typename T> __device__ T *out(void *p) const { return static_cast<T *>(p) + base; }
 };
 
 // -------------------------------------------------------------- shared memory
-template <typename Op, bool kOut> struct Smem;
-
-template <typename Op> struct Smem<Op, true> {
-  static constexpr int LD = OpTraits<Op>::LD;
-  Op qs[kChunk * LD];   // q * 2^(E - E_end(a-1))      row-major [token][dim]
-  Op qh[kChunk * LD];   // q * 2^E                      row-major
-  Op ks[kChunk * LD];   // k * 2^(E_end(b) - E)         row-major
-  Op kbt[kChunk * LD];  // k * 2^(E_last - E)           transposed [dim][token]
-  Op vt[kChunk * LD];   // v                            transposed [dim][token]
-  float e[kChunk * kLdE];
+// Gate factors below are products of alpha = exp(log_gate) over token ranges of
+// the chunk; with E the log2 cumulative gate from the chunk start they equal
+// the exponentials named in the comments.
+template <typename Op> struct Smem {
+  static constexpr int LD = OpT<Op>::LD;
+  static constexpr int LDT = OpT<Op>::LDT;
+  Op qs[kChunk * LD];   // q 2^(E - E_end(a-1))     [token][dim]
+  Op qh[kChunk * LD];   // q 2^E
+  Op ks[kChunk * LD];   // k 2^(E_end(b) - E)
+  Op kb[kChunk * LDT];  // k 2^(E_last - E)
+  Op vv[kChunk * LDT];  // v
   Op pt[10 * 256];      // score tiles P^T, 4 values per lane, lane-ordered
-  float vec[kNumVec * kHead];
-  float tot[4 * kHead];
-};
-
-template <typename Op> struct Smem<Op, false> {
-  static constexpr int LD = OpTraits<Op>::LD;
-  Op kbt[kChunk * LD];
-  Op vt[kChunk * LD];
-  float e[kChunk * kLdE];
-  float vec[kNumVec * kHead];
-  float tot[4 * kHead];
+  float tot[4 * kHead]; // gate product of each 16-token sub-block
+  Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
+  Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
+  float dec[kHead];     // 2^E_last: decay of the state across the chunk
 };
 
 // ------------------------------------------------------------------- params
 struct Params {
   const void *q, *k, *v, *g;
   void *out;
-  int n_tok, gh, gw, dir;
+  int bh_count, n_tok, gh, gw, dir;
+  float rcp_gh;
   int n_chunk, seg_len, n_seg, n_seg_grid;
-  float *agg, *agg_log2;
-  const float *prev;
+  float *agg, *agg_dec;    // [bh][n_seg][4096] state contribution, [bh][n_seg][64] decay per key dim
+  const float *prev;       // [bh][n_seg][4096] register order (separate-launch path)
+  const float *s0;         // user initial state, row-major [bh][64][64], nullable
+  float *s_final;          // user final state, row-major, nullable
+  int *flags;              // [bh][n_seg] fused path: segment aggregate published
+  int *ctl;                // fused path: [0] ticket, [1] done, [2] epoch, [3] error
 };
 
-template <class Io> struct Layout {
-  static constexpr int V = Io::V;
-  static constexpr int TPR = kHead / V;         // threads per token row
-  static constexpr int RPP = kThreads / TPR;    // rows per pass
-  static constexpr int NP = kChunk / RPP;       // passes per chunk
-};
+enum : int { kCtlTicket = 0, kCtlDone = 1, kCtlEpoch = 2, kCtlError = 3 };
 
-template <class Io, bool kQ>
-__device__ __forceinline__ void load_chunk(const Params &p, const Seq &sq, int c, int tid,
-                                           u4 *rq, u4 *rk, u4 *rv, u4 *rg) {
-  using L = Layout<Io>;
-  using T = typename Io::T;
-  const int col0 = (tid % L::TPR) * L::V;
-#pragma unroll
-  for (int pp = 0; pp < L::NP; ++pp) {
-    const int tau = pp * L::RPP + tid / L::TPR;
-    const int t = c * kChunk + tau;
-    if (t < p.n_tok) {
-      const size_t off = sq.row(t) + col0;
-      if constexpr (kQ) rq[pp] = *reinterpret_cast<const u4 *>(static_cast<const T *>(p.q) + off);
-      rk[pp] = *reinterpret_cast<const u4 *>(static_cast<const T *>(p.k) + off);
-      rv[pp] = *reinterpret_cast<const u4 *>(static_cast<const T *>(p.v) + off);
-      rg[pp] = *reinterpret_cast<const u4 *>(static_cast<const T *>(p.g) + off);
-    } else {  // tail of the last chunk: no key, no value, no decay, no query
-      const u4 z = {0u, 0u, 0u, 0u};
-      if constexpr (kQ) rq[pp] = z;
-      rk[pp] = z;
-      rv[pp] = z;
-      rg[pp] = z;
-    }
-  }
-}
+// Register-order state layout: (wave w, lane l, reg x) holds element (i, j) with
+// i = 16(x/4) + 4(l/16) + x%4 and j = 16w + l%16, at offset w*1024 + x*64 + l.
+__device__ __forceinline__ int state_i(int x, int lane) { return 16 * (x >> 2) + 4 * (lane >> 4) + (x & 3); }
 
-// Cumulative log2-gate of the chunk into sm.e and the per-dim vectors into sm.vec.
-// Ends with the LDS barrier after which e and vec are readable by every wave.
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void gate_prefix(Smem<Op, kOut> &sm, const u4 *rg, int tid) {
-  using L = Layout<Io>;
-  const int col0 = (tid % L::TPR) * L::V;
-#pragma unroll
-  for (int pp = 0; pp < L::NP; ++pp) {
-    const int tau = pp * L::RPP + tid / L::TPR;
-    float x[L::V];
-    Io::cvt(rg[pp], x);
-#pragma unroll
-    for (int e = 0; e < L::V; e += 4) {
-      f4 w = {x[e] * kLog2e, x[e + 1] * kLog2e, x[e + 2] * kLog2e, x[e + 3] * kLog2e};
-      *reinterpret_cast<f4 *>(&sm.e[tau * kLdE + col0 + e]) = w;
-    }
-  }
-  lds_sync();
-  // wave p scans tokens [16p, 16p+16) of dim i = lane
-  const int lane = tid & 63, p = tid >> 6;
-  float loc[16];
-  float run = 0.f;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    run += sm.e[(16 * p + u) * kLdE + lane];
-    loc[u] = run;
-  }
-  sm.tot[p * kHead + lane] = run;
-  lds_sync();
-  const float R0 = sm.tot[lane];
-  const float R1 = R0 + sm.tot[kHead + lane];
-  const float R2 = R1 + sm.tot[2 * kHead + lane];
-  const float R3 = R2 + sm.tot[3 * kHead + lane];
-  const float off = p == 0 ? 0.f : (p == 1 ? R0 : (p == 2 ? R1 : R2));
-#pragma unroll
-  for (int u = 0; u < 16; ++u) sm.e[(16 * p + u) * kLdE + lane] = off + loc[u];
-  float *vec = sm.vec;
-  if (p == 0) {
-    vec[kR0 * kHead + lane] = R0;
-    vec[kR1 * kHead + lane] = R1;
-    vec[kR2 * kHead + lane] = R2;
-    vec[kR3 * kHead + lane] = R3;
-    vec[kDec * kHead + lane] = fast_exp2(R3);
-  } else if (p == 1) {
-    vec[kP2L0 * kHead + lane] = fast_exp2(R3 - R0);
-    vec[kP2L1 * kHead + lane] = fast_exp2(R3 - R1);
-    vec[kP2L2 * kHead + lane] = fast_exp2(R3 - R2);
-  } else if (kOut && p == 2) {
-    vec[kH0 * kHead + lane] = fast_exp2(-0.5f * R0);
-    vec[kH1 * kHead + lane] = fast_exp2(0.5f * (R0 - R1));
-    vec[kH2 * kHead + lane] = fast_exp2(0.5f * (R1 - R2));
-    vec[kH3 * kHead + lane] = fast_exp2(0.5f * (R2 - R3));
-  } else if (kOut && p == 3) {
-    vec[kP2R1 * kHead + lane] = fast_exp2(R0);
-    vec[kP2R2 * kHead + lane] = fast_exp2(R1);
-    vec[kP2R3 * kHead + lane] = fast_exp2(R2);
-    vec[kC20 * kHead + lane] = fast_exp2(R1 - R0);
-    vec[kC30 * kHead + lane] = fast_exp2(R2 - R0);
-    vec[kC31 * kHead + lane] = fast_exp2(R2 - R1);
-  }
-  lds_sync();
-}
-
-// Scaled operand tiles.  kOut: qs, qh, ks (row-major) and kbt, vt (transposed);
-// otherwise only kbt and vt.
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void prep(Smem<Op, kOut> &sm, const u4 *rq, const u4 *rk, const u4 *rv,
-                                     int tid) {
-  using L = Layout<Io>;
-  constexpr int LD = OpTraits<Op>::LD;
-  const int col0 = (tid % L::TPR) * L::V;
-#pragma unroll
-  for (int pp = 0; pp < L::NP; ++pp) {
-    const int tau = pp * L::RPP + tid / L::TPR;
-    const int a = tau >> 4;
-    float kx[L::V], vx[L::V], qx[L::V];
-    Io::cvt(rk[pp], kx);
-    Io::cvt(rv[pp], vx);
-    if constexpr (kOut) Io::cvt(rq[pp], qx);
-    float E[L::V];
-#pragma unroll
-    for (int e = 0; e < L::V; e += 4) {
-      f4 w = *reinterpret_cast<const f4 *>(&sm.e[tau * kLdE + col0 + e]);
-      E[e] = w.x; E[e + 1] = w.y; E[e + 2] = w.z; E[e + 3] = w.w;
-    }
-    if constexpr (kOut) {
-      const float *Rprev = a > 0 ? &sm.vec[(kR0 + a - 1) * kHead + col0] : nullptr;
-      const float *Ra = &sm.vec[(kR0 + a) * kHead + col0];
-      const float *P2R = a > 0 ? &sm.vec[(kP2R1 + a - 1) * kHead + col0] : nullptr;
-      const float *P2L = a < 3 ? &sm.vec[(kP2L0 + a) * kHead + col0] : nullptr;
-      Op qs[L::V], qh[L::V], ks[L::V];
-#pragma unroll
-      for (int e = 0; e < L::V; ++e) {
-        const float rp = Rprev ? Rprev[e] : 0.f;
-        const float qsv = qx[e] * fast_exp2(E[e] - rp);
-        const float qhv = P2R ? qsv * P2R[e] : qsv;
-        const float ksv = kx[e] * fast_exp2(Ra[e] - E[e]);
-        const float kbv = P2L ? ksv * P2L[e] : ksv;
-        qs[e] = (Op)qsv;
-        qh[e] = (Op)qhv;
-        ks[e] = (Op)ksv;
-        sm.kbt[(col0 + e) * LD + tau] = (Op)kbv;
-        sm.vt[(col0 + e) * LD + tau] = (Op)vx[e];
-      }
-#pragma unroll
-      for (int e = 0; e < L::V; ++e) {
-        sm.qs[tau * LD + col0 + e] = qs[e];
-        sm.qh[tau * LD + col0 + e] = qh[e];
-        sm.ks[tau * LD + col0 + e] = ks[e];
-      }
-    } else {
-      const float *El = &sm.vec[kR3 * kHead + col0];
-#pragma unroll
-      for (int e = 0; e < L::V; ++e) {
-        sm.kbt[(col0 + e) * LD + tau] = (Op)(kx[e] * fast_exp2(El[e] - E[e]));
-        sm.vt[(col0 + e) * LD + tau] = (Op)vx[e];
-      }
-    }
-  }
-  lds_sync();
-}
-
-// Exact fp32 diagonal score tile (a, a), used when the sub-block's gate range is
-// too wide for midpoint scaling.  Reads q and k rows again from global memory.
-template <class Io, typename Op>
-__device__ f4 exact_diag(const Params &p, const Seq &sq, const Smem<Op, true> &sm, int c, int a,
-                         int lane) {
-  using T = typename Io::T;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int tau = 16 * a + l16;
-  const int t_tau = c * kChunk + tau;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (t_tau >= p.n_tok) return acc;
-  const T *qrow = static_cast<const T *>(p.q) + sq.row(t_tau);
-  const T *krow[4];
-  bool ok[4];
+// Row offsets of this thread's 4 tokens of chunk c (valid = inside the sequence).
+__device__ __forceinline__ void chunk_rows(const Params &p, const Seq &sq, int c, int wave, int lane,
+                                           uint32_t *off, bool *ok) {
+  const int col = 4 * (lane & 15);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int sig = 16 * a + 4 * g + r;
-    ok[r] = sig <= tau;  // sig <= tau < n_tok, so the row exists
-    krow[r] = ok[r] ? static_cast<const T *>(p.k) + sq.row(c * kChunk + sig) : qrow;
+    const int t = c * kChunk + 16 * wave + 4 * (lane >> 4) + r;
+    ok[r] = t < p.n_tok;
+    off[r] = (ok[r] ? sq.row(t) : 0u) + col;
+  }
+}
+
+// One tensor's rows for those tokens (zeros past the end of the sequence: no
+// key, no value, no decay, no query there).
+template <class Io>
+__device__ __forceinline__ void load_rows(const void *tensor, const Seq &sq, const uint32_t *off,
+                                          const bool *ok, typename Io::Raw *dst) {
+  using T = typename Io::T;
+  using Raw = typename Io::Raw;
+  const T *base = sq.in<T>(tensor);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[r] = ok[r] ? *reinterpret_cast<const Raw *>(base + off[r]) : Raw{};
+}
+
+// First half of a chunk's operand preparation, local to each wave.  Gate
+// products of this thread's 4 tokens x 4 dims inside its wave's 16-token
+// sub-block scale the inputs: qs = q * (product of alpha from the sub-block
+// start through the token), ks = k * (product of alpha after the token to the
+// sub-block end).  qs, ks and v go to LDS, the sub-block product to sm.tot.
+// One exp2 per element; the rest are multiplications and a 4-way exchange
+// between the lane groups of the wave.
+template <class Io, typename Op, bool kOut>
+__device__ __forceinline__ void prep_local(Smem<Op> &sm, const typename Io::Raw *rq,
+                                           const typename Io::Raw *rk, const typename Io::Raw *rv,
+                                           const typename Io::Raw *rg, int wave, int lane,
+                                           op4<Op> *qs, op4<Op> *ks) {
+  constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
+  const int g = lane >> 4, dq = lane & 15;
+  const f4 one = {1.f, 1.f, 1.f, 1.f};
+  f4 a[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a[r] = exp2v(Io::to_f4(rg[r]) * kLog2e);
+  const f4 p1 = a[0] * a[1], p2 = p1 * a[2], p3 = p2 * a[3];  // prefix products in the group
+  const f4 s2 = a[3], s1 = a[2] * a[3], s0 = a[1] * s1;        // suffix products in the group
+  f4 t[4];  // products of the four 4-token groups of this sub-block
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t[m][d] = __shfl(p3[d], dq + 16 * m);
+  const f4 before = g == 0 ? one : (g == 1 ? t[0] : (g == 2 ? t[0] * t[1] : t[0] * t[1] * t[2]));
+  const f4 after = g == 3 ? one : (g == 2 ? t[3] : (g == 1 ? t[2] * t[3] : t[1] * t[2] * t[3]));
+  const f4 pq[4] = {a[0] * before, p1 * before, p2 * before, p3 * before};
+  const f4 pk[4] = {s0 * after, s1 * after, s2 * after, after};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tau = 16 * wave + 4 * g + r;
+    ks[r] = ToOp<Op, Io>::cvt(rk[r]) * to4<Op>(pk[r]);
+    *reinterpret_cast<op4<Op> *>(&sm.vv[tau * LDT + 4 * dq]) = ToOp<Op, Io>::cvt(rv[r]);
+    if constexpr (kOut) {
+      qs[r] = ToOp<Op, Io>::cvt(rq[r]) * to4<Op>(pq[r]);
+      *reinterpret_cast<op4<Op> *>(&sm.qs[tau * LD + 4 * dq]) = qs[r];
+      *reinterpret_cast<op4<Op> *>(&sm.ks[tau * LD + 4 * dq]) = ks[r];
+    }
+  }
+  if (g == 0) *reinterpret_cast<f4 *>(&sm.tot[wave * kHead + 4 * dq]) = t[0] * t[1] * t[2] * t[3];
+}
+
+// Sub-block products t_0..t_3 of this lane's dims.
+template <typename Op>
+__device__ __forceinline__ void sub_block_products(const Smem<Op> &sm, int lane, f4 *t) {
+  const int dq = lane & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) t[a] = *reinterpret_cast<const f4 *>(&sm.tot[a * kHead + 4 * dq]);
+}
+
+// Second half, after the sub-block products of all waves are visible:
+// kb = ks * (product from the sub-block end to the chunk end), qh = qs *
+// (product from the chunk start to the sub-block start), and the per-dim
+// factor vectors.
+template <class Io, typename Op, bool kOut>
+__device__ __forceinline__ void prep_chunk(Smem<Op> &sm, const op4<Op> *qs, const op4<Op> *ks,
+                                           int wave, int lane) {
+  constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
+  const int g = lane >> 4, dq = lane & 15;
+  const f4 one = {1.f, 1.f, 1.f, 1.f};
+  f4 t[4];
+  sub_block_products(sm, lane, t);
+  const f4 fk = wave == 0 ? t[1] * t[2] * t[3] : (wave == 1 ? t[2] * t[3] : (wave == 2 ? t[3] : one));
+  const op4<Op> fkh = to4<Op>(fk);
+  op4<Op> fqh = {};
+  if constexpr (kOut)
+    fqh = to4<Op>(wave == 0 ? one : (wave == 1 ? t[0] : (wave == 2 ? t[0] * t[1] : t[0] * t[1] * t[2])));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tau = 16 * wave + 4 * g + r;
+    *reinterpret_cast<op4<Op> *>(&sm.kb[tau * LDT + 4 * dq]) = ks[r] * fkh;
+    if constexpr (kOut) *reinterpret_cast<op4<Op> *>(&sm.qh[tau * LD + 4 * dq]) = qs[r] * fqh;
+  }
+  if (g == 0) {
+    if (wave == 0) {
+      *reinterpret_cast<f4 *>(&sm.dec[4 * dq]) = t[0] * t[1] * t[2] * t[3];
+    } else if (kOut && wave == 1) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {  // 2^(-T_a/2) = 1/sqrt(product over sub-block a)
+        const f4 h = {__builtin_amdgcn_rsqf(t[a].x), __builtin_amdgcn_rsqf(t[a].y),
+                      __builtin_amdgcn_rsqf(t[a].z), __builtin_amdgcn_rsqf(t[a].w)};
+        *reinterpret_cast<op4<Op> *>(&sm.hv[a * kHead + 4 * dq]) = to4<Op>(h);
+      }
+    } else if (kOut && wave == 2) {
+      *reinterpret_cast<op4<Op> *>(&sm.cv[0 * kHead + 4 * dq]) = to4<Op>(t[1]);
+      *reinterpret_cast<op4<Op> *>(&sm.cv[1 * kHead + 4 * dq]) = to4<Op>(t[1] * t[2]);
+      *reinterpret_cast<op4<Op> *>(&sm.cv[2 * kHead + 4 * dq]) = to4<Op>(t[2]);
+    }
+  }
+}
+
+// Exact fp32 diagonal score tile (a, a) for a sub-block whose gate range is too
+// wide for midpoint scaling.  Re-reads q, k and log_gate rows from global memory.
+template <class Io>
+__device__ f4 exact_diag(const Params &p, const Seq &sq, int c, int a, int lane) {
+  using T = typename Io::T;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int t0 = c * kChunk + 16 * a;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (t0 + l16 >= p.n_tok) return acc;  // query beyond the sequence
+  const T *gb = sq.in<T>(p.g);
+  const T *qrow = sq.in<T>(p.q) + sq.row(t0 + l16);
+  const T *krow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {  // keys 4g+r <= l16 < n_tok exist; later keys are masked
+    const int sl = 4 * g + r;
+    krow[r] = sq.in<T>(p.k) + sq.row(sl <= l16 ? t0 + sl : t0 + l16);
   }
   for (int i = 0; i < kHead; ++i) {
-    const float qi = Io::load1(qrow + i);
-    const float et = sm.e[tau * kLdE + i];
+    // log2 gate sums from the sub-block start at the query and at each key
+    float run = 0.f;
+    float e_sig[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u <= l16; ++u) {
+      run += Io::load1(gb + sq.row(t0 + u) + i) * kLog2e;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (ok[r]) {
-        const int sig = 16 * a + 4 * g + r;
-        acc[r] += qi * Io::load1(krow[r] + i) * fast_exp2(et - sm.e[sig * kLdE + i]);
-      }
+      for (int r = 0; r < 4; ++r)
+        if (u == 4 * g + r) e_sig[r] = run;
     }
+    const float qi = Io::load1(qrow + i);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r <= l16) acc[r] += qi * Io::load1(krow[r] + i) * fast_exp2(run - e_sig[r]);
   }
   return acc;
 }
 
 // Score tiles P^T[sigma][tau] of this chunk into sm.pt (lower block triangle only).
 template <class Io, typename Op>
-__device__ __forceinline__ void scores(const Params &p, const Seq &sq, Smem<Op, true> &sm, int c,
-                                       int tid) {
-  constexpr int LD = OpTraits<Op>::LD;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  for (int s = wave; s < 10; s += 4) {
+__device__ __forceinline__ void scores(const Params &p, const Seq &sq, Smem<Op> &sm, int c,
+                                       int wave, int lane) {
+  constexpr int LD = OpT<Op>::LD;
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int s = wave + 4 * u;
+    if (s >= 10) break;
     const int a = tile_a(s);
     const int b = s - (a * (a + 1)) / 2;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     if (a == b) {
-      const float rng = (a > 0 ? sm.vec[(kR0 + a - 1) * kHead + lane] : 0.f) -
-                        sm.vec[(kR0 + a) * kHead + lane];
-      const bool fast = __all(rng <= OpTraits<Op>::kDiagRange);
+      const bool fast = __all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
       if (fast) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int k0 = 32 * kb + 4 * g;
-          Frag<Op> A = ld_frag(&sm.ks[(16 * b + l16) * LD + k0]);
-          Frag<Op> B = ld_frag(&sm.qs[(16 * a + l16) * LD + k0]);
-          const f8 h = ld_factors(&sm.vec[(kH0 + a) * kHead + k0]);
-          scale(A, h);
-          scale(B, h);
-          acc = mma(A, B, acc);
+          const op8<Op> h = frag_row<Op>(&sm.hv[a * kHead + k0]);
+          acc = mma(frag_row<Op>(&sm.ks[(16 * b + l16) * LD + k0]) * h,
+                    frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]) * h, acc);
         }
       } else {
-        acc = exact_diag<Io, Op>(p, sq, sm, c, a, lane);
+        acc = exact_diag<Io>(p, sq, c, a, lane);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * g + r > l16) acc[r] = 0.f;  // keys after the query
     } else {
-      const int cvec = (a == 2) ? kC20 : (b == 0 ? kC30 : kC31);  // used when b < a-1
+      const int cvec = (a == 2) ? 0 : (b == 0 ? 1 : 2);  // used when b < a-1
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int k0 = 32 * kb + 4 * g;
-        Frag<Op> A = ld_frag(&sm.ks[(16 * b + l16) * LD + k0]);
-        Frag<Op> B = ld_frag(&sm.qs[(16 * a + l16) * LD + k0]);
-        if (b < a - 1) scale(B, ld_factors(&sm.vec[cvec * kHead + k0]));
-        acc = mma(A, B, acc);
+        op8<Op> B = frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]);
+        if (b < a - 1) B = B * frag_row<Op>(&sm.cv[cvec * kHead + k0]);
+        acc = mma(frag_row<Op>(&sm.ks[(16 * b + l16) * LD + k0]), B, acc);
       }
     }
-    Op *dst = &sm.pt[s * 256 + lane * 4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[r] = (Op)acc[r];
+    *reinterpret_cast<op4<Op> *>(&sm.pt[s * 256 + lane * 4]) = to4<Op>(acc);
   }
-  lds_sync();
 }
 
-// ------------------------------------------------------------------ kernels
-// kOut = false: segment aggregate (gla_seg_state).  kOut = true: outputs (gla_seg_out).
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void segment_body(const Params &p) {
-  using L = Layout<Io>;
+// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T, stored at the grid positions.
+template <class Io, typename Op>
+__device__ __forceinline__ void outputs(const Params &p, const Seq &sq, const Smem<Op> &sm, int c,
+                                        int wave, int lane, const f4 *S) {
   using T = typename Io::T;
-  constexpr int LD = OpTraits<Op>::LD;
-  __shared__ Smem<Op, kOut> sm;
+  constexpr int LD = OpT<Op>::LD;
+  const int g = lane >> 4, l16 = lane & 15;
+  op8<Op> vf[2], sf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
+    sf[kb] = cat(to4<Op>(S[2 * kb]), to4<Op>(S[2 * kb + 1]));
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb <= (tt >> 1); ++kb) {
+      const op4<Op> lo = *reinterpret_cast<const op4<Op> *>(&sm.pt[tile_slot(tt, 2 * kb) * 256 + lane * 4]);
+      op4<Op> hi = {};
+      if (2 * kb + 1 <= tt)
+        hi = *reinterpret_cast<const op4<Op> *>(&sm.pt[tile_slot(tt, 2 * kb + 1) * 256 + lane * 4]);
+      acc = mma(vf[kb], cat(lo, hi), acc);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      acc = mma(sf[kb], frag_row<Op>(&sm.qh[(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
+    const int t = c * kChunk + 16 * tt + l16;
+    if (t < p.n_tok) Io::store4(sq.out<T>(p.out) + sq.row(t) + 16 * wave + 4 * g, acc);
+  }
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int bh = blockIdx.x / p.n_seg_grid;
-  const int seg = blockIdx.x - bh * p.n_seg_grid;
-  Seq sq{p.n_tok, p.gh, p.gw, p.dir, (size_t)bh * p.n_tok * kHead};
-
-  // state columns [16*wave, 16*wave+16): S[it][r] = S[16it+4g+r][16*wave+l16]
-  f4 S[4];
-  const size_t st_off = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
+// S <- diag(2^E_last) S + (k 2^(E_last-E))^T V for this wave's value columns.
+template <typename Op>
+__device__ __forceinline__ void carry_state(const Smem<Op> &sm, int wave, int lane, f4 *S) {
+  const int g = lane >> 4;
+  op8<Op> vf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
+    S[it] *= *reinterpret_cast<const f4 *>(&sm.dec[16 * it + 4 * g]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[it][r] = (kOut && p.prev) ? p.prev[st_off + (it * 4 + r) * 64] : 0.f;
+    for (int kb = 0; kb < 2; ++kb) S[it] = mma(frag_tr(sm.kb, 32 * kb, 16 * it, lane), vf[kb], S[it]);
   }
-  float log2_decay = 0.f;  // wave 0, lane = key dim: sum of E_last over the segment
+}
 
-  const int c_begin = seg * p.seg_len;
-  const int c_end = min(c_begin + p.seg_len, p.n_chunk);
-  u4 rq[L::NP], rk[L::NP], rv[L::NP], rg[L::NP];
-  load_chunk<Io, kOut>(p, sq, c_begin, tid, rq, rk, rv, rg);
-
+// Walks chunks [c_begin, c_end) of one sequence, carrying S.  kOut: writes the
+// outputs (S must hold the state entering the first chunk); otherwise only
+// carries S (from zero: the segment's own aggregate) and multiplies the chunk
+// decays into seg_dec (wave 0, lane < 16 holds dims 4*lane..4*lane+3).
+template <class Io, typename Op, bool kOut>
+__device__ __forceinline__ void walk(const Params &p, const Seq &sq, Smem<Op> &sm, int c_begin,
+                                     int c_end, int wave, int lane, f4 *S, f4 &seg_dec) {
+  using Raw = typename Io::Raw;
+  Raw rq[4], rk[4], rv[4], rg[4];
+  uint32_t off[4];
+  bool ok[4];
+  chunk_rows(p, sq, c_begin, wave, lane, off, ok);
+  load_rows<Io>(p.g, sq, off, ok, rg);
+  load_rows<Io>(p.k, sq, off, ok, rk);
+  load_rows<Io>(p.v, sq, off, ok, rv);
+  if constexpr (kOut) load_rows<Io>(p.q, sq, off, ok, rq);
   for (int c = c_begin; c < c_end; ++c) {
-    u4 nq[L::NP], nk[L::NP], nv[L::NP], ng[L::NP];
+    // the next chunk's rows are in flight while this chunk is processed
+    Raw nq[4], nk[4], nv[4], ng[4];
     const bool more = c + 1 < c_end;
-    if (more) load_chunk<Io, kOut>(p, sq, c + 1, tid, nq, nk, nv, ng);
-
-    gate_prefix<Io, Op, kOut>(sm, rg, tid);
-    if (!kOut && wave == 0) log2_decay += sm.vec[kR3 * kHead + lane];
-    prep<Io, Op, kOut>(sm, rq, rk, rv, tid);
-
-    Frag<Op> vf[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) vf[kb] = ld_frag(&sm.vt[(16 * wave + l16) * LD + 32 * kb + 4 * g]);
-
+    if (more) {
+      chunk_rows(p, sq, c + 1, wave, lane, off, ok);
+      load_rows<Io>(p.g, sq, off, ok, ng);
+      load_rows<Io>(p.k, sq, off, ok, nk);
+      load_rows<Io>(p.v, sq, off, ok, nv);
+      if constexpr (kOut) load_rows<Io>(p.q, sq, off, ok, nq);
+    }
+    op4<Op> qs[4], ks[4];
+    prep_local<Io, Op, kOut>(sm, rq, rk, rv, rg, wave, lane, qs, ks);
+    lds_sync();  // sub-block products visible
+    prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane);
+    if (!kOut && wave == 0 && lane < 16) {
+      f4 t[4];
+      sub_block_products(sm, lane, t);
+      seg_dec *= t[0] * t[1] * t[2] * t[3];
+    }
+    lds_sync();  // operand tiles visible
     if constexpr (kOut) {
-      scores<Io, Op>(p, sq, sm, c, tid);
-      Frag<Op> sf[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) to_op(S[2 * kb], S[2 * kb + 1], sf[kb]);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb <= (tt >> 1); ++kb) {
-          f4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-          const Op *plo = &sm.pt[tile_slot(tt, 2 * kb) * 256 + lane * 4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) lo[r] = (float)plo[r];
-          if (2 * kb + 1 <= tt) {
-            const Op *phi = &sm.pt[tile_slot(tt, 2 * kb + 1) * 256 + lane * 4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) hi[r] = (float)phi[r];
-          }
-          Frag<Op> pf;
-          to_op(lo, hi, pf);
-          acc = mma(vf[kb], pf, acc);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          acc = mma(sf[kb], ld_frag(&sm.qh[(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
-        const int t = c * kChunk + 16 * tt + l16;
-        if (t < p.n_tok) Io::store4(static_cast<T *>(p.out) + sq.row(t) + 16 * wave + 4 * g, acc);
-      }
+      scores<Io, Op>(p, sq, sm, c, wave, lane);
+      lds_sync();  // score tiles visible
+      outputs<Io, Op>(p, sq, sm, c, wave, lane, S);
     }
-
-    // carry the state over the chunk: S <- diag(2^E_last) S + (k 2^(E_last-E))^T V
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const f4 dec = *reinterpret_cast<const f4 *>(&sm.vec[kDec * kHead + 16 * it + 4 * g]);
-      S[it] = S[it] * dec;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        S[it] = mma(ld_frag(&sm.kbt[(16 * it + l16) * LD + 32 * kb + 4 * g]), vf[kb], S[it]);
-    }
+    carry_state<Op>(sm, wave, lane, S);
 
     if (more) {
 #pragma unroll
-      for (int pp = 0; pp < L::NP; ++pp) {
-        if constexpr (kOut) rq[pp] = nq[pp];
-        rk[pp] = nk[pp];
-        rv[pp] = nv[pp];
-        rg[pp] = ng[pp];
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kOut) rq[r] = nq[r];
+        rk[r] = nk[r];
+        rv[r] = nv[r];
+        rg[r] = ng[r];
       }
     }
   }
+}
 
-  if constexpr (!kOut) {
+__device__ __forceinline__ void store_state_rowmajor(float *dst, int wave, int lane, const f4 *S) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+  for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead + 16 * wave + (lane & 15)] = S[x >> 2][x & 3];
+}
+__device__ __forceinline__ void load_state_rowmajor(const float *src, int wave, int lane, f4 *S) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p.agg[st_off + (it * 4 + r) * 64] = S[it][r];
-    if (wave == 0) p.agg_log2[((size_t)bh * p.n_seg + seg) * kHead + lane] = log2_decay;
+  for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = src[state_i(x, lane) * kHead + 16 * wave + (lane & 15)];
+}
+
+// ------------------------------------------------------------------ kernels
+template <class Io, typename Op>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_state(Params p) {
+  __shared__ Smem<Op> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x / p.n_seg_grid;
+  const int seg = blockIdx.x - bh * p.n_seg_grid;
+  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
+  f4 S[4] = {};
+  f4 sdec = {1.f, 1.f, 1.f, 1.f};
+  const int c0 = seg * p.seg_len;
+  walk<Io, Op, false>(p, sq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
+  const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) p.agg[st + x * 64] = S[x >> 2][x & 3];
+  if (wave == 0 && lane < 16)
+    *reinterpret_cast<f4 *>(&p.agg_dec[((size_t)bh * p.n_seg + seg) * kHead + 4 * lane]) = sdec;
+}
+
+template <class Io, typename Op>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_out(Params p) {
+  __shared__ Smem<Op> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x / p.n_seg;
+  const int seg = blockIdx.x - bh * p.n_seg;
+  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
+  f4 S[4] = {};
+  if (p.prev) {
+    const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = p.prev[st + x * 64];
   }
-}
-
-template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) void gla_seg_state(Params p) {
-  segment_body<Io, Op, false>(p);
-}
-
-template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) void gla_seg_out(Params p) {
-  segment_body<Io, Op, true>(p);
+  f4 unused = {};
+  const int c0 = seg * p.seg_len;
+  walk<Io, Op, true>(p, sq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
 }
 
 // Boundary-state recurrence over segments, one thread per (sequence, state
 // element): prev[seg] = state entering segment seg; prev[0] = s0 (or 0).
-__global__ __launch_bounds__(kThreads) void gla_seg_scan(const float *agg, const float *agg_log2,
+// Loads of a batch of segments are issued together; only the fused
+// multiply-adds are sequential.
+__global__ __launch_bounds__(kThreads) void gla_seg_scan(const float *agg, const float *agg_dec,
                                                          float *prev, const float *s0,
                                                          float *s_final, int bh_count, int n_seg) {
+  constexpr int kBatch = 16;
   const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
   const int bh = (int)(gid / kStateElems);
   const int e = (int)(gid - (long)bh * kStateElems);
   if (bh >= bh_count) return;
-  // register order -> (i, j): e = w*1024 + x*64 + l, i = 16(x/4) + 4(l/16) + x%4, j = 16w + l%16
   const int w = e >> 10, x = (e >> 6) & 15, l = e & 63;
-  const int i = 16 * (x >> 2) + 4 * (l >> 4) + (x & 3);
+  const int i = state_i(x, l);
   const int j = 16 * w + (l & 15);
   const size_t sbase = (size_t)bh * n_seg;
   float s = s0 ? s0[(size_t)bh * kStateElems + i * kHead + j] : 0.f;
   const int steps = s_final ? n_seg : n_seg - 1;
   prev[sbase * kStateElems + e] = s;
-  for (int seg = 0; seg < steps; ++seg) {
-    s = fast_exp2(agg_log2[(sbase + seg) * kHead + i]) * s + agg[(sbase + seg) * kStateElems + e];
-    if (seg + 1 < n_seg) prev[(sbase + seg + 1) * kStateElems + e] = s;
+  for (int b0 = 0; b0 < steps; b0 += kBatch) {
+    float av[kBatch], dv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int seg = min(b0 + u, steps - 1);
+      av[u] = agg[(sbase + seg) * kStateElems + e];
+      dv[u] = agg_dec[(sbase + seg) * kHead + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (b0 + u < steps) {
+        s = dv[u] * s + av[u];
+        if (b0 + u + 1 < n_seg) prev[(sbase + b0 + u + 1) * kStateElems + e] = s;
+      }
+    }
   }
   if (s_final) s_final[(size_t)bh * kStateElems + i * kHead + j] = s;
 }
 
+// Publication between workgroups (possibly on different XCDs, whose L2 caches
+// are not coherent with each other): the producer's waves each issue an
+// agent-scope release fence after their payload stores, then one thread sets
+// the flag; the consumer polls the flag with relaxed agent-scope loads (no
+// cache maintenance per poll), and after seeing it every wave issues one
+// agent-scope acquire fence before reading the payload.
+
+// Bounded wait for a flag value; records a timeout in ctl[kCtlError].
+__device__ __forceinline__ void wait_flag(const Params &p, const int *f, int want) {
+  int spins = 0;
+  while (__hip_atomic_load(const_cast<int *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+    __builtin_amdgcn_s_sleep(8);
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(p.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
+}
+
+// One launch: segment aggregate -> publish -> combine predecessors -> outputs.
+template <class Io, typename Op>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_fused(Params p) {
+  __shared__ Smem<Op> sm;
+  __shared__ int s_ticket, s_epoch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) {
+    s_ticket = atomicAdd(p.ctl + kCtlTicket, 1);
+    s_epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const int ticket = s_ticket, want = s_epoch + 1;
+  const int seg = ticket / p.bh_count;  // segment-major: predecessors start earlier
+  const int bh = ticket - seg * p.bh_count;
+  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
+  const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
+  const size_t sbase = (size_t)bh * p.n_seg;
+  const size_t lane_off = wave * 1024 + lane;
+
+  // 1. this segment's own aggregate (not needed for the last segment), stored
+  //    row-major [i][j] so that combining reads whole rows.
+  if (seg + 1 < p.n_seg) {
+    f4 A[4] = {};
+    f4 sdec = {1.f, 1.f, 1.f, 1.f};
+    walk<Io, Op, false>(p, sq, sm, c0, c1, wave, lane, A, sdec);
+    float *dst = p.agg + (sbase + seg) * kStateElems + 16 * wave + (lane & 15);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead] = A[x >> 2][x & 3];
+    if (wave == 0 && lane < 16)
+      *reinterpret_cast<f4 *>(&p.agg_dec[(sbase + seg) * kHead + 4 * lane]) = sdec;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's payload is visible ...
+    __syncthreads();                                     // ... for every wave ...
+    if (tid == 0)                                        // ... before the flag is raised
+      __hip_atomic_store(p.flags + sbase + seg, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 2. state entering this segment: s0 carried over the aggregates of segments
+  //    0..seg-1.  Wave w combines rows [16w, 16w+16), lane l column l, so every
+  //    load reads one contiguous 256-byte row; the result goes through LDS (the
+  //    operand tiles are idle here) into the register layout of the output walk.
+  f4 S[4] = {};
+  if (seg > 0 || p.s0) {
+    float X[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      X[r] = p.s0 ? p.s0[(size_t)bh * kStateElems + (16 * wave + r) * kHead + lane] : 0.f;
+    constexpr int kBatch = 6;
+    for (int j0 = 0; j0 < seg; j0 += kBatch) {
+      const int nb = min(kBatch, seg - j0);
+      if (tid < nb) wait_flag(p, p.flags + sbase + j0 + tid, want);
+      __syncthreads();  // the flags seen by one wave hold for the whole workgroup
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      float av[kBatch][16], dv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+          const float *src = p.agg + (sbase + j0 + u) * kStateElems + 16 * wave * kHead + lane;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) av[u][r] = src[r * kHead];
+          dv[u] = p.agg_dec[(sbase + j0 + u) * kHead + 16 * wave + (lane & 15)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < nb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) X[r] = __shfl(dv[u], r) * X[r] + av[u][r];  // decay of row 16w+r
+        }
+      }
+    }
+    float *xs = reinterpret_cast<float *>(sm.qs);  // 64 x 68 floats span qs and qh
+    constexpr int kLdX = 68;
+    static_assert(sizeof(sm.qs) + sizeof(sm.qh) >= kChunk * kLdX * sizeof(float), "xs overflow");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xs[(16 * wave + r) * kLdX + lane] = X[r];
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = xs[state_i(x, lane) * kLdX + 16 * wave + (lane & 15)];
+    __syncthreads();  // the output walk overwrites this LDS
+  }
+
+  // 3. outputs of this segment; the last segment also yields the final state
+  f4 unused = {};
+  walk<Io, Op, true>(p, sq, sm, c0, c1, wave, lane, S, unused);
+  if (p.s_final && seg + 1 == p.n_seg)
+    store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, S);
+
+  // 4. the last workgroup to finish resets the ticket and done counters and
+  //    advances the epoch, so the next call on this workspace starts clean.
+  __syncthreads();
+  if (tid == 0) {
+    const int total = p.bh_count * p.n_seg;
+    if (atomicAdd(p.ctl + kCtlDone, 1) == total - 1) {
+      __hip_atomic_store(p.ctl + kCtlTicket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctl + kCtlDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctl + kCtlEpoch, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Launches `kernel`, bracketed by dispatch-timestamped events while profiling.
+template <typename K, typename... Args>
+void launch(int id, K kernel, unsigned blocks, hipStream_t stream, Args... args) {
+  hipEvent_t t0, t1;
+  if (profile_events(id, stream, &t0, &t1))
+    hipExtLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, stream, t0, t1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, stream, args...);
+}
+
 template <class Io, typename Op>
 int launch_typed(const LaunchArgs &a) {
-  Params p{a.q, a.k, a.v, a.g, a.out, a.n_tok, a.grid_h, a.grid_w, a.direction,
-           a.n_chunk, a.seg_len, a.n_seg, a.n_seg, a.agg, a.agg_log2, nullptr};
+  Params p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.out = a.out;
+  p.bh_count = a.bh; p.n_tok = a.n_tok; p.gh = a.grid_h; p.gw = a.grid_w; p.dir = a.direction;
+  p.rcp_gh = 1.0f / (float)a.grid_h;
+  p.n_chunk = a.n_chunk; p.seg_len = a.seg_len; p.n_seg = a.n_seg; p.n_seg_grid = a.n_seg;
+  p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
+  p.flags = a.flags; p.ctl = a.ctl;
+  const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
+  if (a.fused) {
+    launch(kKernelFused, gla_fused<Io, Op>, n_blocks, a.stream, p);
+    return (int)hipGetLastError();
+  }
   const bool need_scan = a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr;
   if (need_scan) {
     const int n_state_seg = a.s_final ? a.n_seg : a.n_seg - 1;
     if (n_state_seg > 0) {
       Params ps = p;
       ps.n_seg_grid = n_state_seg;
-      profile_mark(kKernelSegState, a.stream, true);
-      hipLaunchKernelGGL((gla_seg_state<Io, Op>), dim3((unsigned)(a.bh * n_state_seg)),
-                         dim3(kThreads), 0, a.stream, ps);
-      profile_mark(kKernelSegState, a.stream, false);
+      launch(kKernelSegState, gla_seg_state<Io, Op>, (unsigned)(a.bh * n_state_seg), a.stream, ps);
     }
     const long threads = (long)a.bh * kStateElems;
-    profile_mark(kKernelSegScan, a.stream, true);
-    hipLaunchKernelGGL(gla_seg_scan, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, a.stream, a.agg, a.agg_log2, a.prev, a.s0, a.s_final,
-                       a.bh, a.n_seg);
-    profile_mark(kKernelSegScan, a.stream, false);
+    launch(kKernelSegScan, gla_seg_scan, (unsigned)((threads + kThreads - 1) / kThreads), a.stream,
+           (const float *)a.agg, (const float *)a.agg_dec, a.prev, a.s0, a.s_final, a.bh,
+           a.n_seg);
     p.prev = a.prev;
   }
-  profile_mark(kKernelSegOut, a.stream, true);
-  hipLaunchKernelGGL((gla_seg_out<Io, Op>), dim3((unsigned)(a.bh * a.n_seg)), dim3(kThreads), 0,
-                     a.stream, p);
-  profile_mark(kKernelSegOut, a.stream, false);
+  launch(kKernelSegOut, gla_seg_out<Io, Op>, n_blocks, a.stream, p);
   return (int)hipGetLastError();
 }
 

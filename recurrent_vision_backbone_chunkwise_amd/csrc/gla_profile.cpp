@@ -23,34 +23,31 @@ struct Mark {
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Mark> g_marks;
-hipEvent_t g_pending[kNumKernels] = {};
 
-const char *kNames[kNumKernels] = {"gla_seg_state", "gla_seg_scan", "gla_seg_out"};
+const char *kNames[kNumKernels] = {"gla_seg_state", "gla_seg_scan", "gla_seg_out", "gla_fused"};
 
 }  // namespace
 
-void profile_mark(int kernel, hipStream_t stream, bool start) {
-  if (!g_on.load(std::memory_order_relaxed)) return;
+bool profile_events(int kernel, hipStream_t stream, hipEvent_t *start, hipEvent_t *stop) {
+  *start = nullptr;
+  *stop = nullptr;
+  if (!g_on.load(std::memory_order_relaxed)) return false;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
     (void)hipGetLastError();
-    return;
+    return false;
+  }
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    (void)hipGetLastError();
+    if (a) (void)hipEventDestroy(a);
+    return false;
   }
   std::lock_guard<std::mutex> lock(g_mu);
-  hipEvent_t ev = nullptr;
-  if (hipEventCreate(&ev) != hipSuccess) {
-    (void)hipGetLastError();
-    return;
-  }
-  (void)hipEventRecord(ev, stream);
-  if (start) {
-    g_pending[kernel] = ev;
-  } else if (g_pending[kernel]) {
-    g_marks.push_back({kernel, g_pending[kernel], ev});
-    g_pending[kernel] = nullptr;
-  } else {
-    (void)hipEventDestroy(ev);
-  }
+  g_marks.push_back({kernel, a, b});
+  *start = a;
+  *stop = b;
+  return true;
 }
 
 }  // namespace gtr
@@ -86,10 +83,6 @@ int gtr_gla_profile_end(double *total_ms, int *launches, int max_kernels) {
     (void)hipEventDestroy(m.stop);
   }
   gtr::g_marks.clear();
-  for (auto &e : gtr::g_pending) {
-    if (e) (void)hipEventDestroy(e);
-    e = nullptr;
-  }
   return rc == GTR_OK ? gtr::kNumKernels : rc;
 }
 

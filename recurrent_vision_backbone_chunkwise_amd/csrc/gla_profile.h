@@ -5,10 +5,18 @@
 
 namespace gtr {
 
-enum KernelId : int { kKernelSegState = 0, kKernelSegScan = 1, kKernelSegOut = 2, kNumKernels = 3 };
+enum KernelId : int {
+  kKernelSegState = 0,
+  kKernelSegScan = 1,
+  kKernelSegOut = 2,
+  kKernelFused = 3,
+  kNumKernels = 4
+};
 
-// Records an event on `stream` before (start = true) or after a kernel launch
-// while profiling is on and the stream is not being captured.  No-op otherwise.
-void profile_mark(int kernel, hipStream_t stream, bool start);
+// While profiling is on and `stream` is not being captured, creates a pair of
+// events for the next launch of `kernel` (to be passed to hipExtLaunchKernelGGL,
+// which timestamps the dispatch itself) and returns true.  Otherwise returns
+// false and leaves both events null.
+bool profile_events(int kernel, hipStream_t stream, hipEvent_t *start, hipEvent_t *stop);
 
 }  // namespace gtr

@@ -44,25 +44,43 @@ def test_binding_constants_match_header():
 
 def test_version_and_sizes():
     assert gla.gtr_gla_version() == 10000
-    # one segment, no state: no workspace needed in practice, but the size query is still defined
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1) == 6 * 25 * (2 * 4096 + 64) * 4
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 0) == 0
-    assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0) == 0
-    assert gla.gtr_gla_auto_chunks_per_segment(1, 16, 128, 128) == 8
-    assert gla.gtr_gla_auto_chunks_per_segment(1, 6, 40, 40) == 1
+    split = gla.GTR_PATH_SPLIT
+    fused = gla.GTR_PATH_FUSED
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
+        6 * 25 * (2 * 4096 + 64) * 4 + (64 + 6 * 25) * 4
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 0, 0) == 0
+    assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0, 0) == 0
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 0, 3) == 0
+
+
+def test_plans():
+    # 128x128 grid = 256 chunks per sequence: the fused path caps segments per sequence
+    pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_FUSED)
+    assert pl["fused"] and pl["n_seg"] <= 24 and pl["seg_len"] * pl["n_seg"] >= 256
+    pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_SPLIT)
+    assert not pl["fused"] and pl["seg_len"] * pl["n_seg"] >= 256
+    pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=4)
+    assert pl["seg_len"] == 4 and pl["n_seg"] == 7
+    pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
+    assert pl["seg_len"] == 1 and pl["n_seg"] == 1
+    with pytest.raises(gla.GlaError):
+        gla.gtr_gla_plan(1, 1, 0, 1)
 
 
 A = 0x10000  # fake, 16-byte aligned, never dereferenced
 
 
 def call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, out=A + 0x400000, B=1, H=1, gh=4,
-         gw=4, dk=64, dv=64, d=0, dt=1, s0=None, sf=None, seg=0):
-    return gla.lib().gtr_gla_fwd_ex(q, k, v, g, out, B, H, gh, gw, dk, dv, d, dt, s0, sf, seg, None)
+         gw=4, dk=64, dv=64, d=0, dt=1, s0=None, sf=None, seg=0, path=0):
+    return gla.lib().gtr_gla_fwd_ex(q, k, v, g, out, B, H, gh, gw, dk, dv, d, dt, s0, sf, seg, path,
+                                    None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(out=None), -1), (dict(B=0), -1), (dict(H=-1), -1), (dict(gh=0), -1),
-    (dict(d=4), -1), (dict(d=-1), -1), (dict(dt=3), -1), (dict(gh=1 << 15, gw=1 << 14), -1),
+    (dict(d=4), -1), (dict(d=-1), -1), (dict(dt=3), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1),
+    (dict(path=3), -1), (dict(path=-1), -1),
     (dict(B=1 << 11, H=1 << 10), -1),
     (dict(dk=32), -2), (dict(dv=128), -2),
     (dict(k=A + 0x100008), -3), (dict(out=A + 0x400004), -3), (dict(s0=A + 0x500002), -3),

@@ -49,31 +49,37 @@ SMALL_GRIDS = [(1, 1), (1, 63), (1, 65), (8, 8), (7, 9), (5, 13), (9, 17), (13, 
                (100, 3), (16, 16)]
 
 
+PATHS = {"fused": 1, "split": 2}
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("direction", [0, 1, 2, 3])
 @pytest.mark.parametrize("grid", SMALL_GRIDS, ids=lambda g: f"{g[0]}x{g[1]}")
-def test_small_grids(grid, direction, dtype):
+def test_small_grids(grid, direction, dtype, path):
     gh, gw = grid
     q, k, v, g = gla_inputs.make_inputs(2, 3, gh, gw, 64, 64, dtype, "light",
                                         seed=gh * 1000 + gw * 10 + direction)
-    check(q, k, v, g, direction, dtype, f"small {gh}x{gw}")
+    check(q, k, v, g, direction, dtype, f"small {gh}x{gw}", path=PATHS[path], chunks_per_segment=1)
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("seg", [1, 2, 3, 4, 6, 7, 0])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_segment_lengths(seg, dtype):
+def test_segment_lengths(seg, dtype, path):
     q, k, v, g = gla_inputs.make_inputs(1, 4, 17, 19, 64, 64, dtype, "heavy", seed=77 + seg)
-    check(q, k, v, g, 3, dtype, f"seg_len={seg}", chunks_per_segment=seg)
+    check(q, k, v, g, 3, dtype, f"seg_len={seg}", chunks_per_segment=seg, path=PATHS[path])
 
 
 # ---- the five benchmark workloads at full size, every listed direction ----------------
 
+@pytest.mark.parametrize("path", ["auto", "fused", "split"])
 @pytest.mark.parametrize("widx", [1, 2, 3, 4, 5])
-def test_workloads_full_size(widx):
+def test_workloads_full_size(widx, path):
     w = gla_inputs.workload(widx)
     for layer, d in enumerate(w.directions):
         q, k, v, g = gla_inputs.workload_inputs(w, layer)
-        e = check(q, k, v, g, d, w.dtype, w.name)
+        e = check(q, k, v, g, d, w.dtype, w.name, path=PATHS.get(path, 0))
         note(f"  {w.name} dir={d}: err_raw={e['err_raw']:.3g} err_excess={e['err_excess']:.3g}")
 
 
@@ -84,8 +90,8 @@ def test_workloads_full_size(widx):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gate_extremes(gate, dtype):
     q, k, v, g = gla_inputs.make_inputs(1, 2, 19, 23, 64, 64, dtype, gate, seed=5)
-    for d in (0, 2):
-        check(q, k, v, g, d, dtype, f"gate={gate}")
+    for d, path in ((0, 1), (2, 2)):
+        check(q, k, v, g, d, dtype, f"gate={gate}", path=path, chunks_per_segment=2)
 
 
 def test_unit_gate_long_sequence():
@@ -96,14 +102,16 @@ def test_unit_gate_long_sequence():
 
 # ---- initial / final state -----------------------------------------------------------------
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_initial_and_final_state(dtype):
+def test_initial_and_final_state(dtype, path):
     B, H, gh, gw = 1, 3, 11, 13
     q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, dtype, "light", seed=8)
     s0 = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(9)) * 0.5
     for d in range(4):
         note(f"state dir={d} dtype={dtype}")
-        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1)
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1,
+                        path=PATHS[path])
         ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
         assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
         es = parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")
@@ -127,13 +135,47 @@ def test_split_sequence_equals_whole():
 
 # ---- execution properties ------------------------------------------------------------------
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_deterministic_bitwise(path):
     q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 4, 40, 40, 64, 64, "f16", "light",
                                                               seed=11))
-    outs = [gla.gla_forward(q, k, v, g, 2) for _ in range(5)]
+    outs = [gla.gla_forward(q, k, v, g, 2, path=PATHS[path], chunks_per_segment=2)
+            for _ in range(5)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+def test_fused_repeated_calls_are_identical():
+    """Many fused calls in a row (segments wait on each other's flags) give bitwise-equal results."""
+    w = gla_inputs.workload(3)
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.workload_inputs(w, 0))
+    first = gla.gla_forward(q, k, v, g, 2, path=1)
+    torch.cuda.synchronize()
+    ref = oracle.gla_forward(*gla_inputs.workload_inputs(w, 0), 2)
+    assert parity_errors(first.double().cpu().numpy(), ref, "f16")["ok"]
+    out = torch.empty_like(first)
+    for i in range(60):
+        gla.gtr_gla_fwd_ex(q, k, v, g, out, 2, path=1, chunks_per_segment=1 + i % 3)
+        if i % 3 == 1:  # a different segmentation only reorders fp32 sums: compare to the oracle
+            torch.cuda.synchronize()
+            assert parity_errors(out.double().cpu().numpy(), ref, "f16")["ok"], i
+    gla.gtr_gla_fwd_ex(q, k, v, g, out, 2, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, first)
+
+
+def test_paths_agree_and_repeat_on_one_workspace():
+    """Different shapes and both paths back to back on one stream reuse one workspace."""
+    shapes = [(1, 6, 40, 40, 1), (2, 3, 17, 19, 3), (1, 6, 40, 40, 2), (1, 2, 64, 64, 1),
+              (2, 3, 17, 19, 1)]
+    for B, H, gh, gw, seg in shapes:
+        q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, "f16", "light", seed=B + gh)
+        ref = oracle.gla_forward(q, k, v, g, 1)
+        for path in (1, 2, 1):
+            note(f"reuse {B}x{H}x{gh}x{gw} seg={seg} path={path}")
+            y = gpu_run(q, k, v, g, 1, chunks_per_segment=seg, path=path)
+            assert parity_errors(y.double().cpu().numpy(), ref, "f16")["ok"]
 
 
 def test_non_default_stream_and_graph_replay():
@@ -176,7 +218,7 @@ def test_capture_refuses_workspace_growth():
     err = None
     with torch.cuda.graph(graph, stream=fresh):
         try:
-            gla.gtr_gla_fwd_ex(q, k, v, g, out, 0, chunks_per_segment=1, stream=fresh)
+            gla.gtr_gla_fwd_ex(q, k, v, g, out, 0, chunks_per_segment=1, path=2, stream=fresh)
         except gla.GlaError as ex:
             err = ex
     assert err is not None and err.code == -8
@@ -194,7 +236,7 @@ def test_pointer_checks_on_gpu():
 
     def chk(o, gh=8, gw=8):
         return L.gtr_gla_check(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), o, 1, 1, gh,
-                               gw, 64, 64, 0, 1, None, None, 0)
+                               gw, 64, 64, 0, 1, None, None, 0, 0)
 
     assert chk(out.data_ptr()) == 0
     assert chk(host_ptr) == -6
@@ -217,10 +259,12 @@ def test_profiling_counts_launches():
                                                               seed=14))
     gla.gtr_gla_profile_begin()
     for _ in range(3):
-        gla.gla_forward(q, k, v, g, 0, chunks_per_segment=5)
+        gla.gla_forward(q, k, v, g, 0, chunks_per_segment=5, path=2)
+    for _ in range(2):
+        gla.gla_forward(q, k, v, g, 0, chunks_per_segment=5, path=1)
     prof = gla.gtr_gla_profile_end()
     assert prof["gla_seg_out"][1] == 3 and prof["gla_seg_state"][1] == 3
-    assert prof["gla_seg_scan"][1] == 3
+    assert prof["gla_seg_scan"][1] == 3 and prof["gla_fused"][1] == 2
     assert all(ms > 0 for ms, n in prof.values())
 
 
