@@ -87,7 +87,7 @@ extern "C" {
 #define GTR_DTYPE_BF16 2
 
 /* launch structure (entry points _ex, _check, _workspace_bytes, _plan) */
-#define GTR_PATH_AUTO 0   /* chosen by the library */
+#define GTR_PATH_AUTO 0   /* chosen by the library from the shape */
 #define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, flag-ordered combine, outputs */
 #define GTR_PATH_SPLIT 2  /* three kernels: segment aggregates, boundary scan, outputs */
 

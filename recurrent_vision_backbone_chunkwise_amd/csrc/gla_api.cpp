@@ -54,9 +54,11 @@ constexpr int kMaxFusedSegments = 24;  // longest aggregate chain one fused work
 // Chunks per segment and launch structure for a shape.  The fused launch reads
 // the aggregates of all earlier segments of its sequence, so it caps the
 // segment count; the three-launch path scans segments in a separate kernel.
+// Automatic choice: the three-launch path, which measures faster on every
+// shape tried (the fused launch walks each segment twice inside one kernel).
 void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
   const long long total = bh * n_chunk;
-  sh->fused = path != GTR_PATH_SPLIT;
+  sh->fused = path == GTR_PATH_FUSED;
   long long len = chunks_per_segment;
   if (len <= 0) {
     // about three resident workgroups per CU on 256 CUs

@@ -89,7 +89,9 @@ struct IoF32 {
   using Raw = u4;  // 16 bytes
   __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
   __device__ static float load1(const T *p) { return *p; }
-  __device__ static void store4(T *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
+  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, 0);
+  }
 };
 
 struct IoF16 {
@@ -98,8 +100,9 @@ struct IoF16 {
   __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
   __device__ static f4 to_f4(Raw r) { return __builtin_convertvector(to_h4(r), f4); }
   __device__ static float load1(const T *p) { return (float)*p; }
-  __device__ static void store4(T *p, f4 v) {
-    *reinterpret_cast<h4 *>(p) = __builtin_convertvector(v, h4);
+  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, __builtin_convertvector(v, h4)), r,
+                                          (int)off, 0, 0);
   }
 };
 
@@ -117,9 +120,9 @@ struct IoBF16 {
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   }
-  __device__ static void store4(T *p, f4 v) {
-    u2 w = {rne(v.x) | (rne(v.y) << 16), rne(v.z) | (rne(v.w) << 16)};
-    *reinterpret_cast<u2 *>(p) = w;
+  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+    const u2 w = {rne(v.x) | (rne(v.y) << 16), rne(v.z) | (rne(v.w) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
   }
 };
 
@@ -222,38 +225,84 @@ __device__ __forceinline__ int tile_slot(int a, int b) { return (a * (a + 1)) / 
 // column-major orders divide by grid_h with a float reciprocal and one exact
 // correction step (t < 2^23, so float(t) is exact and the estimate is off by
 // at most one).
-__device__ __forceinline__ int grid_index(int t, int n_tok, int gh, int gw, int dir, float rcp_gh) {
-  if (dir & 1) t = n_tok - 1 - t;
-  if (dir & 2) {
-    int col = (int)((float)t * rcp_gh);
-    int row = t - col * gh;
-    if (row < 0) {
-      --col;
-      row += gh;
-    } else if (row >= gh) {
-      ++col;
-      row -= gh;
-    }
-    return row * gw + col;
+__device__ __forceinline__ void col_major_pos(int p, int gh, float rcp_gh, int &row, int &col) {
+  col = (int)((float)p * rcp_gh);
+  row = p - col * gh;
+  if (row < 0) {
+    --col;
+    row += gh;
+  } else if (row >= gh) {
+    ++col;
+    row -= gh;
   }
-  (void)gw;
-  return t;
 }
 
-// One sequence: element offsets inside it fit in 32 bits (n_tok <= 2^23 is
-// checked on the host), so loads use a uniform 64-bit base plus a 32-bit offset.
+constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer range: loads give 0, stores drop
+
+// One sequence's tensors as buffer resources: byte offsets are 32-bit and
+// uniform bases live in scalar registers; the range is the sequence's rows
+// (n_tok <= 2^23 rows of at most 256 bytes, checked on the host).
 struct Seq {
+  __amdgpu_buffer_rsrc_t q, k, v, g, o;
   int n_tok, gh, gw, dir;
   float rcp_gh;
-  size_t base;  // element offset of this sequence: bh * n_tok * 64
-  __device__ uint32_t row(int t) const {
-    return (uint32_t)grid_index(t, n_tok, gh, gw, dir, rcp_gh) * kHead;
-  }
-  template <typename T> __device__ const T *in(const void *p) const {
-    return static_cast<const T *>(p) + base;
-  }
-  template <typename T> __device__ T *out(void *p) const { return static_cast<T *>(p) + base; }
 };
+
+template <class Io>
+__device__ __forceinline__ Seq make_seq(const void *q, const void *k, const void *v, const void *g,
+                                        void *o, int bh, int n_tok, int gh, int gw, int dir,
+                                        float rcp_gh) {
+  using T = typename Io::T;
+  const size_t base = (size_t)bh * n_tok * kHead;
+  const int bytes = (int)((uint32_t)n_tok * kHead * sizeof(T));
+  auto rsrc = [&](const void *p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(static_cast<const T *>(p) + base),
+                                             (short)0, bytes, 0x00020000);
+  };
+  return Seq{rsrc(q), rsrc(k), rsrc(v), rsrc(g), rsrc(o), n_tok, gh, gw, dir, rcp_gh};
+}
+
+// Element offset of the row of scan position t (t < n_tok).
+__device__ __forceinline__ uint32_t token_row(const Seq &sq, int t) {
+  const int p = (sq.dir & 1) ? sq.n_tok - 1 - t : t;
+  if (!(sq.dir & 2)) return (uint32_t)p * kHead;
+  int row, col;
+  col_major_pos(p, sq.gh, sq.rcp_gh, row, col);
+  return (uint32_t)(row * sq.gw + col) * kHead;
+}
+
+// Byte offsets of the rows of scan positions t0 .. t0+3 (kOob past the end).
+// Consecutive scan positions step by one grid cell along the scan, so only the
+// first needs a division.
+template <class Io>
+__device__ __forceinline__ void rows4(const Seq &sq, int t0, uint32_t *off) {
+  constexpr uint32_t kRow = kHead * sizeof(typename Io::T);
+  const bool rev = sq.dir & 1;
+  const int p0 = rev ? sq.n_tok - 1 - t0 : t0;
+  if (!(sq.dir & 2)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int p = rev ? p0 - r : p0 + r;
+      off[r] = t0 + r < sq.n_tok ? (uint32_t)p * kRow : kOob;
+    }
+    return;
+  }
+  int row, col;
+  col_major_pos(p0, sq.gh, sq.rcp_gh, row, col);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    off[r] = t0 + r < sq.n_tok ? (uint32_t)(row * sq.gw + col) * kRow : kOob;
+    if (rev) {
+      if (--row < 0) {
+        row = sq.gh - 1;
+        --col;
+      }
+    } else if (++row == sq.gh) {
+      row = 0;
+      ++col;
+    }
+  }
+}
 
 // -------------------------------------------------------------- shared memory
 // Gate factors below are products of alpha = exp(log_gate) over token ranges of
@@ -272,6 +321,7 @@ template <typename Op> struct Smem {
   Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
   Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
   float dec[kHead];     // 2^E_last: decay of the state across the chunk
+  uint32_t rowoff[kChunk];  // byte offset of each token's row (kOob past the end)
 };
 
 // ------------------------------------------------------------------- params
@@ -291,75 +341,103 @@ struct Params {
 
 enum : int { kCtlTicket = 0, kCtlDone = 1, kCtlEpoch = 2, kCtlError = 3 };
 
+template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int bh) {
+  return make_seq<Io>(p.q, p.k, p.v, p.g, p.out, bh, p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh);
+}
+
 // Register-order state layout: (wave w, lane l, reg x) holds element (i, j) with
 // i = 16(x/4) + 4(l/16) + x%4 and j = 16w + l%16, at offset w*1024 + x*64 + l.
 __device__ __forceinline__ int state_i(int x, int lane) { return 16 * (x >> 2) + 4 * (lane >> 4) + (x & 3); }
 
-// Row offsets of this thread's 4 tokens of chunk c (valid = inside the sequence).
-__device__ __forceinline__ void chunk_rows(const Params &p, const Seq &sq, int c, int wave, int lane,
-                                           uint32_t *off, bool *ok) {
-  const int col = 4 * (lane & 15);
+// This thread's slice of one chunk: 4 consecutive tokens 16w+4(l/16)+r, dims
+// 4(l%16)..+3, of each tensor (zeros past the end of the sequence: no key, no
+// value, no decay, no query there), and the tokens' row offsets.
+template <class Io> struct Rows {
+  typename Io::Raw q[4], k[4], v[4], g[4];
+  uint32_t off[4];
+};
+
+template <class Io>
+__device__ __forceinline__ typename Io::Raw buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(typename Io::Raw) == 16)
+    return __builtin_bit_cast(typename Io::Raw, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  else
+    return __builtin_bit_cast(typename Io::Raw, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+
+template <class Io, bool kOut>
+__device__ __forceinline__ void load_chunk(const Seq &sq, int c, int wave, int lane, Rows<Io> &x) {
+  const uint32_t col = 4 * (lane & 15) * sizeof(typename Io::T);
+  rows4<Io>(sq, c * kChunk + 16 * wave + 4 * (lane >> 4), x.off);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int t = c * kChunk + 16 * wave + 4 * (lane >> 4) + r;
-    ok[r] = t < p.n_tok;
-    off[r] = (ok[r] ? sq.row(t) : 0u) + col;
+    const uint32_t o = x.off[r] + col;  // kOob + col stays out of range
+    x.g[r] = buf_load<Io>(sq.g, o);
+    x.k[r] = buf_load<Io>(sq.k, o);
+    x.v[r] = buf_load<Io>(sq.v, o);
+    if constexpr (kOut) x.q[r] = buf_load<Io>(sq.q, o);
   }
 }
 
-// One tensor's rows for those tokens (zeros past the end of the sequence: no
-// key, no value, no decay, no query there).
-template <class Io>
-__device__ __forceinline__ void load_rows(const void *tensor, const Seq &sq, const uint32_t *off,
-                                          const bool *ok, typename Io::Raw *dst) {
-  using T = typename Io::T;
-  using Raw = typename Io::Raw;
-  const T *base = sq.in<T>(tensor);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) dst[r] = ok[r] ? *reinterpret_cast<const Raw *>(base + off[r]) : Raw{};
+// Products across the four 16-lane rows of a wave: x holds this row's value;
+// returns the product over rows < g (before) and over rows > g (after), and the
+// product over all rows.  Two cross-row swaps, no LDS.
+__device__ __forceinline__ void row_products(float x, int g, float &before, float &after, float &all) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float e = __uint_as_float(s16[0]), o = __uint_as_float(s16[1]);  // rows (0,0,2,2), (1,1,3,3)
+  const float partner = (g & 1) ? e : o;                                 // row g^1
+  const float pair = e * o;                                              // rows {0,1} or {2,3}
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+  const float lo = __uint_as_float(s32[0]), hi = __uint_as_float(s32[1]);  // rows {0,1}, rows {2,3}
+  before = ((g & 2) ? lo : 1.f) * ((g & 1) ? partner : 1.f);
+  after = ((g & 2) ? 1.f : hi) * ((g & 1) ? 1.f : partner);
+  all = lo * hi;
 }
 
 // First half of a chunk's operand preparation, local to each wave.  Gate
 // products of this thread's 4 tokens x 4 dims inside its wave's 16-token
 // sub-block scale the inputs: qs = q * (product of alpha from the sub-block
 // start through the token), ks = k * (product of alpha after the token to the
-// sub-block end).  qs, ks and v go to LDS, the sub-block product to sm.tot.
-// One exp2 per element; the rest are multiplications and a 4-way exchange
-// between the lane groups of the wave.
+// sub-block end).  qs, ks and v go to LDS, the sub-block product to sm.tot, the
+// row offsets to sm.rowoff.  One exp2 per element; the rest are multiplications
+// and cross-row swaps.
 template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void prep_local(Smem<Op> &sm, const typename Io::Raw *rq,
-                                           const typename Io::Raw *rk, const typename Io::Raw *rv,
-                                           const typename Io::Raw *rg, int wave, int lane,
+__device__ __forceinline__ void prep_local(Smem<Op> &sm, const Rows<Io> &x, int wave, int lane,
                                            op4<Op> *qs, op4<Op> *ks) {
   constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
   const int g = lane >> 4, dq = lane & 15;
-  const f4 one = {1.f, 1.f, 1.f, 1.f};
   f4 a[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) a[r] = exp2v(Io::to_f4(rg[r]) * kLog2e);
+  for (int r = 0; r < 4; ++r) a[r] = exp2v(Io::to_f4(x.g[r]) * kLog2e);
   const f4 p1 = a[0] * a[1], p2 = p1 * a[2], p3 = p2 * a[3];  // prefix products in the group
   const f4 s2 = a[3], s1 = a[2] * a[3], s0 = a[1] * s1;        // suffix products in the group
-  f4 t[4];  // products of the four 4-token groups of this sub-block
+  f4 before, after, all;
 #pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) t[m][d] = __shfl(p3[d], dq + 16 * m);
-  const f4 before = g == 0 ? one : (g == 1 ? t[0] : (g == 2 ? t[0] * t[1] : t[0] * t[1] * t[2]));
-  const f4 after = g == 3 ? one : (g == 2 ? t[3] : (g == 1 ? t[2] * t[3] : t[1] * t[2] * t[3]));
+  for (int d = 0; d < 4; ++d) {
+    float b, f, t;
+    row_products(p3[d], g, b, f, t);
+    before[d] = b;
+    after[d] = f;
+    all[d] = t;
+  }
   const f4 pq[4] = {a[0] * before, p1 * before, p2 * before, p3 * before};
   const f4 pk[4] = {s0 * after, s1 * after, s2 * after, after};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tau = 16 * wave + 4 * g + r;
-    ks[r] = ToOp<Op, Io>::cvt(rk[r]) * to4<Op>(pk[r]);
-    *reinterpret_cast<op4<Op> *>(&sm.vv[tau * LDT + 4 * dq]) = ToOp<Op, Io>::cvt(rv[r]);
+    ks[r] = ToOp<Op, Io>::cvt(x.k[r]) * to4<Op>(pk[r]);
+    *reinterpret_cast<op4<Op> *>(&sm.vv[tau * LDT + 4 * dq]) = ToOp<Op, Io>::cvt(x.v[r]);
     if constexpr (kOut) {
-      qs[r] = ToOp<Op, Io>::cvt(rq[r]) * to4<Op>(pq[r]);
+      qs[r] = ToOp<Op, Io>::cvt(x.q[r]) * to4<Op>(pq[r]);
       *reinterpret_cast<op4<Op> *>(&sm.qs[tau * LD + 4 * dq]) = qs[r];
       *reinterpret_cast<op4<Op> *>(&sm.ks[tau * LD + 4 * dq]) = ks[r];
     }
   }
-  if (g == 0) *reinterpret_cast<f4 *>(&sm.tot[wave * kHead + 4 * dq]) = t[0] * t[1] * t[2] * t[3];
+  if (g == 0) *reinterpret_cast<f4 *>(&sm.tot[wave * kHead + 4 * dq]) = all;
+  if (kOut && dq == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.rowoff[16 * wave + 4 * g + r] = x.off[r];
+  }
 }
 
 // Sub-block products t_0..t_3 of this lane's dims.
@@ -414,26 +492,26 @@ __device__ __forceinline__ void prep_chunk(Smem<Op> &sm, const op4<Op> *qs, cons
 // Exact fp32 diagonal score tile (a, a) for a sub-block whose gate range is too
 // wide for midpoint scaling.  Re-reads q, k and log_gate rows from global memory.
 template <class Io>
-__device__ f4 exact_diag(const Params &p, const Seq &sq, int c, int a, int lane) {
+__device__ f4 exact_diag(const Params &p, const Seq &sq, size_t base, int c, int a, int lane) {
   using T = typename Io::T;
   const int g = lane >> 4, l16 = lane & 15;
   const int t0 = c * kChunk + 16 * a;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
   if (t0 + l16 >= p.n_tok) return acc;  // query beyond the sequence
-  const T *gb = sq.in<T>(p.g);
-  const T *qrow = sq.in<T>(p.q) + sq.row(t0 + l16);
+  const T *gb = static_cast<const T *>(p.g) + base;
+  const T *qrow = static_cast<const T *>(p.q) + base + token_row(sq, t0 + l16);
   const T *krow[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {  // keys 4g+r <= l16 < n_tok exist; later keys are masked
     const int sl = 4 * g + r;
-    krow[r] = sq.in<T>(p.k) + sq.row(sl <= l16 ? t0 + sl : t0 + l16);
+    krow[r] = static_cast<const T *>(p.k) + base + token_row(sq, sl <= l16 ? t0 + sl : t0 + l16);
   }
   for (int i = 0; i < kHead; ++i) {
     // log2 gate sums from the sub-block start at the query and at each key
     float run = 0.f;
     float e_sig[4] = {0.f, 0.f, 0.f, 0.f};
     for (int u = 0; u <= l16; ++u) {
-      run += Io::load1(gb + sq.row(t0 + u) + i) * kLog2e;
+      run += Io::load1(gb + token_row(sq, t0 + u) + i) * kLog2e;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (u == 4 * g + r) e_sig[r] = run;
@@ -446,62 +524,73 @@ __device__ f4 exact_diag(const Params &p, const Seq &sq, int c, int a, int lane)
   return acc;
 }
 
-// Score tiles P^T[sigma][tau] of this chunk into sm.pt (lower block triangle only).
-template <class Io, typename Op>
-__device__ __forceinline__ void scores(const Params &p, const Seq &sq, Smem<Op> &sm, int c,
-                                       int wave, int lane) {
+// Off-diagonal score tile (a, b), b < a: P^T[sigma][tau] = ks_sigma . (qs_tau * factor).
+template <typename Op>
+__device__ __forceinline__ void off_tile(Smem<Op> &sm, int a, int b, int lane) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
+  const int cvec = (a == 2) ? 0 : (b == 0 ? 1 : 2);  // used when b < a-1
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int s = wave + 4 * u;
-    if (s >= 10) break;
-    const int a = tile_a(s);
-    const int b = s - (a * (a + 1)) / 2;
+  for (int kb = 0; kb < 2; ++kb) {
+    const int k0 = 32 * kb + 4 * g;
+    op8<Op> B = frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]);
+    if (b < a - 1) B = B * frag_row<Op>(&sm.cv[cvec * kHead + k0]);
+    acc = mma(frag_row<Op>(&sm.ks[(16 * b + l16) * LD + k0]), B, acc);
+  }
+  *reinterpret_cast<op4<Op> *>(&sm.pt[tile_slot(a, b) * 256 + lane * 4]) = to4<Op>(acc);
+}
+
+// Score tiles P^T[sigma][tau] of this chunk into sm.pt (lower block triangle
+// only).  Wave w forms the diagonal tile (w, w) and the off-diagonal tiles
+// (1,0),(2,1) | (2,0),(3,2) | (3,0) | (3,1).
+template <class Io, typename Op>
+__device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t base, Smem<Op> &sm,
+                                       int c, int wave, int lane) {
+  constexpr int LD = OpT<Op>::LD;
+  const int g = lane >> 4, l16 = lane & 15;
+  {
+    const int a = wave;
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (a == b) {
-      const bool fast = __all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
-      if (fast) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int k0 = 32 * kb + 4 * g;
-          const op8<Op> h = frag_row<Op>(&sm.hv[a * kHead + k0]);
-          acc = mma(frag_row<Op>(&sm.ks[(16 * b + l16) * LD + k0]) * h,
-                    frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]) * h, acc);
-        }
-      } else {
-        acc = exact_diag<Io>(p, sq, c, a, lane);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * g + r > l16) acc[r] = 0.f;  // keys after the query
-    } else {
-      const int cvec = (a == 2) ? 0 : (b == 0 ? 1 : 2);  // used when b < a-1
+    if (__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int k0 = 32 * kb + 4 * g;
-        op8<Op> B = frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]);
-        if (b < a - 1) B = B * frag_row<Op>(&sm.cv[cvec * kHead + k0]);
-        acc = mma(frag_row<Op>(&sm.ks[(16 * b + l16) * LD + k0]), B, acc);
+        const op8<Op> h = frag_row<Op>(&sm.hv[a * kHead + k0]);
+        acc = mma(frag_row<Op>(&sm.ks[(16 * a + l16) * LD + k0]) * h,
+                  frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]) * h, acc);
       }
+    } else {
+      acc = exact_diag<Io>(p, sq, base, c, a, lane);
     }
-    *reinterpret_cast<op4<Op> *>(&sm.pt[s * 256 + lane * 4]) = to4<Op>(acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r > l16) acc[r] = 0.f;  // keys after the query
+    *reinterpret_cast<op4<Op> *>(&sm.pt[tile_slot(a, a) * 256 + lane * 4]) = to4<Op>(acc);
+  }
+  if (wave == 0) {
+    off_tile(sm, 1, 0, lane);
+    off_tile(sm, 2, 1, lane);
+  } else if (wave == 1) {
+    off_tile(sm, 2, 0, lane);
+    off_tile(sm, 3, 2, lane);
+  } else if (wave == 2) {
+    off_tile(sm, 3, 0, lane);
+  } else {
+    off_tile(sm, 3, 1, lane);
   }
 }
 
 // O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T, stored at the grid positions.
 template <class Io, typename Op>
-__device__ __forceinline__ void outputs(const Params &p, const Seq &sq, const Smem<Op> &sm, int c,
-                                        int wave, int lane, const f4 *S) {
-  using T = typename Io::T;
+__device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op> &sm, int wave, int lane,
+                                        const op8<Op> *vf, const uint32_t *oo, const f4 *S) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
-  op8<Op> vf[2], sf[2];
+  op8<Op> sf[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
-    sf[kb] = cat(to4<Op>(S[2 * kb]), to4<Op>(S[2 * kb + 1]));
-  }
+  for (int kb = 0; kb < 2; ++kb) sf[kb] = cat(to4<Op>(S[2 * kb]), to4<Op>(S[2 * kb + 1]));
+  const uint32_t col = (16 * wave + 4 * g) * sizeof(typename Io::T);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -516,18 +605,14 @@ __device__ __forceinline__ void outputs(const Params &p, const Seq &sq, const Sm
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
       acc = mma(sf[kb], frag_row<Op>(&sm.qh[(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
-    const int t = c * kChunk + 16 * tt + l16;
-    if (t < p.n_tok) Io::store4(sq.out<T>(p.out) + sq.row(t) + 16 * wave + 4 * g, acc);
+    Io::store4(sq.o, oo[tt] + col, acc);
   }
 }
 
 // S <- diag(2^E_last) S + (k 2^(E_last-E))^T V for this wave's value columns.
 template <typename Op>
-__device__ __forceinline__ void carry_state(const Smem<Op> &sm, int wave, int lane, f4 *S) {
+__device__ __forceinline__ void carry_state(const Smem<Op> &sm, int lane, const op8<Op> *vf, f4 *S) {
   const int g = lane >> 4;
-  op8<Op> vf[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     S[it] *= *reinterpret_cast<const f4 *>(&sm.dec[16 * it + 4 * g]);
@@ -536,60 +621,57 @@ __device__ __forceinline__ void carry_state(const Smem<Op> &sm, int wave, int la
   }
 }
 
-// Walks chunks [c_begin, c_end) of one sequence, carrying S.  kOut: writes the
+// One chunk.  Barriers: (1) sub-block products and row offsets visible, (2)
+// operand tiles visible, (3) score tiles visible.  Everything a wave reads from
+// LDS after the last barrier of a chunk (pt, qh, kb, dec) is written only after
+// the first barrier of the next chunk, which no wave passes before every wave has
+// finished this chunk; v and the output row offsets, which the next chunk
+// overwrites before its first barrier, are read into registers before the
+// second one.  The next chunk's rows are loaded into x as soon as this chunk's
+// have gone to LDS, and arrive while the rest of this chunk computes.
+template <class Io, typename Op, bool kOut>
+__device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t base, Smem<Op> &sm,
+                                      Rows<Io> &x, int c, int c_end, int wave, int lane, f4 *S,
+                                      f4 &seg_dec) {
+  op4<Op> qs[4], ks[4];
+  prep_local<Io, Op, kOut>(sm, x, wave, lane, qs, ks);
+  if (c + 1 < c_end) load_chunk<Io, kOut>(sq, c + 1, wave, lane, x);
+  lds_sync();
+  prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane);
+  op8<Op> vf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
+  uint32_t oo[4];
+  if constexpr (kOut) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) oo[tt] = sm.rowoff[16 * tt + (lane & 15)];
+  }
+  if (!kOut && wave == 0 && lane < 16) {
+    f4 t[4];
+    sub_block_products(sm, lane, t);
+    seg_dec *= t[0] * t[1] * t[2] * t[3];
+  }
+  lds_sync();
+  if constexpr (kOut) {
+    scores<Io, Op>(p, sq, base, sm, c, wave, lane);
+    lds_sync();
+    outputs<Io, Op>(sq, sm, wave, lane, vf, oo, S);
+  }
+  carry_state<Op>(sm, lane, vf, S);
+}
+
+// Walks chunks [c_begin, c_end) of sequence bh, carrying S.  kOut: writes the
 // outputs (S must hold the state entering the first chunk); otherwise only
 // carries S (from zero: the segment's own aggregate) and multiplies the chunk
 // decays into seg_dec (wave 0, lane < 16 holds dims 4*lane..4*lane+3).
 template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void walk(const Params &p, const Seq &sq, Smem<Op> &sm, int c_begin,
-                                     int c_end, int wave, int lane, f4 *S, f4 &seg_dec) {
-  using Raw = typename Io::Raw;
-  Raw rq[4], rk[4], rv[4], rg[4];
-  uint32_t off[4];
-  bool ok[4];
-  chunk_rows(p, sq, c_begin, wave, lane, off, ok);
-  load_rows<Io>(p.g, sq, off, ok, rg);
-  load_rows<Io>(p.k, sq, off, ok, rk);
-  load_rows<Io>(p.v, sq, off, ok, rv);
-  if constexpr (kOut) load_rows<Io>(p.q, sq, off, ok, rq);
-  for (int c = c_begin; c < c_end; ++c) {
-    // the next chunk's rows are in flight while this chunk is processed
-    Raw nq[4], nk[4], nv[4], ng[4];
-    const bool more = c + 1 < c_end;
-    if (more) {
-      chunk_rows(p, sq, c + 1, wave, lane, off, ok);
-      load_rows<Io>(p.g, sq, off, ok, ng);
-      load_rows<Io>(p.k, sq, off, ok, nk);
-      load_rows<Io>(p.v, sq, off, ok, nv);
-      if constexpr (kOut) load_rows<Io>(p.q, sq, off, ok, nq);
-    }
-    op4<Op> qs[4], ks[4];
-    prep_local<Io, Op, kOut>(sm, rq, rk, rv, rg, wave, lane, qs, ks);
-    lds_sync();  // sub-block products visible
-    prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane);
-    if (!kOut && wave == 0 && lane < 16) {
-      f4 t[4];
-      sub_block_products(sm, lane, t);
-      seg_dec *= t[0] * t[1] * t[2] * t[3];
-    }
-    lds_sync();  // operand tiles visible
-    if constexpr (kOut) {
-      scores<Io, Op>(p, sq, sm, c, wave, lane);
-      lds_sync();  // score tiles visible
-      outputs<Io, Op>(p, sq, sm, c, wave, lane, S);
-    }
-    carry_state<Op>(sm, wave, lane, S);
-
-    if (more) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (kOut) rq[r] = nq[r];
-        rk[r] = nk[r];
-        rv[r] = nv[r];
-        rg[r] = ng[r];
-      }
-    }
-  }
+__device__ __forceinline__ void walk(const Params &p, int bh, Smem<Op> &sm, int c_begin, int c_end,
+                                     int wave, int lane, f4 *S, f4 &seg_dec) {
+  const Seq sq = seq_of<Io>(p, bh);
+  const size_t base = (size_t)bh * p.n_tok * kHead;
+  Rows<Io> x;
+  load_chunk<Io, kOut>(sq, c_begin, wave, lane, x);
+  for (int c = c_begin; c < c_end; ++c) chunk<Io, Op, kOut>(p, sq, base, sm, x, c, c_end, wave, lane, S, seg_dec);
 }
 
 __device__ __forceinline__ void store_state_rowmajor(float *dst, int wave, int lane, const f4 *S) {
@@ -608,11 +690,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / p.n_seg_grid;
   const int seg = blockIdx.x - bh * p.n_seg_grid;
-  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
   f4 S[4] = {};
   f4 sdec = {1.f, 1.f, 1.f, 1.f};
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, false>(p, sq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
+  walk<Io, Op, false>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
   const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
 #pragma unroll
   for (int x = 0; x < 16; ++x) p.agg[st + x * 64] = S[x >> 2][x & 3];
@@ -626,7 +707,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / p.n_seg;
   const int seg = blockIdx.x - bh * p.n_seg;
-  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
   f4 S[4] = {};
   if (p.prev) {
     const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
@@ -635,7 +715,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   }
   f4 unused = {};
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, true>(p, sq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
+  walk<Io, Op, true>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
 }
 
 // Boundary-state recurrence over segments, one thread per (sequence, state
@@ -709,7 +789,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   const int ticket = s_ticket, want = s_epoch + 1;
   const int seg = ticket / p.bh_count;  // segment-major: predecessors start earlier
   const int bh = ticket - seg * p.bh_count;
-  const Seq sq{p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh, (size_t)bh * p.n_tok * kHead};
   const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
   const size_t sbase = (size_t)bh * p.n_seg;
   const size_t lane_off = wave * 1024 + lane;
@@ -719,7 +798,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   if (seg + 1 < p.n_seg) {
     f4 A[4] = {};
     f4 sdec = {1.f, 1.f, 1.f, 1.f};
-    walk<Io, Op, false>(p, sq, sm, c0, c1, wave, lane, A, sdec);
+    walk<Io, Op, false>(p, bh, sm, c0, c1, wave, lane, A, sdec);
     float *dst = p.agg + (sbase + seg) * kStateElems + 16 * wave + (lane & 15);
 #pragma unroll
     for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead] = A[x >> 2][x & 3];
@@ -778,7 +857,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
   // 3. outputs of this segment; the last segment also yields the final state
   f4 unused = {};
-  walk<Io, Op, true>(p, sq, sm, c0, c1, wave, lane, S, unused);
+  walk<Io, Op, true>(p, bh, sm, c0, c1, wave, lane, S, unused);
   if (p.s_final && seg + 1 == p.n_seg)
     store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, S);
 

@@ -61,7 +61,7 @@ def test_plans():
     pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_SPLIT)
     assert not pl["fused"] and pl["seg_len"] * pl["n_seg"] >= 256
     pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=4)
-    assert pl["seg_len"] == 4 and pl["n_seg"] == 7
+    assert pl["seg_len"] == 4 and pl["n_seg"] == 7 and not pl["fused"]
     pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
     assert pl["seg_len"] == 1 and pl["n_seg"] == 1
     with pytest.raises(gla.GlaError):
