@@ -26,8 +26,8 @@
  *   No softmax and no q.k scale are applied (none is described).
  *
  *   Same article, section 架构: consecutive layers scan the patch grid
- *   left-to-right, right-to-left, top-to-bottom and bottom-to-top, and the
- *   grid arrangement is restored after each scan.  Reading used here
+ *   left-to-right, right-to-left, top-to-bottom and bottom-to-top, and each
+ *   layer hands on its outputs in grid arrangement.  Reading used here
  *   (the article gives no index formula):
  *     direction 0, L->R : row-major order, rows top to bottom;
  *     direction 1, R->L : the L->R sequence reversed (starts bottom-right);
