@@ -49,21 +49,29 @@ struct Shape {
   bool fused;
 };
 
-constexpr int kMaxFusedSegments = 24;  // longest aggregate chain one fused workgroup combines
+// Chunks per segment and launch structure for a shape.
+//  * split: about three resident workgroups per CU on 256 CUs; the boundary
+//    scan runs in its own kernel.
+//  * fused: segments of at most kMaxFusedChunks chunks (each chunk's outputs
+//    wait in registers for the state entering the segment); every segment
+//    reads the aggregates of all earlier segments of its sequence.
+// Automatic choice: fused while a sequence has at most kAutoFusedChunks
+// chunks.  Measured on MI355X the fused launch does not yet beat three
+// launches on any shape (combining predecessors costs one memory round trip per
+// few aggregates), so the threshold is 0 and the choice is always split.
+constexpr int kAutoFusedChunks = 0;
 
-// Chunks per segment and launch structure for a shape.  The fused launch reads
-// the aggregates of all earlier segments of its sequence, so it caps the
-// segment count; the three-launch path scans segments in a separate kernel.
-// Automatic choice: the three-launch path, which measures faster on every
-// shape tried (the fused launch walks each segment twice inside one kernel).
 void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
   const long long total = bh * n_chunk;
-  sh->fused = path == GTR_PATH_FUSED;
+  sh->fused = path == GTR_PATH_FUSED ||
+              (path == GTR_PATH_AUTO && n_chunk <= kAutoFusedChunks &&
+               chunks_per_segment <= gtr::kMaxFusedChunks);
   long long len = chunks_per_segment;
-  if (len <= 0) {
-    // about three resident workgroups per CU on 256 CUs
+  if (sh->fused) {
+    if (len <= 0) len = n_chunk <= 8 ? 1 : (n_chunk <= 32 ? 2 : 3);
+    len = std::min<long long>(len, gtr::kMaxFusedChunks);
+  } else if (len <= 0) {
     len = (total + 767) / 768;
-    if (sh->fused) len = std::max<long long>(len, (n_chunk + kMaxFusedSegments - 1) / kMaxFusedSegments);
     len = std::max<long long>(1, std::min<long long>(len, 32));
   }
   if (len > n_chunk) len = n_chunk;
@@ -153,23 +161,32 @@ int check_device_range(const void *p, size_t bytes, int device, const char *name
   return GTR_OK;
 }
 
+// Fused-path synchronisation words live at positions fixed by the allocation's
+// capacities, never by a call's shape: [header][cap_seqs control lines]
+// [cap_flags flags].  Control lines return to zero after every call and flags
+// only hold epochs, so any shape can follow any other on the same workspace.
 struct Workspace {
   void *data = nullptr;  // float32 aggregates and boundary states
   size_t data_bytes = 0;
-  int *sync = nullptr;   // fused-path control words and flags, zero-initialised
-  size_t sync_words = 0;
+  int *sync = nullptr;   // zero-initialised
+  size_t cap_seqs = 0, cap_flags = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(int device, hipStream_t stream, size_t bytes, size_t words, void **data,
-                  int **sync) {
+int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, size_t flags,
+                  void **data, int **sync, int **flag_words) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace &ws = g_ws[{device, stream}];
-  if (ws.data_bytes >= bytes && ws.sync_words >= words) {
+  const bool sync_ok = (seqs == 0 && flags == 0) || (ws.cap_seqs >= seqs && ws.cap_flags >= flags);
+  auto hand_out = [&] {
     *data = ws.data;
     *sync = ws.sync;
+    *flag_words = ws.sync ? ws.sync + gtr::kSyncHeader + ws.cap_seqs * gtr::kCtlStride : nullptr;
+  };
+  if (ws.data_bytes >= bytes && sync_ok) {
+    hand_out();
     return GTR_OK;
   }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -179,9 +196,9 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t words, vo
   }
   if (cs != hipStreamCaptureStatusNone)
     return fail(GTR_ERR_CAPTURE,
-                "workspace must grow (%zu -> %zu bytes, %zu -> %zu sync words) while the stream "
-                "is being captured; make one call of this shape before capturing",
-                ws.data_bytes, bytes, ws.sync_words, words);
+                "workspace must grow (%zu -> %zu bytes, %zu -> %zu sequences, %zu -> %zu flags) "
+                "while the stream is being captured; make one call of this shape before capturing",
+                ws.data_bytes, bytes, ws.cap_seqs, seqs, ws.cap_flags, flags);
   // Kernels queued earlier on this stream may still use the old buffers.
   if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
   if (ws.data_bytes < bytes) {
@@ -196,27 +213,28 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t words, vo
     }
     ws.data_bytes = want;
   }
-  if (ws.sync_words < words) {
+  if (!sync_ok) {
     if (ws.sync) (void)hipFree(ws.sync);
     ws.sync = nullptr;
-    ws.sync_words = 0;
-    const size_t want = words + words / 4;
-    if (hipMalloc(&ws.sync, want * sizeof(int)) != hipSuccess) {
+    const size_t cs = std::max(ws.cap_seqs, seqs + seqs / 4), cf = std::max(ws.cap_flags, flags + flags / 4);
+    ws.cap_seqs = ws.cap_flags = 0;
+    const size_t words = gtr::kSyncHeader + cs * gtr::kCtlStride + cf;
+    if (hipMalloc(&ws.sync, words * sizeof(int)) != hipSuccess) {
       (void)hipGetLastError();
       ws.sync = nullptr;
-      return fail(GTR_ERR_ALLOC, "hipMalloc of %zu sync words failed", want);
+      return fail(GTR_ERR_ALLOC, "hipMalloc of %zu sync words failed", words);
     }
     // synchronous clear, so that kernels on any stream see zeros
-    if (hipMemset(ws.sync, 0, want * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipMemset(ws.sync, 0, words * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(ws.sync);
       ws.sync = nullptr;
-      return fail(GTR_ERR_ALLOC, "clearing %zu sync words failed", want);
+      return fail(GTR_ERR_ALLOC, "clearing %zu sync words failed", words);
     }
-    ws.sync_words = want;
+    ws.cap_seqs = cs;
+    ws.cap_flags = cf;
   }
-  *data = ws.data;
-  *sync = ws.sync;
+  hand_out();
   return GTR_OK;
 }
 
@@ -327,17 +345,17 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   const bool need_ws = sh.fused || sh.n_seg > 1 || s0 || s_final;
   if (need_ws) {
     void *ws = nullptr;
-    int *sync = nullptr;
-    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.bh, sh.n_seg),
-                       sh.fused ? gtr::sync_words(sh.bh, sh.n_seg) : 0, &ws, &sync);
+    int *sync = nullptr, *flags = nullptr;
+    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.bh, sh.n_seg), sh.fused ? sh.bh : 0,
+                       sh.fused ? sh.bh * sh.n_seg : 0, &ws, &sync, &flags);
     if (rc != GTR_OK) return rc;
     float *f = static_cast<float *>(ws);
     const size_t st = (size_t)sh.bh * sh.n_seg * gtr::kStateElems;
     a.agg = f;
     a.prev = f + st;
     a.agg_dec = f + 2 * st;
-    a.ctl = sync;
-    a.flags = sync ? sync + gtr::kCtlWords : nullptr;
+    a.sync = sync;
+    a.flags = flags;
   }
   const int err = gtr::launch_gla(a);
   if (err != (int)hipSuccess)

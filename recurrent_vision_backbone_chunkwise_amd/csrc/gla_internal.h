@@ -10,6 +10,7 @@ namespace gtr {
 constexpr int kChunk = 64;   // tokens per chunk (the pages' operator uses 64)
 constexpr int kHead = 64;    // d_k = d_v handled by this build
 constexpr int kStateElems = kHead * kHead;
+constexpr int kMaxFusedChunks = 3;  // chunks per segment of the one-launch path (outputs held in registers)
 
 struct LaunchArgs {
   const void *q, *k, *v, *g;
@@ -26,24 +27,26 @@ struct LaunchArgs {
   float *agg;        // [bh][n_seg][4096] segment state contributions
   float *agg_dec;   // [bh][n_seg][64]   segment decay factor per key dim
   float *prev;       // [bh][n_seg][4096] state entering each segment
-  int *flags;        // [bh][n_seg] fused path: aggregate-published flags (zeroed at allocation)
-  int *ctl;          // fused path: ticket, done, epoch, error words (zeroed at allocation)
+  int *sync;         // fused path: header + per-sequence control lines (zeroed at allocation)
+  int *flags;        // [bh][n_seg] fused path: aggregate-published flags, after the control lines
   const float *s0;   // user initial state, row-major [bh][64][64], nullable
   float *s_final;    // user final state, row-major [bh][64][64], nullable
   bool fused;        // one launch (gla_fused) instead of three
   hipStream_t stream;
 };
 
-constexpr int kCtlWords = 64;  // control block (only the first 4 words are used)
+constexpr int kSyncHeader = 32;  // fused-path header words (epoch, sequences done, error)
+constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (ticket, done)
 
 // Float workspace bytes for (bh, n_seg): agg, prev and agg_dec.
 inline size_t workspace_bytes(size_t bh, size_t n_seg) {
   return bh * n_seg * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
-// Synchronisation words for the fused path: control block + one flag per segment.
-// They live in their own zero-initialised allocation and only ever hold epoch
-// numbers, so a flag can never be confused with left-over data.
-inline size_t sync_words(size_t bh, size_t n_seg) { return kCtlWords + bh * n_seg; }
+// Synchronisation words for the fused path: a control line per sequence, then
+// one flag per segment.  They live in their own zero-initialised allocation;
+// flags only ever hold epoch numbers, so a flag can never be confused with
+// left-over data.
+inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (kCtlStride + n_seg); }
 
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);

@@ -308,12 +308,11 @@ __device__ __forceinline__ void rows4(const Seq &sq, int t0, uint32_t *off) {
 // Gate factors below are products of alpha = exp(log_gate) over token ranges of
 // the chunk; with E the log2 cumulative gate from the chunk start they equal
 // the exponentials named in the comments.
-template <typename Op> struct Smem {
+template <typename Op, int NQ> struct Smem {
   static constexpr int LD = OpT<Op>::LD;
   static constexpr int LDT = OpT<Op>::LDT;
   Op qs[kChunk * LD];   // q 2^(E - E_end(a-1))     [token][dim]
-  Op qh[kChunk * LD];   // q 2^E
-  Op ks[kChunk * LD];   // k 2^(E_end(b) - E)
+  Op ks[kChunk * LD];   // k 2^(E_end(b) - E)       (qs and ks are adjacent: see gla_fused)
   Op kb[kChunk * LDT];  // k 2^(E_last - E)
   Op vv[kChunk * LDT];  // v
   Op pt[10 * 256];      // score tiles P^T, 4 values per lane, lane-ordered
@@ -321,7 +320,11 @@ template <typename Op> struct Smem {
   Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
   Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
   float dec[kHead];     // 2^E_last: decay of the state across the chunk
-  uint32_t rowoff[kChunk];  // byte offset of each token's row (kOob past the end)
+  // One slot per chunk whose outputs wait for the state entering the segment
+  // (NQ = 1 when outputs are stored as each chunk completes).
+  uint32_t rowoff[NQ][kChunk];  // byte offset of each token's row (kOob past the end)
+  float dcum[NQ][kHead];        // decay from the segment start to the chunk start
+  Op qh[NQ][kChunk * LD];       // q 2^E
 };
 
 // ------------------------------------------------------------------- params
@@ -335,11 +338,18 @@ struct Params {
   const float *prev;       // [bh][n_seg][4096] register order (separate-launch path)
   const float *s0;         // user initial state, row-major [bh][64][64], nullable
   float *s_final;          // user final state, row-major, nullable
+  int *sync;               // fused path: header, per-sequence control lines (kSync* words)
   int *flags;              // [bh][n_seg] fused path: segment aggregate published
-  int *ctl;                // fused path: [0] ticket, [1] done, [2] epoch, [3] error
 };
 
-enum : int { kCtlTicket = 0, kCtlDone = 1, kCtlEpoch = 2, kCtlError = 3 };
+// Fused-path synchronisation words.  Header: the epoch (number of completed
+// fused calls on this workspace), the count of sequences finished in the
+// current call, and an error word (-1 after a wait gave up).  Per sequence: its
+// ticket and done counters.  After every call all words other than the epoch
+// and the flags are back at 0 (or -1); flags hold epochs, all below the next
+// call's epoch + 1, whatever shape wrote them.
+enum : int { kSyncEpoch = 0, kSyncSeqDone = 1, kSyncError = 2 };
+enum : int { kCtlTicket = 0, kCtlDone = 1 };
 
 template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int bh) {
   return make_seq<Io>(p.q, p.k, p.v, p.g, p.out, bh, p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh);
@@ -399,11 +409,11 @@ __device__ __forceinline__ void row_products(float x, int g, float &before, floa
 // sub-block scale the inputs: qs = q * (product of alpha from the sub-block
 // start through the token), ks = k * (product of alpha after the token to the
 // sub-block end).  qs, ks and v go to LDS, the sub-block product to sm.tot, the
-// row offsets to sm.rowoff.  One exp2 per element; the rest are multiplications
+// row offsets to sm.rowoff[slot].  One exp2 per element; the rest are multiplications
 // and cross-row swaps.
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void prep_local(Smem<Op> &sm, const Rows<Io> &x, int wave, int lane,
-                                           op4<Op> *qs, op4<Op> *ks) {
+template <class Io, typename Op, bool kOut, int NQ>
+__device__ __forceinline__ void prep_local(Smem<Op, NQ> &sm, const Rows<Io> &x, int wave, int lane,
+                                           int slot, op4<Op> *qs, op4<Op> *ks) {
   constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
   const int g = lane >> 4, dq = lane & 15;
   f4 a[4];
@@ -436,13 +446,13 @@ __device__ __forceinline__ void prep_local(Smem<Op> &sm, const Rows<Io> &x, int 
   if (g == 0) *reinterpret_cast<f4 *>(&sm.tot[wave * kHead + 4 * dq]) = all;
   if (kOut && dq == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.rowoff[16 * wave + 4 * g + r] = x.off[r];
+    for (int r = 0; r < 4; ++r) sm.rowoff[slot][16 * wave + 4 * g + r] = x.off[r];
   }
 }
 
 // Sub-block products t_0..t_3 of this lane's dims.
-template <typename Op>
-__device__ __forceinline__ void sub_block_products(const Smem<Op> &sm, int lane, f4 *t) {
+template <typename Op, int NQ>
+__device__ __forceinline__ void sub_block_products(const Smem<Op, NQ> &sm, int lane, f4 *t) {
   const int dq = lane & 15;
 #pragma unroll
   for (int a = 0; a < 4; ++a) t[a] = *reinterpret_cast<const f4 *>(&sm.tot[a * kHead + 4 * dq]);
@@ -452,9 +462,9 @@ __device__ __forceinline__ void sub_block_products(const Smem<Op> &sm, int lane,
 // kb = ks * (product from the sub-block end to the chunk end), qh = qs *
 // (product from the chunk start to the sub-block start), and the per-dim
 // factor vectors.
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void prep_chunk(Smem<Op> &sm, const op4<Op> *qs, const op4<Op> *ks,
-                                           int wave, int lane) {
+template <class Io, typename Op, bool kOut, int NQ>
+__device__ __forceinline__ void prep_chunk(Smem<Op, NQ> &sm, const op4<Op> *qs, const op4<Op> *ks,
+                                           int wave, int lane, int slot) {
   constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
   const int g = lane >> 4, dq = lane & 15;
   const f4 one = {1.f, 1.f, 1.f, 1.f};
@@ -469,7 +479,7 @@ __device__ __forceinline__ void prep_chunk(Smem<Op> &sm, const op4<Op> *qs, cons
   for (int r = 0; r < 4; ++r) {
     const int tau = 16 * wave + 4 * g + r;
     *reinterpret_cast<op4<Op> *>(&sm.kb[tau * LDT + 4 * dq]) = ks[r] * fkh;
-    if constexpr (kOut) *reinterpret_cast<op4<Op> *>(&sm.qh[tau * LD + 4 * dq]) = qs[r] * fqh;
+    if constexpr (kOut) *reinterpret_cast<op4<Op> *>(&sm.qh[slot][tau * LD + 4 * dq]) = qs[r] * fqh;
   }
   if (g == 0) {
     if (wave == 0) {
@@ -525,8 +535,8 @@ __device__ f4 exact_diag(const Params &p, const Seq &sq, size_t base, int c, int
 }
 
 // Off-diagonal score tile (a, b), b < a: P^T[sigma][tau] = ks_sigma . (qs_tau * factor).
-template <typename Op>
-__device__ __forceinline__ void off_tile(Smem<Op> &sm, int a, int b, int lane) {
+template <typename Op, int NQ>
+__device__ __forceinline__ void off_tile(Smem<Op, NQ> &sm, int a, int b, int lane) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
   const int cvec = (a == 2) ? 0 : (b == 0 ? 1 : 2);  // used when b < a-1
@@ -544,8 +554,8 @@ __device__ __forceinline__ void off_tile(Smem<Op> &sm, int a, int b, int lane) {
 // Score tiles P^T[sigma][tau] of this chunk into sm.pt (lower block triangle
 // only).  Wave w forms the diagonal tile (w, w) and the off-diagonal tiles
 // (1,0),(2,1) | (2,0),(3,2) | (3,0) | (3,1).
-template <class Io, typename Op>
-__device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t base, Smem<Op> &sm,
+template <class Io, typename Op, int NQ>
+__device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t base, Smem<Op, NQ> &sm,
                                        int c, int wave, int lane) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
@@ -581,10 +591,19 @@ __device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t ba
   }
 }
 
-// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T, stored at the grid positions.
-template <class Io, typename Op>
-__device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op> &sm, int wave, int lane,
-                                        const op8<Op> *vf, const uint32_t *oo, const f4 *S) {
+// How a walk treats each chunk.
+enum : int {
+  kAgg = 0,    // state only: no queries, no outputs
+  kStore = 1,  // outputs formed with the state carried so far and stored
+  kKeep = 2,   // outputs formed with the state carried so far and kept in registers
+};
+
+// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T: stored at the grid
+// positions (kStore) or kept in keep[tt] (kKeep).
+template <class Io, typename Op, int kMode, int NQ>
+__device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op, NQ> &sm, int wave, int lane,
+                                        int slot, const op8<Op> *vf, const uint32_t *oo, const f4 *S,
+                                        f4 *keep) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
   op8<Op> sf[2];
@@ -604,14 +623,17 @@ __device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op> &sm, int w
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      acc = mma(sf[kb], frag_row<Op>(&sm.qh[(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
-    Io::store4(sq.o, oo[tt] + col, acc);
+      acc = mma(sf[kb], frag_row<Op>(&sm.qh[slot][(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
+    if constexpr (kMode == kKeep)
+      keep[tt] = acc;
+    else
+      Io::store4(sq.o, oo[tt] + col, acc);
   }
 }
 
 // S <- diag(2^E_last) S + (k 2^(E_last-E))^T V for this wave's value columns.
-template <typename Op>
-__device__ __forceinline__ void carry_state(const Smem<Op> &sm, int lane, const op8<Op> *vf, f4 *S) {
+template <typename Op, int NQ>
+__device__ __forceinline__ void carry_state(const Smem<Op, NQ> &sm, int lane, const op8<Op> *vf, f4 *S) {
   const int g = lane >> 4;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -621,79 +643,82 @@ __device__ __forceinline__ void carry_state(const Smem<Op> &sm, int lane, const 
   }
 }
 
-// One chunk.  Barriers: (1) sub-block products and row offsets visible, (2)
-// operand tiles visible, (3) score tiles visible.  Everything a wave reads from
-// LDS after the last barrier of a chunk (pt, qh, kb, dec) is written only after
-// the first barrier of the next chunk, which no wave passes before every wave has
-// finished this chunk; v and the output row offsets, which the next chunk
-// overwrites before its first barrier, are read into registers before the
-// second one.  The next chunk's rows are loaded into x as soon as this chunk's
-// have gone to LDS, and arrive while the rest of this chunk computes.
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t base, Smem<Op> &sm,
-                                      Rows<Io> &x, int c, int c_end, int wave, int lane, f4 *S,
-                                      f4 &seg_dec) {
+// One chunk, using LDS slot `slot` for what must outlive it.  Barriers: (1)
+// sub-block products and row offsets visible, (2) operand tiles visible, (3)
+// score tiles visible.  Everything a wave reads from LDS after the last barrier
+// of a chunk (pt, qh, kb, dec) is written only after the first barrier of the
+// next chunk, which no wave passes before every wave has finished this chunk;
+// v and the output row offsets, which the next chunk overwrites before its
+// first barrier, are read into registers before the second one.  The next
+// chunk's rows are loaded into x as soon as this chunk's have gone to LDS, and
+// arrive while the rest of this chunk computes.  seg_dec (wave 0, lanes < 16,
+// dims 4*lane..+3) accumulates the chunk decays; kKeep also records the decay
+// from the segment start to this chunk in sm.dcum[slot].
+template <class Io, typename Op, int kMode, int NQ>
+__device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t base, Smem<Op, NQ> &sm,
+                                      Rows<Io> &x, int c, int c_end, int wave, int lane, int slot,
+                                      f4 *S, f4 &seg_dec, f4 *keep) {
+  constexpr bool kOut = kMode != kAgg;
   op4<Op> qs[4], ks[4];
-  prep_local<Io, Op, kOut>(sm, x, wave, lane, qs, ks);
+  prep_local<Io, Op, kOut>(sm, x, wave, lane, slot, qs, ks);
   if (c + 1 < c_end) load_chunk<Io, kOut>(sq, c + 1, wave, lane, x);
   lds_sync();
-  prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane);
+  prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, slot);
   op8<Op> vf[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
   uint32_t oo[4];
-  if constexpr (kOut) {
+  if constexpr (kMode == kStore) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) oo[tt] = sm.rowoff[16 * tt + (lane & 15)];
+    for (int tt = 0; tt < 4; ++tt) oo[tt] = sm.rowoff[slot][16 * tt + (lane & 15)];
   }
-  if (!kOut && wave == 0 && lane < 16) {
+  if (kMode != kStore && wave == 0 && lane < 16) {
     f4 t[4];
     sub_block_products(sm, lane, t);
+    if constexpr (kMode == kKeep) *reinterpret_cast<f4 *>(&sm.dcum[slot][4 * lane]) = seg_dec;
     seg_dec *= t[0] * t[1] * t[2] * t[3];
   }
   lds_sync();
   if constexpr (kOut) {
     scores<Io, Op>(p, sq, base, sm, c, wave, lane);
     lds_sync();
-    outputs<Io, Op>(sq, sm, wave, lane, vf, oo, S);
+    outputs<Io, Op, kMode>(sq, sm, wave, lane, slot, vf, oo, S, keep);
   }
   carry_state<Op>(sm, lane, vf, S);
 }
 
-// Walks chunks [c_begin, c_end) of sequence bh, carrying S.  kOut: writes the
-// outputs (S must hold the state entering the first chunk); otherwise only
-// carries S (from zero: the segment's own aggregate) and multiplies the chunk
-// decays into seg_dec (wave 0, lane < 16 holds dims 4*lane..4*lane+3).
-template <class Io, typename Op, bool kOut>
-__device__ __forceinline__ void walk(const Params &p, int bh, Smem<Op> &sm, int c_begin, int c_end,
+// Walks chunks [c_begin, c_end) of sequence bh, carrying S (kAgg or kStore):
+// kStore writes the outputs (S must hold the state entering the first chunk);
+// kAgg only carries S (from zero: the segment's own aggregate) and multiplies
+// the chunk decays into seg_dec.
+template <class Io, typename Op, int kMode, int NQ>
+__device__ __forceinline__ void walk(const Params &p, int bh, Smem<Op, NQ> &sm, int c_begin, int c_end,
                                      int wave, int lane, f4 *S, f4 &seg_dec) {
+  static_assert(kMode != kKeep, "kKeep walks are unrolled by their kernel");
   const Seq sq = seq_of<Io>(p, bh);
   const size_t base = (size_t)bh * p.n_tok * kHead;
   Rows<Io> x;
-  load_chunk<Io, kOut>(sq, c_begin, wave, lane, x);
-  for (int c = c_begin; c < c_end; ++c) chunk<Io, Op, kOut>(p, sq, base, sm, x, c, c_end, wave, lane, S, seg_dec);
+  load_chunk<Io, kMode != kAgg>(sq, c_begin, wave, lane, x);
+  for (int c = c_begin; c < c_end; ++c)
+    chunk<Io, Op, kMode>(p, sq, base, sm, x, c, c_end, wave, lane, 0, S, seg_dec, nullptr);
 }
 
 __device__ __forceinline__ void store_state_rowmajor(float *dst, int wave, int lane, const f4 *S) {
 #pragma unroll
   for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead + 16 * wave + (lane & 15)] = S[x >> 2][x & 3];
 }
-__device__ __forceinline__ void load_state_rowmajor(const float *src, int wave, int lane, f4 *S) {
-#pragma unroll
-  for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = src[state_i(x, lane) * kHead + 16 * wave + (lane & 15)];
-}
 
 // ------------------------------------------------------------------ kernels
 template <class Io, typename Op>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_state(Params p) {
-  __shared__ Smem<Op> sm;
+  __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / p.n_seg_grid;
   const int seg = blockIdx.x - bh * p.n_seg_grid;
   f4 S[4] = {};
   f4 sdec = {1.f, 1.f, 1.f, 1.f};
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, false>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
+  walk<Io, Op, kAgg>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
   const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
 #pragma unroll
   for (int x = 0; x < 16; ++x) p.agg[st + x * 64] = S[x >> 2][x & 3];
@@ -703,7 +728,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 template <class Io, typename Op>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_out(Params p) {
-  __shared__ Smem<Op> sm;
+  __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / p.n_seg;
   const int seg = blockIdx.x - bh * p.n_seg;
@@ -715,7 +740,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
   }
   f4 unused = {};
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, true>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
+  walk<Io, Op, kStore>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
 }
 
 // Boundary-state recurrence over segments, one thread per (sequence, state
@@ -756,84 +781,126 @@ __global__ __launch_bounds__(kThreads) void gla_seg_scan(const float *agg, const
   if (s_final) s_final[(size_t)bh * kStateElems + i * kHead + j] = s;
 }
 
-// Publication between workgroups (possibly on different XCDs, whose L2 caches
-// are not coherent with each other): the producer's waves each issue an
-// agent-scope release fence after their payload stores, then one thread sets
-// the flag; the consumer polls the flag with relaxed agent-scope loads (no
-// cache maintenance per poll), and after seeing it every wave issues one
-// agent-scope acquire fence before reading the payload.
+// Publication between workgroups, which may sit on different XCDs whose L2
+// caches are not kept coherent with each other.  Every word that crosses
+// workgroups (aggregate, decay, flag) is written and read with agent-scope
+// atomic accesses, which the compiler emits as device-scope (sc1) stores and
+// loads: a store completes only once it is visible at device scope, and a
+// load never returns a copy that is stale at that scope.  The producer waits
+// for its payload stores to complete (vmcnt), the workgroup synchronises, and
+// then one thread stores the flag; the consumer issues its payload loads only
+// after it has read the flag.  No cache-wide writeback or invalidation is
+// needed, as it would be for plain stores and loads behind release/acquire
+// fences.
+__device__ __forceinline__ void store_shared(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's stores have completed.
+__device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Bounded wait for a flag value; records a timeout in ctl[kCtlError].
-__device__ __forceinline__ void wait_flag(const Params &p, const int *f, int want) {
+// Bounded wait for a flag value; records a timeout in the error word.
+__device__ __forceinline__ void wait_flag(int *sync, const int *f, int want) {
   int spins = 0;
   while (__hip_atomic_load(const_cast<int *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
-    __builtin_amdgcn_s_sleep(8);
+    __builtin_amdgcn_s_sleep(2);
     if (++spins > kSpinLimit) {
-      __hip_atomic_store(p.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + kSyncError, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
   }
 }
 
-// One launch: segment aggregate -> publish -> combine predecessors -> outputs.
-template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_fused(Params p) {
-  __shared__ Smem<Op> sm;
+// One launch, one walk.  A workgroup takes a segment (at most kSeg chunks) in
+// start order and:
+//   1. walks it from a zero state, keeping each chunk's outputs in registers
+//      (intra-segment part: scores plus the state carried inside the segment)
+//      and ending with the segment's own aggregate A and decay D;
+//   2. publishes (A, D) for the segments after it;
+//   3. combines s0 and the aggregates of the segments before it into S_prev,
+//      the state entering the segment;
+//   4. adds each chunk's share of S_prev, (q 2^E * Dcum) S_prev with Dcum the
+//      decay from the segment start to the chunk, and stores the outputs.
+// Inputs are read from HBM once.
+template <class Io, typename Op, int kSeg>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg == 1 ? 3 : 2, kSeg == 1 ? 3 : 2))) void gla_fused(Params p) {
+  __shared__ Smem<Op, kSeg> sm;
   __shared__ int s_ticket, s_epoch;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  // The sequence is fixed by the block index; the segment is the order in which
+  // this sequence's workgroups start (a per-sequence ticket), so every segment a
+  // workgroup waits for belongs to a workgroup that is already running.
+  const int bh = blockIdx.x % p.bh_count;
+  int *ctl = p.sync + kSyncHeader + (size_t)bh * kCtlStride;
   if (tid == 0) {
-    s_ticket = atomicAdd(p.ctl + kCtlTicket, 1);
-    s_epoch = __hip_atomic_load(p.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ticket = __hip_atomic_fetch_add(ctl + kCtlTicket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_epoch = __hip_atomic_load(p.sync + kSyncEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  const int ticket = s_ticket, want = s_epoch + 1;
-  const int seg = ticket / p.bh_count;  // segment-major: predecessors start earlier
-  const int bh = ticket - seg * p.bh_count;
+  const int seg = s_ticket, want = s_epoch + 1;
   const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
   const size_t sbase = (size_t)bh * p.n_seg;
-  const size_t lane_off = wave * 1024 + lane;
+  const Seq sq = seq_of<Io>(p, bh);
+  const size_t base = (size_t)bh * p.n_tok * kHead;
 
-  // 1. this segment's own aggregate (not needed for the last segment), stored
-  //    row-major [i][j] so that combining reads whole rows.
-  if (seg + 1 < p.n_seg) {
-    f4 A[4] = {};
-    f4 sdec = {1.f, 1.f, 1.f, 1.f};
-    walk<Io, Op, false>(p, bh, sm, c0, c1, wave, lane, A, sdec);
-    float *dst = p.agg + (sbase + seg) * kStateElems + 16 * wave + (lane & 15);
+  // 1. the segment from a zero state
+  f4 keep[kSeg][4];
+  f4 L[4] = {};
+  f4 sdec = {1.f, 1.f, 1.f, 1.f};
+  {
+    Rows<Io> x;
+    load_chunk<Io, true>(sq, c0, wave, lane, x);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead] = A[x >> 2][x & 3];
-    if (wave == 0 && lane < 16)
-      *reinterpret_cast<f4 *>(&p.agg_dec[(sbase + seg) * kHead + 4 * lane]) = sdec;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's payload is visible ...
-    __syncthreads();                                     // ... for every wave ...
-    if (tid == 0)                                        // ... before the flag is raised
+    for (int j = 0; j < kSeg; ++j)
+      if (c0 + j < c1) chunk<Io, Op, kKeep>(p, sq, base, sm, x, c0 + j, c1, wave, lane, j, L, sdec, keep[j]);
+  }
+  // decay across the whole segment, read in step 5; tot is not read after a
+  // chunk's last barrier, so wave 0 may overwrite it while others finish
+  float *segdec = sm.tot;
+  if (wave == 0 && lane < 16) *reinterpret_cast<f4 *>(&segdec[4 * lane]) = sdec;
+
+  // 2. publish the aggregate (the last segment has no successor), row-major [i][j]
+  if (seg + 1 < p.n_seg) {
+    float *dst = p.agg + (sbase + seg) * kStateElems + 16 * wave + l16;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) store_shared(dst + state_i(x, lane) * kHead, L[x >> 2][x & 3]);
+    if (wave == 0 && lane < 16) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) store_shared(&p.agg_dec[(sbase + seg) * kHead + 4 * lane + d], sdec[d]);
+    }
+    stores_complete();  // this wave's payload is visible at device scope ...
+    __syncthreads();    // ... for every wave ...
+    if (tid == 0)       // ... before the flag is raised
       __hip_atomic_store(p.flags + sbase + seg, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // 2. state entering this segment: s0 carried over the aggregates of segments
-  //    0..seg-1.  Wave w combines rows [16w, 16w+16), lane l column l, so every
-  //    load reads one contiguous 256-byte row; the result goes through LDS (the
-  //    operand tiles are idle here) into the register layout of the output walk.
+  // 3. S_prev: s0 carried over the aggregates of segments 0..seg-1.  Wave w
+  //    combines rows [16w, 16w+16), lane l column l, so every load reads one
+  //    contiguous 256-byte row; the result goes through LDS (qs and ks, idle
+  //    now) into the register layout.
+  const bool have_prev = seg > 0 || p.s0 != nullptr;
   f4 S[4] = {};
-  if (seg > 0 || p.s0) {
+  if (have_prev) {
     float X[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       X[r] = p.s0 ? p.s0[(size_t)bh * kStateElems + (16 * wave + r) * kHead + lane] : 0.f;
-    constexpr int kBatch = 6;
+    constexpr int kBatch = 4;
     for (int j0 = 0; j0 < seg; j0 += kBatch) {
       const int nb = min(kBatch, seg - j0);
-      if (tid < nb) wait_flag(p, p.flags + sbase + j0 + tid, want);
+      if (tid < nb) wait_flag(p.sync, p.flags + sbase + j0 + tid, want);
       __syncthreads();  // the flags seen by one wave hold for the whole workgroup
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       float av[kBatch][16], dv[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (u < nb) {
           const float *src = p.agg + (sbase + j0 + u) * kStateElems + 16 * wave * kHead + lane;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) av[u][r] = src[r * kHead];
-          dv[u] = p.agg_dec[(sbase + j0 + u) * kHead + 16 * wave + (lane & 15)];
+          for (int r = 0; r < 16; ++r) av[u][r] = load_shared(src + r * kHead);
+          dv[u] = load_shared(p.agg_dec + (sbase + j0 + u) * kHead + 16 * wave + l16);
         }
       }
 #pragma unroll
@@ -844,32 +911,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         }
       }
     }
-    float *xs = reinterpret_cast<float *>(sm.qs);  // 64 x 68 floats span qs and qh
+    float *xs = reinterpret_cast<float *>(sm.qs);
     constexpr int kLdX = 68;
-    static_assert(sizeof(sm.qs) + sizeof(sm.qh) >= kChunk * kLdX * sizeof(float), "xs overflow");
+    static_assert(sizeof(sm.qs) + sizeof(sm.ks) >= kChunk * kLdX * sizeof(float),
+                  "xs must fit in qs and ks, which are adjacent");
 #pragma unroll
     for (int r = 0; r < 16; ++r) xs[(16 * wave + r) * kLdX + lane] = X[r];
     __syncthreads();
 #pragma unroll
-    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = xs[state_i(x, lane) * kLdX + 16 * wave + (lane & 15)];
-    __syncthreads();  // the output walk overwrites this LDS
+    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = xs[state_i(x, lane) * kLdX + 16 * wave + l16];
   }
 
-  // 3. outputs of this segment; the last segment also yields the final state
-  f4 unused = {};
-  walk<Io, Op, true>(p, bh, sm, c0, c1, wave, lane, S, unused);
-  if (p.s_final && seg + 1 == p.n_seg)
-    store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, S);
+  // 4. add each chunk's share of S_prev and store
+  const uint32_t col = (16 * wave + 4 * g) * sizeof(typename Io::T);
+  constexpr int LD = OpT<Op>::LD;
+#pragma unroll
+  for (int j = 0; j < kSeg; ++j) {
+    if (c0 + j >= c1) break;
+    if (have_prev) {
+      op8<Op> sf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]);
+        const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]);
+        sf[kb] = cat(to4<Op>(S[2 * kb] * d0), to4<Op>(S[2 * kb + 1] * d1));
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) Io::store4(sq.o, sm.rowoff[j][16 * tt + l16] + col, keep[j][tt]);
+  }
 
-  // 4. the last workgroup to finish resets the ticket and done counters and
-  //    advances the epoch, so the next call on this workspace starts clean.
-  __syncthreads();
+  // 5. the last segment also yields the final state: D S_prev + A
+  if (p.s_final && seg + 1 == p.n_seg) {
+    __syncthreads();  // segdec visible
+#pragma unroll
+    for (int it = 0; it < 4; ++it) L[it] += *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
+    store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, L);
+  }
+
+  // 6. a sequence's last workgroup resets its ticket and done counters; the
+  //    last sequence to finish resets the sequence count and advances the
+  //    epoch, so the next call on this workspace (ordered after this kernel by
+  //    the stream) starts clean.
   if (tid == 0) {
-    const int total = p.bh_count * p.n_seg;
-    if (atomicAdd(p.ctl + kCtlDone, 1) == total - 1) {
-      __hip_atomic_store(p.ctl + kCtlTicket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctl + kCtlDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctl + kCtlEpoch, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(ctl + kCtlDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.n_seg - 1) {
+      __hip_atomic_store(ctl + kCtlTicket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctl + kCtlDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(p.sync + kSyncSeqDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          p.bh_count - 1) {
+        __hip_atomic_store(p.sync + kSyncSeqDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.sync + kSyncEpoch, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -892,10 +989,17 @@ int launch_typed(const LaunchArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.n_chunk = a.n_chunk; p.seg_len = a.seg_len; p.n_seg = a.n_seg; p.n_seg_grid = a.n_seg;
   p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
-  p.flags = a.flags; p.ctl = a.ctl;
+  p.flags = a.flags; p.sync = a.sync;
   const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
   if (a.fused) {
-    launch(kKernelFused, gla_fused<Io, Op>, n_blocks, a.stream, p);
+    if (a.seg_len <= 1)
+      launch(kKernelFused, gla_fused<Io, Op, 1>, n_blocks, a.stream, p);
+    else if (a.seg_len == 2)
+      launch(kKernelFused, gla_fused<Io, Op, 2>, n_blocks, a.stream, p);
+    else if (a.seg_len == 3)
+      launch(kKernelFused, gla_fused<Io, Op, 3>, n_blocks, a.stream, p);
+    else
+      return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
     return (int)hipGetLastError();
   }
   const bool need_scan = a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr;

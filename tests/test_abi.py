@@ -48,20 +48,30 @@ def test_version_and_sizes():
     fused = gla.GTR_PATH_FUSED
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
-        6 * 25 * (2 * 4096 + 64) * 4 + (64 + 6 * 25) * 4
+        6 * 25 * (2 * 4096 + 64) * 4 + (32 + 6 * (32 + 25)) * 4
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 0, 0) == 0
     assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0, 0) == 0
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 0, 3) == 0
 
 
 def test_plans():
-    # 128x128 grid = 256 chunks per sequence: the fused path caps segments per sequence
+    # one launch caps segments at 3 chunks; the automatic choice is three launches
     pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_FUSED)
-    assert pl["fused"] and pl["n_seg"] <= 24 and pl["seg_len"] * pl["n_seg"] >= 256
+    assert pl["fused"] and pl["seg_len"] == 3 and pl["n_seg"] == 86
+    pl = gla.gtr_gla_plan(1, 16, 128, 128, chunks_per_segment=9, path=gla.GTR_PATH_FUSED)
+    assert pl["fused"] and pl["seg_len"] == 3
+    pl = gla.gtr_gla_plan(1, 16, 128, 128)
+    assert not pl["fused"] and pl["seg_len"] * pl["n_seg"] >= 256
     pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_SPLIT)
     assert not pl["fused"] and pl["seg_len"] * pl["n_seg"] >= 256
+    pl = gla.gtr_gla_plan(1, 6, 40, 40, path=gla.GTR_PATH_FUSED)
+    assert pl["fused"] and pl["seg_len"] == 2 and pl["n_seg"] == 13
+    pl = gla.gtr_gla_plan(1, 6, 40, 40)
+    assert not pl["fused"]
     pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=4)
     assert pl["seg_len"] == 4 and pl["n_seg"] == 7 and not pl["fused"]
+    pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=3, path=gla.GTR_PATH_FUSED)
+    assert pl["seg_len"] == 3 and pl["n_seg"] == 9 and pl["fused"]
     pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
     assert pl["seg_len"] == 1 and pl["n_seg"] == 1
     with pytest.raises(gla.GlaError):

@@ -102,20 +102,35 @@ def test_unit_gate_long_sequence():
 
 # ---- initial / final state -----------------------------------------------------------------
 
+@pytest.mark.parametrize("seg", [1, 3])
 @pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_initial_and_final_state(dtype, path):
+def test_initial_and_final_state(dtype, path, seg):
     B, H, gh, gw = 1, 3, 11, 13
     q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, dtype, "light", seed=8)
     s0 = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(9)) * 0.5
     for d in range(4):
-        note(f"state dir={d} dtype={dtype}")
-        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1,
+        note(f"state dir={d} dtype={dtype} seg={seg}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg,
                         path=PATHS[path])
         ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
         assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
         es = parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")
         assert es["ok"], es
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("grid", [(8, 8), (11, 13), (7, 9)], ids=lambda g: f"{g[0]}x{g[1]}")
+def test_final_state_from_zero(grid, path):
+    """Final state with no initial state, including a single segment."""
+    gh, gw = grid
+    q, k, v, g = gla_inputs.make_inputs(1, 2, gh, gw, 64, 64, "f16", "light", seed=12)
+    for seg in (1, 3):
+        note(f"final state {gh}x{gw} seg={seg} path={path}")
+        y, sf = gpu_run(q, k, v, g, 1, want_state=True, chunks_per_segment=seg, path=PATHS[path])
+        ref, sref = oracle.gla_forward(q, k, v, g, 1, want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, "f16")["ok"]
+        assert parity_errors(sf.double().cpu().numpy(), sref, "f16")["ok"]
 
 
 def test_split_sequence_equals_whole():
