@@ -50,8 +50,8 @@ struct Shape {
 };
 
 // Chunks per segment and launch structure for a shape.
-//  * split: about three resident workgroups per CU on 256 CUs; the boundary
-//    scan runs in its own kernel.
+//  * split: the length split_segment_length picks; the boundary scan runs in
+//    its own kernel.
 //  * fused: segments of at most kMaxFusedChunks chunks (each chunk's outputs
 //    wait in registers for the state entering the segment); every segment
 //    reads the aggregates of all earlier segments of its sequence.
@@ -61,8 +61,32 @@ struct Shape {
 // few aggregates), so the threshold is 0 and the choice is always split.
 constexpr int kAutoFusedChunks = 0;
 
+// Segment length of the three-launch path.  Each CU walks its workgroups'
+// chunks, two workgroups already saturate it and one alone runs about 1.35x
+// slower per chunk (measured on MI355X), so the cost of a length s is the chunk
+// load of the busiest CU in the output kernel, half that for the state kernel
+// (which moves 3/5 of the bytes and skips the last segment), plus the
+// boundary scan, which grows with the segment count.
+long long split_segment_length(long long bh, int n_chunk) {
+  constexpr long long kCUs = 256;
+  auto load = [&](long long groups, long long s) {
+    const long long waves = (groups + kCUs - 1) / kCUs;
+    return (double)(waves * s) * (waves <= 1 ? 1.35 : 1.0);
+  };
+  long long best = 1;
+  double best_cost = 1e300;
+  for (long long s = 1; s <= 32 && s <= n_chunk; ++s) {
+    const long long n_seg = (n_chunk + s - 1) / s;
+    const double cost = load(bh * n_seg, s) + 0.5 * load(bh * (n_seg - 1), s) + 0.06 * (double)n_seg;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
 void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
-  const long long total = bh * n_chunk;
   sh->fused = path == GTR_PATH_FUSED ||
               (path == GTR_PATH_AUTO && n_chunk <= kAutoFusedChunks &&
                chunks_per_segment <= gtr::kMaxFusedChunks);
@@ -71,8 +95,7 @@ void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh
     if (len <= 0) len = n_chunk <= 8 ? 1 : (n_chunk <= 32 ? 2 : 3);
     len = std::min<long long>(len, gtr::kMaxFusedChunks);
   } else if (len <= 0) {
-    len = (total + 767) / 768;
-    len = std::max<long long>(1, std::min<long long>(len, 32));
+    len = split_segment_length(bh, n_chunk);
   }
   if (len > n_chunk) len = n_chunk;
   sh->seg_len = (int)len;

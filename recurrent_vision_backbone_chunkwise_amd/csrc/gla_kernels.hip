@@ -308,23 +308,25 @@ __device__ __forceinline__ void rows4(const Seq &sq, int t0, uint32_t *off) {
 // Gate factors below are products of alpha = exp(log_gate) over token ranges of
 // the chunk; with E the log2 cumulative gate from the chunk start they equal
 // the exponentials named in the comments.
+// Every member is 16-byte aligned so that fragment reads compile to single
+// 8- and 16-byte LDS accesses.
 template <typename Op, int NQ> struct Smem {
   static constexpr int LD = OpT<Op>::LD;
   static constexpr int LDT = OpT<Op>::LDT;
-  Op qs[kChunk * LD];   // q 2^(E - E_end(a-1))     [token][dim]
-  Op ks[kChunk * LD];   // k 2^(E_end(b) - E)       (qs and ks are adjacent: see gla_fused)
-  Op kb[kChunk * LDT];  // k 2^(E_last - E)
-  Op vv[kChunk * LDT];  // v
-  Op pt[10 * 256];      // score tiles P^T, 4 values per lane, lane-ordered
-  float tot[4 * kHead]; // gate product of each 16-token sub-block
-  Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
-  Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
-  float dec[kHead];     // 2^E_last: decay of the state across the chunk
+  alignas(16) Op qs[kChunk * LD];   // q 2^(E - E_end(a-1))     [token][dim]
+  alignas(16) Op ks[kChunk * LD];   // k 2^(E_end(b) - E)       (qs and ks are adjacent: see gla_fused)
+  alignas(16) Op kb[kChunk * LDT];  // k 2^(E_last - E)
+  alignas(16) Op vv[kChunk * LDT];  // v
+  alignas(16) Op pt[10 * 256];      // score tiles P^T, 4 values per lane, lane-ordered
+  alignas(16) float tot[4 * kHead]; // gate product of each 16-token sub-block
+  alignas(16) Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
+  alignas(16) Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
+  alignas(16) float dec[kHead];     // 2^E_last: decay of the state across the chunk
   // One slot per chunk whose outputs wait for the state entering the segment
   // (NQ = 1 when outputs are stored as each chunk completes).
-  uint32_t rowoff[NQ][kChunk];  // byte offset of each token's row (kOob past the end)
-  float dcum[NQ][kHead];        // decay from the segment start to the chunk start
-  Op qh[NQ][kChunk * LD];       // q 2^E
+  alignas(16) uint32_t rowoff[NQ][kChunk];  // byte offset of each token's row (kOob past the end)
+  alignas(16) float dcum[NQ][kHead];        // decay from the segment start to the chunk start
+  alignas(16) Op qh[NQ][kChunk * LD];       // q 2^E
 };
 
 // ------------------------------------------------------------------- params
