@@ -16,7 +16,6 @@ replay stream.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,18 +41,20 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=50)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes ten times (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
     return ap.parse_args()
 
 
-def kernel_sources_digest() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "recurrent_vision_backbone_chunkwise_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
-    return h.hexdigest()[:16]
+def copy_calibration(n_bytes: int) -> None:
+    import torch
+    src = torch.ones(n_bytes // 2, dtype=torch.float16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n_bytes, "launches": 10}), flush=True)
 
 
 def measured_traffic(kernel: str, workload: str, digest: str):
@@ -75,6 +76,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "sharding of this operator is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -157,7 +162,8 @@ def main():
     }
     avg_s = kern[dominant]["avg_us"] * 1e-6
     achieved = alg_bytes[dominant] / avg_s / 1e9
-    digest = kernel_sources_digest()
+    from recurrent_vision_backbone_chunkwise_amd.build import source_digest
+    digest = source_digest()
     traffic = measured_traffic(dominant, w.name, digest)
     path_gbs = value * (3 * w.d_k + 2 * w.d_v) * elt / 1e9
     roofline = {

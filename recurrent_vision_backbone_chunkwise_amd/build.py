@@ -5,6 +5,7 @@ Run ``python -m recurrent_vision_backbone_chunkwise_amd.build`` or call
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -25,6 +26,17 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_profile.cpp"]
+
+
+def source_digest() -> str:
+    """Short digest of the kernel and host sources: ties measurements to the code they measured."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _hipcc() -> str:
