@@ -55,11 +55,12 @@ struct Shape {
 //  * fused: segments of at most kMaxFusedChunks chunks (each chunk's outputs
 //    wait in registers for the state entering the segment); every segment
 //    reads the aggregates of all earlier segments of its sequence.
-// Automatic choice: fused while a sequence has at most kAutoFusedChunks
-// chunks.  Measured on MI355X the fused launch does not yet beat three
-// launches on any shape (combining predecessors costs one memory round trip per
-// few aggregates), so the threshold is 0 and the choice is always split.
-constexpr int kAutoFusedChunks = 0;
+// Automatic choice (measured on MI355X): the fused launch wins for short
+// sequences (at most kAutoFusedChunks chunks, so each segment folds few
+// predecessors) when there are enough of them to fill the chip with
+// 3-chunk segments; otherwise three launches.
+constexpr int kAutoFusedChunks = 32;
+constexpr long long kAutoFusedMinGroups = 256;
 
 // Segment length of the three-launch path.  Each CU walks its workgroups'
 // chunks, two workgroups already saturate it and one alone runs about 1.35x
@@ -87,12 +88,13 @@ long long split_segment_length(long long bh, int n_chunk) {
 }
 
 void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
+  const long long fused_groups = bh * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
   sh->fused = path == GTR_PATH_FUSED ||
               (path == GTR_PATH_AUTO && n_chunk <= kAutoFusedChunks &&
-               chunks_per_segment <= gtr::kMaxFusedChunks);
+               fused_groups >= kAutoFusedMinGroups && chunks_per_segment <= gtr::kMaxFusedChunks);
   long long len = chunks_per_segment;
   if (sh->fused) {
-    if (len <= 0) len = n_chunk <= 8 ? 1 : (n_chunk <= 32 ? 2 : 3);
+    if (len <= 0) len = gtr::kMaxFusedChunks;
     len = std::min<long long>(len, gtr::kMaxFusedChunks);
   } else if (len <= 0) {
     len = split_segment_length(bh, n_chunk);

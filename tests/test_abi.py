@@ -55,7 +55,7 @@ def test_version_and_sizes():
 
 
 def test_plans():
-    # one launch caps segments at 3 chunks; the automatic choice is three launches
+    # one launch caps segments at 3 chunks
     pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_FUSED)
     assert pl["fused"] and pl["seg_len"] == 3 and pl["n_seg"] == 86
     pl = gla.gtr_gla_plan(1, 16, 128, 128, chunks_per_segment=9, path=gla.GTR_PATH_FUSED)
@@ -65,9 +65,13 @@ def test_plans():
     pl = gla.gtr_gla_plan(1, 16, 128, 128, path=gla.GTR_PATH_SPLIT)
     assert not pl["fused"] and pl["seg_len"] * pl["n_seg"] >= 256
     pl = gla.gtr_gla_plan(1, 6, 40, 40, path=gla.GTR_PATH_FUSED)
-    assert pl["fused"] and pl["seg_len"] == 2 and pl["n_seg"] == 13
-    pl = gla.gtr_gla_plan(1, 6, 40, 40)
-    assert not pl["fused"]
+    assert pl["fused"] and pl["seg_len"] == 3 and pl["n_seg"] == 9
+    pl = gla.gtr_gla_plan(1, 6, 40, 40)  # few short sequences: three launches
+    assert not pl["fused"] and pl["seg_len"] == 1
+    pl = gla.gtr_gla_plan(8, 6, 40, 40)  # many short sequences: one launch
+    assert pl["fused"] and pl["seg_len"] == 3 and pl["n_seg"] == 9
+    pl = gla.gtr_gla_plan(1, 16, 64, 64)  # 64 chunks per sequence: three launches
+    assert not pl["fused"] and pl["seg_len"] == 2
     pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=4)
     assert pl["seg_len"] == 4 and pl["n_seg"] == 7 and not pl["fused"]
     pl = gla.gtr_gla_plan(1, 6, 40, 40, chunks_per_segment=3, path=gla.GTR_PATH_FUSED)
