@@ -89,9 +89,7 @@ struct IoF32 {
   using Raw = u4;  // 16 bytes
   __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
   __device__ static float load1(const T *p) { return *p; }
-  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, (int)off, 0, 0);
-  }
+  __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u4, v); }
 };
 
 struct IoF16 {
@@ -100,10 +98,7 @@ struct IoF16 {
   __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
   __device__ static f4 to_f4(Raw r) { return __builtin_convertvector(to_h4(r), f4); }
   __device__ static float load1(const T *p) { return (float)*p; }
-  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, __builtin_convertvector(v, h4)), r,
-                                          (int)off, 0, 0);
-  }
+  __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u2, __builtin_convertvector(v, h4)); }
 };
 
 struct IoBF16 {
@@ -120,10 +115,7 @@ struct IoBF16 {
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   }
-  __device__ static void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
-    const u2 w = {rne(v.x) | (rne(v.y) << 16), rne(v.z) | (rne(v.w) << 16)};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
-  }
+  __device__ static Raw pack(f4 v) { return u2{rne(v.x) | (rne(v.y) << 16), rne(v.z) | (rne(v.w) << 16)}; }
 };
 
 // ------------------------------------------------------------ MFMA operands
@@ -136,6 +128,8 @@ template <typename Op> struct OpT;
 template <> struct OpT<_Float16> {
   using V4 = h4;
   using V8 = h8;
+  using Bits = uint16_t;          // one output element in the I/O format
+  static constexpr int LDO = 72;  // row stride of the output tile (16 rows hit distinct banks)
   static constexpr int LD = 68;
   static constexpr int LDT = 80;
   static constexpr float kDiagMin = 1.52587890625e-05f;  // 2^-16
@@ -143,6 +137,8 @@ template <> struct OpT<_Float16> {
 template <> struct OpT<float> {
   using V4 = f4;
   using V8 = f8;
+  using Bits = uint32_t;
+  static constexpr int LDO = 68;
   static constexpr int LD = 68;
   static constexpr int LDT = 68;
   static constexpr float kDiagMin = 7.888609052210118e-31f;  // 2^-100
@@ -378,6 +374,14 @@ __device__ __forceinline__ typename Io::Raw buf_load(__amdgpu_buffer_rsrc_t r, u
     return __builtin_bit_cast(typename Io::Raw, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+template <class Io>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, typename Io::Raw v) {
+  if constexpr (sizeof(typename Io::Raw) == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+
 template <class Io, bool kOut>
 __device__ __forceinline__ void load_chunk(const Seq &sq, int c, int wave, int lane, Rows<Io> &x) {
   const uint32_t col = 4 * (lane & 15) * sizeof(typename Io::T);
@@ -601,18 +605,17 @@ enum : int {
   kKeep = 2,   // outputs formed with the state carried so far and kept in registers
 };
 
-// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T: stored at the grid
-// positions (kStore) or kept in keep[tt] (kKeep).
+// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T: rounded to the I/O format
+// into the output tile ot[token][dim] (kStore), or kept in keep[tt] (kKeep).
 template <class Io, typename Op, int kMode, int NQ>
-__device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op, NQ> &sm, int wave, int lane,
-                                        int slot, const op8<Op> *vf, const uint32_t *oo, const f4 *S,
+__device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int lane, int slot,
+                                        const op8<Op> *vf, const f4 *S, typename OpT<Op>::Bits *ot,
                                         f4 *keep) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
   op8<Op> sf[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) sf[kb] = cat(to4<Op>(S[2 * kb]), to4<Op>(S[2 * kb + 1]));
-  const uint32_t col = (16 * wave + 4 * g) * sizeof(typename Io::T);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -630,7 +633,8 @@ __device__ __forceinline__ void outputs(const Seq &sq, const Smem<Op, NQ> &sm, i
     if constexpr (kMode == kKeep)
       keep[tt] = acc;
     else
-      Io::store4(sq.o, oo[tt] + col, acc);
+      *reinterpret_cast<typename Io::Raw *>(&ot[(16 * tt + l16) * OpT<Op>::LDO + 16 * wave + 4 * g]) =
+          Io::pack(acc);
   }
 }
 
@@ -646,6 +650,20 @@ __device__ __forceinline__ void carry_state(const Smem<Op, NQ> &sm, int lane, co
   }
 }
 
+// Stores a finished output tile: this thread's 4 tokens (rows off[r]) x 4
+// dims, so each store instruction writes whole 128/256-byte rows.
+template <class Io, typename Op>
+__device__ __forceinline__ void flush_tile(const Seq &sq, const typename OpT<Op>::Bits *ot,
+                                           const uint32_t *off, int wave, int lane) {
+  const int g = lane >> 4, dq = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const typename Io::Raw v =
+        *reinterpret_cast<const typename Io::Raw *>(&ot[(16 * wave + 4 * g + r) * OpT<Op>::LDO + 4 * dq]);
+    buf_store<Io>(sq.o, off[r] + 4 * dq * sizeof(typename Io::T), v);
+  }
+}
+
 // One chunk, using LDS slot `slot` for what must outlive it.  Barriers: (1)
 // sub-block products and row offsets visible, (2) operand tiles visible, (3)
 // score tiles visible.  Everything a wave reads from LDS after the last barrier
@@ -656,25 +674,32 @@ __device__ __forceinline__ void carry_state(const Smem<Op, NQ> &sm, int lane, co
 // chunk's rows are loaded into x as soon as this chunk's have gone to LDS, and
 // arrive while the rest of this chunk computes.  seg_dec (wave 0, lanes < 16,
 // dims 4*lane..+3) accumulates the chunk decays; kKeep also records the decay
-// from the segment start to this chunk in sm.dcum[slot].
+// from the segment start to this chunk in sm.dcum[slot].  kStore: the previous
+// chunk's output tile (complete at this chunk's first barrier, rewritten only
+// after its third) is stored after the first barrier; pend carries the row
+// offsets of the tile's tokens from chunk to chunk.
 template <class Io, typename Op, int kMode, int NQ>
 __device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t base, Smem<Op, NQ> &sm,
                                       Rows<Io> &x, int c, int c_end, int wave, int lane, int slot,
-                                      f4 *S, f4 &seg_dec, f4 *keep) {
+                                      f4 *S, f4 &seg_dec, f4 *keep, typename OpT<Op>::Bits *ot,
+                                      uint32_t *pend, bool have_pend) {
   constexpr bool kOut = kMode != kAgg;
   op4<Op> qs[4], ks[4];
   prep_local<Io, Op, kOut>(sm, x, wave, lane, slot, qs, ks);
+  uint32_t cur[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cur[r] = x.off[r];
   if (c + 1 < c_end) load_chunk<Io, kOut>(sq, c + 1, wave, lane, x);
   lds_sync();
+  if constexpr (kMode == kStore) {
+    if (have_pend) flush_tile<Io, Op>(sq, ot, pend, wave, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pend[r] = cur[r];
+  }
   prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, slot);
   op8<Op> vf[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
-  uint32_t oo[4];
-  if constexpr (kMode == kStore) {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) oo[tt] = sm.rowoff[slot][16 * tt + (lane & 15)];
-  }
   if (kMode != kStore && wave == 0 && lane < 16) {
     f4 t[4];
     sub_block_products(sm, lane, t);
@@ -685,7 +710,7 @@ __device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t bas
   if constexpr (kOut) {
     scores<Io, Op>(p, sq, base, sm, c, wave, lane);
     lds_sync();
-    outputs<Io, Op, kMode>(sq, sm, wave, lane, slot, vf, oo, S, keep);
+    outputs<Io, Op, kMode>(sm, wave, lane, slot, vf, S, ot, keep);
   }
   carry_state<Op>(sm, lane, vf, S);
 }
@@ -696,14 +721,21 @@ __device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t bas
 // the chunk decays into seg_dec.
 template <class Io, typename Op, int kMode, int NQ>
 __device__ __forceinline__ void walk(const Params &p, int bh, Smem<Op, NQ> &sm, int c_begin, int c_end,
-                                     int wave, int lane, f4 *S, f4 &seg_dec) {
+                                     int wave, int lane, f4 *S, f4 &seg_dec,
+                                     typename OpT<Op>::Bits *ot = nullptr) {
   static_assert(kMode != kKeep, "kKeep walks are unrolled by their kernel");
   const Seq sq = seq_of<Io>(p, bh);
   const size_t base = (size_t)bh * p.n_tok * kHead;
   Rows<Io> x;
+  uint32_t pend[4];
   load_chunk<Io, kMode != kAgg>(sq, c_begin, wave, lane, x);
   for (int c = c_begin; c < c_end; ++c)
-    chunk<Io, Op, kMode>(p, sq, base, sm, x, c, c_end, wave, lane, 0, S, seg_dec, nullptr);
+    chunk<Io, Op, kMode>(p, sq, base, sm, x, c, c_end, wave, lane, 0, S, seg_dec, nullptr, ot, pend,
+                         c > c_begin);
+  if constexpr (kMode == kStore) {
+    lds_sync();  // the last output tile is complete
+    flush_tile<Io, Op>(sq, ot, pend, wave, lane);
+  }
 }
 
 __device__ __forceinline__ void store_state_rowmajor(float *dst, int wave, int lane, const f4 *S) {
@@ -729,8 +761,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     *reinterpret_cast<f4 *>(&p.agg_dec[((size_t)bh * p.n_seg + seg) * kHead + 4 * lane]) = sdec;
 }
 
+// (Its output tile brings LDS to 63.6 KB at 16-bit I/O: two workgroups per CU.)
 template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_out(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_seg_out(Params p) {
   __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / p.n_seg;
@@ -741,9 +774,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
     for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = p.prev[st + x * 64];
   }
+  __shared__ __attribute__((aligned(16))) typename OpT<Op>::Bits ot[kChunk * OpT<Op>::LDO];
   f4 unused = {};
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, kStore>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused);
+  walk<Io, Op, kStore>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused, ot);
 }
 
 // Boundary-state recurrence over segments, one thread per (sequence, state
@@ -864,7 +898,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
     load_chunk<Io, true>(sq, c0, wave, lane, x);
 #pragma unroll
     for (int j = 0; j < kSeg; ++j)
-      if (c0 + j < c1) chunk<Io, Op, kKeep>(p, sq, base, sm, x, c0 + j, c1, wave, lane, j, L, sdec, keep[j]);
+      if (c0 + j < c1)
+        chunk<Io, Op, kKeep>(p, sq, base, sm, x, c0 + j, c1, wave, lane, j, L, sdec, keep[j], nullptr,
+                             nullptr, false);
   }
   // decay across the whole segment, read in step 5; tot is not read after a
   // chunk's last barrier, so wave 0 may overwrite it while others finish
@@ -997,7 +1033,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
           keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) Io::store4(sq.o, sm.rowoff[j][16 * tt + l16] + col, keep[j][tt]);
+    for (int tt = 0; tt < 4; ++tt) buf_store<Io>(sq.o, sm.rowoff[j][16 * tt + l16] + col, Io::pack(keep[j][tt]));
   }
 
   // 5. a sequence's last workgroup resets its ticket and done counters; the
