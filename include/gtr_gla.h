@@ -62,8 +62,13 @@
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
  *
- * Supported sizes (first build): d_k = d_v = 64; 1 <= grid_h*grid_w <= 2^23;
- * 1 <= B*H <= 2^20.  Pointers must be 16-byte aligned.
+ * Supported sizes (first build): d_k = d_v = 64; 0 <= grid_h*grid_w <= 2^23;
+ * 0 <= B*H <= 2^20.  Pointers must be 16-byte aligned.
+ *
+ * Empty calls: with B*H == 0 or no tokens there is nothing to compute and
+ * tensor pointers may be NULL; the call returns GTR_OK without touching the
+ * device, except that with tokens == 0, B*H > 0 and s_final given, s_final
+ * receives s0 (or zeros) - the state after an empty scan is the state before.
  */
 #ifndef GTR_GLA_H
 #define GTR_GLA_H
@@ -93,7 +98,7 @@ extern "C" {
 
 /* return codes: 0 on success, negative on error */
 #define GTR_OK 0
-#define GTR_ERR_INVALID_ARG (-1)  /* null pointer, size <= 0 or too large, bad direction/dtype/path */
+#define GTR_ERR_INVALID_ARG (-1)  /* null pointer, negative or too large size, bad direction/dtype/path */
 #define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v other than 64 */
 #define GTR_ERR_ALIGNMENT (-3)    /* a pointer is not 16-byte aligned */
 #define GTR_ERR_ALIAS (-4)        /* out (or s_final) overlaps an input */

@@ -47,6 +47,7 @@ struct Shape {
   long long bh, n_tok;
   int n_chunk, seg_len, n_seg;
   bool fused;
+  bool empty;  // B*H == 0 or no tokens: nothing to compute
 };
 
 // Chunks per segment and launch structure for a shape.
@@ -88,6 +89,11 @@ long long split_segment_length(long long bh, int n_chunk) {
 }
 
 void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
+  if (bh == 0 || n_chunk == 0) {
+    sh->fused = false;
+    sh->seg_len = sh->n_seg = 0;
+    return;
+  }
   const long long fused_groups = bh * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
   sh->fused = path == GTR_PATH_FUSED ||
               (path == GTR_PATH_AUTO && n_chunk <= kAutoFusedChunks &&
@@ -107,9 +113,10 @@ void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh
 // Shape, direction and dtype checks; fills `shape`.
 int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
                    int dtype, int chunks_per_segment, int path, Shape *shape) {
-  if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || d_k <= 0 || d_v <= 0)
-    return fail(GTR_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d grid=%dx%d d_k=%d d_v=%d)", B,
-                H, grid_h, grid_w, d_k, d_v);
+  if (B < 0 || H < 0 || grid_h < 0 || grid_w < 0 || d_k <= 0 || d_v <= 0)
+    return fail(GTR_ERR_INVALID_ARG,
+                "sizes must be >= 0 and head sizes > 0 (B=%d H=%d grid=%dx%d d_k=%d d_v=%d)", B, H,
+                grid_h, grid_w, d_k, d_v);
   if (direction < 0 || direction > 3)
     return fail(GTR_ERR_INVALID_ARG, "direction %d not in 0..3", direction);
   if (dtype < 0 || dtype > 2) return fail(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
@@ -123,6 +130,7 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
     return fail(GTR_ERR_UNSUPPORTED, "d_k=%d d_v=%d: this build supports d_k = d_v = 64", d_k, d_v);
   shape->bh = bh;
   shape->n_tok = n_tok;
+  shape->empty = bh == 0 || n_tok == 0;
   shape->n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
   plan(bh, shape->n_chunk, path, chunks_per_segment, shape);
   if (bh * shape->n_seg > 0x7fffffffLL)
@@ -135,12 +143,13 @@ int validate(const void *q, const void *k, const void *v, const void *g, const v
              int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
              const float *s0, const float *s_final, int chunks_per_segment, int path,
              Shape *shape) {
-  if (!q || !k || !v || !g || !out)
-    return fail(GTR_ERR_INVALID_ARG, "null tensor pointer (q=%p k=%p v=%p log_gate=%p out=%p)", q, k,
-                v, g, out);
   int rc = validate_shape(B, H, grid_h, grid_w, d_k, d_v, direction, dtype, chunks_per_segment,
                           path, shape);
   if (rc != GTR_OK) return rc;
+  // tensors of zero elements may be null
+  if (!shape->empty && (!q || !k || !v || !g || !out))
+    return fail(GTR_ERR_INVALID_ARG, "null tensor pointer (q=%p k=%p v=%p log_gate=%p out=%p)", q, k,
+                v, g, out);
   const void *ptrs[7] = {q, k, v, g, out, s0, s_final};
   const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
   for (int i = 0; i < 7; ++i)
@@ -288,6 +297,8 @@ int check_call(const void *q, const void *k, const void *v, const void *log_gate
   int rc = validate(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
                     s_final, chunks_per_segment, path, sh);
   if (rc != GTR_OK) return rc;
+  // nothing to compute and no state to hand back: no device work at all
+  if (sh->empty && (sh->bh == 0 || !s_final)) return GTR_OK;
   int n_dev = 0;
   if (hipGetDeviceCount(&n_dev) != hipSuccess || n_dev <= 0) {
     (void)hipGetLastError();
@@ -315,7 +326,7 @@ int check_call(const void *q, const void *k, const void *v, const void *log_gate
     const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
     const size_t sizes[7] = {nb, nb, nb, nb, nb, sb, sb};
     for (int i = 0; i < 7; ++i) {
-      if (!ptrs[i]) continue;
+      if (!ptrs[i] || sizes[i] == 0) continue;
       rc = check_device_range(ptrs[i], sizes[i], *device, names[i]);
       if (rc != GTR_OK) return rc;
     }
@@ -345,6 +356,14 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   int rc = check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, s0,
                       s_final, chunks_per_segment, path, &sh, &device, stream, true);
   if (rc != GTR_OK) return rc;
+  if (sh.empty) {
+    // no tokens: the state after the sequence is the state before it
+    if (sh.bh == 0 || !s_final) return GTR_OK;
+    const int err = gtr::launch_state_copy(s0, s_final, sh.bh * gtr::kStateElems, stream);
+    if (err != (int)hipSuccess)
+      return fail(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+    return GTR_OK;
+  }
 
   gtr::LaunchArgs a{};
   a.q = q;
@@ -422,6 +441,7 @@ size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, in
   if (validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, dtype, chunks_per_segment, path, &sh) !=
       GTR_OK)
     return 0;
+  if (sh.empty) return 0;
   return gtr::workspace_bytes(sh.bh, sh.n_seg) +
          (sh.fused ? gtr::sync_words(sh.bh, sh.n_seg) * sizeof(int) : 0);
 }

@@ -51,4 +51,7 @@ inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (k
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);
 
+// s_final[i] = s0 ? s0[i] : 0 for i < n (a call with no tokens).  Returns a hipError_t value.
+int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t stream);
+
 }  // namespace gtr

@@ -1105,6 +1105,19 @@ int launch_typed(const LaunchArgs &a) {
 
 }  // namespace
 
+namespace {
+__global__ __launch_bounds__(kThreads) void gla_state_copy(const float *s0, float *s_final, long long n) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) s_final[i] = s0 ? s0[i] : 0.f;
+}
+}  // namespace
+
+int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t stream) {
+  hipLaunchKernelGGL(gla_state_copy, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     stream, s0, s_final, n);
+  return (int)hipGetLastError();
+}
+
 int launch_gla(const LaunchArgs &a) {
   switch (a.dtype) {
     case 0: return launch_typed<IoF32, float>(a);

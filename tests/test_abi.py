@@ -78,8 +78,9 @@ def test_plans():
     assert pl["seg_len"] == 3 and pl["n_seg"] == 9 and pl["fused"]
     pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
     assert pl["seg_len"] == 1 and pl["n_seg"] == 1
+    assert gla.gtr_gla_plan(1, 1, 0, 1) == {"seg_len": 0, "n_seg": 0, "fused": False}  # no tokens
     with pytest.raises(gla.GlaError):
-        gla.gtr_gla_plan(1, 1, 0, 1)
+        gla.gtr_gla_plan(1, 1, -1, 1)
 
 
 A = 0x10000  # fake, 16-byte aligned, never dereferenced
@@ -92,7 +93,8 @@ def call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, out=A + 0x400000, 
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), -1), (dict(out=None), -1), (dict(B=0), -1), (dict(H=-1), -1), (dict(gh=0), -1),
+    (dict(q=None), -1), (dict(out=None), -1), (dict(B=-1), -1), (dict(H=-1), -1), (dict(gh=-1), -1),
+    (dict(dk=0), -1),
     (dict(d=4), -1), (dict(d=-1), -1), (dict(dt=3), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1),
     (dict(path=3), -1), (dict(path=-1), -1),
     (dict(B=1 << 11, H=1 << 10), -1),
@@ -106,11 +108,23 @@ def test_argument_errors_before_any_hip_call(kw, code):
     assert gla.gtr_gla_last_error() != ""
 
 
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(gh=0), dict(gw=0), dict(B=0, gh=0),
+                                dict(B=0, q=None, k=None, v=None, g=None, out=None),
+                                dict(gh=0, q=None, k=None, v=None, g=None, out=None),
+                                dict(B=0, sf=A + 0x500000)])
+def test_empty_calls_succeed_without_device_work(kw):
+    """No sequence or no token: nothing to compute; null tensor pointers are allowed."""
+    assert call(**kw) == 0
+    assert gla.gtr_gla_workspace_bytes(kw.get("B", 1), kw.get("H", 1), kw.get("gh", 4), kw.get("gw", 4),
+                                       64, 64, 1) == 0
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
                     reason="a GPU is visible")
 def test_valid_call_without_gpu_reports_no_device():
     assert call() == -5
     assert "device" in gla.gtr_gla_last_error()
+    assert call(gh=0, sf=A + 0x500000) == -5  # no tokens but a final state to write
     assert call(q=None) == -1  # argument errors still come first
 
 

@@ -133,6 +133,53 @@ def test_final_state_from_zero(grid, path):
         assert parity_errors(sf.double().cpu().numpy(), sref, "f16")["ok"]
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_empty_calls(path):
+    """No tokens: out is empty and the final state is s0 (or zero); no sequences: nothing happens."""
+    s0 = torch.randn(2, 3, 64, 64, generator=torch.Generator().manual_seed(14)).to(DEV)
+    x = torch.empty(2, 3, 0, 5, 64, dtype=torch.float16, device=DEV)
+    y, sf = gpu_run(x, x, x, x, 0, s0=s0, want_state=True, path=PATHS[path])
+    assert y.shape == x.shape and torch.equal(sf, s0)
+    y, sf = gpu_run(x, x, x, x, 2, want_state=True, path=PATHS[path])
+    assert torch.count_nonzero(sf) == 0
+    z = torch.empty(0, 3, 4, 5, 64, dtype=torch.float16, device=DEV)
+    assert gpu_run(z, z, z, z, 1, path=PATHS[path]).shape == z.shape
+
+
+def test_maximum_grid():
+    """2^23 tokens (2048 x 4096): 1 GB per tensor, byte offsets up to 2^30.  Outputs depend only on
+    earlier scan positions, so the first 4096 positions of every direction are checked against the
+    oracle on the truncated grid those positions cover; every output must be finite, and carrying
+    the state from the top half into the bottom half must give the whole call's final state."""
+    gh, gw = 2048, 4096
+    gen = torch.Generator(device=DEV).manual_seed(15)
+    shape = (1, 1, gh, gw, 64)
+    q = torch.randn(shape, generator=gen, device=DEV).half()
+    k = (torch.randn(shape, generator=gen, device=DEV) / 8).half()
+    v = torch.randn(shape, generator=gen, device=DEV).half()
+    g = (torch.nn.functional.logsigmoid(torch.randn(shape, generator=gen, device=DEV)) / 16).half()
+    views = {  # direction -> the grid slice its first 4096 scan positions cover
+        0: (slice(0, 1), slice(None)), 1: (slice(gh - 1, gh), slice(None)),
+        2: (slice(None), slice(0, 2)), 3: (slice(None), slice(gw - 2, gw)),
+    }
+    for d, (rs, cs) in views.items():
+        note(f"maximum grid dir={d}")
+        y = gpu_run(q, k, v, g, d)
+        assert bool(torch.isfinite(y).all())
+        part = [t[:, :, rs, cs].contiguous().cpu() for t in (q, k, v, g)]
+        ref = oracle.gla_forward(*part, d)
+        e = parity_errors(y[:, :, rs, cs].double().cpu().numpy(), ref, "f16")
+        assert e["ok"], e
+        del y
+    half = gh // 2
+    _, s_whole = gpu_run(q, k, v, g, 0, want_state=True)
+    _, s_top = gpu_run(*[t[:, :, :half].contiguous() for t in (q, k, v, g)], 0, want_state=True)
+    _, s_bot = gpu_run(*[t[:, :, half:].contiguous() for t in (q, k, v, g)], 0, s0=s_top,
+                       want_state=True)
+    err = (s_bot - s_whole).abs().max() / s_whole.pow(2).mean().sqrt()
+    assert float(err) < 1e-4, float(err)
+
+
 def test_split_sequence_equals_whole():
     """Top rows then bottom rows with the state carried equals one L->R call."""
     B, H, gh, gw, r = 1, 2, 40, 40, 17
