@@ -93,7 +93,8 @@ extern "C" {
 
 /* launch structure (entry points _ex, _check, _workspace_bytes, _plan) */
 #define GTR_PATH_AUTO 0   /* chosen by the library from the shape */
-#define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, flag-ordered combine, outputs */
+#define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, flag-ordered combine, outputs;
+                             at most 768 chunks (49152 tokens) per sequence */
 #define GTR_PATH_SPLIT 2  /* three kernels: segment aggregates, boundary scan, outputs */
 
 /* return codes: 0 on success, negative on error */
@@ -108,6 +109,7 @@ extern "C" {
 #define GTR_ERR_ALLOC (-7)        /* workspace allocation failed */
 #define GTR_ERR_CAPTURE (-8)      /* workspace would have to grow during stream capture */
 #define GTR_ERR_LAUNCH (-9)       /* a kernel launch failed */
+#define GTR_ERR_TIMEOUT (-10)     /* a one-launch-path wait between workgroups gave up (see gtr_gla_stream_status) */
 
 /*
  * Generic entry point: dtype selects the element type (GTR_DTYPE_*).
@@ -140,7 +142,10 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
  *            walks with its state held in registers (<= 0 = chosen by the
  *            library from the shape);
  *   path     GTR_PATH_AUTO, GTR_PATH_FUSED or GTR_PATH_SPLIT.
- * Any segment length and path give the same result up to rounding.
+ * Any segment length and path give the same result up to rounding; the same
+ * shape, segment length and path give bitwise the same result on every call.
+ * GTR_PATH_FUSED with more than 256 segments per sequence is refused
+ * (GTR_ERR_INVALID_ARG): each segment folds every earlier one.
  * The initial state makes a long scan splittable: running the two halves of
  * a sequence with the first half's s_final as the second half's s0 equals one
  * call on the whole sequence.
@@ -180,6 +185,17 @@ int gtr_gla_version(void);
 
 /* Frees every cached workspace (synchronises each device that has one). */
 void gtr_gla_release_workspaces(void);
+
+/*
+ * Health of the one-launch path on `stream` (current device).  Its workgroups
+ * wait on each other with bounded spins; a wait that gives up (after seconds:
+ * only possible if workgroups of the call could not all make progress) leaves
+ * that call's outputs undefined and marks the stream's workspace.  This call
+ * synchronises `stream`, returns GTR_ERR_TIMEOUT if any wait on it gave up
+ * since the previous check (and clears the mark), else GTR_OK.  Not allowed
+ * while `stream` is being captured (GTR_ERR_CAPTURE).
+ */
+int gtr_gla_stream_status(hipStream_t stream);
 
 /*
  * Per-kernel timing (measurement aid).  Between gtr_gla_profile_begin() and

@@ -24,7 +24,7 @@ GTR_PATH_AUTO, GTR_PATH_FUSED, GTR_PATH_SPLIT = 0, 1, 2
 ERRORS = {
     0: "GTR_OK", -1: "GTR_ERR_INVALID_ARG", -2: "GTR_ERR_UNSUPPORTED", -3: "GTR_ERR_ALIGNMENT",
     -4: "GTR_ERR_ALIAS", -5: "GTR_ERR_NO_DEVICE", -6: "GTR_ERR_POINTER", -7: "GTR_ERR_ALLOC",
-    -8: "GTR_ERR_CAPTURE", -9: "GTR_ERR_LAUNCH",
+    -8: "GTR_ERR_CAPTURE", -9: "GTR_ERR_LAUNCH", -10: "GTR_ERR_TIMEOUT",
 }
 DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
                torch.bfloat16: GTR_DTYPE_BF16}
@@ -33,7 +33,8 @@ DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
            "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
-           "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name")
+           "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name",
+           "gtr_gla_stream_status")
 
 
 class GlaError(RuntimeError):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.gtr_gla_profile_end.restype = ctypes.c_int
     L.gtr_gla_kernel_name.argtypes = [i]
     L.gtr_gla_kernel_name.restype = ctypes.c_char_p
+    L.gtr_gla_stream_status.argtypes = [st]
+    L.gtr_gla_stream_status.restype = i
     _lib = L
     return L
 
@@ -132,6 +135,11 @@ def gtr_gla_profile_end() -> dict:
 
 def gtr_gla_kernel_name(kernel: int) -> str:
     return lib().gtr_gla_kernel_name(kernel).decode()
+
+
+def gtr_gla_stream_status(stream=None) -> None:
+    """Synchronises `stream`; raises GlaError (GTR_ERR_TIMEOUT) if a one-launch wait on it gave up."""
+    _check(lib().gtr_gla_stream_status(_stream_handle(stream)))
 
 
 def _check(rc: int) -> None:

@@ -135,6 +135,11 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
   plan(bh, shape->n_chunk, path, chunks_per_segment, shape);
   if (bh * shape->n_seg > 0x7fffffffLL)
     return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", bh * shape->n_seg);
+  if (shape->fused && shape->n_seg > gtr::kMaxFusedSegments)
+    return fail(GTR_ERR_INVALID_ARG,
+                "one-launch path: %d segments exceed %d (at most %d chunks per sequence); use "
+                "GTR_PATH_SPLIT or GTR_PATH_AUTO",
+                shape->n_seg, gtr::kMaxFusedSegments, gtr::kMaxFusedSegments * gtr::kMaxFusedChunks);
   return GTR_OK;
 }
 
@@ -461,6 +466,39 @@ int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int chunks_per_segment, i
 const char *gtr_gla_last_error(void) { return g_last_error.c_str(); }
 
 int gtr_gla_version(void) { return kVersion; }
+
+int gtr_gla_stream_status(hipStream_t stream) {
+  g_last_error.clear();
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GTR_ERR_NO_DEVICE, "no HIP device available");
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(GTR_ERR_CAPTURE, "stream status cannot be read while the stream is being captured");
+  (void)hipGetLastError();
+  int *sync = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws.find({device, stream});
+    if (it != g_ws.end()) sync = it->second.sync;
+  }
+  if (hipStreamSynchronize(stream) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    return fail(GTR_ERR_LAUNCH, "stream synchronisation failed: %s", hipGetErrorString(e));
+  }
+  if (!sync) return GTR_OK;
+  int word = 0;
+  if (hipMemcpy(&word, sync + gtr::kSyncErrorWord, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    return fail(GTR_ERR_LAUNCH, "reading the workspace status failed: %s", hipGetErrorString(e));
+  }
+  if (word == 0) return GTR_OK;
+  const int zero = 0;
+  (void)hipMemcpy(sync + gtr::kSyncErrorWord, &zero, sizeof(int), hipMemcpyHostToDevice);
+  return fail(GTR_ERR_TIMEOUT, "a wait between workgroups of the one-launch path gave up on this stream");
+}
 
 void gtr_gla_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);

@@ -11,6 +11,10 @@ constexpr int kChunk = 64;   // tokens per chunk (the pages' operator uses 64)
 constexpr int kHead = 64;    // d_k = d_v handled by this build
 constexpr int kStateElems = kHead * kHead;
 constexpr int kMaxFusedChunks = 3;  // chunks per segment of the one-launch path (outputs held in registers)
+// Segments per sequence of the one-launch path.  Every segment folds the
+// aggregates of all earlier ones in a fixed order (so results do not depend on
+// timing), which costs O(segments^2) cache reads per sequence.
+constexpr int kMaxFusedSegments = 256;
 
 struct LaunchArgs {
   const void *q, *k, *v, *g;
@@ -36,6 +40,7 @@ struct LaunchArgs {
 };
 
 constexpr int kSyncHeader = 32;  // fused-path header words (epoch, sequences done, error)
+constexpr int kSyncEpochWord = 0, kSyncSeqDoneWord = 1, kSyncErrorWord = 2;
 constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (ticket, done)
 
 // Float workspace bytes for (bh, n_seg): agg, prev and agg_dec.

@@ -334,7 +334,6 @@ struct Params {
   int n_chunk, seg_len, n_seg, n_seg_grid;
   float *agg, *agg_dec;    // [bh][n_seg][4096] state contribution, [bh][n_seg][64] decay per key dim
   const float *prev;       // [bh][n_seg][4096] register order (separate-launch path)
-  float *incl;             // [bh][n_seg][4096] row-major inclusive prefixes (fused path)
   const float *s0;         // user initial state, row-major [bh][64][64], nullable
   float *s_final;          // user final state, row-major, nullable
   int *sync;               // fused path: header, per-sequence control lines (kSync* words)
@@ -347,7 +346,7 @@ struct Params {
 // ticket and done counters.  After every call all words other than the epoch
 // and the flags are back at 0 (or -1); flags hold epochs, all below the next
 // call's epoch + 1, whatever shape wrote them.
-enum : int { kSyncEpoch = 0, kSyncSeqDone = 1, kSyncError = 2 };
+enum : int { kSyncEpoch = kSyncEpochWord, kSyncSeqDone = kSyncSeqDoneWord, kSyncError = kSyncErrorWord };
 enum : int { kCtlTicket = 0, kCtlDone = 1 };
 
 template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int bh) {
@@ -867,7 +866,7 @@ __device__ __forceinline__ int wait_flag(int *sync, const int *f, int want) {
 template <class Io, typename Op, int kSeg>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg == 1 ? 3 : 2, kSeg == 1 ? 3 : 2))) void gla_fused(Params p) {
   __shared__ Smem<Op, kSeg> sm;
-  __shared__ int s_ticket, s_epoch, s_flag[4];
+  __shared__ int s_ticket, s_epoch;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   // The sequence is fixed by the block index; the segment is the order in which
@@ -880,10 +879,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
     s_epoch = __hip_atomic_load(p.sync + kSyncEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  // Flag values of this call (epoch E = calls completed on this workspace):
-  // 2E+1 once a segment's aggregate is published, 2E+2 once its inclusive
-  // prefix is too.  Earlier calls left at most 2E.
-  const int seg = s_ticket, want_agg = 2 * s_epoch + 1, want_prefix = 2 * s_epoch + 2;
+  // flag value of this call: the epoch (calls completed on this workspace) + 1;
+  // earlier calls left at most the epoch
+  const int seg = s_ticket, want = s_epoch + 1;
   const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
   const size_t sbase = (size_t)bh * p.n_seg;
   const Seq sq = seq_of<Io>(p, bh);
@@ -919,16 +917,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
     stores_complete();  // this wave's payload is visible at device scope ...
     __syncthreads();    // ... for every wave ...
     if (tid == 0)       // ... before the flag is raised
-      __hip_atomic_store(p.flags + sbase + seg, want_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.flags + sbase + seg, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // 3. S_prev, folded backwards from the nearest predecessor: aggregates are
-  //    added with the decay of the segments between, until a predecessor whose
-  //    inclusive prefix (the state after it, s0 included) is already published
-  //    ends the walk; a walk that reaches the start adds the decayed s0.  Wave
-  //    w combines rows [16w, 16w+16), lane l column l, so every load reads one
-  //    contiguous 256-byte row; the result goes through LDS (qs and ks, idle
-  //    now) into the register layout.
+  // 3. S_prev: the aggregates of all earlier segments, folded backwards from
+  //    the nearest, each with the decay of the segments between, plus the
+  //    decayed s0.  The order is fixed, so the result does not depend on which
+  //    workgroups finished first.  Wave w combines rows [16w, 16w+16), lane l
+  //    column l, so every load reads one contiguous 256-byte row; the result
+  //    goes through LDS (qs and ks, idle now) into the register layout.
   const bool have_prev = seg > 0 || p.s0 != nullptr;
   f4 S[4] = {};
   if (have_prev) {
@@ -939,29 +936,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
       dacc[r] = 1.f;
     }
     constexpr int kBatch = 4;
-    bool reached_prefix = false;
-    for (int i = seg - 1; i >= 0 && !reached_prefix;) {
+    for (int i = seg - 1; i >= 0;) {
       const int nb = min(kBatch, i + 1);
-      if (tid < nb) s_flag[tid] = wait_flag(p.sync, p.flags + sbase + i - tid, want_agg);
+      if (tid < nb) wait_flag(p.sync, p.flags + sbase + i - tid, want);
       __syncthreads();  // the flags seen by one wave hold for the whole workgroup
-      int stop = nb;    // first predecessor in this batch with a published prefix
-      for (int u = nb - 1; u >= 0; --u)
-        if (s_flag[u] == want_prefix) stop = u;
-      __syncthreads();  // s_flag is rewritten by the next batch
       float av[kBatch][16], dv[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (u < nb && u <= stop) {
-          const size_t off = (sbase + i - u) * kStateElems + 16 * wave * kHead + lane;
-          const float *src = (u == stop ? p.incl : p.agg) + off;
+        if (u < nb) {
+          const float *src = p.agg + (sbase + i - u) * kStateElems + 16 * wave * kHead + lane;
 #pragma unroll
           for (int r = 0; r < 16; ++r) av[u][r] = load_shared(src + r * kHead);
-          dv[u] = u == stop ? 1.f : load_shared(p.agg_dec + (sbase + i - u) * kHead + 16 * wave + l16);
+          dv[u] = load_shared(p.agg_dec + (sbase + i - u) * kHead + 16 * wave + l16);
         }
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        if (u < nb && u <= stop) {
+        if (u < nb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             X[r] += dacc[r] * av[u][r];
@@ -969,10 +960,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
           }
         }
       }
-      reached_prefix = stop < nb;
       i -= nb;
     }
-    if (!reached_prefix && p.s0) {
+    if (p.s0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         X[r] += dacc[r] * p.s0[(size_t)bh * kStateElems + (16 * wave + r) * kHead + lane];
@@ -988,27 +978,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
     for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = xs[state_i(x, lane) * kLdX + 16 * wave + l16];
   }
 
-  // 3b. the state after this segment, D S_prev + A: published as this
-  //     segment's inclusive prefix for the segments after it, and the final
-  //     state after the last segment.
-  const bool want_after = seg + 1 < p.n_seg || p.s_final != nullptr;
-  if (want_after && !have_prev) __syncthreads();  // segdec visible
-  f4 after[4];
+  // 3b. the final state after the last segment: D S_prev + A
+  if (p.s_final && seg + 1 == p.n_seg) {
+    if (!have_prev) __syncthreads();  // segdec visible
+    f4 after[4];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) after[it] = L[it];
-  if (want_after && have_prev) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) after[it] += *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
-  }
-  if (seg + 1 < p.n_seg) {
-    float *dst = p.incl + (sbase + seg) * kStateElems + 16 * wave + l16;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) store_shared(dst + state_i(x, lane) * kHead, after[x >> 2][x & 3]);
-    stores_complete();
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(p.flags + sbase + seg, want_prefix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (p.s_final) {
+    for (int it = 0; it < 4; ++it) {
+      after[it] = L[it];
+      if (have_prev) after[it] += *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
+    }
     store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, after);
   }
 
@@ -1071,7 +1049,6 @@ int launch_typed(const LaunchArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.n_chunk = a.n_chunk; p.seg_len = a.seg_len; p.n_seg = a.n_seg; p.n_seg_grid = a.n_seg;
   p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
-  p.incl = a.prev;
   p.flags = a.flags; p.sync = a.sync;
   const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
   if (a.fused) {

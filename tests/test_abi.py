@@ -79,6 +79,11 @@ def test_plans():
     pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
     assert pl["seg_len"] == 1 and pl["n_seg"] == 1
     assert gla.gtr_gla_plan(1, 1, 0, 1) == {"seg_len": 0, "n_seg": 0, "fused": False}  # no tokens
+    # the one-launch path folds every earlier segment: at most 256 of 3 chunks
+    assert gla.gtr_gla_plan(1, 1, 768, 64, path=gla.GTR_PATH_FUSED)["n_seg"] == 256
+    with pytest.raises(gla.GlaError):
+        gla.gtr_gla_plan(1, 1, 769, 64, path=gla.GTR_PATH_FUSED)
+    assert gla.gtr_gla_plan(1, 1, 769, 64, chunks_per_segment=3)["fused"] is False
     with pytest.raises(gla.GlaError):
         gla.gtr_gla_plan(1, 1, -1, 1)
 
