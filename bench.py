@@ -16,6 +16,7 @@ replay stream.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -36,6 +37,8 @@ def parse():
                     help="1..5; default 2 = 40x40 grid, fp16, B1 H6, four directions")
     ap.add_argument("--chunks-per-segment", type=int, default=0)
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto")
+    ap.add_argument("--head-dims", type=int, nargs=2, metavar=("D_K", "D_V"), default=None,
+                    help="run the workload with these head dims instead of 64 x 64")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -93,9 +96,12 @@ def main():
         raise RuntimeError("no GPU visible")
     dev = torch.device("cuda:0")
     w = gla_inputs.workload(args.workload)
+    if args.head_dims and tuple(args.head_dims) != (w.d_k, w.d_v):
+        dk, dv = args.head_dims
+        w = dataclasses.replace(w, d_k=dk, d_v=dv, name=f"{w.name}_dk{dk}_dv{dv}")
     cps = args.chunks_per_segment
     path = {"auto": 0, "fused": 1, "split": 2}[args.path]
-    plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, cps, path)
+    plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, cps, path, w.d_k, w.d_v)
 
     cpu_inputs = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
     inputs = [[x.to(dev) for x in ins] for ins in cpu_inputs]

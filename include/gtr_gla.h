@@ -170,11 +170,12 @@ int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_g
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                                int dtype, int chunks_per_segment, int path);
 
-/* The plan the library uses for a shape (d_k = d_v = 64): chunks per segment,
- * segments per sequence, and 1 if one fused kernel runs (0: three kernels).
+/* The plan the library uses for a shape: chunks per segment, segments per
+ * sequence, and 1 if one fused kernel runs (0: three kernels).  The kernels
+ * walk B*H*ceil(d_v/64) sequences, one per 64-wide block of value columns.
  * Any output pointer may be NULL.  Returns 0 or an argument error. */
-int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int chunks_per_segment, int path,
-                 int *seg_len, int *n_seg, int *fused);
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,
+                 int path, int *seg_len, int *n_seg, int *fused);
 
 /* Message for the last error returned on this thread ("" if none).  The string
  * is owned by the library and stays valid until the next call on this thread. */

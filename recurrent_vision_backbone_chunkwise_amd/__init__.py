@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
     L.gtr_gla_fwd_ex.argtypes = sig + [i, fp, fp, i, i, st]
     L.gtr_gla_check.argtypes = sig + [i, fp, fp, i, i]
     ip = ctypes.POINTER(ctypes.c_int)
-    L.gtr_gla_plan.argtypes = [i] * 6 + [ip, ip, ip]
+    L.gtr_gla_plan.argtypes = [i] * 8 + [ip, ip, ip]
     for name in ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
                  "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version", "gtr_gla_plan"):
         getattr(L, name).restype = ctypes.c_int
@@ -106,11 +106,12 @@ def gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYP
                                          path)
 
 
-def gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment=0, path=GTR_PATH_AUTO) -> dict:
+def gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment=0, path=GTR_PATH_AUTO, d_k=64,
+                 d_v=64) -> dict:
     """{"seg_len", "n_seg", "fused"} the library uses for this shape."""
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(lib().gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment, path, ctypes.byref(a),
-                              ctypes.byref(b), ctypes.byref(c)))
+    _check(lib().gtr_gla_plan(B, H, grid_h, grid_w, d_k, d_v, chunks_per_segment, path,
+                              ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return {"seg_len": a.value, "n_seg": b.value, "fused": bool(c.value)}
 
 

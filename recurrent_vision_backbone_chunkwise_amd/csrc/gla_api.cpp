@@ -23,6 +23,7 @@ namespace {
 constexpr int kVersion = 10000;  // 1.0.0
 constexpr long long kMaxTokens = 1LL << 23;  // element offsets inside a sequence fit in 32 bits
 constexpr long long kMaxSeqs = 1LL << 20;
+constexpr int kMaxHeadDim = 2 * gtr::kHead;  // two 64-wide key or value blocks
 
 thread_local std::string g_last_error;
 
@@ -45,6 +46,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 struct Shape {
   long long bh, n_tok;
+  int dk, dv;
+  int nk, nvb;     // 64-wide key blocks and value blocks per head
+  long long seqs;  // sequences the kernels walk: B*H*nvb
   int n_chunk, seg_len, n_seg;
   bool fused;
   bool empty;  // B*H == 0 or no tokens: nothing to compute
@@ -88,7 +92,9 @@ long long split_segment_length(long long bh, int n_chunk) {
   return best;
 }
 
-void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
+// `bh` counts the sequences the kernels walk (B*H*value blocks); `nk` the key
+// blocks, which only the three-launch path handles beyond one.
+void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
   if (bh == 0 || n_chunk == 0) {
     sh->fused = false;
     sh->seg_len = sh->n_seg = 0;
@@ -96,7 +102,7 @@ void plan(long long bh, int n_chunk, int path, int chunks_per_segment, Shape *sh
   }
   const long long fused_groups = bh * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
   sh->fused = path == GTR_PATH_FUSED ||
-              (path == GTR_PATH_AUTO && n_chunk <= kAutoFusedChunks &&
+              (path == GTR_PATH_AUTO && nk == 1 && n_chunk <= kAutoFusedChunks &&
                fused_groups >= kAutoFusedMinGroups && chunks_per_segment <= gtr::kMaxFusedChunks);
   long long len = chunks_per_segment;
   if (sh->fused) {
@@ -126,15 +132,27 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
   if (n_tok > kMaxTokens)
     return fail(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^23 tokens", grid_h, grid_w);
   if (bh > kMaxSeqs) return fail(GTR_ERR_INVALID_ARG, "B*H = %lld exceeds 2^20", bh);
-  if (d_k != gtr::kHead || d_v != gtr::kHead)
-    return fail(GTR_ERR_UNSUPPORTED, "d_k=%d d_v=%d: this build supports d_k = d_v = 64", d_k, d_v);
+  if (d_k % 4 || d_v % 4 || d_k > kMaxHeadDim || d_v > kMaxHeadDim)
+    return fail(GTR_ERR_UNSUPPORTED, "d_k=%d d_v=%d: head dims must be multiples of 4, at most %d",
+                d_k, d_v, kMaxHeadDim);
+  // byte offsets inside one sequence's rows stay below 2^31
+  if (n_tok * std::max(d_k, d_v) * elem_size(dtype) > (1LL << 31))
+    return fail(GTR_ERR_INVALID_ARG, "%lld tokens of %d elements exceed 2^31 bytes per sequence",
+                n_tok, std::max(d_k, d_v));
   shape->bh = bh;
   shape->n_tok = n_tok;
+  shape->dk = d_k;
+  shape->dv = d_v;
+  shape->nk = (d_k + gtr::kHead - 1) / gtr::kHead;
+  shape->nvb = (d_v + gtr::kHead - 1) / gtr::kHead;
+  shape->seqs = bh * shape->nvb;
   shape->empty = bh == 0 || n_tok == 0;
   shape->n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  plan(bh, shape->n_chunk, path, chunks_per_segment, shape);
-  if (bh * shape->n_seg > 0x7fffffffLL)
-    return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", bh * shape->n_seg);
+  if (path == GTR_PATH_FUSED && shape->nk > 1)
+    return fail(GTR_ERR_UNSUPPORTED, "one-launch path: d_k=%d, at most 64", d_k);
+  plan(shape->seqs, shape->nk, shape->n_chunk, path, chunks_per_segment, shape);
+  if (shape->seqs * shape->n_seg * shape->nk > 0x7fffffffLL)
+    return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", shape->seqs * shape->n_seg);
   if (shape->fused && shape->n_seg > gtr::kMaxFusedSegments)
     return fail(GTR_ERR_INVALID_ARG,
                 "one-launch path: %d segments exceed %d (at most %d chunks per sequence); use "
@@ -160,18 +178,19 @@ int validate(const void *q, const void *k, const void *v, const void *g, const v
   for (int i = 0; i < 7; ++i)
     if (ptrs[i] && (reinterpret_cast<uintptr_t>(ptrs[i]) & 15u))
       return fail(GTR_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
-  const size_t nb = (size_t)(shape->bh * shape->n_tok * gtr::kHead) * elem_size(dtype);
-  const size_t sb = (size_t)shape->bh * gtr::kStateElems * sizeof(float);
+  const size_t kb = (size_t)(shape->bh * shape->n_tok * d_k) * elem_size(dtype);
+  const size_t vb = (size_t)(shape->bh * shape->n_tok * d_v) * elem_size(dtype);
+  const size_t sb = (size_t)shape->bh * d_k * d_v * sizeof(float);
   const void *ins[5] = {q, k, v, g, s0};
-  const size_t in_bytes[5] = {nb, nb, nb, nb, sb};
+  const size_t in_bytes[5] = {kb, kb, vb, kb, sb};
   for (int i = 0; i < 5; ++i) {
     if (!ins[i]) continue;
-    if (overlaps(out, nb, ins[i], in_bytes[i]))
+    if (overlaps(out, vb, ins[i], in_bytes[i]))
       return fail(GTR_ERR_ALIAS, "out overlaps %s", names[i]);
     if (s_final && overlaps(s_final, sb, ins[i], in_bytes[i]))
       return fail(GTR_ERR_ALIAS, "s_final overlaps %s", names[i]);
   }
-  if (s_final && overlaps(s_final, sb, out, nb)) return fail(GTR_ERR_ALIAS, "s_final overlaps out");
+  if (s_final && overlaps(s_final, sb, out, vb)) return fail(GTR_ERR_ALIAS, "s_final overlaps out");
   return GTR_OK;
 }
 
@@ -325,11 +344,12 @@ int check_call(const void *q, const void *k, const void *v, const void *log_gate
   // Pointer queries are not capture-safe on every runtime; calls being captured
   // rely on the same checks having passed for an eager call before capture.
   if (!capturing && !skip_pointer_checks()) {
-    const size_t nb = (size_t)(sh->bh * sh->n_tok * gtr::kHead) * elem_size(dtype);
-    const size_t sb = (size_t)sh->bh * gtr::kStateElems * sizeof(float);
+    const size_t kb = (size_t)(sh->bh * sh->n_tok * d_k) * elem_size(dtype);
+    const size_t vb = (size_t)(sh->bh * sh->n_tok * d_v) * elem_size(dtype);
+    const size_t sb = (size_t)sh->bh * d_k * d_v * sizeof(float);
     const void *ptrs[7] = {q, k, v, log_gate, out, s0, s_final};
     const char *names[7] = {"q", "k", "v", "log_gate", "out", "s0", "s_final"};
-    const size_t sizes[7] = {nb, nb, nb, nb, nb, sb, sb};
+    const size_t sizes[7] = {kb, kb, vb, kb, vb, sb, sb};
     for (int i = 0; i < 7; ++i) {
       if (!ptrs[i] || sizes[i] == 0) continue;
       rc = check_device_range(ptrs[i], sizes[i], *device, names[i]);
@@ -364,7 +384,7 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   if (sh.empty) {
     // no tokens: the state after the sequence is the state before it
     if (sh.bh == 0 || !s_final) return GTR_OK;
-    const int err = gtr::launch_state_copy(s0, s_final, sh.bh * gtr::kStateElems, stream);
+    const int err = gtr::launch_state_copy(s0, s_final, sh.bh * d_k * d_v, stream);
     if (err != (int)hipSuccess)
       return fail(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
     return GTR_OK;
@@ -376,7 +396,11 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   a.v = v;
   a.g = log_gate;
   a.out = out;
-  a.bh = (int)sh.bh;
+  a.bh = (int)sh.seqs;
+  a.d_k = d_k;
+  a.d_v = d_v;
+  a.nk = sh.nk;
+  a.nvb = sh.nvb;
   a.grid_h = grid_h;
   a.grid_w = grid_w;
   a.n_tok = (int)sh.n_tok;
@@ -395,11 +419,11 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   if (need_ws) {
     void *ws = nullptr;
     int *sync = nullptr, *flags = nullptr;
-    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.bh, sh.n_seg), sh.fused ? sh.bh : 0,
-                       sh.fused ? sh.bh * sh.n_seg : 0, &ws, &sync, &flags);
+    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk),
+                       sh.fused ? sh.seqs : 0, sh.fused ? sh.seqs * sh.n_seg : 0, &ws, &sync, &flags);
     if (rc != GTR_OK) return rc;
     float *f = static_cast<float *>(ws);
-    const size_t st = (size_t)sh.bh * sh.n_seg * gtr::kStateElems;
+    const size_t st = (size_t)sh.seqs * sh.n_seg * sh.nk * gtr::kStateElems;
     a.agg = f;
     a.prev = f + st;
     a.agg_dec = f + 2 * st;
@@ -447,15 +471,16 @@ size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, in
       GTR_OK)
     return 0;
   if (sh.empty) return 0;
-  return gtr::workspace_bytes(sh.bh, sh.n_seg) +
-         (sh.fused ? gtr::sync_words(sh.bh, sh.n_seg) * sizeof(int) : 0);
+  return gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk) +
+         (sh.fused ? gtr::sync_words(sh.seqs, sh.n_seg) * sizeof(int) : 0);
 }
 
-int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int chunks_per_segment, int path,
-                 int *seg_len, int *n_seg, int *fused) {
+int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,
+                 int path, int *seg_len, int *n_seg, int *fused) {
   Shape sh;
-  const int rc = validate_shape(B, H, grid_h, grid_w, gtr::kHead, gtr::kHead, 0, GTR_DTYPE_F16,
-                                chunks_per_segment, path, &sh);
+  g_last_error.clear();
+  const int rc = validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, GTR_DTYPE_F16, chunks_per_segment,
+                                path, &sh);
   if (rc != GTR_OK) return rc;
   if (seg_len) *seg_len = sh.seg_len;
   if (n_seg) *n_seg = sh.n_seg;

@@ -8,7 +8,7 @@
 namespace gtr {
 
 constexpr int kChunk = 64;   // tokens per chunk (the pages' operator uses 64)
-constexpr int kHead = 64;    // d_k = d_v handled by this build
+constexpr int kHead = 64;    // width of a key or value block (d_k, d_v <= 2 blocks)
 constexpr int kStateElems = kHead * kHead;
 constexpr int kMaxFusedChunks = 3;  // chunks per segment of the one-launch path (outputs held in registers)
 // Segments per sequence of the one-launch path.  Every segment folds the
@@ -19,7 +19,9 @@ constexpr int kMaxFusedSegments = 256;
 struct LaunchArgs {
   const void *q, *k, *v, *g;
   void *out;
-  int bh;            // B*H sequences
+  int bh;            // sequences: B*H*nvb (each head's value columns in 64-wide blocks)
+  int d_k, d_v;      // head dims (multiples of 4, at most 128)
+  int nk, nvb;       // 64-wide key blocks (1 or 2) and value blocks per head
   int grid_h, grid_w;
   int n_tok;         // grid_h*grid_w
   int direction;
@@ -28,13 +30,13 @@ struct LaunchArgs {
   int seg_len;       // chunks per segment
   int n_seg;         // ceil(n_chunk / seg_len)
   // workspace (float32), all in the register-order state layout
-  float *agg;        // [bh][n_seg][4096] segment state contributions
-  float *agg_dec;   // [bh][n_seg][64]   segment decay factor per key dim
-  float *prev;       // [bh][n_seg][4096] state entering each segment
+  float *agg;        // [seq][n_seg][nk][4096] segment state contributions
+  float *agg_dec;    // [seq][n_seg][nk][64]   segment decay factor per key dim
+  float *prev;       // [seq][n_seg][nk][4096] state entering each segment
   int *sync;         // fused path: header + per-sequence control lines (zeroed at allocation)
   int *flags;        // [bh][n_seg] fused path: aggregate-published flags, after the control lines
-  const float *s0;   // user initial state, row-major [bh][64][64], nullable
-  float *s_final;    // user final state, row-major [bh][64][64], nullable
+  const float *s0;   // user initial state, row-major [B*H][d_k][d_v], nullable
+  float *s_final;    // user final state, row-major [B*H][d_k][d_v], nullable
   bool fused;        // one launch (gla_fused) instead of three
   hipStream_t stream;
 };
@@ -43,9 +45,9 @@ constexpr int kSyncHeader = 32;  // fused-path header words (epoch, sequences do
 constexpr int kSyncEpochWord = 0, kSyncSeqDoneWord = 1, kSyncErrorWord = 2;
 constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (ticket, done)
 
-// Float workspace bytes for (bh, n_seg): agg, prev and agg_dec.
-inline size_t workspace_bytes(size_t bh, size_t n_seg) {
-  return bh * n_seg * (2 * (size_t)kStateElems + kHead) * sizeof(float);
+// Float workspace bytes for (sequences, n_seg, key blocks): agg, prev and agg_dec.
+inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
+  return seqs * n_seg * nk * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
 // Synchronisation words for the fused path: a control line per sequence, then
 // one flag per segment.  They live in their own zero-initialised allocation;

@@ -88,7 +88,7 @@ struct IoF32 {
   using T = float;
   using Raw = u4;  // 16 bytes
   __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
-  __device__ static float load1(const T *p) { return *p; }
+  __device__ static float from_bits(uint32_t b) { return __uint_as_float(b); }
   __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u4, v); }
 };
 
@@ -97,7 +97,7 @@ struct IoF16 {
   using Raw = u2;  // 8 bytes
   __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
   __device__ static f4 to_f4(Raw r) { return __builtin_convertvector(to_h4(r), f4); }
-  __device__ static float load1(const T *p) { return (float)*p; }
+  __device__ static float from_bits(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
   __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u2, __builtin_convertvector(v, h4)); }
 };
 
@@ -109,7 +109,7 @@ struct IoBF16 {
               __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
   }
   __device__ static h4 to_h4(Raw r) { return __builtin_convertvector(to_f4(r), h4); }
-  __device__ static float load1(const T *p) { return __uint_as_float((uint32_t)*p << 16); }
+  __device__ static float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
   __device__ static uint32_t rne(float f) {  // round to nearest even, quiet NaN kept
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
@@ -234,52 +234,55 @@ __device__ __forceinline__ void col_major_pos(int p, int gh, float rcp_gh, int &
 }
 
 constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer range: loads give 0, stores drop
+constexpr uint32_t kNoRow = 0xffffffffu;  // grid cell of a scan position past the end
 
 // One sequence's tensors as buffer resources: byte offsets are 32-bit and
-// uniform bases live in scalar registers; the range is the sequence's rows
-// (n_tok <= 2^23 rows of at most 256 bytes, checked on the host).
+// uniform bases live in scalar registers.  A sequence is one (batch, head) and
+// one 64-wide block of value columns: q, k and log_gate rows hold d_k elements,
+// v and out rows d_v, and the v/out resources start at the block's first
+// column.  Every range is at most 2^31 bytes (checked on the host), so kOob
+// plus a column offset is past all of them.
 struct Seq {
   __amdgpu_buffer_rsrc_t q, k, v, g, o;
   int n_tok, gh, gw, dir;
   float rcp_gh;
+  uint32_t kpitch, vpitch;  // bytes per grid cell of q/k/log_gate and of v/out
+  int dk, dv;               // key dims, value columns of this block (<= 64)
 };
 
-template <class Io>
-__device__ __forceinline__ Seq make_seq(const void *q, const void *k, const void *v, const void *g,
-                                        void *o, int bh, int n_tok, int gh, int gw, int dir,
-                                        float rcp_gh) {
-  using T = typename Io::T;
-  const size_t base = (size_t)bh * n_tok * kHead;
-  const int bytes = (int)((uint32_t)n_tok * kHead * sizeof(T));
-  auto rsrc = [&](const void *p) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(static_cast<const T *>(p) + base),
-                                             (short)0, bytes, 0x00020000);
-  };
-  return Seq{rsrc(q), rsrc(k), rsrc(v), rsrc(g), rsrc(o), n_tok, gh, gw, dir, rcp_gh};
+// Byte offset of (cell, col), or kOob for a missing row or a masked column.
+__device__ __forceinline__ uint32_t cell_at(uint32_t cell, uint32_t pitch, uint32_t col) {
+  return (cell == kNoRow || col == kOob) ? kOob : cell * pitch + col;
+}
+// Byte offset in a q/k/log_gate row of 4 key dims starting at d (kOob past d_k).
+template <class Io> __device__ __forceinline__ uint32_t key_col(const Seq &sq, int d) {
+  return d < sq.dk ? (uint32_t)d * (uint32_t)sizeof(typename Io::T) : kOob;
+}
+// Byte offset in a v/out row of this block's 4 value columns starting at j.
+template <class Io> __device__ __forceinline__ uint32_t val_col(const Seq &sq, int j) {
+  return j < sq.dv ? (uint32_t)j * (uint32_t)sizeof(typename Io::T) : kOob;
 }
 
-// Element offset of the row of scan position t (t < n_tok).
-__device__ __forceinline__ uint32_t token_row(const Seq &sq, int t) {
+// Grid cell of scan position t (t < n_tok).
+__device__ __forceinline__ uint32_t token_cell(const Seq &sq, int t) {
   const int p = (sq.dir & 1) ? sq.n_tok - 1 - t : t;
-  if (!(sq.dir & 2)) return (uint32_t)p * kHead;
+  if (!(sq.dir & 2)) return (uint32_t)p;
   int row, col;
   col_major_pos(p, sq.gh, sq.rcp_gh, row, col);
-  return (uint32_t)(row * sq.gw + col) * kHead;
+  return (uint32_t)(row * sq.gw + col);
 }
 
-// Byte offsets of the rows of scan positions t0 .. t0+3 (kOob past the end).
-// Consecutive scan positions step by one grid cell along the scan, so only the
-// first needs a division.
-template <class Io>
-__device__ __forceinline__ void rows4(const Seq &sq, int t0, uint32_t *off) {
-  constexpr uint32_t kRow = kHead * sizeof(typename Io::T);
+// Grid cells of scan positions t0 .. t0+3 (kNoRow past the end).  Consecutive
+// scan positions step by one grid cell along the scan, so only the first needs
+// a division.
+__device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell) {
   const bool rev = sq.dir & 1;
   const int p0 = rev ? sq.n_tok - 1 - t0 : t0;
   if (!(sq.dir & 2)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = rev ? p0 - r : p0 + r;
-      off[r] = t0 + r < sq.n_tok ? (uint32_t)p * kRow : kOob;
+      cell[r] = t0 + r < sq.n_tok ? (uint32_t)p : kNoRow;
     }
     return;
   }
@@ -287,7 +290,7 @@ __device__ __forceinline__ void rows4(const Seq &sq, int t0, uint32_t *off) {
   col_major_pos(p0, sq.gh, sq.rcp_gh, row, col);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    off[r] = t0 + r < sq.n_tok ? (uint32_t)(row * sq.gw + col) * kRow : kOob;
+    cell[r] = t0 + r < sq.n_tok ? (uint32_t)(row * sq.gw + col) : kNoRow;
     if (rev) {
       if (--row < 0) {
         row = sq.gh - 1;
@@ -329,12 +332,13 @@ template <typename Op, int NQ> struct Smem {
 struct Params {
   const void *q, *k, *v, *g;
   void *out;
-  int bh_count, n_tok, gh, gw, dir;
+  int bh_count, n_tok, gh, gw, dir;  // bh_count: sequences (batch x head x value block)
   float rcp_gh;
+  int dk, dv, nvb;  // key dims, value dims, 64-wide value blocks per head
   int n_chunk, seg_len, n_seg, n_seg_grid;
-  float *agg, *agg_dec;    // [bh][n_seg][4096] state contribution, [bh][n_seg][64] decay per key dim
-  const float *prev;       // [bh][n_seg][4096] register order (separate-launch path)
-  const float *s0;         // user initial state, row-major [bh][64][64], nullable
+  float *agg, *agg_dec;    // [seq][n_seg][key block][4096] state contribution, [..][64] decay per key dim
+  const float *prev;       // [seq][n_seg][key block][4096] register order (separate-launch path)
+  const float *s0;         // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;          // user final state, row-major, nullable
   int *sync;               // fused path: header, per-sequence control lines (kSync* words)
   int *flags;              // [bh][n_seg] fused path: segment aggregate published
@@ -349,8 +353,38 @@ struct Params {
 enum : int { kSyncEpoch = kSyncEpochWord, kSyncSeqDone = kSyncSeqDoneWord, kSyncError = kSyncErrorWord };
 enum : int { kCtlTicket = 0, kCtlDone = 1 };
 
-template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int bh) {
-  return make_seq<Io>(p.q, p.k, p.v, p.g, p.out, bh, p.n_tok, p.gh, p.gw, p.dir, p.rcp_gh);
+template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int seq) {
+  using T = typename Io::T;
+  constexpr uint32_t elt = sizeof(T);
+  const int bh = seq / p.nvb, vb = seq - bh * p.nvb;
+  const size_t kbase = (size_t)bh * p.n_tok * p.dk;
+  const size_t vbase = (size_t)bh * p.n_tok * p.dv + (size_t)kHead * vb;
+  const uint32_t kbytes = (uint32_t)p.n_tok * (uint32_t)p.dk * elt;
+  const uint32_t vbytes = (uint32_t)p.n_tok * (uint32_t)p.dv * elt - (uint32_t)(kHead * vb) * elt;
+  auto rsrc = [](const void *ptr, size_t base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(static_cast<const T *>(ptr) + base),
+                                             (short)0, (int)bytes, 0x00020000);
+  };
+  return Seq{rsrc(p.q, kbase, kbytes), rsrc(p.k, kbase, kbytes), rsrc(p.v, vbase, vbytes),
+             rsrc(p.g, kbase, kbytes), rsrc(p.out, vbase, vbytes), p.n_tok, p.gh, p.gw, p.dir,
+             p.rcp_gh, (uint32_t)p.dk * elt, (uint32_t)p.dv * elt, p.dk,
+             min(kHead, p.dv - kHead * vb)};
+}
+
+// Element (i, j) of a sequence's state in the caller's row-major [B*H][d_k][d_v]
+// layout, or -1 outside it (i counts within the head, j within the value block).
+__device__ __forceinline__ long long user_state_index(const Params &p, int seq, int i, int j) {
+  const int bh = seq / p.nvb, vb = seq - bh * p.nvb;
+  const int jj = kHead * vb + j;
+  if (i >= p.dk || jj >= p.dv) return -1;
+  return ((long long)bh * p.dk + i) * p.dv + jj;
+}
+// Row i = 0 of a sequence's value block in the caller's state, and whether
+// this lane's column j of the block exists.
+__device__ __forceinline__ size_t user_state_row0(const Params &p, int seq, int j, bool &col_ok) {
+  const int bh = seq / p.nvb, vb = seq - bh * p.nvb;
+  col_ok = kHead * vb + j < p.dv;
+  return (size_t)bh * p.dk * p.dv + (size_t)(kHead * vb + j);
 }
 
 // Register-order state layout: (wave w, lane l, reg x) holds element (i, j) with
@@ -358,11 +392,12 @@ template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int b
 __device__ __forceinline__ int state_i(int x, int lane) { return 16 * (x >> 2) + 4 * (lane >> 4) + (x & 3); }
 
 // This thread's slice of one chunk: 4 consecutive tokens 16w+4(l/16)+r, dims
-// 4(l%16)..+3, of each tensor (zeros past the end of the sequence: no key, no
-// value, no decay, no query there), and the tokens' row offsets.
+// 4(l%16)..+3 of one 64-wide key block and of the value block, of each tensor
+// (zeros past the end of the sequence and past d_k or d_v: no key, no value,
+// no decay, no query there), and the tokens' grid cells.
 template <class Io> struct Rows {
   typename Io::Raw q[4], k[4], v[4], g[4];
-  uint32_t off[4];
+  uint32_t off[4];  // grid cells (kNoRow past the end)
 };
 
 template <class Io>
@@ -381,16 +416,20 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
 
-template <class Io, bool kOut>
-__device__ __forceinline__ void load_chunk(const Seq &sq, int c, int wave, int lane, Rows<Io> &x) {
-  const uint32_t col = 4 * (lane & 15) * sizeof(typename Io::T);
-  rows4<Io>(sq, c * kChunk + 16 * wave + 4 * (lane >> 4), x.off);
+// kFirst: the chunk's first key block, which also finds the tokens' grid
+// cells and loads v; later key blocks reuse the cells.
+template <class Io, bool kOut, bool kFirst>
+__device__ __forceinline__ void load_chunk(const Seq &sq, int c, int kb, int wave, int lane, Rows<Io> &x) {
+  const int dq = lane & 15;
+  if constexpr (kFirst) cells4(sq, c * kChunk + 16 * wave + 4 * (lane >> 4), x.off);
+  const uint32_t kc = key_col<Io>(sq, kHead * kb + 4 * dq);
+  const uint32_t vc = val_col<Io>(sq, 4 * dq);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint32_t o = x.off[r] + col;  // kOob + col stays out of range
+    const uint32_t o = cell_at(x.off[r], sq.kpitch, kc);
     x.g[r] = buf_load<Io>(sq.g, o);
     x.k[r] = buf_load<Io>(sq.k, o);
-    x.v[r] = buf_load<Io>(sq.v, o);
+    if constexpr (kFirst) x.v[r] = buf_load<Io>(sq.v, cell_at(x.off[r], sq.vpitch, vc));
     if constexpr (kOut) x.q[r] = buf_load<Io>(sq.q, o);
   }
 }
@@ -414,12 +453,12 @@ __device__ __forceinline__ void row_products(float x, int g, float &before, floa
 // products of this thread's 4 tokens x 4 dims inside its wave's 16-token
 // sub-block scale the inputs: qs = q * (product of alpha from the sub-block
 // start through the token), ks = k * (product of alpha after the token to the
-// sub-block end).  qs, ks and v go to LDS, the sub-block product to sm.tot, the
-// row offsets to sm.rowoff[slot].  One exp2 per element; the rest are multiplications
-// and cross-row swaps.
+// sub-block end).  qs, ks and (first key block) v go to LDS, the sub-block
+// product to sm.tot, the grid cells to sm.rowoff[slot].  One exp2 per element;
+// the rest are multiplications and cross-row swaps.
 template <class Io, typename Op, bool kOut, int NQ>
 __device__ __forceinline__ void prep_local(Smem<Op, NQ> &sm, const Rows<Io> &x, int wave, int lane,
-                                           int slot, op4<Op> *qs, op4<Op> *ks) {
+                                           int slot, op4<Op> *qs, op4<Op> *ks, bool first) {
   constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
   const int g = lane >> 4, dq = lane & 15;
   f4 a[4];
@@ -442,7 +481,7 @@ __device__ __forceinline__ void prep_local(Smem<Op, NQ> &sm, const Rows<Io> &x, 
   for (int r = 0; r < 4; ++r) {
     const int tau = 16 * wave + 4 * g + r;
     ks[r] = ToOp<Op, Io>::cvt(x.k[r]) * to4<Op>(pk[r]);
-    *reinterpret_cast<op4<Op> *>(&sm.vv[tau * LDT + 4 * dq]) = ToOp<Op, Io>::cvt(x.v[r]);
+    if (first) *reinterpret_cast<op4<Op> *>(&sm.vv[tau * LDT + 4 * dq]) = ToOp<Op, Io>::cvt(x.v[r]);
     if constexpr (kOut) {
       qs[r] = ToOp<Op, Io>::cvt(x.q[r]) * to4<Op>(pq[r]);
       *reinterpret_cast<op4<Op> *>(&sm.qs[tau * LD + 4 * dq]) = qs[r];
@@ -450,7 +489,7 @@ __device__ __forceinline__ void prep_local(Smem<Op, NQ> &sm, const Rows<Io> &x, 
     }
   }
   if (g == 0) *reinterpret_cast<f4 *>(&sm.tot[wave * kHead + 4 * dq]) = all;
-  if (kOut && dq == 0) {
+  if (kOut && first && dq == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.rowoff[slot][16 * wave + 4 * g + r] = x.off[r];
   }
@@ -505,37 +544,46 @@ __device__ __forceinline__ void prep_chunk(Smem<Op, NQ> &sm, const op4<Op> *qs, 
   }
 }
 
-// Exact fp32 diagonal score tile (a, a) for a sub-block whose gate range is too
-// wide for midpoint scaling.  Re-reads q, k and log_gate rows from global memory.
+// One element of a q/k/log_gate row, as float.
+template <class Io> __device__ __forceinline__ float key_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(typename Io::T) == 4)
+    return Io::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  else
+    return Io::from_bits(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+
+// Exact fp32 diagonal score tile (a, a) of key block kb for a sub-block whose
+// gate range is too wide for midpoint scaling.  Re-reads q, k and log_gate
+// elements from global memory.
 template <class Io>
-__device__ f4 exact_diag(const Params &p, const Seq &sq, size_t base, int c, int a, int lane) {
-  using T = typename Io::T;
+__device__ f4 exact_diag(const Seq &sq, int c, int a, int kb, int lane) {
+  constexpr uint32_t elt = sizeof(typename Io::T);
   const int g = lane >> 4, l16 = lane & 15;
   const int t0 = c * kChunk + 16 * a;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (t0 + l16 >= p.n_tok) return acc;  // query beyond the sequence
-  const T *gb = static_cast<const T *>(p.g) + base;
-  const T *qrow = static_cast<const T *>(p.q) + base + token_row(sq, t0 + l16);
-  const T *krow[4];
+  if (t0 + l16 >= sq.n_tok) return acc;  // query beyond the sequence
+  const uint32_t qrow = token_cell(sq, t0 + l16) * sq.kpitch;
+  uint32_t krow[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {  // keys 4g+r <= l16 < n_tok exist; later keys are masked
     const int sl = 4 * g + r;
-    krow[r] = static_cast<const T *>(p.k) + base + token_row(sq, sl <= l16 ? t0 + sl : t0 + l16);
+    krow[r] = token_cell(sq, sl <= l16 ? t0 + sl : t0 + l16) * sq.kpitch;
   }
-  for (int i = 0; i < kHead; ++i) {
+  const int i_end = min(kHead * (kb + 1), sq.dk);
+  for (int i = kHead * kb; i < i_end; ++i) {
     // log2 gate sums from the sub-block start at the query and at each key
     float run = 0.f;
     float e_sig[4] = {0.f, 0.f, 0.f, 0.f};
     for (int u = 0; u <= l16; ++u) {
-      run += Io::load1(gb + token_row(sq, t0 + u) + i) * kLog2e;
+      run += key_elem<Io>(sq.g, token_cell(sq, t0 + u) * sq.kpitch + i * elt) * kLog2e;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (u == 4 * g + r) e_sig[r] = run;
     }
-    const float qi = Io::load1(qrow + i);
+    const float qi = key_elem<Io>(sq.q, qrow + i * elt);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * g + r <= l16) acc[r] += qi * Io::load1(krow[r] + i) * fast_exp2(run - e_sig[r]);
+      if (4 * g + r <= l16) acc[r] += qi * key_elem<Io>(sq.k, krow[r] + i * elt) * fast_exp2(run - e_sig[r]);
   }
   return acc;
 }
@@ -561,8 +609,7 @@ __device__ __forceinline__ void off_tile(Smem<Op, NQ> &sm, int a, int b, int lan
 // only).  Wave w forms the diagonal tile (w, w) and the off-diagonal tiles
 // (1,0),(2,1) | (2,0),(3,2) | (3,0) | (3,1).
 template <class Io, typename Op, int NQ>
-__device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t base, Smem<Op, NQ> &sm,
-                                       int c, int wave, int lane) {
+__device__ __forceinline__ void scores(const Seq &sq, Smem<Op, NQ> &sm, int c, int kb, int wave, int lane) {
   constexpr int LD = OpT<Op>::LD;
   const int g = lane >> 4, l16 = lane & 15;
   {
@@ -577,7 +624,7 @@ __device__ __forceinline__ void scores(const Params &p, const Seq &sq, size_t ba
                   frag_row<Op>(&sm.qs[(16 * a + l16) * LD + k0]) * h, acc);
       }
     } else {
-      acc = exact_diag<Io>(p, sq, base, c, a, lane);
+      acc = exact_diag<Io>(sq, c, a, kb, lane);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -604,9 +651,11 @@ enum : int {
   kKeep = 2,   // outputs formed with the state carried so far and kept in registers
 };
 
-// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T: rounded to the I/O format
-// into the output tile ot[token][dim] (kStore), or kept in keep[tt] (kKeep).
-template <class Io, typename Op, int kMode, int NQ>
+// O^T[16w:16w+16][chunk] = V^T P^T + S^T (q 2^E)^T for one key block, added to
+// keep[tt] (kAcc: an earlier key block's part).  The last key block (kFinal)
+// rounds the sum to the I/O format into the output tile ot[token][dim]
+// (kStore) or leaves it in keep (kKeep); earlier ones leave it in keep.
+template <class Io, typename Op, int kMode, bool kAcc, bool kFinal, int NQ>
 __device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int lane, int slot,
                                         const op8<Op> *vf, const f4 *S, typename OpT<Op>::Bits *ot,
                                         f4 *keep) {
@@ -618,6 +667,7 @@ __device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int la
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kAcc) acc = keep[tt];
 #pragma unroll
     for (int kb = 0; kb <= (tt >> 1); ++kb) {
       const op4<Op> lo = *reinterpret_cast<const op4<Op> *>(&sm.pt[tile_slot(tt, 2 * kb) * 256 + lane * 4]);
@@ -629,11 +679,11 @@ __device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int la
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
       acc = mma(sf[kb], frag_row<Op>(&sm.qh[slot][(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
-    if constexpr (kMode == kKeep)
-      keep[tt] = acc;
-    else
+    if constexpr (kMode == kStore && kFinal)
       *reinterpret_cast<typename Io::Raw *>(&ot[(16 * tt + l16) * OpT<Op>::LDO + 16 * wave + 4 * g]) =
           Io::pack(acc);
+    else
+      keep[tt] = acc;
   }
 }
 
@@ -649,172 +699,223 @@ __device__ __forceinline__ void carry_state(const Smem<Op, NQ> &sm, int lane, co
   }
 }
 
-// Stores a finished output tile: this thread's 4 tokens (rows off[r]) x 4
-// dims, so each store instruction writes whole 128/256-byte rows.
+// Stores a finished output tile: this thread's 4 tokens (grid cells cell[r])
+// x 4 dims, so each store instruction writes whole rows of the value block.
 template <class Io, typename Op>
 __device__ __forceinline__ void flush_tile(const Seq &sq, const typename OpT<Op>::Bits *ot,
-                                           const uint32_t *off, int wave, int lane) {
+                                           const uint32_t *cell, int wave, int lane) {
   const int g = lane >> 4, dq = lane & 15;
+  const uint32_t vc = val_col<Io>(sq, 4 * dq);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const typename Io::Raw v =
         *reinterpret_cast<const typename Io::Raw *>(&ot[(16 * wave + 4 * g + r) * OpT<Op>::LDO + 4 * dq]);
-    buf_store<Io>(sq.o, off[r] + 4 * dq * sizeof(typename Io::T), v);
+    buf_store<Io>(sq.o, cell_at(cell[r], sq.vpitch, vc), v);
   }
 }
 
-// One chunk, using LDS slot `slot` for what must outlive it.  Barriers: (1)
-// sub-block products and row offsets visible, (2) operand tiles visible, (3)
-// score tiles visible.  Everything a wave reads from LDS after the last barrier
-// of a chunk (pt, qh, kb, dec) is written only after the first barrier of the
-// next chunk, which no wave passes before every wave has finished this chunk;
-// v and the output row offsets, which the next chunk overwrites before its
-// first barrier, are read into registers before the second one.  The next
-// chunk's rows are loaded into x as soon as this chunk's have gone to LDS, and
-// arrive while the rest of this chunk computes.  seg_dec (wave 0, lanes < 16,
-// dims 4*lane..+3) accumulates the chunk decays; kKeep also records the decay
-// from the segment start to this chunk in sm.dcum[slot].  kStore: the previous
-// chunk's output tile (complete at this chunk's first barrier, rewritten only
-// after its third) is stored after the first barrier; pend carries the row
-// offsets of the tile's tokens from chunk to chunk.
-template <class Io, typename Op, int kMode, int NQ>
-__device__ __forceinline__ void chunk(const Params &p, const Seq &sq, size_t base, Smem<Op, NQ> &sm,
-                                      Rows<Io> &x, int c, int c_end, int wave, int lane, int slot,
-                                      f4 *S, f4 &seg_dec, f4 *keep, typename OpT<Op>::Bits *ot,
-                                      uint32_t *pend, bool have_pend) {
+// One chunk, using LDS slot `slot` for what must outlive it, as NK passes, one
+// per 64-wide key block: each pass carries its block's state S[kb] and adds its
+// part of the outputs (the scores and q S both sum over key dims); v is loaded
+// and staged once.  Barriers per pass: (1) sub-block products and grid cells
+// visible, (2) operand tiles visible, (3) score tiles visible.  Everything a
+// wave reads from LDS after the last barrier of a pass (pt, qh, kb, dec) is
+// written only after the first barrier of the next pass, which no wave passes
+// before every wave has finished this one; v and the output grid cells, which
+// the next chunk overwrites before its first barrier, are read into registers
+// before the second one.  The next pass's rows (the next key block, or the next
+// chunk's first) are loaded into x as soon as this pass's have gone to LDS,
+// and arrive while the rest of this pass computes.  seg_dec[kb] (wave 0, lanes
+// < 16, dims 4*lane..+3) accumulates the chunk decays; kKeep also records the
+// decay from the segment start to this chunk in sm.dcum[slot].  kStore: the
+// previous chunk's output tile (complete at this chunk's first barrier,
+// rewritten only after its last pass's third) is stored after the first
+// barrier; pend carries the grid cells of the tile's tokens from chunk to chunk.
+template <class Io, typename Op, int kMode, int NK, int NQ>
+__device__ __forceinline__ void chunk(const Seq &sq, Smem<Op, NQ> &sm, Rows<Io> &x, int c, int c_end,
+                                      int wave, int lane, int slot, f4 (*S)[4], f4 *seg_dec, f4 *keep,
+                                      typename OpT<Op>::Bits *ot, uint32_t *pend, bool have_pend) {
+  static_assert(kMode != kKeep || NK == 1, "outputs kept across a segment use one key block");
   constexpr bool kOut = kMode != kAgg;
-  op4<Op> qs[4], ks[4];
-  prep_local<Io, Op, kOut>(sm, x, wave, lane, slot, qs, ks);
-  uint32_t cur[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) cur[r] = x.off[r];
-  if (c + 1 < c_end) load_chunk<Io, kOut>(sq, c + 1, wave, lane, x);
-  lds_sync();
-  if constexpr (kMode == kStore) {
-    if (have_pend) flush_tile<Io, Op>(sq, ot, pend, wave, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pend[r] = cur[r];
-  }
-  prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, slot);
   op8<Op> vf[2];
+  f4 part[4];  // outputs summed over the key blocks so far
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_tr(sm.vv, 32 * kb, 16 * wave, lane);
-  if (kMode != kStore && wave == 0 && lane < 16) {
-    f4 t[4];
-    sub_block_products(sm, lane, t);
-    if constexpr (kMode == kKeep) *reinterpret_cast<f4 *>(&sm.dcum[slot][4 * lane]) = seg_dec;
-    seg_dec *= t[0] * t[1] * t[2] * t[3];
-  }
-  lds_sync();
-  if constexpr (kOut) {
-    scores<Io, Op>(p, sq, base, sm, c, wave, lane);
+  for (int kb = 0; kb < NK; ++kb) {
+    const bool first = kb == 0;
+    op4<Op> qs[4], ks[4];
+    prep_local<Io, Op, kOut>(sm, x, wave, lane, slot, qs, ks, first);
+    uint32_t cur[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cur[r] = x.off[r];
+    if (kb + 1 < NK)
+      load_chunk<Io, kOut, false>(sq, c, kb + 1, wave, lane, x);
+    else if (c + 1 < c_end)
+      load_chunk<Io, kOut, true>(sq, c + 1, 0, wave, lane, x);
     lds_sync();
-    outputs<Io, Op, kMode>(sm, wave, lane, slot, vf, S, ot, keep);
+    if constexpr (kMode == kStore) {
+      if (first) {
+        if (have_pend) flush_tile<Io, Op>(sq, ot, pend, wave, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pend[r] = cur[r];
+      }
+    }
+    prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, slot);
+    if (first) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) vf[b] = frag_tr(sm.vv, 32 * b, 16 * wave, lane);
+    }
+    if (kMode != kStore && wave == 0 && lane < 16) {
+      f4 t[4];
+      sub_block_products(sm, lane, t);
+      if constexpr (kMode == kKeep) *reinterpret_cast<f4 *>(&sm.dcum[slot][4 * lane]) = seg_dec[kb];
+      seg_dec[kb] *= t[0] * t[1] * t[2] * t[3];
+    }
+    lds_sync();
+    if constexpr (kOut) {
+      scores<Io, Op>(sq, sm, c, kb, wave, lane);
+      lds_sync();
+      f4 *acc = kMode == kKeep ? keep : part;
+      if (kb == 0 && kb + 1 == NK)
+        outputs<Io, Op, kMode, false, true>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+      else if (kb == 0)
+        outputs<Io, Op, kMode, false, false>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+      else if (kb + 1 == NK)
+        outputs<Io, Op, kMode, true, true>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+      else
+        outputs<Io, Op, kMode, true, false>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+    }
+    carry_state<Op>(sm, lane, vf, S[kb]);
   }
-  carry_state<Op>(sm, lane, vf, S);
 }
 
-// Walks chunks [c_begin, c_end) of sequence bh, carrying S (kAgg or kStore):
+// Walks chunks [c_begin, c_end) of sequence `seq`, carrying S (kAgg or kStore):
 // kStore writes the outputs (S must hold the state entering the first chunk);
 // kAgg only carries S (from zero: the segment's own aggregate) and multiplies
 // the chunk decays into seg_dec.
-template <class Io, typename Op, int kMode, int NQ>
-__device__ __forceinline__ void walk(const Params &p, int bh, Smem<Op, NQ> &sm, int c_begin, int c_end,
-                                     int wave, int lane, f4 *S, f4 &seg_dec,
+template <class Io, typename Op, int kMode, int NK, int NQ>
+__device__ __forceinline__ void walk(const Params &p, int seq, Smem<Op, NQ> &sm, int c_begin, int c_end,
+                                     int wave, int lane, f4 (*S)[4], f4 *seg_dec,
                                      typename OpT<Op>::Bits *ot = nullptr) {
   static_assert(kMode != kKeep, "kKeep walks are unrolled by their kernel");
-  const Seq sq = seq_of<Io>(p, bh);
-  const size_t base = (size_t)bh * p.n_tok * kHead;
+  const Seq sq = seq_of<Io>(p, seq);
   Rows<Io> x;
   uint32_t pend[4];
-  load_chunk<Io, kMode != kAgg>(sq, c_begin, wave, lane, x);
+  load_chunk<Io, kMode != kAgg, true>(sq, c_begin, 0, wave, lane, x);
   for (int c = c_begin; c < c_end; ++c)
-    chunk<Io, Op, kMode>(p, sq, base, sm, x, c, c_end, wave, lane, 0, S, seg_dec, nullptr, ot, pend,
-                         c > c_begin);
+    chunk<Io, Op, kMode, NK>(sq, sm, x, c, c_end, wave, lane, 0, S, seg_dec, nullptr, ot, pend,
+                             c > c_begin);
   if constexpr (kMode == kStore) {
     lds_sync();  // the last output tile is complete
     flush_tile<Io, Op>(sq, ot, pend, wave, lane);
   }
 }
 
-__device__ __forceinline__ void store_state_rowmajor(float *dst, int wave, int lane, const f4 *S) {
+// Writes key block kb of a register-order state into the caller's row-major
+// [B*H][d_k][d_v] state (elements past d_k or d_v are not written).
+__device__ __forceinline__ void store_user_state(const Params &p, float *dst, int seq, int kb, int wave,
+                                                 int lane, const f4 *S) {
+  bool col_ok;
+  float *d = dst + user_state_row0(p, seq, 16 * wave + (lane & 15), col_ok);
 #pragma unroll
-  for (int x = 0; x < 16; ++x) dst[state_i(x, lane) * kHead + 16 * wave + (lane & 15)] = S[x >> 2][x & 3];
+  for (int x = 0; x < 16; ++x) {
+    const int i = kHead * kb + state_i(x, lane);
+    if (col_ok && i < p.dk) d[(size_t)i * p.dv] = S[x >> 2][x & 3];
+  }
 }
 
 // ------------------------------------------------------------------ kernels
-template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void gla_seg_state(Params p) {
+// Workspace layout: [seq][segment][key block] then 4096 register-order state
+// elements, or 64 decays.
+template <int NK> __device__ __forceinline__ size_t ws_block(const Params &p, int seq, int seg, int kb) {
+  return ((size_t)seq * p.n_seg + seg) * NK + kb;
+}
+
+template <class Io, typename Op, int NK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : 2, NK == 1 ? 3 : 2))) void gla_seg_state(Params p) {
   __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / p.n_seg_grid;
-  const int seg = blockIdx.x - bh * p.n_seg_grid;
-  f4 S[4] = {};
-  f4 sdec = {1.f, 1.f, 1.f, 1.f};
-  const int c0 = seg * p.seg_len;
-  walk<Io, Op, kAgg>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
-  const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
+  const int seq = blockIdx.x / p.n_seg_grid;
+  const int seg = blockIdx.x - seq * p.n_seg_grid;
+  f4 S[NK][4] = {};
+  f4 sdec[NK];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) p.agg[st + x * 64] = S[x >> 2][x & 3];
-  if (wave == 0 && lane < 16)
-    *reinterpret_cast<f4 *>(&p.agg_dec[((size_t)bh * p.n_seg + seg) * kHead + 4 * lane]) = sdec;
+  for (int kb = 0; kb < NK; ++kb) sdec[kb] = f4{1.f, 1.f, 1.f, 1.f};
+  const int c0 = seg * p.seg_len;
+  walk<Io, Op, kAgg, NK>(p, seq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, sdec);
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) {
+    const size_t st = ws_block<NK>(p, seq, seg, kb) * kStateElems + wave * 1024 + lane;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) p.agg[st + x * 64] = S[kb][x >> 2][x & 3];
+    if (wave == 0 && lane < 16)
+      *reinterpret_cast<f4 *>(&p.agg_dec[ws_block<NK>(p, seq, seg, kb) * kHead + 4 * lane]) = sdec[kb];
+  }
 }
 
 // (Its output tile brings LDS to 63.6 KB at 16-bit I/O: two workgroups per CU.)
-template <class Io, typename Op>
+template <class Io, typename Op, int NK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_seg_out(Params p) {
   __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / p.n_seg;
-  const int seg = blockIdx.x - bh * p.n_seg;
-  f4 S[4] = {};
+  const int seq = blockIdx.x / p.n_seg;
+  const int seg = blockIdx.x - seq * p.n_seg;
+  f4 S[NK][4] = {};
   if (p.prev) {
-    const size_t st = ((size_t)bh * p.n_seg + seg) * kStateElems + wave * 1024 + lane;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = p.prev[st + x * 64];
+    for (int kb = 0; kb < NK; ++kb) {
+      const size_t st = ws_block<NK>(p, seq, seg, kb) * kStateElems + wave * 1024 + lane;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) S[kb][x >> 2][x & 3] = p.prev[st + x * 64];
+    }
   }
   __shared__ __attribute__((aligned(16))) typename OpT<Op>::Bits ot[kChunk * OpT<Op>::LDO];
-  f4 unused = {};
+  f4 unused[NK];
   const int c0 = seg * p.seg_len;
-  walk<Io, Op, kStore>(p, bh, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused, ot);
+  walk<Io, Op, kStore, NK>(p, seq, sm, c0, min(c0 + p.seg_len, p.n_chunk), wave, lane, S, unused, ot);
 }
 
-// Boundary-state recurrence over segments, one thread per (sequence, state
-// element): prev[seg] = state entering segment seg; prev[0] = s0 (or 0).
-// Loads of a batch of segments are issued together; only the fused
-// multiply-adds are sequential.
-__global__ __launch_bounds__(kThreads) void gla_seg_scan(const float *agg, const float *agg_dec,
-                                                         float *prev, const float *s0,
-                                                         float *s_final, int bh_count, int n_seg) {
+// Boundary-state recurrence over segments, one thread per (sequence, key
+// block, state element): prev[seg] = state entering segment seg; prev[0] = s0
+// (or 0).  Loads of a batch of segments are issued together; only the fused
+// multiply-adds are sequential.  Segments are NK*4096 floats apart, a
+// compile-time stride, so a batch's loads share one address.
+template <int NK>
+__global__ __launch_bounds__(kThreads) void gla_seg_scan(Params p) {
   constexpr int kBatch = 32;
+  constexpr int kPerSeq = NK * kStateElems;
   const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
-  const int bh = (int)(gid / kStateElems);
-  const int e = (int)(gid - (long)bh * kStateElems);
-  if (bh >= bh_count) return;
+  const int seq = (int)(gid / kPerSeq);
+  if (seq >= p.bh_count) return;
+  const int eb = (int)(gid - (long)seq * kPerSeq);
+  const int kb = eb / kStateElems, e = eb - kb * kStateElems;
   const int w = e >> 10, x = (e >> 6) & 15, l = e & 63;
   const int i = state_i(x, l);
-  const int j = 16 * w + (l & 15);
-  const size_t sbase = (size_t)bh * n_seg;
-  float s = s0 ? s0[(size_t)bh * kStateElems + i * kHead + j] : 0.f;
-  const int steps = s_final ? n_seg : n_seg - 1;
-  prev[sbase * kStateElems + e] = s;
+  const int n_seg = p.n_seg;
+  const size_t first = (size_t)seq * n_seg * NK + kb;  // workspace block of segment 0
+  const float *agg = p.agg + first * kStateElems + e;
+  const float *dec = p.agg_dec + first * kHead + i;
+  float *prev = const_cast<float *>(p.prev) + first * kStateElems + e;
+  const long long user = (p.s0 || p.s_final) ? user_state_index(p, seq, kHead * kb + i, 16 * w + (l & 15)) : -1;
+  float s = (p.s0 && user >= 0) ? p.s0[user] : 0.f;
+  const int steps = p.s_final ? n_seg : n_seg - 1;
+  prev[0] = s;
   for (int b0 = 0; b0 < steps; b0 += kBatch) {
     float av[kBatch], dv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int seg = min(b0 + u, steps - 1);
-      av[u] = agg[(sbase + seg) * kStateElems + e];
-      dv[u] = agg_dec[(sbase + seg) * kHead + i];
+      av[u] = agg[(size_t)seg * kPerSeq];
+      dv[u] = dec[(size_t)seg * NK * kHead];
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + u < steps) {
         s = dv[u] * s + av[u];
-        if (b0 + u + 1 < n_seg) prev[(sbase + b0 + u + 1) * kStateElems + e] = s;
+        if (b0 + u + 1 < n_seg) prev[(size_t)(b0 + u + 1) * kPerSeq] = s;
       }
     }
   }
-  if (s_final) s_final[(size_t)bh * kStateElems + i * kHead + j] = s;
+  if (p.s_final && user >= 0) p.s_final[user] = s;
 }
 
 // Publication between workgroups, which may sit on different XCDs whose L2
@@ -885,7 +986,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
   const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
   const size_t sbase = (size_t)bh * p.n_seg;
   const Seq sq = seq_of<Io>(p, bh);
-  const size_t base = (size_t)bh * p.n_tok * kHead;
 
   // 1. the segment from a zero state
   f4 keep[kSeg][4];
@@ -893,12 +993,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
   f4 sdec = {1.f, 1.f, 1.f, 1.f};
   {
     Rows<Io> x;
-    load_chunk<Io, true>(sq, c0, wave, lane, x);
+    load_chunk<Io, true, true>(sq, c0, 0, wave, lane, x);
 #pragma unroll
     for (int j = 0; j < kSeg; ++j)
       if (c0 + j < c1)
-        chunk<Io, Op, kKeep>(p, sq, base, sm, x, c0 + j, c1, wave, lane, j, L, sdec, keep[j], nullptr,
-                             nullptr, false);
+        chunk<Io, Op, kKeep, 1>(sq, sm, x, c0 + j, c1, wave, lane, j, &L, &sdec, keep[j], nullptr,
+                                nullptr, false);
   }
   // decay across the whole segment, read in step 5; tot is not read after a
   // chunk's last barrier, so wave 0 may overwrite it while others finish
@@ -963,9 +1063,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
       i -= nb;
     }
     if (p.s0) {
+      bool col_ok;
+      const float *s0 = p.s0 + user_state_row0(p, bh, lane, col_ok);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        X[r] += dacc[r] * p.s0[(size_t)bh * kStateElems + (16 * wave + r) * kHead + lane];
+      for (int r = 0; r < 16; ++r)  // row 16w + r: uniform across the wave
+        if (col_ok && 16 * wave + r < p.dk) X[r] += dacc[r] * s0[(size_t)(16 * wave + r) * p.dv];
     }
     float *xs = reinterpret_cast<float *>(sm.qs);
     constexpr int kLdX = 68;
@@ -987,11 +1089,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
       after[it] = L[it];
       if (have_prev) after[it] += *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
     }
-    store_state_rowmajor(p.s_final + (size_t)bh * kStateElems, wave, lane, after);
+    store_user_state(p, p.s_final, bh, 0, wave, lane, after);
   }
 
   // 4. add each chunk's share of S_prev and store
-  const uint32_t col = (16 * wave + 4 * g) * sizeof(typename Io::T);
+  const uint32_t col = val_col<Io>(sq, 16 * wave + 4 * g);
   constexpr int LD = OpT<Op>::LD;
 #pragma unroll
   for (int j = 0; j < kSeg; ++j) {
@@ -1011,7 +1113,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
           keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
     }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) buf_store<Io>(sq.o, sm.rowoff[j][16 * tt + l16] + col, Io::pack(keep[j][tt]));
+    for (int tt = 0; tt < 4; ++tt)
+      buf_store<Io>(sq.o, cell_at(sm.rowoff[j][16 * tt + l16], sq.vpitch, col), Io::pack(keep[j][tt]));
   }
 
   // 5. a sequence's last workgroup resets its ticket and done counters; the
@@ -1041,17 +1144,19 @@ void launch(int id, K kernel, unsigned blocks, hipStream_t stream, Args... args)
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, stream, args...);
 }
 
-template <class Io, typename Op>
+template <class Io, typename Op, int NK>
 int launch_typed(const LaunchArgs &a) {
   Params p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.out = a.out;
   p.bh_count = a.bh; p.n_tok = a.n_tok; p.gh = a.grid_h; p.gw = a.grid_w; p.dir = a.direction;
+  p.dk = a.d_k; p.dv = a.d_v; p.nvb = a.nvb;
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.n_chunk = a.n_chunk; p.seg_len = a.seg_len; p.n_seg = a.n_seg; p.n_seg_grid = a.n_seg;
   p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
   p.flags = a.flags; p.sync = a.sync;
   const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
   if (a.fused) {
+    if constexpr (NK != 1) return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
     if (a.seg_len <= 1)
       launch(kKernelFused, gla_fused<Io, Op, 1>, n_blocks, a.stream, p);
     else if (a.seg_len == 2)
@@ -1068,15 +1173,13 @@ int launch_typed(const LaunchArgs &a) {
     if (n_state_seg > 0) {
       Params ps = p;
       ps.n_seg_grid = n_state_seg;
-      launch(kKernelSegState, gla_seg_state<Io, Op>, (unsigned)(a.bh * n_state_seg), a.stream, ps);
+      launch(kKernelSegState, gla_seg_state<Io, Op, NK>, (unsigned)(a.bh * n_state_seg), a.stream, ps);
     }
-    const long threads = (long)a.bh * kStateElems;
-    launch(kKernelSegScan, gla_seg_scan, (unsigned)((threads + kThreads - 1) / kThreads), a.stream,
-           (const float *)a.agg, (const float *)a.agg_dec, a.prev, a.s0, a.s_final, a.bh,
-           a.n_seg);
     p.prev = a.prev;
+    const long threads = (long)a.bh * NK * kStateElems;
+    launch(kKernelSegScan, gla_seg_scan<NK>, (unsigned)((threads + kThreads - 1) / kThreads), a.stream, p);
   }
-  launch(kKernelSegOut, gla_seg_out<Io, Op>, n_blocks, a.stream, p);
+  launch(kKernelSegOut, gla_seg_out<Io, Op, NK>, n_blocks, a.stream, p);
   return (int)hipGetLastError();
 }
 
@@ -1096,10 +1199,11 @@ int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t 
 }
 
 int launch_gla(const LaunchArgs &a) {
+  const bool two = a.nk == 2;
   switch (a.dtype) {
-    case 0: return launch_typed<IoF32, float>(a);
-    case 1: return launch_typed<IoF16, _Float16>(a);
-    case 2: return launch_typed<IoBF16, _Float16>(a);
+    case 0: return two ? launch_typed<IoF32, float, 2>(a) : launch_typed<IoF32, float, 1>(a);
+    case 1: return two ? launch_typed<IoF16, _Float16, 2>(a) : launch_typed<IoF16, _Float16, 1>(a);
+    case 2: return two ? launch_typed<IoBF16, _Float16, 2>(a) : launch_typed<IoBF16, _Float16, 1>(a);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -49,7 +49,12 @@ def test_version_and_sizes():
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
         6 * 25 * (2 * 4096 + 64) * 4 + (32 + 6 * (32 + 25)) * 4
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 0, 0) == 0
+    # head dims: value columns in 64-wide blocks are sequences of their own, key blocks share one
+    per = (2 * 4096 + 64) * 4
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 1, split) == 6 * 25 * per
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 128, 1, 1, split) == 12 * 25 * per
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 128, 64, 1, 1, split) == 6 * 25 * 2 * per
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 132, 64, 1, 0, 0) == 0
     assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0, 0) == 0
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 0, 3) == 0
 
@@ -86,6 +91,12 @@ def test_plans():
     assert gla.gtr_gla_plan(1, 1, 769, 64, chunks_per_segment=3)["fused"] is False
     with pytest.raises(gla.GlaError):
         gla.gtr_gla_plan(1, 1, -1, 1)
+    # head dims: the kernels walk one sequence per 64-wide value block; d_k > 64 takes three launches
+    assert gla.gtr_gla_plan(8, 6, 40, 40, d_k=32, d_v=32)["fused"]
+    assert not gla.gtr_gla_plan(8, 6, 40, 40, d_k=128, d_v=64)["fused"]
+    with pytest.raises(gla.GlaError):
+        gla.gtr_gla_plan(8, 6, 40, 40, path=gla.GTR_PATH_FUSED, d_k=128)
+    assert gla.gtr_gla_plan(1, 6, 40, 40, d_k=64, d_v=128) == gla.gtr_gla_plan(1, 12, 40, 40)
 
 
 A = 0x10000  # fake, 16-byte aligned, never dereferenced
@@ -103,7 +114,7 @@ def call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, out=A + 0x400000, 
     (dict(d=4), -1), (dict(d=-1), -1), (dict(dt=3), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1),
     (dict(path=3), -1), (dict(path=-1), -1),
     (dict(B=1 << 11, H=1 << 10), -1),
-    (dict(dk=32), -2), (dict(dv=128), -2),
+    (dict(dk=132), -2), (dict(dv=30), -2), (dict(dk=256), -2), (dict(dk=128, path=1), -2),
     (dict(k=A + 0x100008), -3), (dict(out=A + 0x400004), -3), (dict(s0=A + 0x500002), -3),
     (dict(out=A + 0x200000), -4), (dict(out=A + 0x300000 + 0x400), -4),
     (dict(sf=A + 0x400000), -4), (dict(s0=A + 0x500000, sf=A + 0x500000), -4),

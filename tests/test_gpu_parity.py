@@ -100,6 +100,52 @@ def test_unit_gate_long_sequence():
     check(q, k, v, g, 1, "f16", "ones 128x128")
 
 
+# ---- head dims: 64-wide key blocks walked together, value blocks as sequences of their own,
+#      narrower heads masked --------------------------------------------------------------
+
+HEAD_DIMS = [(32, 32), (32, 64), (64, 32), (128, 64), (64, 128), (128, 128), (32, 128), (128, 32),
+             (4, 8), (96, 76), (124, 4)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("dims", HEAD_DIMS, ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+def test_head_dims(dims, dtype):
+    dk, dv = dims
+    q, k, v, g = gla_inputs.make_inputs(2, 3, 9, 17, dk, dv, dtype, "light", seed=dk * 1000 + dv)
+    runs = [(2, 1), (2, 3), (0, 0)] + ([(1, 2)] if dk <= 64 else [])  # (path, chunks per segment)
+    for d in range(4):
+        path, seg = runs[d % len(runs)]
+        check(q, k, v, g, d, dtype, f"dk={dk} dv={dv}", path=path, chunks_per_segment=seg)
+
+
+@pytest.mark.parametrize("dims", [(128, 64), (64, 128), (32, 96), (128, 128), (100, 36)],
+                         ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_head_dims_state(dims, dtype):
+    dk, dv = dims
+    B, H, gh, gw = 1, 2, 11, 13
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, dk, dv, dtype, "light", seed=dk + dv)
+    s0 = torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(dk * dv)) * 0.5
+    runs = [(2, 1), (2, 4)] + ([(1, 1), (1, 3)] if dk <= 64 else [])
+    for d, (path, seg) in zip(range(4), runs * 2):
+        note(f"state dk={dk} dv={dv} dir={d} dtype={dtype} path={path} seg={seg}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg,
+                        path=path)
+        ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
+        es = parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")
+        assert es["ok"], es
+
+
+@pytest.mark.parametrize("gate", ["const:-30", "mixed_extreme", "ones"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gate_extremes_wide_heads(gate, dtype):
+    """The exact diagonal tiles of the second key block, and masked value columns."""
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 13, 11, 128, 96, dtype, gate, seed=21)
+    for d, seg in ((1, 1), (3, 2)):
+        check(q, k, v, g, d, dtype, f"wide gate={gate}", path=2, chunks_per_segment=seg)
+
+
 # ---- initial / final state -----------------------------------------------------------------
 
 @pytest.mark.parametrize("seg", [1, 3])
