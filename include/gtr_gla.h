@@ -62,8 +62,10 @@
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
  *
- * Supported sizes (first build): d_k = d_v = 64; 0 <= grid_h*grid_w <= 2^23;
- * 0 <= B*H <= 2^20.  Pointers must be 16-byte aligned.
+ * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
+ * case; the one-launch path takes d_k <= 64); 0 <= grid_h*grid_w <= 2^23 and
+ * grid_h*grid_w*max(d_k, d_v)*element bytes <= 2^31; 0 <= B*H <= 2^20.
+ * Pointers must be 16-byte aligned.
  *
  * Empty calls: with B*H == 0 or no tokens there is nothing to compute and
  * tensor pointers may be NULL; the call returns GTR_OK without touching the
@@ -100,7 +102,8 @@ extern "C" {
 /* return codes: 0 on success, negative on error */
 #define GTR_OK 0
 #define GTR_ERR_INVALID_ARG (-1)  /* null pointer, negative or too large size, bad direction/dtype/path */
-#define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v other than 64 */
+#define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v above 128 or not a multiple of 4;
+                                     d_k > 64 on GTR_PATH_FUSED */
 #define GTR_ERR_ALIGNMENT (-3)    /* a pointer is not 16-byte aligned */
 #define GTR_ERR_ALIAS (-4)        /* out (or s_final) overlaps an input */
 #define GTR_ERR_NO_DEVICE (-5)    /* no usable HIP device */

@@ -115,6 +115,7 @@ def call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, out=A + 0x400000, 
     (dict(path=3), -1), (dict(path=-1), -1),
     (dict(B=1 << 11, H=1 << 10), -1),
     (dict(dk=132), -2), (dict(dv=30), -2), (dict(dk=256), -2), (dict(dk=128, path=1), -2),
+    (dict(gh=1 << 11, gw=1 << 12, dk=128, dt=0), -1),  # 2^23 rows of 512 bytes: past 2^31 bytes
     (dict(k=A + 0x100008), -3), (dict(out=A + 0x400004), -3), (dict(s0=A + 0x500002), -3),
     (dict(out=A + 0x200000), -4), (dict(out=A + 0x300000 + 0x400), -4),
     (dict(sf=A + 0x400000), -4), (dict(s0=A + 0x500000, sf=A + 0x500000), -4),

@@ -254,6 +254,16 @@ def test_deterministic_bitwise(path):
         assert torch.equal(o, outs[0])
 
 
+def test_deterministic_bitwise_wide_heads():
+    """Two key blocks and two value blocks (d_k = 128, d_v = 96): repeated calls are bitwise equal."""
+    q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 3, 23, 29, 128, 96, "bf16", "light",
+                                                              seed=22))
+    outs = [gla.gla_forward(q, k, v, g, 3, chunks_per_segment=2) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
 def test_streams_run_concurrently_with_their_own_workspaces():
     """Calls in flight on two streams at once (each stream has its own workspace) give the results
     of the same calls made one after the other; no one-launch wait gives up."""
