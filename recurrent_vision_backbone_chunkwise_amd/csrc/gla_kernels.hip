@@ -36,6 +36,12 @@
 //   * wave w owns value columns [16w, 16w+16): it forms O^T = V^T P^T +
 //     S^T (q 2^E)^T for those columns and carries S[:, 16w:16w+16].
 //
+// Head dims.  The tiles are 64 wide.  Narrower heads load zeros past d_k or
+// d_v and drop those stores; with d_v = 128 each 64-column value block is a
+// sequence of its own (the recurrence is independent per value column); with
+// d_k = 128 every chunk runs as two passes, one per 64-wide key block, each
+// carrying its block's state and adding its part to the same outputs.
+//
 // MFMA fragment convention (checked on gfx950): for v_mfma_f32_16x16x32_f16
 // lane l holds A row l%16 and B column l%16 with k-slots 8*(l/16)+e, and the
 // 16x16 fp32 result holds column l%16, rows 4*(l/16)+r.  Operands here use the
@@ -323,7 +329,7 @@ template <typename Op, int NQ> struct Smem {
   alignas(16) float dec[kHead];     // 2^E_last: decay of the state across the chunk
   // One slot per chunk whose outputs wait for the state entering the segment
   // (NQ = 1 when outputs are stored as each chunk completes).
-  alignas(16) uint32_t rowoff[NQ][kChunk];  // byte offset of each token's row (kOob past the end)
+  alignas(16) uint32_t rowoff[NQ][kChunk];  // grid cell of each token (kNoRow past the end)
   alignas(16) float dcum[NQ][kHead];        // decay from the segment start to the chunk start
   alignas(16) Op qh[NQ][kChunk * LD];       // q 2^E
 };
