@@ -102,3 +102,54 @@ def workload_inputs(w: Workload, layer: int):
     """Inputs of call ``layer`` (0-based position in the step) of workload ``w``."""
     return make_inputs(w.B, w.H, w.grid_h, w.grid_w, w.d_k, w.d_v, w.dtype, w.gate,
                        seed=1000 * w.index + layer)
+
+
+# ---- Spatial SwiGLU block (the layer's other half) ------------------------------------------
+#
+# Recipe: ``torch.Generator('cpu').manual_seed(seed)``; draw, in this order and as float32,
+# x ~ N(0, 1) [B, grid_h, grid_w, C], w_in ~ N(0, 1/C) [C, 2F], conv_w ~ N(0, 1/9) [3, 3, F],
+# conv_b ~ N(0, 0.1^2) [F] and w_out ~ N(0, 1/F) [F, C]; then round to the I/O dtype.  The
+# pages give neither the channel width nor the hidden width of the block; the workloads take
+# C = heads x 64 of the matching attention workload and F = 8C/3 rounded up to a multiple
+# of 64 (the usual SwiGLU width).
+
+@dataclass(frozen=True)
+class SwigluWorkload:
+    name: str
+    B: int
+    grid_h: int
+    grid_w: int
+    C: int
+    F: int
+    dtype: str
+    seed: int
+
+    @property
+    def n_tok(self) -> int:
+        return self.grid_h * self.grid_w
+
+
+SWIGLU_WORKLOADS = (
+    SwigluWorkload("swiglu_grid40x40_c384_f1024_f16", 1, 40, 40, 384, 1024, "f16", 7001),
+    SwigluWorkload("swiglu_grid128x128_c1024_f2752_f16", 1, 128, 128, 1024, 2752, "f16", 7002),
+)
+
+
+def swiglu_workload(idx_or_name) -> SwigluWorkload:
+    for i, w in enumerate(SWIGLU_WORKLOADS, start=1):
+        if i == idx_or_name or w.name == idx_or_name:
+            return w
+    raise KeyError(idx_or_name)
+
+
+def make_swiglu_inputs(B, grid_h, grid_w, C, F, dtype="f16", seed=0, bias=True):
+    """Return (x, w_in, conv_w, conv_b or None, w_out) as CPU tensors of the I/O dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn((B, grid_h, grid_w, C), generator=g, dtype=torch.float32)
+    w_in = torch.randn((C, 2 * F), generator=g, dtype=torch.float32) / math.sqrt(C)
+    conv_w = torch.randn((3, 3, F), generator=g, dtype=torch.float32) / 3.0
+    conv_b = torch.randn((F,), generator=g, dtype=torch.float32) * 0.1
+    w_out = torch.randn((F, C), generator=g, dtype=torch.float32) / math.sqrt(F)
+    t = TORCH_DTYPES[dtype]
+    return (x.to(t), w_in.to(t), conv_w.to(t), conv_b.to(t) if bias else None, w_out.to(t))

@@ -30,7 +30,16 @@ def ulp(x, dtype: str) -> np.ndarray:
     return np.exp2(e - mant)
 
 
-def parity_errors(y, o, dtype: str) -> dict:
+# Spatial SwiGLU block: the same gates, except bfloat16, whose hidden activations
+# are rounded to bfloat16 before the output projection (the projection's
+# operands share the I/O type).  That second rounding alone leaves about 0.8e-2
+# of rms after the output's own half-ulp is removed (two roundings of 2^-9
+# each, the first passed through W_o with about unit gain, measured on the
+# block's workloads in an fp64 simulation); the bound is twice that.
+SWIGLU_TOLERANCE = {"f32": 1e-4, "f16": 1e-2, "bf16": 2e-2}
+
+
+def parity_errors(y, o, dtype: str, tolerance: dict | None = None) -> dict:
     y = np.asarray(y, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     if y.shape != o.shape:
@@ -46,7 +55,8 @@ def parity_errors(y, o, dtype: str) -> dict:
     floor = float(np.max(0.5 * ulp(o, dtype))) / rms if d.size else 0.0
     if not finite:
         raw = excess = float("inf")
+    tol = (tolerance or TOLERANCE)[dtype]
     res = {"err_raw": raw, "err_excess": excess, "rounding_floor": floor, "rms": rms,
-           "tol": TOLERANCE[dtype], "gated_on": GATED_ON[dtype]}
-    res["ok"] = res[GATED_ON[dtype]] <= TOLERANCE[dtype]
+           "tol": tol, "gated_on": GATED_ON[dtype]}
+    res["ok"] = res[GATED_ON[dtype]] <= tol
     return res
