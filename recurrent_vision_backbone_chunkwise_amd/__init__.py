@@ -29,12 +29,12 @@ ERRORS = {
 DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
                torch.bfloat16: GTR_DTYPE_BF16}
 
-# Every symbol include/gtr_gla.h declares.
+# Every symbol include/gtr_gla.h and include/gtr_swiglu.h declare.
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
            "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
            "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name",
-           "gtr_gla_stream_status")
+           "gtr_gla_stream_status", "gtr_swiglu_fwd", "gtr_swiglu_workspace_bytes")
 
 
 class GlaError(RuntimeError):
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.gtr_gla_kernel_name.restype = ctypes.c_char_p
     L.gtr_gla_stream_status.argtypes = [st]
     L.gtr_gla_stream_status.restype = i
+    L.gtr_swiglu_fwd.argtypes = [vp] * 6 + [i] * 6 + [st]
+    L.gtr_swiglu_fwd.restype = i
+    L.gtr_swiglu_workspace_bytes.argtypes = [i] * 6
+    L.gtr_swiglu_workspace_bytes.restype = ctypes.c_size_t
     _lib = L
     return L
 
@@ -215,3 +219,42 @@ def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = F
     gtr_gla_fwd_ex(q, k, v, log_gate, out, direction, s0=s0, s_final=s_final,
                    chunks_per_segment=chunks_per_segment, path=path, stream=stream)
     return (out, s_final) if want_state else out
+
+
+# ---- Spatial SwiGLU block (include/gtr_swiglu.h) ------------------------------------------------
+
+def gtr_swiglu_workspace_bytes(B, grid_h, grid_w, C, F, dtype=GTR_DTYPE_F16) -> int:
+    return lib().gtr_swiglu_workspace_bytes(B, grid_h, grid_w, C, F, dtype)
+
+
+def gtr_swiglu_fwd(x, w_in, conv_w, conv_b, w_out, out, stream=None) -> None:
+    """out <- Spatial SwiGLU of x (asynchronous).  x, out [B, grid_h, grid_w, C]; w_in [C, 2F];
+    conv_w [3, 3, F]; conv_b [F] or None; w_out [F, C]; one dtype throughout."""
+    named = (("x", x), ("w_in", w_in), ("conv_w", conv_w), ("conv_b", conv_b), ("w_out", w_out),
+             ("out", out))
+    for name, t in named:
+        if t is None and name == "conv_b":
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, x has {x.dtype}")
+    if x.dtype not in DTYPE_CODES or x.dim() != 4:
+        raise ValueError("x must be [B, grid_h, grid_w, C] of float32, float16 or bfloat16")
+    B, gh, gw, C = x.shape
+    F = w_out.shape[0]
+    if tuple(w_in.shape) != (C, 2 * F) or tuple(conv_w.shape) != (3, 3, F) \
+            or tuple(w_out.shape) != (F, C) or out.shape != x.shape \
+            or (conv_b is not None and tuple(conv_b.shape) != (F,)):
+        raise ValueError("shape mismatch between x, w_in, conv_w, conv_b, w_out and out")
+    _check(lib().gtr_swiglu_fwd(x.data_ptr(), w_in.data_ptr(), conv_w.data_ptr(),
+                                conv_b.data_ptr() if conv_b is not None else None,
+                                w_out.data_ptr(), out.data_ptr(), B, gh, gw, C, F,
+                                DTYPE_CODES[x.dtype], _stream_handle(stream)))
+
+
+def swiglu_forward(x, w_in, conv_w, conv_b, w_out, stream=None):
+    """Allocating convenience wrapper around gtr_swiglu_fwd."""
+    out = torch.empty_like(x)
+    gtr_swiglu_fwd(x, w_in, conv_w, conv_b, w_out, out, stream=stream)
+    return out

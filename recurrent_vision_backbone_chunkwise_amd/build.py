@@ -25,7 +25,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_profile.cpp"]
+SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_profile.cpp", "swiglu.hip"]
 
 
 def source_digest() -> str:
@@ -65,7 +65,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
             print(msg)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lrocblas", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

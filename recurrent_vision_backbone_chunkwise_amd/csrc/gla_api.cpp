@@ -306,6 +306,37 @@ bool skip_pointer_checks() {
 
 }  // namespace
 
+namespace gtr {
+
+int set_error(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int check_device_pointer(const void *p, size_t bytes, int device, const char *name) {
+  return check_device_range(p, bytes, device, name);
+}
+
+bool pointer_checks_off() { return skip_pointer_checks(); }
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+}  // namespace gtr
+
 extern "C" {
 
 }  // extern "C"

@@ -55,6 +55,17 @@ inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
 // left-over data.
 inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (kCtlStride + n_seg); }
 
+// Host helpers shared by the entry points (defined in gla_api.cpp): record an
+// error message for gtr_gla_last_error() and return `code`; clear it; check a
+// device pointer against the current device and a byte count; whether pointer
+// queries are switched off (GTR_GLA_SKIP_POINTER_CHECKS=1); whether `stream`
+// is being captured.
+int set_error(int code, const char *fmt, ...);
+void clear_error();
+int check_device_pointer(const void *p, size_t bytes, int device, const char *name);
+bool pointer_checks_off();
+bool stream_capturing(hipStream_t stream);
+
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);
 

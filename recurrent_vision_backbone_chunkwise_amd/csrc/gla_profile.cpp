@@ -24,7 +24,8 @@ std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Mark> g_marks;
 
-const char *kNames[kNumKernels] = {"gla_seg_state", "gla_seg_scan", "gla_seg_out", "gla_fused"};
+const char *kNames[kNumKernels] = {"gla_seg_state",  "gla_seg_scan", "gla_seg_out",    "gla_fused",
+                                   "swiglu_gemm_in", "swiglu_mix",   "swiglu_gemm_out"};
 
 }  // namespace
 
@@ -48,6 +49,13 @@ bool profile_events(int kernel, hipStream_t stream, hipEvent_t *start, hipEvent_
   *start = a;
   *stop = b;
   return true;
+}
+
+ProfileScope::ProfileScope(int kernel, hipStream_t s) : stream(s) {
+  if (profile_events(kernel, s, &start, &stop)) (void)hipEventRecord(start, s);
+}
+ProfileScope::~ProfileScope() {
+  if (stop) (void)hipEventRecord(stop, stream);
 }
 
 }  // namespace gtr

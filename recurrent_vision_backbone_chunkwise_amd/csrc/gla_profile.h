@@ -10,7 +10,10 @@ enum KernelId : int {
   kKernelSegScan = 1,
   kKernelSegOut = 2,
   kKernelFused = 3,
-  kNumKernels = 4
+  kKernelSwigluIn = 4,   // Spatial SwiGLU input projection (library GEMM)
+  kKernelSwigluMix = 5,  // depthwise 3x3 + SiLU gate
+  kKernelSwigluOut = 6,  // output projection (library GEMM)
+  kNumKernels = 7
 };
 
 // While profiling is on and `stream` is not being captured, creates a pair of
@@ -18,5 +21,14 @@ enum KernelId : int {
 // which timestamps the dispatch itself) and returns true.  Otherwise returns
 // false and leaves both events null.
 bool profile_events(int kernel, hipStream_t stream, hipEvent_t *start, hipEvent_t *stop);
+
+// Records start/stop on `stream` around work enqueued between the two calls
+// (library calls that do not take events themselves); no-ops while off.
+struct ProfileScope {
+  ProfileScope(int kernel, hipStream_t stream);
+  ~ProfileScope();
+  hipStream_t stream;
+  hipEvent_t start, stop;
+};
 
 }  // namespace gtr

@@ -1,0 +1,292 @@
+// Spatial SwiGLU block of a GTR layer (include/gtr_swiglu.h) for gfx950.
+//
+// The block (x-techcon article on GTR, section 架构 / Architecture: SwiGLU
+// with a 3 x 3 per-channel convolution in the value branch, so that adjacent
+// patches exchange information) runs as three steps on the caller's stream:
+//   1. u = x W_in           rocBLAS GEMM, fp32 accumulation, u stored in fp32
+//   2. h = SiLU(u_g) * (DWConv3x3(u_v) + b)   swiglu_mix below, h in the I/O type
+//   3. out = h W_out        rocBLAS GEMM, fp32 accumulation
+// The projections are plain dense GEMMs, the library's job; the step between
+// them is bandwidth-bound elementwise work with a 3 x 3 neighbourhood, done by
+// one kernel that reads u once per tap (neighbouring taps are cache hits) and
+// writes h once.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gla_internal.h"
+#include "gla_profile.h"
+#include "gtr_swiglu.h"
+
+namespace gtr {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef uint16_t b4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMixThreads = 256;
+
+// Four consecutive elements of the I/O type, widened to or narrowed from fp32.
+__device__ __forceinline__ f4 load4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+__device__ __forceinline__ f4 load4(const _Float16 *p) {
+  return __builtin_convertvector(*reinterpret_cast<const h4 *>(p), f4);
+}
+__device__ __forceinline__ f4 load4(const uint16_t *p) {  // bfloat16 bits
+  const b4 b = *reinterpret_cast<const b4 *>(p);
+  return f4{__uint_as_float((uint32_t)b.x << 16), __uint_as_float((uint32_t)b.y << 16),
+            __uint_as_float((uint32_t)b.z << 16), __uint_as_float((uint32_t)b.w << 16)};
+}
+__device__ __forceinline__ void store4(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
+__device__ __forceinline__ void store4(_Float16 *p, f4 v) {
+  *reinterpret_cast<h4 *>(p) = __builtin_convertvector(v, h4);
+}
+__device__ __forceinline__ uint16_t bf16_rne(float f) {  // round to nearest even, quiet NaN kept
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ void store4(uint16_t *p, f4 v) {
+  *reinterpret_cast<b4 *>(p) = b4{bf16_rne(v.x), bf16_rne(v.y), bf16_rne(v.z), bf16_rne(v.w)};
+}
+
+// One thread per (token, 4 channels); consecutive threads take consecutive
+// channels of one token, so every read of a u row is coalesced.  u is
+// [tokens][2F] fp32 (gate in [0, F), value in [F, 2F)); h is [tokens][F].
+template <typename T>
+__global__ __launch_bounds__(kMixThreads) void swiglu_mix(const float *__restrict__ u,
+                                                          const T *__restrict__ conv_w,
+                                                          const T *__restrict__ conv_b,
+                                                          T *__restrict__ h, int grid_h, int grid_w,
+                                                          int F, long long n_threads) {
+  const long long gid = (long long)blockIdx.x * kMixThreads + threadIdx.x;
+  if (gid >= n_threads) return;
+  const int groups = F >> 2;
+  const long long m = gid / groups;
+  const int f = (int)(gid - m * groups) * 4;
+  const int per_image = grid_h * grid_w;
+  const long long image = m / per_image;
+  const int cell = (int)(m - image * per_image);
+  const int y = cell / grid_w, x = cell - y * grid_w;
+  const size_t ld = 2 * (size_t)F;
+  const f4 g = load4(u + (size_t)m * ld + f);
+  f4 acc = conv_b ? load4(conv_b + f) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dy = 0; dy < 3; ++dy) {
+    const int yy = y + dy - 1;
+    if (yy < 0 || yy >= grid_h) continue;
+#pragma unroll
+    for (int dx = 0; dx < 3; ++dx) {
+      const int xx = x + dx - 1;
+      if (xx < 0 || xx >= grid_w) continue;
+      const size_t mm = (size_t)image * per_image + (size_t)yy * grid_w + xx;
+      acc += load4(conv_w + (dy * 3 + dx) * (size_t)F + f) * load4(u + mm * ld + F + f);
+    }
+  }
+  f4 s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = g[e] / (1.f + __expf(-g[e]));  // SiLU; -inf gate gives -0
+  store4(h + (size_t)m * F + f, s * acc);
+}
+
+template <typename T>
+int launch_mix(const float *u, const void *conv_w, const void *conv_b, void *h, int grid_h,
+               int grid_w, int F, long long tokens, hipStream_t stream) {
+  const long long n = tokens * (F / 4);
+  const unsigned blocks = (unsigned)((n + kMixThreads - 1) / kMixThreads);
+  hipEvent_t t0, t1;
+  if (profile_events(kKernelSwigluMix, stream, &t0, &t1))
+    hipExtLaunchKernelGGL(swiglu_mix<T>, dim3(blocks), dim3(kMixThreads), 0, stream, t0, t1, 0, u,
+                          static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
+                          static_cast<T *>(h), grid_h, grid_w, F, n);
+  else
+    hipLaunchKernelGGL(swiglu_mix<T>, dim3(blocks), dim3(kMixThreads), 0, stream, u,
+                       static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
+                       static_cast<T *>(h), grid_h, grid_w, F, n);
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------ host side
+
+constexpr long long kMaxTokens = 1LL << 24;
+constexpr int kMaxWidth = 1 << 16;
+
+int elem_bytes(int dtype) { return dtype == GTR_DTYPE_F32 ? 4 : 2; }
+
+rocblas_datatype blas_type(int dtype) {
+  return dtype == GTR_DTYPE_F32 ? rocblas_datatype_f32_r
+                                : (dtype == GTR_DTYPE_F16 ? rocblas_datatype_f16_r : rocblas_datatype_bf16_r);
+}
+
+struct Sizes {
+  long long tokens;
+  size_t u_bytes, h_bytes;  // workspace parts, each rounded up to 256 bytes
+};
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int validate(int B, int grid_h, int grid_w, int C, int F, int dtype, Sizes *sz) {
+  if (dtype < 0 || dtype > 2) return set_error(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
+  if (B < 0 || grid_h < 0 || grid_w < 0)
+    return set_error(GTR_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d grid=%dx%d)", B, grid_h, grid_w);
+  if (C < 8 || F < 8 || C % 8 || F % 8 || C > kMaxWidth || F > kMaxWidth)
+    return set_error(GTR_ERR_UNSUPPORTED, "C=%d F=%d: widths must be multiples of 8 from 8 to %d", C,
+                     F, kMaxWidth);
+  const long long tokens = (long long)B * grid_h * grid_w;
+  if (tokens > kMaxTokens)
+    return set_error(GTR_ERR_INVALID_ARG, "%lld tokens exceed 2^24", tokens);
+  sz->tokens = tokens;
+  sz->u_bytes = round256((size_t)tokens * 2 * F * sizeof(float));
+  sz->h_bytes = round256((size_t)tokens * F * elem_bytes(dtype));
+  return GTR_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+std::mutex g_mu;  // guards the workspaces and the rocBLAS handles (one per device)
+std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+std::map<int, rocblas_handle> g_blas;
+
+int workspace(int device, hipStream_t stream, size_t bytes, void **out) {
+  auto &ws = g_ws[{device, stream}];
+  if (ws.second >= bytes) {
+    *out = ws.first;
+    return GTR_OK;
+  }
+  if (stream_capturing(stream))
+    return set_error(GTR_ERR_CAPTURE,
+                     "workspace must grow (%zu -> %zu bytes) while the stream is being captured; "
+                     "make one call of this shape before capturing",
+                     ws.second, bytes);
+  if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
+  if (ws.first) (void)hipFree(ws.first);
+  ws = {nullptr, 0};
+  void *p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", bytes);
+  }
+  ws = {p, bytes};
+  *out = p;
+  return GTR_OK;
+}
+
+int blas_handle(int device, rocblas_handle *h) {
+  auto it = g_blas.find(device);
+  if (it != g_blas.end()) {
+    *h = it->second;
+    return GTR_OK;
+  }
+  rocblas_handle nh = nullptr;
+  if (rocblas_create_handle(&nh) != rocblas_status_success)
+    return set_error(GTR_ERR_ALLOC, "rocblas_create_handle failed on device %d", device);
+  g_blas[device] = nh;
+  *h = nh;
+  return GTR_OK;
+}
+
+// Row-major C[rows][n] = A[rows][k] B[k][n], as the column-major product
+// C^T = B^T A^T that rocBLAS computes.
+int gemm(rocblas_handle h, int rows, int n, int k, const void *a, rocblas_datatype at, const void *b,
+         rocblas_datatype bt, void *c, rocblas_datatype ct, const char *what) {
+  const float one = 1.f, zero = 0.f;
+  const rocblas_status st =
+      rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, n, rows, k, &one, b, bt, n, a,
+                      at, k, &zero, c, ct, n, c, ct, n, rocblas_datatype_f32_r,
+                      rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success)
+    return set_error(GTR_ERR_LAUNCH, "%s: rocblas_gemm_ex failed (%s)", what, rocblas_status_to_string(st));
+  return GTR_OK;
+}
+
+}  // namespace
+}  // namespace gtr
+
+extern "C" {
+
+size_t gtr_swiglu_workspace_bytes(int B, int grid_h, int grid_w, int C, int F, int dtype) {
+  gtr::Sizes sz;
+  if (gtr::validate(B, grid_h, grid_w, C, F, dtype, &sz) != GTR_OK || sz.tokens == 0) return 0;
+  return sz.u_bytes + sz.h_bytes;
+}
+
+int gtr_swiglu_fwd(const void *x, const void *w_in, const void *conv_w, const void *conv_b,
+                   const void *w_out, void *out, int B, int grid_h, int grid_w, int C, int F,
+                   int dtype, hipStream_t stream) {
+  using namespace gtr;
+  clear_error();
+  Sizes sz;
+  int rc = validate(B, grid_h, grid_w, C, F, dtype, &sz);
+  if (rc != GTR_OK) return rc;
+  if (sz.tokens == 0) return GTR_OK;  // nothing to compute
+  if (!x || !w_in || !conv_w || !w_out || !out)
+    return set_error(GTR_ERR_INVALID_ARG, "null pointer (x=%p w_in=%p conv_w=%p w_out=%p out=%p)", x,
+                     w_in, conv_w, w_out, out);
+  const size_t e = elem_bytes(dtype);
+  const void *ptrs[6] = {x, w_in, conv_w, conv_b, w_out, out};
+  const char *names[6] = {"x", "w_in", "conv_w", "conv_b", "w_out", "out"};
+  const size_t bytes[6] = {(size_t)sz.tokens * C * e, (size_t)C * 2 * F * e, (size_t)9 * F * e,
+                           (size_t)F * e, (size_t)F * C * e, (size_t)sz.tokens * C * e};
+  for (int i = 0; i < 6; ++i)
+    if (ptrs[i] && (reinterpret_cast<uintptr_t>(ptrs[i]) & 15u))
+      return set_error(GTR_ERR_ALIGNMENT, "%s=%p is not 16-byte aligned", names[i], ptrs[i]);
+  for (int i = 0; i < 5; ++i)
+    if (ptrs[i] && overlaps(out, bytes[5], ptrs[i], bytes[i]))
+      return set_error(GTR_ERR_ALIAS, "out overlaps %s", names[i]);
+  int n_dev = 0, device = 0;
+  if (hipGetDeviceCount(&n_dev) != hipSuccess || n_dev <= 0 || hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(GTR_ERR_NO_DEVICE, "no HIP device available");
+  }
+  const bool capturing = stream_capturing(stream);
+  if (!capturing && !pointer_checks_off()) {
+    for (int i = 0; i < 6; ++i) {
+      if (!ptrs[i]) continue;
+      rc = check_device_pointer(ptrs[i], bytes[i], device, names[i]);
+      if (rc != GTR_OK) return rc;
+    }
+  }
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  void *ws = nullptr;
+  rc = workspace(device, stream, sz.u_bytes + sz.h_bytes, &ws);
+  if (rc != GTR_OK) return rc;
+  rocblas_handle blas = nullptr;
+  rc = blas_handle(device, &blas);
+  if (rc != GTR_OK) return rc;
+  if (rocblas_set_stream(blas, stream) != rocblas_status_success)
+    return set_error(GTR_ERR_LAUNCH, "rocblas_set_stream failed");
+  float *u = static_cast<float *>(ws);
+  void *h = static_cast<char *>(ws) + sz.u_bytes;
+  const rocblas_datatype t = blas_type(dtype);
+  const int M = (int)sz.tokens;
+  {
+    ProfileScope scope(kKernelSwigluIn, stream);
+    rc = gemm(blas, M, 2 * F, C, x, t, w_in, t, u, rocblas_datatype_f32_r, "input projection");
+  }
+  if (rc != GTR_OK) return rc;
+  int err;
+  switch (dtype) {
+    case GTR_DTYPE_F32: err = launch_mix<float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    case GTR_DTYPE_F16: err = launch_mix<_Float16>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    default: err = launch_mix<uint16_t>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+  }
+  if (err != (int)hipSuccess)
+    return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  {
+    ProfileScope scope(kKernelSwigluOut, stream);
+    rc = gemm(blas, M, C, F, h, t, w_out, t, out, t, "output projection");
+  }
+  return rc;
+}
+
+}  // extern "C"

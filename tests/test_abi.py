@@ -11,12 +11,13 @@ import recurrent_vision_backbone_chunkwise_amd as gla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gtr_gla.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gtr_gla.h", "gtr_swiglu.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gtr_gla_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gtr_[a-z]\w*)\s*\(", text)))
 
 
 def declared_constants():
@@ -164,3 +165,38 @@ def test_binding_refuses_cpu_tensors():
 def test_single_hip_runtime_mapped():
     gla.lib()
     assert len(gla.hip_runtimes_mapped()) == 1
+
+
+# ---- Spatial SwiGLU entry point ------------------------------------------------------------
+
+def swiglu_call(x=A, w_in=A + 0x1000000, conv_w=A + 0x2000000, conv_b=A + 0x3000000,
+                w_out=A + 0x4000000, out=A + 0x5000000, B=1, gh=4, gw=4, C=16, F=32, dt=1):
+    return gla.lib().gtr_swiglu_fwd(x, w_in, conv_w, conv_b, w_out, out, B, gh, gw, C, F, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), -1), (dict(B=-1), -1), (dict(gh=-2), -1), (dict(x=None), -1), (dict(w_out=None), -1),
+    (dict(B=1 << 10, gh=1 << 8, gw=1 << 7), -1),
+    (dict(C=12), -2), (dict(F=4), -2), (dict(C=0), -2), (dict(F=1 << 17), -2),
+    (dict(x=A + 8), -3), (dict(conv_b=A + 0x3000004), -3),
+    (dict(out=A), -4), (dict(out=A + 0x1000000 + 64), -4),
+])
+def test_swiglu_argument_errors_before_any_hip_call(kw, code):
+    assert swiglu_call(**kw) == code
+    assert gla.gtr_gla_last_error() != ""
+
+
+def test_swiglu_empty_calls_and_sizes():
+    assert swiglu_call(B=0, x=None, out=None) == 0
+    assert swiglu_call(gh=0) == 0
+    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 1) == 1600 * 2048 * 4 + 1600 * 1024 * 2
+    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 0) == 1600 * 2048 * 4 + 1600 * 1024 * 4
+    assert gla.gtr_swiglu_workspace_bytes(0, 40, 40, 384, 1024, 1) == 0
+    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 12, 1024, 1) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
+                    reason="a GPU is visible")
+def test_swiglu_valid_call_without_gpu_reports_no_device():
+    assert swiglu_call() == -5
+    assert swiglu_call(conv_b=None) == -5
