@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=50)
+    ap.add_argument("--op", choices=["gla", "swiglu"], default="gla",
+                    help="gla: the attention forward (default); swiglu: the Spatial SwiGLU block")
+    ap.add_argument("--swiglu-workload", type=int, default=1,
+                    help="1 = 40x40 grid, C 384, F 1024; 2 = 128x128 grid, C 1024, F 2752 (fp16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes ten times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
@@ -82,6 +86,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.op == "swiglu":
+        swiglu_main(args)
         return
 
     import torch
@@ -235,6 +242,112 @@ def cpu_baseline(w, cpu_inputs, budget_s):
             "kind": "oracle",
             "sample": f"the full step ({len(w.directions)} calls, {w.name}) x {reps} repetitions, "
                       f"{t_total:.1f} s of oracle time, fp64 token-by-token recurrence"}
+
+
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # MI355X dense
+
+
+def swiglu_main(args):
+    """One step = one Spatial SwiGLU block over the workload's grid (inputs resident in HBM)."""
+    import torch
+
+    import gla_inputs
+    import recurrent_vision_backbone_chunkwise_amd as gla
+
+    if not os.path.exists(gla.LIB_PATH):
+        from recurrent_vision_backbone_chunkwise_amd import build as hip_build
+        hip_build.build()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible")
+    w = gla_inputs.swiglu_workload(args.swiglu_workload)
+    cpu_in = gla_inputs.make_swiglu_inputs(w.B, w.grid_h, w.grid_w, w.C, w.F, w.dtype, seed=w.seed)
+    ins = [t.to("cuda:0") for t in cpu_in]
+    out = torch.empty_like(ins[0])
+    stream = torch.cuda.Stream()
+
+    def step():
+        gla.gtr_swiglu_fwd(*ins, out, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay() if graph is not None else step()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    tokens = w.B * w.n_tok
+    value = tokens / (ms_per_step * 1e-3)
+
+    gla.gtr_gla_profile_begin()
+    with torch.cuda.stream(stream):
+        for _ in range(args.profile_steps):
+            step()
+    prof = gla.gtr_gla_profile_end()
+    torch.cuda.synchronize()
+    kern = {n: 1e3 * ms / c for n, (ms, c) in prof.items() if c > 0}
+    elt = 4 if w.dtype == "f32" else 2
+    M, C, F = tokens, w.C, w.F
+    # algorithmic work per launch: GEMM flops; the mix kernel reads u once (fp16 for fp16 I/O,
+    # else fp32) and writes h once
+    work = {
+        "swiglu_gemm_in": ("mfma", 2.0 * M * C * 2 * F),
+        "swiglu_gemm_out": ("mfma", 2.0 * M * F * C),
+        "swiglu_mix": ("hbm", float(M * (2 * F * (2 if w.dtype == "f16" else 4) + F * elt) + 10 * F * elt)),
+    }
+    per = {}
+    for name, us in kern.items():
+        bound, amount = work[name]
+        if bound == "mfma":
+            ach, peak, unit = amount / (us * 1e-6) / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        else:
+            ach, peak, unit = amount / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+        per[name] = {"avg_us": round(us, 3), "bound": bound, "achieved": round(ach, 1), "peak": peak,
+                     "unit": unit, "frac": round(ach / peak, 4)}
+    dominant = max(kern, key=kern.get)
+    d = per[dominant]
+    roofline = {"bound": d["bound"], "kernel": dominant, "achieved": d["achieved"], "peak": d["peak"],
+                "unit": d["unit"], "frac": d["frac"], "traffic": None, "kernels": per}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import swiglu as oracle_swiglu
+        rows = max(1, min(w.grid_h, int(args.cpu_seconds * 4)))
+        sample = [cpu_in[0][:, :rows].contiguous()] + list(cpu_in[1:])
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle_swiglu.spatial_swiglu(*sample)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 1000:
+                break
+        t = time.perf_counter() - t0
+        cpu = {"value": round(reps * w.B * rows * w.grid_w / t, 1), "unit": "tokens/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"the first {rows} grid rows of {w.name} x {reps} repetitions, {t:.1f} s, "
+                         "fp64 numpy (BLAS threads as the host provides)"}
+    line = {
+        "metric": "Spatial SwiGLU block tokens/sec (B*N), one MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "grid": [w.grid_h, w.grid_w], "C": C, "F": F,
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

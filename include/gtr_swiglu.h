@@ -22,8 +22,9 @@
  *   conv_b  : [F], or NULL for no bias
  *   w_out   : [F][C]
  * Arithmetic: the projections are library GEMMs (rocBLAS) with fp32
- * accumulation; u is kept in fp32; h is rounded to the I/O dtype before the
- * output projection; out is rounded to the I/O dtype.
+ * accumulation; u is kept in fp16 for fp16 I/O and in fp32 otherwise; h is
+ * rounded to the I/O dtype before the output projection; out is rounded to the
+ * I/O dtype.
  *
  * Ownership and errors as in gtr_gla.h: device pointers owned by the caller,
  * 16-byte aligned; out must not overlap an input; the library owns a

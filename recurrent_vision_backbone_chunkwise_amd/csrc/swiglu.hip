@@ -3,7 +3,8 @@
 // The block (x-techcon article on GTR, section 架构 / Architecture: SwiGLU
 // with a 3 x 3 per-channel convolution in the value branch, so that adjacent
 // patches exchange information) runs as three steps on the caller's stream:
-//   1. u = x W_in           rocBLAS GEMM, fp32 accumulation, u stored in fp32
+//   1. u = x W_in           rocBLAS GEMM, fp32 accumulation; u stored in fp16
+//                           for fp16 I/O, else in fp32
 //   2. h = SiLU(u_g) * (DWConv3x3(u_v) + b)   swiglu_mix below, h in the I/O type
 //   3. out = h W_out        rocBLAS GEMM, fp32 accumulation
 // The projections are plain dense GEMMs, the library's job; the step between
@@ -58,9 +59,9 @@ __device__ __forceinline__ void store4(uint16_t *p, f4 v) {
 
 // One thread per (token, 4 channels); consecutive threads take consecutive
 // channels of one token, so every read of a u row is coalesced.  u is
-// [tokens][2F] fp32 (gate in [0, F), value in [F, 2F)); h is [tokens][F].
-template <typename T>
-__global__ __launch_bounds__(kMixThreads) void swiglu_mix(const float *__restrict__ u,
+// [tokens][2F] of type U (gate in [0, F), value in [F, 2F)); h is [tokens][F].
+template <typename T, typename U>
+__global__ __launch_bounds__(kMixThreads) void swiglu_mix(const U *__restrict__ u,
                                                           const T *__restrict__ conv_w,
                                                           const T *__restrict__ conv_b,
                                                           T *__restrict__ h, int grid_h, int grid_w,
@@ -95,18 +96,20 @@ __global__ __launch_bounds__(kMixThreads) void swiglu_mix(const float *__restric
   store4(h + (size_t)m * F + f, s * acc);
 }
 
-template <typename T>
-int launch_mix(const float *u, const void *conv_w, const void *conv_b, void *h, int grid_h,
+template <typename T, typename U>
+int launch_mix(const void *u_ws, const void *conv_w, const void *conv_b, void *h, int grid_h,
                int grid_w, int F, long long tokens, hipStream_t stream) {
+  const U *u = static_cast<const U *>(u_ws);
+  auto kernel = swiglu_mix<T, U>;
   const long long n = tokens * (F / 4);
   const unsigned blocks = (unsigned)((n + kMixThreads - 1) / kMixThreads);
   hipEvent_t t0, t1;
   if (profile_events(kKernelSwigluMix, stream, &t0, &t1))
-    hipExtLaunchKernelGGL(swiglu_mix<T>, dim3(blocks), dim3(kMixThreads), 0, stream, t0, t1, 0, u,
+    hipExtLaunchKernelGGL(kernel, dim3(blocks), dim3(kMixThreads), 0, stream, t0, t1, 0, u,
                           static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
                           static_cast<T *>(h), grid_h, grid_w, F, n);
   else
-    hipLaunchKernelGGL(swiglu_mix<T>, dim3(blocks), dim3(kMixThreads), 0, stream, u,
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kMixThreads), 0, stream, u,
                        static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
                        static_cast<T *>(h), grid_h, grid_w, F, n);
   return (int)hipGetLastError();
@@ -118,6 +121,9 @@ constexpr long long kMaxTokens = 1LL << 24;
 constexpr int kMaxWidth = 1 << 16;
 
 int elem_bytes(int dtype) { return dtype == GTR_DTYPE_F32 ? 4 : 2; }
+// u keeps the I/O precision for fp16 (one more fp16 rounding, well inside the
+// fp16 tolerance) and fp32 otherwise (bf16 has no precision to spare).
+int u_bytes_per_elem(int dtype) { return dtype == GTR_DTYPE_F16 ? 2 : 4; }
 
 rocblas_datatype blas_type(int dtype) {
   return dtype == GTR_DTYPE_F32 ? rocblas_datatype_f32_r
@@ -142,7 +148,7 @@ int validate(int B, int grid_h, int grid_w, int C, int F, int dtype, Sizes *sz) 
   if (tokens > kMaxTokens)
     return set_error(GTR_ERR_INVALID_ARG, "%lld tokens exceed 2^24", tokens);
   sz->tokens = tokens;
-  sz->u_bytes = round256((size_t)tokens * 2 * F * sizeof(float));
+  sz->u_bytes = round256((size_t)tokens * 2 * F * u_bytes_per_elem(dtype));
   sz->h_bytes = round256((size_t)tokens * F * elem_bytes(dtype));
   return GTR_OK;
 }
@@ -265,20 +271,21 @@ int gtr_swiglu_fwd(const void *x, const void *w_in, const void *conv_w, const vo
   if (rc != GTR_OK) return rc;
   if (rocblas_set_stream(blas, stream) != rocblas_status_success)
     return set_error(GTR_ERR_LAUNCH, "rocblas_set_stream failed");
-  float *u = static_cast<float *>(ws);
+  void *u = ws;
   void *h = static_cast<char *>(ws) + sz.u_bytes;
   const rocblas_datatype t = blas_type(dtype);
   const int M = (int)sz.tokens;
   {
     ProfileScope scope(kKernelSwigluIn, stream);
-    rc = gemm(blas, M, 2 * F, C, x, t, w_in, t, u, rocblas_datatype_f32_r, "input projection");
+    rc = gemm(blas, M, 2 * F, C, x, t, w_in, t, u,
+              dtype == GTR_DTYPE_F16 ? rocblas_datatype_f16_r : rocblas_datatype_f32_r, "input projection");
   }
   if (rc != GTR_OK) return rc;
   int err;
   switch (dtype) {
-    case GTR_DTYPE_F32: err = launch_mix<float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
-    case GTR_DTYPE_F16: err = launch_mix<_Float16>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
-    default: err = launch_mix<uint16_t>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    case GTR_DTYPE_F32: err = launch_mix<float, float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    case GTR_DTYPE_F16: err = launch_mix<_Float16, _Float16>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    default: err = launch_mix<uint16_t, float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
   }
   if (err != (int)hipSuccess)
     return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));

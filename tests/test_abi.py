@@ -189,7 +189,8 @@ def test_swiglu_argument_errors_before_any_hip_call(kw, code):
 def test_swiglu_empty_calls_and_sizes():
     assert swiglu_call(B=0, x=None, out=None) == 0
     assert swiglu_call(gh=0) == 0
-    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 1) == 1600 * 2048 * 4 + 1600 * 1024 * 2
+    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 1) == 1600 * 2048 * 2 + 1600 * 1024 * 2
+    assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 2) == 1600 * 2048 * 4 + 1600 * 1024 * 2
     assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 384, 1024, 0) == 1600 * 2048 * 4 + 1600 * 1024 * 4
     assert gla.gtr_swiglu_workspace_bytes(0, 40, 40, 384, 1024, 1) == 0
     assert gla.gtr_swiglu_workspace_bytes(1, 40, 40, 12, 1024, 1) == 0
