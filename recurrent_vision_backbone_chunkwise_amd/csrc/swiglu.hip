@@ -9,8 +9,8 @@
 //   3. out = h W_out        rocBLAS GEMM, fp32 accumulation
 // The projections are plain dense GEMMs, the library's job; the step between
 // them is bandwidth-bound elementwise work with a 3 x 3 neighbourhood, done by
-// one kernel that reads u once per tap (neighbouring taps are cache hits) and
-// writes h once.
+// one kernel that stages each tile's value columns (with a one-token halo) in
+// LDS and writes h once.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -57,61 +57,112 @@ __device__ __forceinline__ void store4(uint16_t *p, f4 v) {
   *reinterpret_cast<b4 *>(p) = b4{bf16_rne(v.x), bf16_rne(v.y), bf16_rne(v.z), bf16_rne(v.w)};
 }
 
-// One thread per (token, 4 channels); consecutive threads take consecutive
-// channels of one token, so every read of a u row is coalesced.  u is
-// [tokens][2F] of type U (gate in [0, F), value in [F, 2F)); h is [tokens][F].
+// Tiles of kTileY x kTileX tokens of one image and kSlice channels.  The value
+// columns of the tile and its one-token halo are staged once in LDS (fp32), so
+// each value is read from memory about 1.4 times instead of nine; the gate is
+// read once and h written once.  Thread t handles channel group t % 16 (four
+// channels) for every 16th token of the tile; its nine taps and bias stay in
+// registers.  u is [tokens][2F] of type U (gate in [0, F), value in [F, 2F));
+// h is [tokens][F].
+constexpr int kTileY = 8, kTileX = 16, kSlice = 64;
+constexpr int kGroups = kSlice / 4;                        // 16 channel groups
+constexpr int kHaloY = kTileY + 2, kHaloX = kTileX + 2;    // 10 x 18 positions
+
+__device__ __forceinline__ f4 load4(const f4 *p) { return *p; }
+
 template <typename T, typename U>
 __global__ __launch_bounds__(kMixThreads) void swiglu_mix(const U *__restrict__ u,
                                                           const T *__restrict__ conv_w,
                                                           const T *__restrict__ conv_b,
                                                           T *__restrict__ h, int grid_h, int grid_w,
-                                                          int F, long long n_threads) {
-  const long long gid = (long long)blockIdx.x * kMixThreads + threadIdx.x;
-  if (gid >= n_threads) return;
-  const int groups = F >> 2;
-  const long long m = gid / groups;
-  const int f = (int)(gid - m * groups) * 4;
-  const int per_image = grid_h * grid_w;
-  const long long image = m / per_image;
-  const int cell = (int)(m - image * per_image);
-  const int y = cell / grid_w, x = cell - y * grid_w;
+                                                          int F, int slices, int tiles_x, int tiles_y) {
+  __shared__ f4 val[kHaloY * kHaloX * kGroups];  // 46 KB
+  const int tid = threadIdx.x;
+  // block -> (image, tile row, tile column, channel slice), slice fastest
+  unsigned b = blockIdx.x;
+  const int slice = (int)(b % (unsigned)slices);
+  b /= (unsigned)slices;
+  const int tile_x = (int)(b % (unsigned)tiles_x);
+  b /= (unsigned)tiles_x;
+  const int tile_y = (int)(b % (unsigned)tiles_y);
+  const int image = (int)(b / (unsigned)tiles_y);
+  const int x0 = tile_x * kTileX, y0 = tile_y * kTileY, c0 = slice * kSlice;
   const size_t ld = 2 * (size_t)F;
-  const f4 g = load4(u + (size_t)m * ld + f);
-  f4 acc = conv_b ? load4(conv_b + f) : f4{0.f, 0.f, 0.f, 0.f};
+  const size_t image_base = (size_t)image * grid_h * grid_w;
+  const int j = tid % kGroups;
+  const int c = c0 + 4 * j;
+  const bool live = c < F;
+  // Every load of the tile goes out before any is used: the halo's value
+  // columns (zero outside the grid and past F) and this thread's gates.
+  constexpr int kStaged = kHaloY * kHaloX * kGroups;
+  constexpr int kPerThread = (kStaged + kMixThreads - 1) / kMixThreads;  // 12
+  constexpr int kTokensPerThread = kTileY * kTileX * kGroups / kMixThreads;  // 8
+  f4 staged[kPerThread];
 #pragma unroll
-  for (int dy = 0; dy < 3; ++dy) {
-    const int yy = y + dy - 1;
-    if (yy < 0 || yy >= grid_h) continue;
-#pragma unroll
-    for (int dx = 0; dx < 3; ++dx) {
-      const int xx = x + dx - 1;
-      if (xx < 0 || xx >= grid_w) continue;
-      const size_t mm = (size_t)image * per_image + (size_t)yy * grid_w + xx;
-      acc += load4(conv_w + (dy * 3 + dx) * (size_t)F + f) * load4(u + mm * ld + F + f);
-    }
+  for (int k = 0; k < kPerThread; ++k) {
+    const int i = tid + k * kMixThreads;
+    const int pos = i / kGroups;
+    const int yy = y0 - 1 + pos / kHaloX, xx = x0 - 1 + pos % kHaloX;
+    const int cc = c0 + 4 * (i % kGroups);
+    staged[k] = f4{0.f, 0.f, 0.f, 0.f};
+    if (i < kStaged && yy >= 0 && yy < grid_h && xx >= 0 && xx < grid_w && cc < F)
+      staged[k] = load4(u + (image_base + (size_t)yy * grid_w + xx) * ld + F + cc);
   }
-  f4 s;
+  f4 gate[kTokensPerThread];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) s[e] = g[e] / (1.f + __expf(-g[e]));  // SiLU; -inf gate gives -0
-  store4(h + (size_t)m * F + f, s * acc);
+  for (int k = 0; k < kTokensPerThread; ++k) {
+    const int t = tid / kGroups + k * (kMixThreads / kGroups);
+    const int y = y0 + t / kTileX, x = x0 + t % kTileX;
+    gate[k] = f4{0.f, 0.f, 0.f, 0.f};
+    if (live && y < grid_h && x < grid_w) gate[k] = load4(u + (image_base + (size_t)y * grid_w + x) * ld + c);
+  }
+  f4 w[9], bias = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) w[k] = load4(conv_w + (size_t)k * F + c);
+    if (conv_b) bias = load4(conv_b + c);
+  }
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k)
+    if (tid + k * kMixThreads < kStaged) val[tid + k * kMixThreads] = staged[k];
+  __syncthreads();
+  if (!live) return;
+#pragma unroll
+  for (int k = 0; k < kTokensPerThread; ++k) {
+    const int t = tid / kGroups + k * (kMixThreads / kGroups);
+    const int ty = t / kTileX, tx = t - ty * kTileX;
+    const int y = y0 + ty, x = x0 + tx;
+    if (y >= grid_h || x >= grid_w) continue;
+    f4 acc = bias;
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy)
+#pragma unroll
+      for (int dx = 0; dx < 3; ++dx)
+        acc += w[dy * 3 + dx] * val[((ty + dy) * kHaloX + tx + dx) * kGroups + j];
+    f4 sg;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sg[e] = gate[k][e] / (1.f + __expf(-gate[k][e]));  // SiLU; -inf gives -0
+    store4(h + (image_base + (size_t)y * grid_w + x) * F + c, sg * acc);
+  }
 }
 
 template <typename T, typename U>
-int launch_mix(const void *u_ws, const void *conv_w, const void *conv_b, void *h, int grid_h,
-               int grid_w, int F, long long tokens, hipStream_t stream) {
+int launch_mix(const void *u_ws, const void *conv_w, const void *conv_b, void *h, int B, int grid_h,
+               int grid_w, int F, hipStream_t stream) {
   const U *u = static_cast<const U *>(u_ws);
   auto kernel = swiglu_mix<T, U>;
-  const long long n = tokens * (F / 4);
-  const unsigned blocks = (unsigned)((n + kMixThreads - 1) / kMixThreads);
+  const int slices = (F + kSlice - 1) / kSlice;
+  const int tiles_x = (grid_w + kTileX - 1) / kTileX, tiles_y = (grid_h + kTileY - 1) / kTileY;
+  const dim3 grid((unsigned)((long long)B * tiles_y * tiles_x * slices));  // < 2^31 (checked on the host)
   hipEvent_t t0, t1;
   if (profile_events(kKernelSwigluMix, stream, &t0, &t1))
-    hipExtLaunchKernelGGL(kernel, dim3(blocks), dim3(kMixThreads), 0, stream, t0, t1, 0, u,
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kMixThreads), 0, stream, t0, t1, 0, u,
                           static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
-                          static_cast<T *>(h), grid_h, grid_w, F, n);
+                          static_cast<T *>(h), grid_h, grid_w, F, slices, tiles_x, tiles_y);
   else
-    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kMixThreads), 0, stream, u,
-                       static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
-                       static_cast<T *>(h), grid_h, grid_w, F, n);
+    hipLaunchKernelGGL(kernel, grid, dim3(kMixThreads), 0, stream, u, static_cast<const T *>(conv_w),
+                       static_cast<const T *>(conv_b), static_cast<T *>(h), grid_h, grid_w, F, slices,
+                       tiles_x, tiles_y);
   return (int)hipGetLastError();
 }
 
@@ -147,6 +198,11 @@ int validate(int B, int grid_h, int grid_w, int C, int F, int dtype, Sizes *sz) 
   const long long tokens = (long long)B * grid_h * grid_w;
   if (tokens > kMaxTokens)
     return set_error(GTR_ERR_INVALID_ARG, "%lld tokens exceed 2^24", tokens);
+  const long long blocks = (long long)B * ((grid_h + kTileY - 1) / kTileY) *
+                           ((grid_w + kTileX - 1) / kTileX) * ((F + kSlice - 1) / kSlice);
+  if (blocks >= (1LL << 31))
+    return set_error(GTR_ERR_INVALID_ARG, "%lld workgroups of %dx%d tokens exceed 2^31", blocks, kTileY,
+                     kTileX);
   sz->tokens = tokens;
   sz->u_bytes = round256((size_t)tokens * 2 * F * u_bytes_per_elem(dtype));
   sz->h_bytes = round256((size_t)tokens * F * elem_bytes(dtype));
@@ -283,9 +339,9 @@ int gtr_swiglu_fwd(const void *x, const void *w_in, const void *conv_w, const vo
   if (rc != GTR_OK) return rc;
   int err;
   switch (dtype) {
-    case GTR_DTYPE_F32: err = launch_mix<float, float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
-    case GTR_DTYPE_F16: err = launch_mix<_Float16, _Float16>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
-    default: err = launch_mix<uint16_t, float>(u, conv_w, conv_b, h, grid_h, grid_w, F, sz.tokens, stream); break;
+    case GTR_DTYPE_F32: err = launch_mix<float, float>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
+    case GTR_DTYPE_F16: err = launch_mix<_Float16, _Float16>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
+    default: err = launch_mix<uint16_t, float>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
   }
   if (err != (int)hipSuccess)
     return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));

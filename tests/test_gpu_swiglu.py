@@ -45,7 +45,8 @@ def check(ins, dtype, label):
 @pytest.mark.parametrize("bias", [True, False])
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", [(1, 1, 1, 8, 8), (1, 1, 9, 16, 24), (1, 7, 1, 16, 40),
-                                   (2, 5, 7, 32, 48), (3, 9, 13, 64, 136), (1, 17, 19, 128, 344)],
+                                   (2, 5, 7, 32, 48), (3, 9, 13, 64, 136), (1, 17, 19, 128, 344),
+                                   (2, 8, 16, 64, 64), (1, 33, 47, 32, 72)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_small_shapes(shape, dtype, bias):
     B, gh, gw, C, F = shape
