@@ -53,6 +53,8 @@ def _load():
     dp = ctypes.POINTER(ctypes.c_double)
     lib.gla_oracle_f64.restype = ctypes.c_int
     lib.gla_oracle_f64.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_int] * 7 + [dp, dp, ctypes.c_int]
+    lib.gla_oracle_bwd_f64.restype = ctypes.c_int
+    lib.gla_oracle_bwd_f64.argtypes = [dp] * 12 + [ctypes.c_int] * 8
     lib.gla_oracle_scan_index.restype = ctypes.c_long
     lib.gla_oracle_scan_index.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int]
     _lib = lib
@@ -112,3 +114,31 @@ def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = F
     if return_threads:
         res.append(rc)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def gla_backward(q, k, v, log_gate, dout, direction: int, s0=None, ds_final=None,
+                 want_ds0: bool = False, n_threads: int = 0):
+    """Token-by-token fp64 gradients of the forward pass (see gla_oracle_bwd_f64).
+
+    Returns (dq, dk, dv, dlog_gate) as float64 in the layouts of q, k, v and
+    log_gate, plus ds0 when ``want_ds0``.  ds_final is dL/dS_final (optional)."""
+    q, k, v, g, do = to_f64(q), to_f64(k), to_f64(v), to_f64(log_gate), to_f64(dout)
+    B, H, gh, gw, dk_ = q.shape
+    dv_ = v.shape[4]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:4] != q.shape[:4] or do.shape != v.shape:
+        raise ValueError("bad shapes")
+    st = (B, H, dk_, dv_)
+    s0a = to_f64(s0) if s0 is not None else None
+    dsf = to_f64(ds_final) if ds_final is not None else None
+    for a in (s0a, dsf):
+        if a is not None and a.shape != st:
+            raise ValueError(f"bad state shape {a.shape}")
+    dq, dk = np.empty_like(q), np.empty_like(k)
+    dv, dg = np.empty_like(v), np.empty_like(g)
+    ds0 = np.empty(st, dtype=np.float64) if want_ds0 else None
+    rc = _load().gla_oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(do), _ptr(s0a),
+                                    _ptr(dsf), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(ds0),
+                                    B, H, gh, gw, dk_, dv_, int(direction), int(n_threads))
+    if rc < 0:
+        raise ValueError(f"gla_oracle_bwd_f64 failed with code {rc}")
+    return (dq, dk, dv, dg, ds0) if want_ds0 else (dq, dk, dv, dg)

@@ -151,3 +151,123 @@ int gla_oracle_f64(const double *q, const double *k, const double *v,
     if (failed) return -4;
     return used;
 }
+
+/*
+ * Backward pass of the same recurrence, by the chain rule applied to it one
+ * token at a time (no chunking, no identities): given dout = dL/dout and,
+ * optionally, ds_final = dL/dS_final, it returns dq, dk, dv, dlog_gate and,
+ * optionally, ds0 = dL/ds0.
+ *
+ *   forward sweep:  S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,  keeping every S_{t-1};
+ *                   dq_t = S_t dout_t^T                     (o_t = q_t S_t)
+ *   reverse sweep:  G = ds_final (or 0);  for t = N-1 .. 0:
+ *                     G      += q_t^T dout_t                 (G = dL/dS_t)
+ *                     dk_t    = G v_t^T,  dv_t = k_t G       (from k_t^T v_t)
+ *                     dlog_gate_t[i] = alpha_t[i] sum_j G[i,j] S_{t-1}[i,j]
+ *                     G       = diag(alpha_t) G              (dL/dS_{t-1})
+ *                   ds0 = G.
+ *
+ * Layouts as the forward pass; dq, dk, dlog_gate like q, dv like v.  Each
+ * thread keeps the N states of one sequence (N * d_k * d_v doubles).  Returns
+ * the thread count, or -1 null pointer, -2 bad size, -3 bad direction, -4 out
+ * of memory.
+ */
+int gla_oracle_bwd_f64(const double *q, const double *k, const double *v,
+                       const double *log_gate, const double *dout, const double *s0,
+                       const double *ds_final, double *dq, double *dk, double *dv,
+                       double *dlog_gate, double *ds0, int B, int H, int grid_h, int grid_w,
+                       int d_k, int d_v, int direction, int n_threads)
+{
+    if (!q || !k || !v || !log_gate || !dout || !dq || !dk || !dv || !dlog_gate) return -1;
+    if (B <= 0 || H <= 0 || grid_h <= 0 || grid_w <= 0 || d_k <= 0 || d_v <= 0)
+        return -2;
+    if (direction < 0 || direction > 3) return -3;
+
+    const long n_tok = (long)grid_h * grid_w;
+    const long n_seq = (long)B * H;
+    const long kv = (long)d_k * d_v;
+    int used = 1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+    if (n_threads > n_seq) n_threads = (int)n_seq;
+    if (n_threads < 1) n_threads = 1;
+#else
+    n_threads = 1;
+#endif
+
+#pragma omp parallel num_threads(n_threads)
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double *prev = (double *)malloc(sizeof(double) * (size_t)(n_tok * kv));  /* S_{t-1}, all t */
+        double *S = (double *)malloc(sizeof(double) * (size_t)kv);
+        double *G = (double *)malloc(sizeof(double) * (size_t)kv);
+        if (!prev || !S || !G) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long bh = 0; bh < n_seq; ++bh) {
+            if (!prev || !S || !G) continue;
+            const double *qs = q + bh * n_tok * d_k, *ks = k + bh * n_tok * d_k;
+            const double *gs = log_gate + bh * n_tok * d_k;
+            const double *vs = v + bh * n_tok * d_v, *dos = dout + bh * n_tok * d_v;
+            double *dqs = dq + bh * n_tok * d_k, *dks = dk + bh * n_tok * d_k;
+            double *dvs = dv + bh * n_tok * d_v, *dgs = dlog_gate + bh * n_tok * d_k;
+
+            if (s0) memcpy(S, s0 + bh * kv, sizeof(double) * (size_t)kv);
+            else memset(S, 0, sizeof(double) * (size_t)kv);
+            for (long t = 0; t < n_tok; ++t) {
+                const long n = gla_oracle_scan_index(t, grid_h, grid_w, direction);
+                memcpy(prev + t * kv, S, sizeof(double) * (size_t)kv);
+                for (int i = 0; i < d_k; ++i) {
+                    const double a = exp(gs[n * d_k + i]);
+                    for (int j = 0; j < d_v; ++j)
+                        S[(long)i * d_v + j] = a * S[(long)i * d_v + j] + ks[n * d_k + i] * vs[n * d_v + j];
+                }
+                for (int i = 0; i < d_k; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < d_v; ++j) acc += S[(long)i * d_v + j] * dos[n * d_v + j];
+                    dqs[n * d_k + i] = acc;
+                }
+            }
+
+            if (ds_final) memcpy(G, ds_final + bh * kv, sizeof(double) * (size_t)kv);
+            else memset(G, 0, sizeof(double) * (size_t)kv);
+            for (long t = n_tok - 1; t >= 0; --t) {
+                const long n = gla_oracle_scan_index(t, grid_h, grid_w, direction);
+                const double *Sp = prev + t * kv;
+                for (int i = 0; i < d_k; ++i)
+                    for (int j = 0; j < d_v; ++j)
+                        G[(long)i * d_v + j] += qs[n * d_k + i] * dos[n * d_v + j];
+                for (int i = 0; i < d_k; ++i) {
+                    double acc = 0.0, da = 0.0;
+                    for (int j = 0; j < d_v; ++j) {
+                        acc += G[(long)i * d_v + j] * vs[n * d_v + j];
+                        da += G[(long)i * d_v + j] * Sp[(long)i * d_v + j];
+                    }
+                    dks[n * d_k + i] = acc;
+                    dgs[n * d_k + i] = exp(gs[n * d_k + i]) * da;
+                }
+                for (int j = 0; j < d_v; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < d_k; ++i) acc += ks[n * d_k + i] * G[(long)i * d_v + j];
+                    dvs[n * d_v + j] = acc;
+                }
+                for (int i = 0; i < d_k; ++i) {
+                    const double a = exp(gs[n * d_k + i]);
+                    for (int j = 0; j < d_v; ++j) G[(long)i * d_v + j] *= a;
+                }
+            }
+            if (ds0) memcpy(ds0 + bh * kv, G, sizeof(double) * (size_t)kv);
+        }
+        free(prev);
+        free(S);
+        free(G);
+    }
+    if (failed) return -4;
+    return used;
+}

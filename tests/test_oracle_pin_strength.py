@@ -70,3 +70,43 @@ def test_mutant_is_caught(tmp_path, name):
     lib = build_mutant(tmp_path, name, old, new)
     rc, out = run_pins(lib)
     assert rc != 0, f"mutant {name} passed every pin:\n{out}"
+
+
+# Mistakes planted in the backward pass; the backward pins (tests/test_oracle_bwd.py) must fail.
+BWD_MUTANTS = {
+    "bwd_dq_from_old_state": ("acc += S[(long)i * d_v + j] * dos[n * d_v + j];",
+                              "acc += prev[t * kv + (long)i * d_v + j] * dos[n * d_v + j];"),
+    "bwd_extra_decay": ("G[(long)i * d_v + j] += qs[n * d_k + i] * dos[n * d_v + j];",
+                        "G[(long)i * d_v + j] = exp(gs[n * d_k + i]) * G[(long)i * d_v + j]"
+                        " + qs[n * d_k + i] * dos[n * d_v + j];"),
+    "bwd_gate_grad_without_alpha": ("dgs[n * d_k + i] = exp(gs[n * d_k + i]) * da;",
+                                    "dgs[n * d_k + i] = da;"),
+    "bwd_dk_transposed_state": ("acc += G[(long)i * d_v + j] * vs[n * d_v + j];",
+                                "acc += G[(long)(j % d_k) * d_v + (i % d_v)] * vs[n * d_v + j];"),
+    "bwd_dv_uses_query": ("acc += ks[n * d_k + i] * G[(long)i * d_v + j];",
+                          "acc += qs[n * d_k + i] * G[(long)i * d_v + j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(tmp_path, name):
+    old, new = BWD_MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new, 1))
+    lib = oracle.build_from(str(path), str(tmp_path / f"{name}.so"))
+    env = dict(os.environ, GLA_ORACLE_LIB_OVERRIDE=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} passed every backward pin:\n{r.stdout[-2000:]}"
+
+
+def test_unmodified_backward_passes(tmp_path):
+    lib = oracle.build_from(SRC, str(tmp_path / "clean_bwd.so"))
+    env = dict(os.environ, GLA_ORACLE_LIB_OVERRIDE=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_bwd.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:]
