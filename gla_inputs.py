@@ -153,3 +153,10 @@ def make_swiglu_inputs(B, grid_h, grid_w, C, F, dtype="f16", seed=0, bias=True):
     w_out = torch.randn((F, C), generator=g, dtype=torch.float32) / math.sqrt(F)
     t = TORCH_DTYPES[dtype]
     return (x.to(t), w_in.to(t), conv_w.to(t), conv_b.to(t) if bias else None, w_out.to(t))
+
+
+def make_output_grad(shape, dtype="f16", seed=0):
+    """dL/dout for the backward pass: N(0, 1) of the given shape, rounded to the I/O dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=g, dtype=torch.float32).to(TORCH_DTYPES[dtype])

@@ -180,6 +180,21 @@ size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, in
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,
                  int path, int *seg_len, int *n_seg, int *fused);
 
+/* Backward pass of gtr_gla_fwd_ex: given dout = dL/dout (laid out like out)
+ * and optionally ds_final = dL/ds_final (float32 [B][H][d_k][d_v], NULL = 0),
+ * writes dq, dk, dlog_gate (like q) and dv (like v), and ds0 = dL/ds0 when
+ * ds0 is not NULL.  s0 is the forward call's initial state (NULL = zero).
+ * Gradients follow the recurrence of gtr_gla_fwd by the chain rule (x-techcon
+ * article on GTR, section 架构 / Architecture, for the recurrence).  Head dims
+ * are multiples of 4 up to 64 (GTR_ERR_UNSUPPORTED otherwise); every output
+ * must be distinct from every input and from the others; the other rules are
+ * those of gtr_gla_fwd_ex.  Asynchronous on `stream`; the library keeps a
+ * separate per-(device, stream) backward workspace. */
+int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gate, const void *dout,
+                const float *s0, const float *ds_final, void *dq, void *dk, void *dv, void *dlog_gate,
+                float *ds0, int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
+                int dtype, hipStream_t stream);
+
 /* Message for the last error returned on this thread ("" if none).  The string
  * is owned by the library and stays valid until the next call on this thread. */
 const char *gtr_gla_last_error(void);

@@ -34,7 +34,7 @@ EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf1
            "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
            "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name",
-           "gtr_gla_stream_status", "gtr_swiglu_fwd", "gtr_swiglu_workspace_bytes")
+           "gtr_gla_stream_status", "gtr_gla_bwd", "gtr_swiglu_fwd", "gtr_swiglu_workspace_bytes")
 
 
 class GlaError(RuntimeError):
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.gtr_gla_kernel_name.restype = ctypes.c_char_p
     L.gtr_gla_stream_status.argtypes = [st]
     L.gtr_gla_stream_status.restype = i
+    L.gtr_gla_bwd.argtypes = [vp] * 5 + [fp, fp] + [vp] * 4 + [fp] + [i] * 8 + [st]
+    L.gtr_gla_bwd.restype = i
     L.gtr_swiglu_fwd.argtypes = [vp] * 6 + [i] * 6 + [st]
     L.gtr_swiglu_fwd.restype = i
     L.gtr_swiglu_workspace_bytes.argtypes = [i] * 6
@@ -219,6 +221,40 @@ def gla_forward(q, k, v, log_gate, direction: int, s0=None, want_state: bool = F
     gtr_gla_fwd_ex(q, k, v, log_gate, out, direction, s0=s0, s_final=s_final,
                    chunks_per_segment=chunks_per_segment, path=path, stream=stream)
     return (out, s_final) if want_state else out
+
+
+def gtr_gla_bwd(q, k, v, log_gate, dout, dq, dk, dv, dlog_gate, direction: int, s0=None,
+                ds_final=None, ds0=None, stream=None) -> None:
+    """Gradients of gtr_gla_fwd_ex (asynchronous): dq, dk, dlog_gate like q, dv like v; ds0
+    (optional, float32 [B, H, d_k, d_v]) receives dL/ds0.  ds_final is dL/ds_final."""
+    B, H, gh, gw, d_k, d_v = _shapes(q, k, v, log_gate, dout)
+    for name, t, like in (("dq", dq, q), ("dk", dk, q), ("dv", dv, v), ("dlog_gate", dlog_gate, q)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() \
+                or t.shape != like.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like its input")
+    for name, t in (("s0", s0), ("ds_final", ds_final), ("ds0", ds0)):
+        if t is not None and (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
+                              or tuple(t.shape) != (B, H, d_k, d_v)):
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor [B, H, d_k, d_v]")
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    _check(lib().gtr_gla_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(),
+                             dout.data_ptr(), ptr(s0), ptr(ds_final), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), dlog_gate.data_ptr(), ptr(ds0), B, H, gh, gw, d_k, d_v,
+                             int(direction), DTYPE_CODES[q.dtype], _stream_handle(stream)))
+
+
+def gla_backward(q, k, v, log_gate, dout, direction: int, s0=None, ds_final=None,
+                 want_ds0: bool = False, stream=None):
+    """Allocating wrapper: returns (dq, dk, dv, dlog_gate) and ds0 when asked."""
+    dq, dk, dlg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(log_gate)
+    dv = torch.empty_like(v)
+    ds0 = None
+    if want_ds0:
+        ds0 = torch.empty(q.shape[0], q.shape[1], q.shape[4], v.shape[4], dtype=torch.float32,
+                          device=q.device)
+    gtr_gla_bwd(q, k, v, log_gate, dout, dq, dk, dv, dlg, direction, s0=s0, ds_final=ds_final,
+                ds0=ds0, stream=stream)
+    return (dq, dk, dv, dlg, ds0) if want_ds0 else (dq, dk, dv, dlg)
 
 
 # ---- Spatial SwiGLU block (include/gtr_swiglu.h) ------------------------------------------------

@@ -25,7 +25,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_profile.cpp", "swiglu.hip"]
+SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_bwd.cpp", "gla_profile.cpp", "swiglu.hip"]
 
 
 def source_digest() -> str:

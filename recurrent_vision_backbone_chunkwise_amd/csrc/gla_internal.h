@@ -38,6 +38,24 @@ struct LaunchArgs {
   const float *s0;   // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;    // user final state, row-major [B*H][d_k][d_v], nullable
   bool fused;        // one launch (gla_fused) instead of three
+  bool states_only;  // split path without outputs: only the states entering each segment (prev)
+  bool want_prev;    // split path: write prev for every segment even where the outputs need no scan
+  bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass; d_k <= 64, split path)
+  hipStream_t stream;
+};
+
+// One launch of the backward chunk kernel (gla_bwd_dqk): for every 64-token
+// chunk of every sequence, along `direction`,
+//   out_tau = 2^E_tau * (S_prev a_tau^T) + sum_{sigma <= tau} (a_tau . b_sigma) kop_sigma * 2^(E_tau - E_sigma)
+// with E the log2 cumulative gate from the chunk start (per d_k dim) and S_prev
+// the state entering the chunk.  Used for dq (kop = k, a = dout, b = v, forward
+// states) and dk (kop = q, a = v, b = dout, reversed scan, state gradients).
+struct BwdArgs {
+  const void *kop, *aop, *bop, *g;  // [bh][grid][d_k], [bh][grid][d_v] twice, [bh][grid][d_k]
+  void *out;                        // [bh][grid][d_k]
+  float *off;                       // [bh][grid][d_k] fp32: out without its self term (sigma = tau)
+  const float *prev;                // [bh][n_chunk][4096] register order
+  int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
   hipStream_t stream;
 };
 
@@ -65,6 +83,21 @@ void clear_error();
 int check_device_pointer(const void *p, size_t bytes, int device, const char *name);
 bool pointer_checks_off();
 bool stream_capturing(hipStream_t stream);
+
+// Backward-pass launchers (hipError_t values).
+int launch_gla_bwd_dqk(const BwdArgs &a);
+// g_lag at the grid cell of scan position t = log_gate of position t+1 (0 at the last position).
+int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, int d_k, int direction,
+                    int dtype, hipStream_t stream);
+// dlog_gate_t = sum_{u >= t} (q_u dq_u - k_u dk_u) + rowsum(ds_final * s_final) along `direction`,
+// with dq, dk the fp32 results of the backward chunk kernel without their (cancelling) self
+// terms; totals: [bh][n_chunk][64] fp32 scratch.  ds_final / s_final may be null.
+int launch_dgate(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
+                 const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w, int d_k,
+                 int d_v, int n_chunk, int direction, int dtype, hipStream_t stream);
+// ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][d_k][d_v].
+int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
+               int direction, int dtype, hipStream_t stream);
 
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);

@@ -95,6 +95,7 @@ struct IoF32 {
   using Raw = u4;  // 16 bytes
   __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b); }
+  __device__ static T narrow(float v) { return v; }
   __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u4, v); }
 };
 
@@ -104,6 +105,7 @@ struct IoF16 {
   __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
   __device__ static f4 to_f4(Raw r) { return __builtin_convertvector(to_h4(r), f4); }
   __device__ static float from_bits(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+  __device__ static T narrow(float v) { return (_Float16)v; }
   __device__ static Raw pack(f4 v) { return __builtin_bit_cast(u2, __builtin_convertvector(v, h4)); }
 };
 
@@ -116,6 +118,7 @@ struct IoBF16 {
   }
   __device__ static h4 to_h4(Raw r) { return __builtin_convertvector(to_f4(r), h4); }
   __device__ static float from_bits(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static T narrow(float v) { return (T)rne(v); }
   __device__ static uint32_t rne(float f) {  // round to nearest even, quiet NaN kept
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
@@ -208,6 +211,12 @@ template <> struct ToOp<_Float16, IoBF16> {
 };
 template <> struct ToOp<float, IoF32> {
   __device__ static f4 cvt(u4 r) { return IoF32::to_f4(r); }
+};
+template <> struct ToOp<float, IoF16> {  // fp32 operands for 16-bit I/O (backward pass)
+  __device__ static f4 cvt(u2 r) { return IoF16::to_f4(r); }
+};
+template <> struct ToOp<float, IoBF16> {
+  __device__ static f4 cvt(u2 r) { return IoBF16::to_f4(r); }
 };
 
 __device__ __forceinline__ void cvt4(f4 x, h4 &y) { y = __builtin_convertvector(x, h4); }
@@ -1173,7 +1182,8 @@ int launch_typed(const LaunchArgs &a) {
       return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
     return (int)hipGetLastError();
   }
-  const bool need_scan = a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr;
+  const bool need_scan =
+      a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr || a.states_only || a.want_prev;
   if (need_scan) {
     const int n_state_seg = a.s_final ? a.n_seg : a.n_seg - 1;
     if (n_state_seg > 0) {
@@ -1185,8 +1195,294 @@ int launch_typed(const LaunchArgs &a) {
     const long threads = (long)a.bh * NK * kStateElems;
     launch(kKernelSegScan, gla_seg_scan<NK>, (unsigned)((threads + kThreads - 1) / kThreads), a.stream, p);
   }
+  if (a.states_only) return (int)hipGetLastError();
   launch(kKernelSegOut, gla_seg_out<Io, Op, NK>, n_blocks, a.stream, p);
   return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------ backward pass
+//
+// Gradients of the recurrence (chain rule through S_t = diag(alpha_t) S_{t-1}
+// + k_t^T v_t, o_t = q_t S_t).  With G_t = dL/dS_t, which obeys the same kind
+// of recurrence run backwards (G_t = q_t^T dout_t + diag(alpha_{t+1}) G_{t+1}):
+//   dq_t = S_t dout_t^T,   dk_t = G_t v_t^T,   dv_t = k_t G_t,
+//   dlog_gate_t = sum_{u >= t} (q_u dq_u - k_u dk_u)  (+ rowsum(dS_final S_final)).
+// Read along the reversed scan, G is a forward state with keys q, values dout
+// and each position's gate taken from the next position, so dv is a forward
+// pass of this library and its state scan gives G at every chunk boundary.
+// dq and dk contract a state over its value side instead of its key side;
+// gla_bwd_dqk forms them per chunk from the boundary states.
+
+// Transposed fragment (as frag_tr) of a row-major tile with row stride `stride`.
+__device__ __forceinline__ h8 frag_tr_ld(const _Float16 *tile, int stride, int r0, int c0, int lane) {
+  const int src = lane & 15, g = lane >> 4;
+  const int row = r0 + 4 * g + (src >> 2), col = c0 + 4 * (src & 3);
+  auto tr = [&](int r) {
+    lds_s4 *ptr = (lds_s4 *)((lds_h *)tile + r * stride + col);
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ptr));
+  };
+  return cat(tr(row), tr(row + 16));
+}
+__device__ __forceinline__ f8 frag_tr_ld(const float *tile, int stride, int r0, int c0, int lane) {
+  const int g = lane >> 4, col = c0 + (lane & 15);
+  f8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = tile[(r0 + 4 * g + e) * stride + col];
+    f[4 + e] = tile[(r0 + 16 + 4 * g + e) * stride + col];
+  }
+  return f;
+}
+
+// Per-dim factor 2^(E_start(a) - E_end(b)) between key sub-block b and query
+// sub-block a > b (1 for adjacent blocks).
+template <typename Op, int NQ>
+__device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int b, int i) {
+  if (b == a - 1) return 1.f;
+  const int idx = (a == 2) ? 0 : (b == 0 ? 1 : 2);
+  return (float)sm.cv[idx * kHead + i];
+}
+
+// One workgroup per chunk.  The forward chunk preparation runs with the query
+// set to one, which leaves in LDS exactly the factors needed here:
+//   qs = 2^(E_tau - E_start(a))       (per token and dim, <= 1)
+//   ks = kop 2^(E_end(b) - E_sigma)   (keys referenced to their sub-block end)
+//   hv, cv, tot                       (midpoint and block-pair factors)
+//   vv = a                            (the score query rows)
+// The scores P = a b^T are formed on MFMA into LDS (lower block triangle,
+// sigma < tau on the diagonal tiles; the self scores P[tau][tau] are kept in
+// fp32).  Wave w then owns dims [16w, 16w+16) of every token:
+//   out^T = 2^(E_tau - E_start(a)) (S 2^E_start(a) a^T + sum_{b<a} (ks c_ab)^T P^T
+//           + hv (ks hv)^T P_aa^T) + P[tau][tau] kop_tau,
+// every MFMA operand factor <= 1 except the diagonal midpoint factors (<= 2^8);
+// a diagonal sub-block whose gate range is too wide for that is summed exactly
+// in fp32.  `off` receives out without its self term (sigma = tau) in fp32:
+// the gate gradient sums q dq - k dk, where the self terms of dq and dk are
+// equal and cancel, so leaving them out keeps their rounding out of it.
+template <class Io, typename Op>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off) {
+  using T = typename Io::T;
+  constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
+  __shared__ Smem<Op, 1> sm;
+  __shared__ __attribute__((aligned(16))) Op bs[kChunk * LD];  // score keys b [sigma][j], then kop [tau][i]
+  __shared__ __attribute__((aligned(16))) Op ps[kChunk * LD];  // P [tau][sigma], sigma < tau
+  __shared__ float self_score[kChunk];                         // P [tau][tau]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
+  const Seq sq = seq_of<Io>(p, seq);  // k: kop, v: a, g: gates, o: b (read only)
+  const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<T *>(out) + (size_t)seq * p.n_tok * p.dk, (short)0,
+      (int)((uint32_t)p.n_tok * (uint32_t)p.dk * sizeof(T)), 0x00020000);
+
+  // this lane's operand row i = 16w + l16 of the state entering the chunk, at
+  // the k-slots of an MFMA operand (register-order workspace layout)
+  const int i_row = 16 * wave + l16;
+  float srow[16];
+  {
+    const float *st = p.prev + ((size_t)seq * p.n_chunk + c) * kStateElems;
+    const int x = 4 * (i_row >> 4) + (i_row & 3), lo = 16 * ((i_row & 15) >> 2);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * kb + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+        srow[8 * kb + e] = st[(j >> 4) * 1024 + x * 64 + lo + (j & 15)];
+      }
+  }
+  Rows<Io> x;
+  load_chunk<Io, false, true>(sq, c, 0, wave, lane, x);
+  typename Io::Raw brow[4];
+  {
+    const uint32_t vc = val_col<Io>(sq, 4 * l16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) brow[r] = buf_load<Io>(sq.o, cell_at(x.off[r], sq.vpitch, vc));
+  }
+  const typename Io::Raw one = Io::pack(f4{1.f, 1.f, 1.f, 1.f});
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x.q[r] = one;
+  op4<Op> qs[4], ks[4];
+  prep_local<Io, Op, true, 1>(sm, x, wave, lane, 0, qs, ks, true);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(brow[r]);
+  lds_sync();
+  prep_chunk<Io, Op, true, 1>(sm, qs, ks, wave, lane, 0);
+  lds_sync();
+
+  // P tiles of query block `wave` (zero above the diagonal, so every tile is finite)
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (b <= wave) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        acc = mma(frag_row<Op>(&sm.vv[(16 * wave + l16) * LDT + 32 * kb + 4 * g4]),
+                  frag_row<Op>(&bs[(16 * b + l16) * LD + 32 * kb + 4 * g4]), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tau = 16 * wave + 4 * g4 + r, sigma = 16 * b + l16;
+      ps[tau * LD + sigma] = (Op)((b < wave || (b == wave && sigma < tau)) ? acc[r] : 0.f);
+      if (b == wave && sigma == tau) self_score[tau] = acc[r];
+    }
+  }
+  lds_sync();
+  // every wave has read the score keys: the tile now takes kop itself
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(x.k[r]);
+  lds_sync();
+
+  float es = 1.f;  // 2^E_start(a) for dim i_row
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f}, accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {  // state entering the chunk
+      op8<Op> sf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sf[e] = (Op)(srow[8 * kb + e] * es);
+      acc = mma(sf, frag_row<Op>(&sm.vv[(16 * a + l16) * LDT + 32 * kb + 4 * g4]), acc);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {  // earlier sub-blocks
+      if (2 * kb >= a) break;
+      const float f0 = block_factor(sm, a, 2 * kb, i_row);
+      const float f1 = 2 * kb + 1 < a ? block_factor(sm, a, 2 * kb + 1, i_row) : 0.f;
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * wave, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xk[e] = (Op)((float)xk[e] * (e < 4 ? f0 : f1));
+      acc = mma(xk, frag_row<Op>(&ps[(16 * a + l16) * LD + 32 * kb + 4 * g4]), acc);
+    }
+    const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
+    if (!exact) {  // own sub-block, referenced at its midpoint
+      const int kb = a >> 1;
+      const float h = (float)sm.hv[a * kHead + i_row];
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * wave, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xk[e] = (Op)(((e < 4) == ((a & 1) == 0)) ? (float)xk[e] * h : 0.f);
+      accd = mma(xk, frag_row<Op>(&ps[(16 * a + l16) * LD + 32 * kb + 4 * g4]), accd);
+    }
+    const int tau = 16 * a + l16;
+    const int d0 = 16 * wave + 4 * g4;
+    f4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f1 = (float)sm.qs[tau * LD + d0 + r];
+      o[r] = f1 * (acc[r] + (float)sm.hv[a * kHead + d0 + r] * accd[r]);
+    }
+    const bool live = c * kChunk + tau < p.n_tok;
+    if (exact && live) {  // exact fp32 sum over the earlier tokens of the own sub-block
+      constexpr uint32_t elt = sizeof(T);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = d0 + r;
+        if (i >= p.dk) continue;
+        float ex = 0.f;
+        float run = key_elem<Io>(sq.g, sm.rowoff[0][tau] * sq.kpitch + i * elt) * kLog2e;
+        for (int s2 = tau - 1; s2 >= 16 * a; --s2) {
+          const uint32_t cell = sm.rowoff[0][s2];
+          // 2^(E_tau - E_s2): the log2 gates of tokens s2+1 .. tau
+          ex += (float)ps[tau * LD + s2] * key_elem<Io>(sq.k, cell * sq.kpitch + i * elt) * fast_exp2(run);
+          run += key_elem<Io>(sq.g, cell * sq.kpitch + i * elt) * kLog2e;
+        }
+        o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
+      }
+    }
+    f4 full;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) full[r] = o[r] + self_score[tau] * (float)bs[tau * LD + d0 + r];
+    const uint32_t cell = sm.rowoff[0][tau];
+    buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
+    if (cell != kNoRow && d0 < p.dk)
+      *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = o;
+    es *= sm.tot[a * kHead + i_row];
+  }
+}
+
+// Grid cell of scan position t (plain arguments; see token_cell).
+__device__ __forceinline__ uint32_t scan_cell(int t, int n_tok, int gh, int gw, int dir, float rcp_gh) {
+  const int p = (dir & 1) ? n_tok - 1 - t : t;
+  if (!(dir & 2)) return (uint32_t)p;
+  int row, col;
+  col_major_pos(p, gh, rcp_gh, row, col);
+  return (uint32_t)(row * gw + col);
+}
+
+// One thread per (sequence, scan position, 4 dims).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gla_gate_lag(const T *g, T *lag, int n_tok, int gh, int gw,
+                                                         int dir, float rcp_gh, int dk, long long n) {
+  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= n) return;
+  const int groups = dk / 4;
+  const long long per_seq = (long long)n_tok * groups;
+  const long long seq = gid / per_seq;
+  const int rem = (int)(gid - seq * per_seq);
+  const int t = rem / groups, j = 4 * (rem - (rem / groups) * groups);
+  const size_t base = (size_t)seq * n_tok * dk;
+  T *dst = lag + base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * dk + j;
+  if (t + 1 < n_tok) {
+    const T *src = g + base + (size_t)scan_cell(t + 1, n_tok, gh, gw, dir, rcp_gh) * dk + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = src[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = T(0);
+  }
+}
+
+template <class Io> __device__ __forceinline__ float elem(const typename Io::T *p) {
+  if constexpr (sizeof(typename Io::T) == 4)
+    return Io::from_bits(__float_as_uint(*reinterpret_cast<const float *>(p)));
+  else
+    return Io::from_bits(*reinterpret_cast<const uint16_t *>(p));
+}
+
+// Chunk totals of q dq - k dk per dim (dq and dk without their self terms, fp32):
+// one workgroup of 64 threads per (sequence, chunk).
+template <class Io>
+__global__ __launch_bounds__(64) void gla_dgate_totals(const typename Io::T *q, const typename Io::T *k,
+                                                       const float *dq, const float *dk,
+                                                       float *totals, int n_tok, int gh, int gw, int dir,
+                                                       float rcp_gh, int d_k, int n_chunk) {
+  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk, i = threadIdx.x;
+  float sum = 0.f;
+  if (i < d_k) {
+    const size_t base = (size_t)seq * n_tok * d_k + i;
+    const int t1 = min(n_tok, (c + 1) * kChunk);
+    for (int t = c * kChunk; t < t1; ++t) {
+      const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k;
+      sum += elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
+    }
+  }
+  totals[((size_t)seq * n_chunk + c) * kHead + i] = sum;
+}
+
+// dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then a
+// reverse running sum inside the chunk.
+template <class Io>
+__global__ __launch_bounds__(64) void gla_dgate_apply(const typename Io::T *q, const typename Io::T *k,
+                                                      const float *dq, const float *dk,
+                                                      const float *ds_final, const float *s_final,
+                                                      const float *totals, typename Io::T *dg, int n_tok,
+                                                      int gh, int gw, int dir, float rcp_gh, int d_k,
+                                                      int d_v, int n_chunk) {
+  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk, i = threadIdx.x;
+  if (i >= d_k) return;
+  float run = 0.f;
+  if (ds_final && s_final) {
+    const size_t row = ((size_t)seq * d_k + i) * d_v;
+    for (int j = 0; j < d_v; ++j) run += ds_final[row + j] * s_final[row + j];
+  }
+  for (int c2 = n_chunk - 1; c2 > c; --c2) run += totals[((size_t)seq * n_chunk + c2) * kHead + i];
+  const size_t base = (size_t)seq * n_tok * d_k + i;
+  for (int t = min(n_tok, (c + 1) * kChunk) - 1; t >= c * kChunk; --t) {
+    const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k;
+    run += elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
+    dg[at] = Io::narrow(run);
+  }
 }
 
 }  // namespace
@@ -1206,10 +1502,130 @@ int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t 
 
 int launch_gla(const LaunchArgs &a) {
   const bool two = a.nk == 2;
+  if (a.fp32_operands && !two && !a.fused) {
+    switch (a.dtype) {
+      case 1: return launch_typed<IoF16, float, 1>(a);
+      case 2: return launch_typed<IoBF16, float, 1>(a);
+      default: break;
+    }
+  }
   switch (a.dtype) {
     case 0: return two ? launch_typed<IoF32, float, 2>(a) : launch_typed<IoF32, float, 1>(a);
     case 1: return two ? launch_typed<IoF16, _Float16, 2>(a) : launch_typed<IoF16, _Float16, 1>(a);
     case 2: return two ? launch_typed<IoBF16, _Float16, 2>(a) : launch_typed<IoBF16, _Float16, 1>(a);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gtr
+
+// ------------------------------------------------------- backward launchers
+namespace gtr {
+namespace {
+
+// ds0 = diag(alpha_0) G_0: one thread per state element.
+template <class Io>
+__global__ __launch_bounds__(kThreads) void gla_ds0(const typename Io::T *g, const float *g0, float *ds0,
+                                                    int n_tok, int gh, int gw, int dir, float rcp_gh,
+                                                    int d_k, int d_v, long long n) {
+  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= n) return;
+  const long long per_seq = (long long)d_k * d_v;
+  const long long seq = gid / per_seq;
+  const int i = (int)((gid - seq * per_seq) / d_v);
+  const size_t at = (size_t)seq * n_tok * d_k + (size_t)scan_cell(0, n_tok, gh, gw, dir, rcp_gh) * d_k + i;
+  ds0[gid] = expf(elem<Io>(g + at)) * g0[gid];
+}
+
+template <class Io, typename Op>
+int launch_bwd_typed(const BwdArgs &a) {
+  Params p{};
+  p.q = a.kop; p.k = a.kop; p.v = a.aop; p.g = a.g; p.out = const_cast<void *>(a.bop);
+  p.bh_count = a.bh; p.n_tok = a.n_tok; p.gh = a.grid_h; p.gw = a.grid_w; p.dir = a.direction;
+  p.rcp_gh = 1.0f / (float)a.grid_h;
+  p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
+  p.n_chunk = a.n_chunk; p.prev = a.prev;
+  auto kernel = gla_bwd_dqk<Io, Op>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(a.bh * a.n_chunk)), dim3(kThreads), 0, a.stream, p, a.out, a.off);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+// fp32 MFMA operands for every I/O type: the gate gradient sums dq and dk terms
+// whose pairs cancel between the two kernels, so their operands must not carry
+// 16-bit rounding (or 16-bit underflow of strongly decayed factors).
+int launch_gla_bwd_dqk(const BwdArgs &a) {
+  switch (a.dtype) {
+    case 0: return launch_bwd_typed<IoF32, float>(a);
+    case 1: return launch_bwd_typed<IoF16, float>(a);
+    case 2: return launch_bwd_typed<IoBF16, float>(a);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, int d_k, int direction,
+                    int dtype, hipStream_t stream) {
+  const int n_tok = grid_h * grid_w;
+  const long long n = (long long)bh * n_tok * (d_k / 4);
+  const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
+  const float rcp = 1.0f / (float)grid_h;
+  if (dtype == 0)
+    hipLaunchKernelGGL(gla_gate_lag<float>, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const float *>(g),
+                       static_cast<float *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
+  else
+    hipLaunchKernelGGL(gla_gate_lag<uint16_t>, dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t *>(g), static_cast<uint16_t *>(g_lag), n_tok, grid_h,
+                       grid_w, direction, rcp, d_k, n);
+  return (int)hipGetLastError();
+}
+
+namespace {
+template <class Io>
+int launch_dgate_typed(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
+                       const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w,
+                       int d_k, int d_v, int n_chunk, int direction, hipStream_t stream) {
+  using T = typename Io::T;
+  const int n_tok = grid_h * grid_w;
+  const float rcp = 1.0f / (float)grid_h;
+  const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k);
+  const float *dqq = dq, *dkk = dk;
+  const dim3 grid((unsigned)(bh * n_chunk));
+  hipLaunchKernelGGL(gla_dgate_totals<Io>, grid, dim3(64), 0, stream, qq, kk, dqq, dkk, totals, n_tok, grid_h,
+                     grid_w, direction, rcp, d_k, n_chunk);
+  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(64), 0, stream, qq, kk, dqq, dkk, ds_final, s_final, totals,
+                     static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk);
+  return (int)hipGetLastError();
+}
+
+template <class Io>
+int launch_ds0_typed(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k,
+                     int d_v, int direction, hipStream_t stream) {
+  const long long n = (long long)bh * d_k * d_v;
+  hipLaunchKernelGGL(gla_ds0<Io>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     static_cast<const typename Io::T *>(g), g0, ds0, grid_h * grid_w, grid_h, grid_w,
+                     direction, 1.0f / (float)grid_h, d_k, d_v, n);
+  return (int)hipGetLastError();
+}
+}  // namespace
+
+int launch_dgate(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
+                 const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w, int d_k,
+                 int d_v, int n_chunk, int direction, int dtype, hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_dgate_typed<IoF32>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 1: return launch_dgate_typed<IoF16>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 2: return launch_dgate_typed<IoBF16>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
+               int direction, int dtype, hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_ds0_typed<IoF32>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
+    case 1: return launch_ds0_typed<IoF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
+    case 2: return launch_ds0_typed<IoBF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,115 @@
+"""Backward pass through the C ABI (gtr_gla_bwd) vs the fp64 backward oracle (needs an MI355X).
+
+Every gradient uses the forward pass's gate: max|y - o| / rms(o) <= 1e-4 (fp32 I/O),
+<= 1e-2 (fp16 I/O), and for bf16 the excess over the output's half-ulp <= 1e-2.
+"""
+import sys
+
+import pytest
+import torch
+
+import gla_inputs
+import oracle
+import recurrent_vision_backbone_chunkwise_amd as gla
+from oracle.compare import parity_errors
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = ("f32", "f16", "bf16")
+NAMES = ("dq", "dk", "dv", "dlog_gate", "ds0")
+
+
+def note(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def check(q, k, v, g, direction, dtype, label, s0=None, dsf=None, seed=0):
+    dout = gla_inputs.make_output_grad(v.shape, dtype, seed=seed)
+    note(f"bwd {label} dir={direction} dtype={dtype} shape={tuple(q.shape)} dv={v.shape[-1]} "
+         f"s0={s0 is not None} dsf={dsf is not None}")
+    dev = [t.to(DEV) for t in (q, k, v, g, dout)]
+    got = gla.gla_backward(*dev, direction, s0=s0.to(DEV) if s0 is not None else None,
+                           ds_final=dsf.to(DEV) if dsf is not None else None, want_ds0=True)
+    torch.cuda.synchronize()
+    ref = oracle.gla_backward(q, k, v, g, dout, direction, s0=s0.double().numpy() if s0 is not None else None,
+                              ds_final=dsf.double().numpy() if dsf is not None else None, want_ds0=True)
+    errs = {}
+    for name, y, o in zip(NAMES, got, ref):
+        # ds0 is fp32, formed from 16-bit operands for 16-bit I/O (as the forward's final state)
+        e = parity_errors(y.double().cpu().numpy(), o, ("f32" if dtype == "f32" else "f16") if name == "ds0" else dtype)
+        errs[name] = round(e["err_raw"], 6)
+        if e["rounding_floor"] > e["tol"]:
+            # the output type cannot hold these gradients (e.g. ~1e-13 in fp16): judge what it can
+            assert e["err_excess"] <= e["tol"], f"{label} {name}: {e}"
+        else:
+            assert e["ok"], f"{label} {name}: {e}"
+    return errs
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("direction", [0, 1, 2, 3])
+@pytest.mark.parametrize("grid", [(1, 1), (1, 63), (7, 9), (9, 17), (13, 11)], ids=lambda g: f"{g[0]}x{g[1]}")
+def test_small_grids(grid, direction, dtype):
+    gh, gw = grid
+    q, k, v, g = gla_inputs.make_inputs(2, 3, gh, gw, 64, 64, dtype, "light", seed=gh * 100 + gw + direction)
+    check(q, k, v, g, direction, dtype, f"{gh}x{gw}", seed=direction)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_initial_and_final_state(dtype):
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 11, 13, 64, 64, dtype, "light", seed=31)
+    gen = torch.Generator().manual_seed(32)
+    s0 = torch.randn(1, 2, 64, 64, generator=gen) * 0.5
+    dsf = torch.randn(1, 2, 64, 64, generator=gen) * 0.1
+    for d in range(4):
+        check(q, k, v, g, d, dtype, "state", s0=s0, dsf=dsf, seed=33 + d)
+
+
+@pytest.mark.parametrize("gate", ["const:-30", "mixed_extreme", "ones", "scale:4"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gate_extremes(gate, dtype):
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 19, 23, 64, 64, dtype, gate, seed=34)
+    for d in (0, 3):
+        check(q, k, v, g, d, dtype, f"gate={gate}", seed=35 + d)
+
+
+@pytest.mark.parametrize("dims", [(32, 32), (64, 32), (32, 64), (4, 8), (48, 60)], ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_head_dims(dims, dtype):
+    dk, dv = dims
+    q, k, v, g = gla_inputs.make_inputs(2, 2, 9, 17, dk, dv, dtype, "light", seed=dk + dv)
+    gen = torch.Generator().manual_seed(dk * dv)
+    s0 = torch.randn(2, 2, dk, dv, generator=gen) * 0.5
+    dsf = torch.randn(2, 2, dk, dv, generator=gen) * 0.1
+    for d in (1, 2):
+        check(q, k, v, g, d, dtype, f"dk={dk} dv={dv}", s0=s0, dsf=dsf, seed=36 + d)
+
+
+@pytest.mark.parametrize("widx", [2, 4])
+def test_workload_shapes(widx):
+    w = gla_inputs.workload(widx)
+    q, k, v, g = gla_inputs.workload_inputs(w, 0)
+    note(f"errors {check(q, k, v, g, w.directions[0], w.dtype, w.name, seed=37)}")
+
+
+def test_unsupported_width_and_empty_calls():
+    q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 1, 4, 4, 128, 64, "f16", "light", seed=38))
+    with pytest.raises(gla.GlaError) as ex:
+        gla.gla_backward(q, k, v, g, torch.zeros_like(v), 0)
+    assert ex.value.code == -2
+    x = torch.empty(2, 3, 0, 5, 64, dtype=torch.float16, device=DEV)
+    dsf = torch.randn(2, 3, 64, 64, device=DEV)
+    res = gla.gla_backward(x, x, x, x, x, 1, ds_final=dsf, want_ds0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(res[4], dsf)  # no tokens: the final state is the initial one
+
+
+def test_repeat_calls_are_bitwise_equal():
+    q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 4, 23, 29, 64, 64, "bf16", "light", seed=39))
+    dout = gla_inputs.make_output_grad(v.shape, "bf16", seed=40).to(DEV)
+    first = gla.gla_backward(q, k, v, g, dout, 2)
+    for _ in range(3):
+        again = gla.gla_backward(q, k, v, g, dout, 2)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)

@@ -402,7 +402,7 @@ def test_profiling_counts_launches():
     prof = gla.gtr_gla_profile_end()
     assert prof["gla_seg_out"][1] == 3 and prof["gla_seg_state"][1] == 3
     assert prof["gla_seg_scan"][1] == 3 and prof["gla_fused"][1] == 2
-    assert all(ms > 0 for ms, n in prof.values())
+    assert all(ms > 0 for ms, n in prof.values() if n > 0)
 
 
 def test_single_runtime_and_library_loaded():
