@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=50)
-    ap.add_argument("--op", choices=["gla", "swiglu"], default="gla",
-                    help="gla: the attention forward (default); swiglu: the Spatial SwiGLU block")
+    ap.add_argument("--op", choices=["gla", "bwd", "swiglu"], default="gla",
+                    help="gla: the attention forward (default); bwd: its backward pass; "
+                         "swiglu: the Spatial SwiGLU block")
     ap.add_argument("--swiglu-workload", type=int, default=1,
                     help="1 = 40x40 grid, C 384, F 1024; 2 = 128x128 grid, C 1024, F 2752 (fp16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -89,6 +90,9 @@ def main():
         return
     if args.op == "swiglu":
         swiglu_main(args)
+        return
+    if args.op == "bwd":
+        bwd_main(args)
         return
 
     import torch
@@ -245,6 +249,108 @@ def cpu_baseline(w, cpu_inputs, budget_s):
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # MI355X dense
+
+
+def bwd_main(args):
+    """One step = the backward pass of every call of the workload's round (dout seeded, inputs and
+    gradients resident in HBM)."""
+    import torch
+
+    import gla_inputs
+    import recurrent_vision_backbone_chunkwise_amd as gla
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible")
+    w = gla_inputs.workload(args.workload)
+    cpu_in = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
+    douts = [gla_inputs.make_output_grad(ins[2].shape, w.dtype, seed=9000 + i) for i, ins in enumerate(cpu_in)]
+    ins = [[t.to("cuda:0") for t in x] + [d.to("cuda:0")] for x, d in zip(cpu_in, douts)]
+    grads = [[torch.empty_like(x[0]), torch.empty_like(x[1]), torch.empty_like(x[2]), torch.empty_like(x[3])]
+             for x in ins]
+    stream = torch.cuda.Stream()
+
+    def step():
+        for (q, k, v, g, do), (dq, dk, dv, dg), d in zip(ins, grads, w.directions):
+            gla.gtr_gla_bwd(q, k, v, g, do, dq, dk, dv, dg, d, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay() if graph is not None else step()
+        stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    tokens_per_call = w.B * w.H * w.n_tok
+    tokens = tokens_per_call * len(w.directions)
+    value = tokens / (ms_per_step * 1e-3)
+
+    gla.gtr_gla_profile_begin()
+    with torch.cuda.stream(stream):
+        for _ in range(args.profile_steps):
+            step()
+    prof = gla.gtr_gla_profile_end()
+    torch.cuda.synchronize()
+    kern = {n: (1e3 * ms / c, c / args.profile_steps) for n, (ms, c) in prof.items() if c > 0}
+    dominant = max(kern, key=lambda n: kern[n][0] * kern[n][1])
+    elt = 4 if w.dtype == "f32" else 2
+    dk, dv = w.d_k, w.d_v
+    chunks = w.B * w.H * ((w.n_tok + 63) // 64)
+    # the chunk kernel: reads kop, gates, a, b and writes its output (algorithmic bytes); its
+    # contractions are the lower-triangle scores, the state term and the intra-chunk sum (fp32 MFMA)
+    bytes_dqk = tokens_per_call * (3 * dk + 2 * dv) * elt
+    flops_dqk = chunks * (2 * 64 * 64 * dv * 10 / 16 + 2 * 64 * dk * dv + 2 * 64 * 32 * dk)
+    us = kern["gla_bwd_dqk"][0]
+    t_hbm, t_mfma = bytes_dqk / (HBM_PEAK_GBS * 1e9), flops_dqk / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
+    if t_mfma > t_hbm:
+        rl = {"bound": "mfma", "achieved": flops_dqk / (us * 1e-6) / 1e12, "peak": MFMA_PEAK_TFLOPS["f32"],
+              "unit": "TFLOP/s"}
+    else:
+        rl = {"bound": "hbm", "achieved": bytes_dqk / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    rl["frac"] = round(rl["achieved"] / rl["peak"], 4)
+    rl["achieved"] = round(rl["achieved"], 1)
+    roofline = {**rl, "kernel": "gla_bwd_dqk", "traffic": None, "dominant_kernel": dominant,
+                "kernels": {n: {"avg_us": round(t, 3), "per_step": c} for n, (t, c) in kern.items()}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0, reps, threads = time.perf_counter(), 0, 1
+        while True:
+            for x, d, di in zip(cpu_in, douts, w.directions):
+                oracle.gla_backward(*x, d, di)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 100:
+                break
+        t = time.perf_counter() - t0
+        cpu = {"value": round(reps * tokens / t, 1), "unit": "tokens/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"the full step ({len(w.directions)} calls, {w.name}) x {reps}, {t:.1f} s, "
+                         "fp64 chain rule token by token"}
+    line = {
+        "metric": "GLA backward tokens/sec (B*H*N), one MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "d_k": dk,
+                   "d_v": dv, "io_dtype": w.dtype, "calls_per_step": len(w.directions),
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def swiglu_main(args):

@@ -131,7 +131,7 @@ def gtr_gla_profile_begin() -> None:
 
 def gtr_gla_profile_end() -> dict:
     """{kernel name: (total ms, launches)} for the kernels launched since profile_begin."""
-    n = 8
+    n = 16
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int * n)()
     rc = lib().gtr_gla_profile_end(ms, cnt, n)

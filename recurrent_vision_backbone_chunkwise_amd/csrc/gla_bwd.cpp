@@ -182,12 +182,15 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   if ((rc = launched(gtr::launch_gate_lag(log_gate, lag, (int)bh, grid_h, grid_w, d_k, direction, dtype,
                                           stream))) != GTR_OK)
     return rc;
-  gtr::LaunchArgs r = f;  // 3. dv and the state gradients along the reversed scan
+  gtr::LaunchArgs r = f;  // 3. the state gradients along the reversed scan, then dv from them
   r.q = k; r.k = q; r.v = dout; r.g = lag; r.out = dv;
   r.direction = direction ^ 1;
-  r.s0 = ds_final; r.s_final = g0; r.states_only = false; r.want_prev = true;
+  r.s0 = ds_final; r.s_final = g0;
   scan_area(lay.rev, r);
   if ((rc = launched(gtr::launch_gla(r))) != GTR_OK) return rc;
+  gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands
+  o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
+  if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
   gtr::BwdArgs b{};  // 4. dq
   float *dq_off = reinterpret_cast<float *>(ws + lay.dq_off), *dk_off = reinterpret_cast<float *>(ws + lay.dk_off);
   b.kop = k; b.aop = dout; b.bop = v; b.g = log_gate; b.out = dq; b.off = dq_off; b.prev = f.prev;

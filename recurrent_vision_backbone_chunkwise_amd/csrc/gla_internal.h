@@ -41,6 +41,7 @@ struct LaunchArgs {
   bool states_only;  // split path without outputs: only the states entering each segment (prev)
   bool want_prev;    // split path: write prev for every segment even where the outputs need no scan
   bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass; d_k <= 64, split path)
+  bool outputs_only;   // split path: only the output kernel, entering each segment with prev as given
   hipStream_t stream;
 };
 

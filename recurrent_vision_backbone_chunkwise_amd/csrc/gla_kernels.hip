@@ -1184,7 +1184,9 @@ int launch_typed(const LaunchArgs &a) {
   }
   const bool need_scan =
       a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr || a.states_only || a.want_prev;
-  if (need_scan) {
+  if (a.outputs_only) {
+    p.prev = a.prev;
+  } else if (need_scan) {
     const int n_state_seg = a.s_final ? a.n_seg : a.n_seg - 1;
     if (n_state_seg > 0) {
       Params ps = p;
@@ -1440,50 +1442,87 @@ template <class Io> __device__ __forceinline__ float elem(const typename Io::T *
     return Io::from_bits(*reinterpret_cast<const uint16_t *>(p));
 }
 
-// Chunk totals of q dq - k dk per dim (dq and dk without their self terms, fp32):
-// one workgroup of 64 threads per (sequence, chunk).
+// x_t = q_t dq_t - k_t dk_t (dq and dk without their self terms, fp32) for the
+// 64 tokens of one chunk: thread (r, i) of 256 takes tokens 16r .. 16r+15 of
+// dim i, so each wave reads whole rows; tokens past the end give 0.
 template <class Io>
-__global__ __launch_bounds__(64) void gla_dgate_totals(const typename Io::T *q, const typename Io::T *k,
-                                                       const float *dq, const float *dk,
-                                                       float *totals, int n_tok, int gh, int gw, int dir,
-                                                       float rcp_gh, int d_k, int n_chunk) {
-  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk, i = threadIdx.x;
-  float sum = 0.f;
-  if (i < d_k) {
-    const size_t base = (size_t)seq * n_tok * d_k + i;
-    const int t1 = min(n_tok, (c + 1) * kChunk);
-    for (int t = c * kChunk; t < t1; ++t) {
-      const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k;
-      sum += elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
+__device__ __forceinline__ void dgate_terms(const typename Io::T *q, const typename Io::T *k, const float *dq,
+                                            const float *dk, size_t base, int c, int r, int i, int n_tok,
+                                            int gh, int gw, int dir, float rcp_gh, int d_k, float *x) {
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int t = c * kChunk + 16 * r + u;
+    x[u] = 0.f;
+    if (t < n_tok && i < d_k) {
+      const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i;
+      x[u] = elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
     }
   }
-  totals[((size_t)seq * n_chunk + c) * kHead + i] = sum;
 }
 
-// dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then a
-// reverse running sum inside the chunk.
+// Chunk totals of x per dim: one workgroup per (sequence, chunk).
 template <class Io>
-__global__ __launch_bounds__(64) void gla_dgate_apply(const typename Io::T *q, const typename Io::T *k,
-                                                      const float *dq, const float *dk,
-                                                      const float *ds_final, const float *s_final,
-                                                      const float *totals, typename Io::T *dg, int n_tok,
-                                                      int gh, int gw, int dir, float rcp_gh, int d_k,
-                                                      int d_v, int n_chunk) {
-  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk, i = threadIdx.x;
-  if (i >= d_k) return;
+__global__ __launch_bounds__(kThreads) void gla_dgate_totals(const typename Io::T *q, const typename Io::T *k,
+                                                             const float *dq, const float *dk, float *totals,
+                                                             int n_tok, int gh, int gw, int dir, float rcp_gh,
+                                                             int d_k, int n_chunk) {
+  __shared__ float part[4][kHead];
+  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk;
+  const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
+  float x[16];
+  dgate_terms<Io>(q, k, dq, dk, (size_t)seq * n_tok * d_k, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) sum += x[u];
+  part[r][i] = sum;
+  __syncthreads();
+  if (r == 0) totals[((size_t)seq * n_chunk + c) * kHead + i] = part[0][i] + part[1][i] + part[2][i] + part[3][i];
+}
+
+// dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then the
+// reverse running sum inside the chunk, quarter by quarter.
+template <class Io>
+__global__ __launch_bounds__(kThreads) void gla_dgate_apply(const typename Io::T *q, const typename Io::T *k,
+                                                            const float *dq, const float *dk,
+                                                            const float *ds_final, const float *s_final,
+                                                            const float *totals, typename Io::T *dg, int n_tok,
+                                                            int gh, int gw, int dir, float rcp_gh, int d_k,
+                                                            int d_v, int n_chunk) {
+  __shared__ float part[4][kHead];
+  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk;
+  const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
+  const size_t base = (size_t)seq * n_tok * d_k;
+  float x[16];
+  dgate_terms<Io>(q, k, dq, dk, base, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) sum += x[u];
+  part[r][i] = sum;
+  // what follows this quarter: the later quarters, the later chunks, the final-state term
   float run = 0.f;
-  if (ds_final && s_final) {
-    const size_t row = ((size_t)seq * d_k + i) * d_v;
-    for (int j = 0; j < d_v; ++j) run += ds_final[row + j] * s_final[row + j];
+  if (i < d_k) {
+    if (r == 0 && ds_final && s_final) {
+      const size_t row = ((size_t)seq * d_k + i) * d_v;
+      for (int j = 0; j < d_v; ++j) run += ds_final[row + j] * s_final[row + j];
+    }
+    for (int c2 = n_chunk - 1 - r; c2 > c; c2 -= 4) run += totals[((size_t)seq * n_chunk + c2) * kHead + i];
   }
-  for (int c2 = n_chunk - 1; c2 > c; --c2) run += totals[((size_t)seq * n_chunk + c2) * kHead + i];
-  const size_t base = (size_t)seq * n_tok * d_k + i;
-  for (int t = min(n_tok, (c + 1) * kChunk) - 1; t >= c * kChunk; --t) {
-    const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k;
-    run += elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
-    dg[at] = Io::narrow(run);
+  __syncthreads();
+  float later = 0.f;
+  for (int r2 = r + 1; r2 < 4; ++r2) later += part[r2][i];
+  __syncthreads();
+  part[r][i] = run;  // this thread's share of the later chunks and the final-state term
+  __syncthreads();
+  run = later + part[0][i] + part[1][i] + part[2][i] + part[3][i];
+  if (i >= d_k) return;
+#pragma unroll
+  for (int u = 15; u >= 0; --u) {
+    const int t = c * kChunk + 16 * r + u;
+    run += x[u];
+    if (t < n_tok) dg[base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i] = Io::narrow(run);
   }
 }
+
 
 }  // namespace
 
@@ -1519,6 +1558,7 @@ int launch_gla(const LaunchArgs &a) {
 
 }  // namespace gtr
 
+
 // ------------------------------------------------------- backward launchers
 namespace gtr {
 namespace {
@@ -1545,8 +1585,7 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
-  auto kernel = gla_bwd_dqk<Io, Op>;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)(a.bh * a.n_chunk)), dim3(kThreads), 0, a.stream, p, a.out, a.off);
+  launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off);
   return (int)hipGetLastError();
 }
 
@@ -1571,12 +1610,11 @@ int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, 
   const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
   const float rcp = 1.0f / (float)grid_h;
   if (dtype == 0)
-    hipLaunchKernelGGL(gla_gate_lag<float>, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const float *>(g),
-                       static_cast<float *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
+    launch(kKernelBwdLag, gla_gate_lag<float>, blocks, stream, static_cast<const float *>(g),
+           static_cast<float *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
   else
-    hipLaunchKernelGGL(gla_gate_lag<uint16_t>, dim3(blocks), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t *>(g), static_cast<uint16_t *>(g_lag), n_tok, grid_h,
-                       grid_w, direction, rcp, d_k, n);
+    launch(kKernelBwdLag, gla_gate_lag<uint16_t>, blocks, stream, static_cast<const uint16_t *>(g),
+           static_cast<uint16_t *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
   return (int)hipGetLastError();
 }
 
@@ -1591,9 +1629,10 @@ int launch_dgate_typed(const void *q, const void *k, const float *dq, const floa
   const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k);
   const float *dqq = dq, *dkk = dk;
   const dim3 grid((unsigned)(bh * n_chunk));
-  hipLaunchKernelGGL(gla_dgate_totals<Io>, grid, dim3(64), 0, stream, qq, kk, dqq, dkk, totals, n_tok, grid_h,
+  ProfileScope scope(kKernelBwdDgate, stream);
+  hipLaunchKernelGGL(gla_dgate_totals<Io>, grid, dim3(kThreads), 0, stream, qq, kk, dqq, dkk, totals, n_tok, grid_h,
                      grid_w, direction, rcp, d_k, n_chunk);
-  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(64), 0, stream, qq, kk, dqq, dkk, ds_final, s_final, totals,
+  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(kThreads), 0, stream, qq, kk, dqq, dkk, ds_final, s_final, totals,
                      static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk);
   return (int)hipGetLastError();
 }
@@ -1602,9 +1641,9 @@ template <class Io>
 int launch_ds0_typed(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k,
                      int d_v, int direction, hipStream_t stream) {
   const long long n = (long long)bh * d_k * d_v;
-  hipLaunchKernelGGL(gla_ds0<Io>, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
-                     static_cast<const typename Io::T *>(g), g0, ds0, grid_h * grid_w, grid_h, grid_w,
-                     direction, 1.0f / (float)grid_h, d_k, d_v, n);
+  launch(kKernelBwdDs0, gla_ds0<Io>, (unsigned)((n + kThreads - 1) / kThreads), stream,
+         static_cast<const typename Io::T *>(g), g0, ds0, grid_h * grid_w, grid_h, grid_w, direction,
+         1.0f / (float)grid_h, d_k, d_v, n);
   return (int)hipGetLastError();
 }
 }  // namespace

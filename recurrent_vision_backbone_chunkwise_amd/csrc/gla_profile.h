@@ -13,7 +13,11 @@ enum KernelId : int {
   kKernelSwigluIn = 4,   // Spatial SwiGLU input projection (library GEMM)
   kKernelSwigluMix = 5,  // depthwise 3x3 + SiLU gate
   kKernelSwigluOut = 6,  // output projection (library GEMM)
-  kNumKernels = 7
+  kKernelBwdDqk = 7,     // backward chunk kernel (dq, dk)
+  kKernelBwdLag = 8,     // gates lagged by one scan position
+  kKernelBwdDgate = 9,   // gate gradient (chunk totals, then running sums)
+  kKernelBwdDs0 = 10,    // gradient of the initial state
+  kNumKernels = 11
 };
 
 // While profiling is on and `stream` is not being captured, creates a pair of
