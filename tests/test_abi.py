@@ -201,3 +201,36 @@ def test_swiglu_empty_calls_and_sizes():
 def test_swiglu_valid_call_without_gpu_reports_no_device():
     assert swiglu_call() == -5
     assert swiglu_call(conv_b=None) == -5
+
+
+# ---- backward entry point --------------------------------------------------------------------
+
+def bwd_call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, do=A + 0x400000, s0=None, dsf=None,
+             dq=A + 0x500000, dk=A + 0x600000, dv=A + 0x700000, dg=A + 0x800000, ds0=None, B=1, H=1,
+             gh=4, gw=4, dkk=64, dvv=64, d=0, dt=1):
+    return gla.lib().gtr_gla_bwd(q, k, v, g, do, s0, dsf, dq, dk, dv, dg, ds0, B, H, gh, gw, dkk, dvv, d, dt,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=4), -1), (dict(dt=3), -1), (dict(B=-1), -1), (dict(q=None), -1), (dict(dg=None), -1),
+    (dict(do=None), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1),
+    (dict(dkk=128), -2), (dict(dvv=30), -2),
+    (dict(dq=A + 0x500008), -3), (dict(ds0=A + 0x900004), -3),
+    (dict(dq=A), -4), (dict(dv=A + 0x400000), -4), (dict(dk=A + 0x500000), -4),
+])
+def test_backward_argument_errors_before_any_hip_call(kw, code):
+    assert bwd_call(**kw) == code
+    assert gla.gtr_gla_last_error() != ""
+
+
+def test_backward_empty_calls():
+    assert bwd_call(B=0) == 0
+    assert bwd_call(gh=0, q=None, k=None, v=None, g=None, do=None, dq=None, dk=None, dv=None, dg=None) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
+                    reason="a GPU is visible")
+def test_backward_valid_call_without_gpu_reports_no_device():
+    assert bwd_call() == -5
+    assert bwd_call(gh=0, ds0=A + 0x900000, dsf=A + 0xa00000) == -5  # no tokens, ds0 = ds_final
