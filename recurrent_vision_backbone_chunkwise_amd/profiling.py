@@ -69,9 +69,15 @@ def counter_per_dispatch(directory: str, counter: str) -> dict[str, float]:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def portable_command(command: str) -> str:
+    """The command with this checkout's absolute root written as $REPO."""
+    return command.replace(os.path.abspath(ROOT) + "/", "$REPO/")
+
+
 def cmd_stats(a) -> None:
     rows = kernel_stats(a.dir)
-    lines = [f"# rocprofv3 kernel trace ({a.title})", f"# command: {a.command}",
+    lines = [f"# rocprofv3 kernel trace ({a.title})",
+             f"# command ($REPO is the repository root): {portable_command(a.command)}",
              f"# kernel sources: {source_digest()}", "",
              f"{'kernel':60s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'% time':>7s}"]
     for r in sorted(rows, key=lambda r: -r["total_us"]):
