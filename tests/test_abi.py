@@ -234,3 +234,17 @@ def test_backward_empty_calls():
 def test_backward_valid_call_without_gpu_reports_no_device():
     assert bwd_call() == -5
     assert bwd_call(gh=0, ds0=A + 0x900000, dsf=A + 0xa00000) == -5  # no tokens, ds0 = ds_final
+
+
+def test_kernel_names_match_the_header():
+    """gtr_gla_kernel_name() gives the ids gtr_gla.h documents for gtr_gla_profile_end()."""
+    names = ["gla_seg_state", "gla_seg_scan", "gla_seg_out", "gla_fused", "swiglu_gemm_in",
+             "swiglu_mix", "swiglu_gemm_out", "gla_bwd_dqk", "gla_bwd_lag", "gla_bwd_dgate",
+             "gla_bwd_ds0"]
+    L = gla.lib()
+    assert [L.gtr_gla_kernel_name(i).decode() for i in range(len(names))] == names
+    assert L.gtr_gla_kernel_name(len(names)) == b"" and L.gtr_gla_kernel_name(-1) == b""
+    header = open(os.path.join(ROOT, "include", "gtr_gla.h")).read()
+    assert f"number of kernel ids ({len(names)})" in header
+    for i, n in enumerate(names):
+        assert f"{i} {n}" in header, n
