@@ -93,35 +93,47 @@ __global__ __launch_bounds__(kMixThreads) void swiglu_mix(const U *__restrict__ 
   const int c = c0 + 4 * j;
   const bool live = c < F;
   // Every load of the tile goes out before any is used: the halo's value
-  // columns (zero outside the grid and past F) and this thread's gates.
+  // columns (zero outside the grid and past F) and this thread's gates.  The
+  // loads are unconditional (a position outside the grid or past F reads
+  // element 0, which exists, and is zeroed afterwards), so no branch separates
+  // them and all are in flight together.
   constexpr int kStaged = kHaloY * kHaloX * kGroups;
   constexpr int kPerThread = (kStaged + kMixThreads - 1) / kMixThreads;  // 12
   constexpr int kTokensPerThread = kTileY * kTileX * kGroups / kMixThreads;  // 8
   f4 staged[kPerThread];
+  bool staged_ok[kPerThread];
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k) {
     const int i = tid + k * kMixThreads;
     const int pos = i / kGroups;
     const int yy = y0 - 1 + pos / kHaloX, xx = x0 - 1 + pos % kHaloX;
     const int cc = c0 + 4 * (i % kGroups);
-    staged[k] = f4{0.f, 0.f, 0.f, 0.f};
-    if (i < kStaged && yy >= 0 && yy < grid_h && xx >= 0 && xx < grid_w && cc < F)
-      staged[k] = load4(u + (image_base + (size_t)yy * grid_w + xx) * ld + F + cc);
+    staged_ok[k] = i < kStaged && yy >= 0 && yy < grid_h && xx >= 0 && xx < grid_w && cc < F;
+    const size_t at = staged_ok[k] ? (image_base + (size_t)yy * grid_w + xx) * ld + F + cc : 0;
+    staged[k] = load4(u + at);
   }
   f4 gate[kTokensPerThread];
+  bool gate_ok[kTokensPerThread];
 #pragma unroll
   for (int k = 0; k < kTokensPerThread; ++k) {
     const int t = tid / kGroups + k * (kMixThreads / kGroups);
     const int y = y0 + t / kTileX, x = x0 + t % kTileX;
-    gate[k] = f4{0.f, 0.f, 0.f, 0.f};
-    if (live && y < grid_h && x < grid_w) gate[k] = load4(u + (image_base + (size_t)y * grid_w + x) * ld + c);
+    gate_ok[k] = live && y < grid_h && x < grid_w;
+    gate[k] = load4(u + (gate_ok[k] ? (image_base + (size_t)y * grid_w + x) * ld + c : 0));
   }
-  f4 w[9], bias = {0.f, 0.f, 0.f, 0.f};
-  if (live) {
+  const int cl = live ? c : 0;
+  f4 w[9];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) w[k] = load4(conv_w + (size_t)k * F + c);
-    if (conv_b) bias = load4(conv_b + c);
-  }
+  for (int k = 0; k < 9; ++k) w[k] = load4(conv_w + (size_t)k * F + cl);
+  f4 bias = load4((conv_b ? conv_b : conv_w) + cl);  // unconditional as well; no bias: zero
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  if (!conv_b) bias = zero;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k)
+    if (!staged_ok[k]) staged[k] = zero;
+#pragma unroll
+  for (int k = 0; k < kTokensPerThread; ++k)
+    if (!gate_ok[k]) gate[k] = zero;
 #pragma unroll
   for (int k = 0; k < kPerThread; ++k)
     if (tid + k * kMixThreads < kStaged) val[tid + k * kMixThreads] = staged[k];
