@@ -12,6 +12,10 @@ replay stream.  Prints one JSON line.
                average duration (HIP events around each launch, eager, on the
                launch stream), against 8 TB/s HBM
   cpu_baseline the fp64 oracle on the host cores, on the same step's inputs
+  cold         the same step on copies of its tensors used in turn, so that
+               more than 512 MB is touched between two uses of one copy (no
+               input is still in the 256 MB Infinity Cache when read again);
+               value is the warm figure above
 """
 from __future__ import annotations
 
@@ -159,6 +163,8 @@ def main():
     ms_per_step = ev_ms / args.steps
     value = tokens_per_step / (ms_per_step * 1e-3)
 
+    cold = cold_round(args, w, inputs, outs, cps, path, stream, tokens_per_step, graph is not None)
+
     # per-kernel durations: HIP events around every launch, eager, same stream
     gla.gtr_gla_profile_begin()
     with torch.cuda.stream(stream):
@@ -221,8 +227,61 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cold": cold,
     }
     print(json.dumps(line), flush=True)
+
+
+COLD_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def cold_round(args, w, inputs, outs, cps, path, stream, tokens_per_step, use_graph):
+    """The same round, timed the same way, on copies of its tensors at other addresses, used in
+    turn, so that more than COLD_BYTES are touched between two uses of one copy and no input is
+    still cached when it is read again.  A round that alone exceeds COLD_BYTES is its own copy."""
+    import torch
+
+    import recurrent_vision_backbone_chunkwise_amd as gla
+
+    round_bytes = sum(t.numel() * t.element_size() for ins in inputs for t in ins)
+    round_bytes += sum(o.numel() * o.element_size() for o in outs)
+    n_sets = max(1, -(-COLD_BYTES // round_bytes))
+    sets = [(inputs, outs)] + [([[t.clone() for t in ins] for ins in inputs],
+                                [torch.empty_like(o) for o in outs]) for _ in range(n_sets - 1)]
+
+    def step(ins_set, out_set):
+        for (q, k, v, g), d, o in zip(ins_set, w.directions, out_set):
+            gla.gtr_gla_fwd_ex(q, k, v, g, o, d, chunks_per_segment=cps, path=path, stream=stream)
+
+    graphs = []
+    with torch.cuda.stream(stream):
+        for ins_set, out_set in sets:
+            step(ins_set, out_set)
+    torch.cuda.synchronize()
+    if use_graph:
+        for ins_set, out_set in sets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                step(ins_set, out_set)
+            graphs.append(gr)
+        for gr in graphs:
+            gr.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for i in range(args.steps):
+            if use_graph:
+                graphs[i % n_sets].replay()
+            else:
+                step(*sets[i % n_sets])
+        stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    del graphs, sets
+    return {"value": round(tokens_per_step / (ms * 1e-3), 1), "ms_per_step": round(ms, 6),
+            "copies": n_sets, "bytes_between_reuse": n_sets * round_bytes}
 
 
 def cpu_baseline(w, cpu_inputs, budget_s):
