@@ -67,6 +67,18 @@
  * grid_h*grid_w*max(d_k, d_v)*element bytes <= 2^31; 0 <= B*H <= 2^20.
  * Pointers must be 16-byte aligned.
  *
+ * Value range.  For fp16 and bf16 I/O the matrix operands are fp16 (products
+ * accumulate in fp32), so whatever becomes an operand must stay within the
+ * fp16 range, |x| <= 65504:
+ *   - the inputs themselves (bf16 values beyond it become infinite);
+ *   - q and k times at most 2^8, on the within-chunk diagonal score tiles
+ *     (|q|, |k| < 256 always suffices there);
+ *   - each within-chunk score, which is at most |q_t|*|k_s| (Euclidean norms
+ *     of a query and an earlier key of the same chunk);
+ *   - each entry of the state entering a chunk.
+ * Beyond these the output is unspecified (typically inf or NaN).  fp32 I/O
+ * uses fp32 operands throughout and has none of these limits.
+ *
  * Empty calls: with B*H == 0 or no tokens there is nothing to compute and
  * tensor pointers may be NULL; the call returns GTR_OK without touching the
  * device, except that with tokens == 0, B*H > 0 and s_final given, s_final

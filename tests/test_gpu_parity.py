@@ -94,6 +94,37 @@ def test_gate_extremes(gate, dtype):
         check(q, k, v, g, d, dtype, f"gate={gate}", path=path, chunks_per_segment=2)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_values_near_the_fp16_operand_limits(dtype):
+    """16-bit I/O runs on fp16 operands (include/gtr_gla.h, value range).  Close to each limit the
+    result still meets the tolerance: |q|, |k| up to ~100 with within-chunk scores up to ~2.5e4 and a
+    steep gate whose 16-token products (~2^-14) push the diagonal midpoint factors to ~2^7; then a
+    unit gate over 40,960 tokens of positive keys and values, whose state grows to ~2.6e4."""
+    cast = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    gen = torch.Generator().manual_seed(31)
+    shape = (1, 2, 16, 20, 64)
+    q = torch.randn(shape, generator=gen) * 25
+    k = torch.randn(shape, generator=gen) * 25
+    v = torch.randn(shape, generator=gen)
+    g = -0.6 + 0.05 * torch.randn(shape, generator=gen)
+    q, k, v, g = (t.to(cast).float().to(cast) for t in (q, k, v, g))
+    chunks = [t.float().reshape(2, 320, 64)[:, :256].reshape(2, 4, 64, 64) for t in (q, k)]
+    scores = torch.einsum("hctd,hcsd->hcts", *chunks).abs().max()
+    assert 5e3 < float(scores) < 6.5e4 and float(q.abs().max()) < 256 and float(k.abs().max()) < 256
+    for d in (0, 2):
+        check(q, k, v, g, d, dtype, "large q, k, steep gate")
+    shape = (1, 1, 160, 256, 64)
+    q = torch.randn(shape, generator=gen) / 64
+    k = torch.randn(shape, generator=gen).abs()
+    v = torch.randn(shape, generator=gen).abs()
+    g = torch.zeros(shape)
+    q, k, v, g = (t.to(cast) for t in (q, k, v, g))
+    _, s_final = oracle.gla_forward(q, k, v, g, 0, want_state=True)
+    assert 2e4 < float(np.abs(s_final).max()) < 6.5e4
+    for path in (0, 1):
+        check(q, k, v, g, 0, dtype, "unit gate, growing state", path=path)
+
+
 def test_unit_gate_long_sequence():
     """alpha = 1 over 16,384 tokens: the state only grows."""
     q, k, v, g = gla_inputs.make_inputs(1, 2, 128, 128, 64, 64, "f16", "ones", seed=6)
