@@ -201,7 +201,10 @@ int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chu
  * are multiples of 4 up to 64 (GTR_ERR_UNSUPPORTED otherwise); every output
  * must be distinct from every input and from the others; the other rules are
  * those of gtr_gla_fwd_ex.  Asynchronous on `stream`; the library keeps a
- * separate per-(device, stream) backward workspace. */
+ * separate per-(device, stream) backward workspace.  For 16-bit I/O the
+ * states and dq, dk come from fp32 operands; dv comes from the forward
+ * kernels run along the reversed scan (keys q, values dout, states dL/dS), so
+ * the value-range rules above apply to q, dout and the state gradients. */
 int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gate, const void *dout,
                 const float *s0, const float *ds_final, void *dq, void *dk, void *dv, void *dlog_gate,
                 float *ds0, int B, int H, int grid_h, int grid_w, int d_k, int d_v, int direction,
