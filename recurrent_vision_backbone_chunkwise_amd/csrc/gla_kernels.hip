@@ -56,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gla_internal.h"
 #include "gla_profile.h"
 
@@ -874,14 +876,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = blockIdx.x / p.n_seg;
   const int seg = blockIdx.x - seq * p.n_seg;
-  f4 S[NK][4] = {};
-  if (p.prev) {
+  // The entering state, read through a buffer resource that is empty when
+  // there is none (every load then returns 0): no branch, so these loads and
+  // the first chunk's are in flight together.
+  f4 S[NK][4];
+  {
+    const float *src = p.prev ? p.prev + ws_block<NK>(p, seq, seg, 0) * kStateElems : nullptr;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(src), (short)0, p.prev ? NK * kStateElems * (int)sizeof(float) : 0, 0x00020000);
 #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      const size_t st = ws_block<NK>(p, seq, seg, kb) * kStateElems + wave * 1024 + lane;
+    for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) S[kb][x >> 2][x & 3] = p.prev[st + x * 64];
-    }
+      for (int x = 0; x < 16; ++x)
+        S[kb][x >> 2][x & 3] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(r, (kb * kStateElems + wave * 1024 + x * 64 + lane) * 4, 0, 0));
   }
   __shared__ __attribute__((aligned(16))) typename OpT<Op>::Bits ot[kChunk * OpT<Op>::LDO];
   f4 unused[NK];
@@ -911,17 +919,23 @@ __global__ __launch_bounds__(kThreads) void gla_seg_scan(Params p) {
   const float *dec = p.agg_dec + first * kHead + i;
   float *prev = const_cast<float *>(p.prev) + first * kStateElems + e;
   const long long user = (p.s0 || p.s_final) ? user_state_index(p, seq, kHead * kb + i, 16 * w + (l & 15)) : -1;
-  float s = (p.s0 && user >= 0) ? p.s0[user] : 0.f;
   const int steps = p.s_final ? n_seg : n_seg - 1;
-  prev[0] = s;
-  for (int b0 = 0; b0 < steps; b0 += kBatch) {
-    float av[kBatch], dv[kBatch];
+  // The first batch's loads go out before s0 is read (clamped, so they are
+  // valid even with no step), so the s0 branch does not delay them.
+  float av[kBatch], dv[kBatch];
+  auto issue = [&](int b0) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int seg = min(b0 + u, steps - 1);
+      const int seg = max(min(b0 + u, steps - 1), 0);
       av[u] = agg[(size_t)seg * kPerSeq];
       dv[u] = dec[(size_t)seg * NK * kHead];
     }
+  };
+  issue(0);
+  float s = (p.s0 && user >= 0) ? p.s0[user] : 0.f;
+  prev[0] = s;
+  for (int b0 = 0; b0 < steps; b0 += kBatch) {
+    if (b0 > 0) issue(b0);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + u < steps) {
@@ -1424,15 +1438,13 @@ __global__ __launch_bounds__(kThreads) void gla_gate_lag(const T *g, T *lag, int
   const int rem = (int)(gid - seq * per_seq);
   const int t = rem / groups, j = 4 * (rem - (rem / groups) * groups);
   const size_t base = (size_t)seq * n_tok * dk;
-  T *dst = lag + base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * dk + j;
-  if (t + 1 < n_tok) {
-    const T *src = g + base + (size_t)scan_cell(t + 1, n_tok, gh, gw, dir, rcp_gh) * dk + j;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = src[e];
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = T(0);
-  }
+  // four elements moved as one vector (8 or 16 bytes; j and dk are multiples of 4)
+  using V = typename std::conditional<sizeof(T) == 4, u4, u2>::type;
+  V *dst = reinterpret_cast<V *>(lag + base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * dk + j);
+  V v = {};
+  if (t + 1 < n_tok)
+    v = *reinterpret_cast<const V *>(g + base + (size_t)scan_cell(t + 1, n_tok, gh, gw, dir, rcp_gh) * dk + j);
+  *dst = v;
 }
 
 template <class Io> __device__ __forceinline__ float elem(const typename Io::T *p) {
@@ -1444,20 +1456,27 @@ template <class Io> __device__ __forceinline__ float elem(const typename Io::T *
 
 // x_t = q_t dq_t - k_t dk_t (dq and dk without their self terms, fp32) for the
 // 64 tokens of one chunk: thread (r, i) of 256 takes tokens 16r .. 16r+15 of
-// dim i, so each wave reads whole rows; tokens past the end give 0.
+// dim i, so each wave reads whole rows; tokens past the end give 0.  The 64
+// loads are unconditional (a masked position reads the sequence's first
+// element), so no branch holds one back until the previous one has returned.
 template <class Io>
 __device__ __forceinline__ void dgate_terms(const typename Io::T *q, const typename Io::T *k, const float *dq,
                                             const float *dk, size_t base, int c, int r, int i, int n_tok,
                                             int gh, int gw, int dir, float rcp_gh, int d_k, float *x) {
+  float qv[16], kv[16], dqv[16], dkv[16];
+  bool ok[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int t = c * kChunk + 16 * r + u;
-    x[u] = 0.f;
-    if (t < n_tok && i < d_k) {
-      const size_t at = base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i;
-      x[u] = elem<Io>(q + at) * dq[at] - elem<Io>(k + at) * dk[at];
-    }
+    ok[u] = t < n_tok && i < d_k;
+    const size_t at = ok[u] ? base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i : base;
+    qv[u] = elem<Io>(q + at);
+    kv[u] = elem<Io>(k + at);
+    dqv[u] = dq[at];
+    dkv[u] = dk[at];
   }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) x[u] = ok[u] ? qv[u] * dqv[u] - kv[u] * dkv[u] : 0.f;
 }
 
 // Chunk totals of x per dim: one workgroup per (sequence, chunk).
@@ -1499,13 +1518,37 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const typename Io::T
   for (int u = 0; u < 16; ++u) sum += x[u];
   part[r][i] = sum;
   // what follows this quarter: the later quarters, the later chunks, the final-state term
+  // (batches of independent loads: a clamped index, then a masked add)
   float run = 0.f;
   if (i < d_k) {
-    if (r == 0 && ds_final && s_final) {
-      const size_t row = ((size_t)seq * d_k + i) * d_v;
-      for (int j = 0; j < d_v; ++j) run += ds_final[row + j] * s_final[row + j];
+    if (r == 0 && ds_final && s_final) {  // rows of d_v floats, d_v a multiple of 4
+      const f4 *a = reinterpret_cast<const f4 *>(ds_final + ((size_t)seq * d_k + i) * d_v);
+      const f4 *b = reinterpret_cast<const f4 *>(s_final + ((size_t)seq * d_k + i) * d_v);
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < d_v / 4; j0 += 4) {
+        f4 av[4], bv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = min(j0 + e, d_v / 4 - 1);
+          av[e] = a[j];
+          bv[e] = b[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < d_v / 4) acc += av[e] * bv[e];
+      }
+      run = acc.x + acc.y + acc.z + acc.w;
     }
-    for (int c2 = n_chunk - 1 - r; c2 > c; c2 -= 4) run += totals[((size_t)seq * n_chunk + c2) * kHead + i];
+    const float *tot = totals + (size_t)seq * n_chunk * kHead + i;
+    constexpr int kBatch = 8;
+    for (int c2 = n_chunk - 1 - r; c2 > c; c2 -= 4 * kBatch) {
+      float tv[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) tv[e] = tot[(size_t)max(c2 - 4 * e, 0) * kHead];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e)
+        if (c2 - 4 * e > c) run += tv[e];
+    }
   }
   __syncthreads();
   float later = 0.f;
