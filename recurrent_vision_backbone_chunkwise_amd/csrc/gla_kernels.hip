@@ -326,23 +326,28 @@ __device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell) {
 // the exponentials named in the comments.
 // Every member is 16-byte aligned so that fragment reads compile to single
 // 8- and 16-byte LDS accesses.
+// NQ = 0: a walk that only carries the state (no outputs) and needs kb, vv,
+// tot and dec alone; the other arrays shrink to one element, so such
+// workgroups take a third of the LDS (more of them fit on a CU).
 template <typename Op, int NQ> struct Smem {
   static constexpr int LD = OpT<Op>::LD;
   static constexpr int LDT = OpT<Op>::LDT;
-  alignas(16) Op qs[kChunk * LD];   // q 2^(E - E_end(a-1))     [token][dim]
-  alignas(16) Op ks[kChunk * LD];   // k 2^(E_end(b) - E)       (qs and ks are adjacent: see gla_fused)
-  alignas(16) Op kb[kChunk * LDT];  // k 2^(E_last - E)
-  alignas(16) Op vv[kChunk * LDT];  // v
-  alignas(16) Op pt[10 * 256];      // score tiles P^T, 4 values per lane, lane-ordered
-  alignas(16) float tot[4 * kHead]; // gate product of each 16-token sub-block
-  alignas(16) Op hv[4 * kHead];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
-  alignas(16) Op cv[3 * kHead];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
-  alignas(16) float dec[kHead];     // 2^E_last: decay of the state across the chunk
+  static constexpr bool kOutTiles = NQ > 0;
+  static constexpr int kSlots = kOutTiles ? NQ : 1;
+  alignas(16) Op qs[kOutTiles ? kChunk * LD : 1];   // q 2^(E - E_end(a-1))     [token][dim]
+  alignas(16) Op ks[kOutTiles ? kChunk * LD : 1];   // k 2^(E_end(b) - E)  (qs and ks are adjacent: see gla_fused)
+  alignas(16) Op kb[kChunk * LDT];                  // k 2^(E_last - E)
+  alignas(16) Op vv[kChunk * LDT];                  // v
+  alignas(16) Op pt[kOutTiles ? 10 * 256 : 1];      // score tiles P^T, 4 values per lane, lane-ordered
+  alignas(16) float tot[4 * kHead];                 // gate product of each 16-token sub-block
+  alignas(16) Op hv[kOutTiles ? 4 * kHead : 1];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
+  alignas(16) Op cv[kOutTiles ? 3 * kHead : 1];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
+  alignas(16) float dec[kHead];                     // 2^E_last: decay of the state across the chunk
   // One slot per chunk whose outputs wait for the state entering the segment
   // (NQ = 1 when outputs are stored as each chunk completes).
-  alignas(16) uint32_t rowoff[NQ][kChunk];  // grid cell of each token (kNoRow past the end)
-  alignas(16) float dcum[NQ][kHead];        // decay from the segment start to the chunk start
-  alignas(16) Op qh[NQ][kChunk * LD];       // q 2^E
+  alignas(16) uint32_t rowoff[kSlots][kOutTiles ? kChunk : 1];  // grid cell of each token (kNoRow past the end)
+  alignas(16) float dcum[kSlots][kOutTiles ? kHead : 1];        // decay from the segment start to the chunk start
+  alignas(16) Op qh[kSlots][kOutTiles ? kChunk * LD : 1];       // q 2^E
 };
 
 // ------------------------------------------------------------------- params
@@ -849,7 +854,7 @@ template <int NK> __device__ __forceinline__ size_t ws_block(const Params &p, in
 
 template <class Io, typename Op, int NK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : 2, NK == 1 ? 3 : 2))) void gla_seg_state(Params p) {
-  __shared__ Smem<Op, 1> sm;
+  __shared__ Smem<Op, 0> sm;  // state only
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = blockIdx.x / p.n_seg_grid;
   const int seg = blockIdx.x - seq * p.n_seg_grid;
