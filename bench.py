@@ -369,14 +369,21 @@ def bwd_main(args):
     dk, dv = w.d_k, w.d_v
     chunks = w.B * w.H * ((w.n_tok + 63) // 64)
     # the chunk kernel: reads kop, gates, a, b and writes its output (algorithmic bytes); its
-    # contractions are the lower-triangle scores, the state term and the intra-chunk sum (fp32 MFMA)
+    # contractions are the lower-triangle scores (fp16 MFMA for 16-bit I/O, whose inputs are exact
+    # in fp16; fp32 otherwise), the state term and the intra-chunk sum (fp32 MFMA).  Its MFMA peak
+    # is the rate that does this mix in the least time.
     bytes_dqk = tokens_per_call * (3 * dk + 2 * dv) * elt
-    flops_dqk = chunks * (2 * 64 * 64 * dv * 10 / 16 + 2 * 64 * dk * dv + 2 * 64 * 32 * dk)
+    flops_scores = chunks * 2 * 64 * 64 * dv * 10 / 16
+    flops_rest = chunks * (2 * 64 * dk * dv + 2 * 64 * 32 * dk)
+    flops_dqk = flops_scores + flops_rest
+    score_peak = MFMA_PEAK_TFLOPS["f32" if w.dtype == "f32" else "f16"]
     us = kern["gla_bwd_dqk"][0]
-    t_hbm, t_mfma = bytes_dqk / (HBM_PEAK_GBS * 1e9), flops_dqk / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
+    t_hbm = bytes_dqk / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_scores / (score_peak * 1e12) + flops_rest / (MFMA_PEAK_TFLOPS["f32"] * 1e12)
     if t_mfma > t_hbm:
-        rl = {"bound": "mfma", "achieved": flops_dqk / (us * 1e-6) / 1e12, "peak": MFMA_PEAK_TFLOPS["f32"],
-              "unit": "TFLOP/s"}
+        rl = {"bound": "mfma", "achieved": flops_dqk / (us * 1e-6) / 1e12,
+              "peak": round(flops_dqk / t_mfma / 1e12, 1), "unit": "TFLOP/s",
+              "peak_mix": f"scores at {score_peak} TFLOP/s, the rest at {MFMA_PEAK_TFLOPS['f32']}"}
     else:
         rl = {"bound": "hbm", "achieved": bytes_dqk / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     rl["frac"] = round(rl["achieved"] / rl["peak"], 4)

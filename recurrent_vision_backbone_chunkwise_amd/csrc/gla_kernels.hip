@@ -327,18 +327,23 @@ __device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell) {
 // Every member is 16-byte aligned so that fragment reads compile to single
 // 8- and 16-byte LDS accesses.
 // NQ = 0: a walk that only carries the state (no outputs) and needs kb, vv,
-// tot and dec alone; the other arrays shrink to one element, so such
-// workgroups take a third of the LDS (more of them fit on a CU).
+// tot and dec alone.  NQ = -1: the backward chunk kernel, which reads the
+// query/key factor tiles (qs, ks, hv, cv, rowoff) but neither the state
+// operand kb nor the score and query tiles (pt, qh, dcum).  Arrays a layout
+// does not use shrink to one element, so its workgroups take less LDS (more
+// of them fit on a CU).
 template <typename Op, int NQ> struct Smem {
   static constexpr int LD = OpT<Op>::LD;
   static constexpr int LDT = OpT<Op>::LDT;
-  static constexpr bool kOutTiles = NQ > 0;
-  static constexpr int kSlots = kOutTiles ? NQ : 1;
+  static constexpr bool kOutTiles = NQ != 0;    // qs, ks, hv, cv, rowoff
+  static constexpr bool kStateTiles = NQ >= 0;  // kb
+  static constexpr bool kQueryTiles = NQ > 0;   // pt, dcum, qh
+  static constexpr int kSlots = NQ > 0 ? NQ : 1;
   alignas(16) Op qs[kOutTiles ? kChunk * LD : 1];   // q 2^(E - E_end(a-1))     [token][dim]
   alignas(16) Op ks[kOutTiles ? kChunk * LD : 1];   // k 2^(E_end(b) - E)  (qs and ks are adjacent: see gla_fused)
-  alignas(16) Op kb[kChunk * LDT];                  // k 2^(E_last - E)
+  alignas(16) Op kb[kStateTiles ? kChunk * LDT : 1];  // k 2^(E_last - E)
   alignas(16) Op vv[kChunk * LDT];                  // v
-  alignas(16) Op pt[kOutTiles ? 10 * 256 : 1];      // score tiles P^T, 4 values per lane, lane-ordered
+  alignas(16) Op pt[kQueryTiles ? 10 * 256 : 1];    // score tiles P^T, 4 values per lane, lane-ordered
   alignas(16) float tot[4 * kHead];                 // gate product of each 16-token sub-block
   alignas(16) Op hv[kOutTiles ? 4 * kHead : 1];     // 2^((E_end(a-1) - E_end(a))/2): diagonal-tile midpoint factor
   alignas(16) Op cv[kOutTiles ? 3 * kHead : 1];     // 2^(E_end(a-1) - E_end(b)) for (a,b) = (2,0), (3,0), (3,1)
@@ -346,8 +351,8 @@ template <typename Op, int NQ> struct Smem {
   // One slot per chunk whose outputs wait for the state entering the segment
   // (NQ = 1 when outputs are stored as each chunk completes).
   alignas(16) uint32_t rowoff[kSlots][kOutTiles ? kChunk : 1];  // grid cell of each token (kNoRow past the end)
-  alignas(16) float dcum[kSlots][kOutTiles ? kHead : 1];        // decay from the segment start to the chunk start
-  alignas(16) Op qh[kSlots][kOutTiles ? kChunk * LD : 1];       // q 2^E
+  alignas(16) float dcum[kSlots][kQueryTiles ? kHead : 1];      // decay from the segment start to the chunk start
+  alignas(16) Op qh[kSlots][kQueryTiles ? kChunk * LD : 1];     // q 2^E
 };
 
 // ------------------------------------------------------------------- params
@@ -545,8 +550,10 @@ __device__ __forceinline__ void prep_chunk(Smem<Op, NQ> &sm, const op4<Op> *qs, 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tau = 16 * wave + 4 * g + r;
-    *reinterpret_cast<op4<Op> *>(&sm.kb[tau * LDT + 4 * dq]) = ks[r] * fkh;
-    if constexpr (kOut) *reinterpret_cast<op4<Op> *>(&sm.qh[slot][tau * LD + 4 * dq]) = qs[r] * fqh;
+    if constexpr (Smem<Op, NQ>::kStateTiles)
+      *reinterpret_cast<op4<Op> *>(&sm.kb[tau * LDT + 4 * dq]) = ks[r] * fkh;
+    if constexpr (kOut && Smem<Op, NQ>::kQueryTiles)
+      *reinterpret_cast<op4<Op> *>(&sm.qh[slot][tau * LD + 4 * dq]) = qs[r] * fqh;
   }
   if (g == 0) {
     if (wave == 0) {
@@ -1270,46 +1277,56 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
 //   ks = kop 2^(E_end(b) - E_sigma)   (keys referenced to their sub-block end)
 //   hv, cv, tot                       (midpoint and block-pair factors)
 //   vv = a                            (the score query rows)
-// The scores P = a b^T are formed on MFMA into LDS (lower block triangle,
-// sigma < tau on the diagonal tiles; the self scores P[tau][tau] are kept in
-// fp32).  Wave w then owns dims [16w, 16w+16) of every token:
+// Wave w owns the 16 tokens of sub-block a = w and all 64 dims.  It forms its
+// transposed score tiles P^T = b a^T against key blocks b <= a on MFMA
+// (sigma < tau on the diagonal tile) and keeps them in registers, where they
+// already are the B operand of the next contraction; then, per 16-dim tile,
 //   out^T = 2^(E_tau - E_start(a)) (S 2^E_start(a) a^T + sum_{b<a} (ks c_ab)^T P^T
 //           + hv (ks hv)^T P_aa^T) + P[tau][tau] kop_tau,
 // every MFMA operand factor <= 1 except the diagonal midpoint factors (<= 2^8);
 // a diagonal sub-block whose gate range is too wide for that is summed exactly
-// in fp32.  `off` receives out without its self term (sigma = tau) in fp32:
-// the gate gradient sums q dq - k dk, where the self terms of dq and dk are
-// equal and cancel, so leaving them out keeps their rounding out of it.
+// in fp32 (its score tile goes through LDS for that).  `off` receives out
+// without its self term (sigma = tau) in fp32: the gate gradient sums
+// q dq - k dk, where the self terms of dq and dk are equal and cancel, so
+// leaving them out keeps their rounding out of it.  With the scores in
+// registers the kernel needs 77 KB of LDS with fp32 operands: two workgroups
+// per CU.  For 16-bit I/O the scores' operands a and b are inputs, exact in
+// fp16, so those tiles run as fp16 MFMAs (exact products, fp32 sums): the
+// same results for an eighth of the instructions.
 template <class Io, typename Op>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off) {
   using T = typename Io::T;
-  constexpr int LD = OpT<Op>::LD, LDT = OpT<Op>::LDT;
-  __shared__ Smem<Op, 1> sm;
+  constexpr int LD = OpT<Op>::LD;
+  __shared__ Smem<Op, -1> sm;
   __shared__ __attribute__((aligned(16))) Op bs[kChunk * LD];  // score keys b [sigma][j], then kop [tau][i]
-  __shared__ __attribute__((aligned(16))) Op ps[kChunk * LD];  // P [tau][sigma], sigma < tau
   __shared__ float self_score[kChunk];                         // P [tau][tau]
+  __shared__ float dtile[4][16 * 16];                          // diagonal P^T [sigma][tau] of each sub-block
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
+  const int a = wave;  // this wave's token sub-block
   const Seq sq = seq_of<Io>(p, seq);  // k: kop, v: a, g: gates, o: b (read only)
   const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<T *>(out) + (size_t)seq * p.n_tok * p.dk, (short)0,
       (int)((uint32_t)p.n_tok * (uint32_t)p.dk * sizeof(T)), 0x00020000);
 
-  // this lane's operand row i = 16w + l16 of the state entering the chunk, at
-  // the k-slots of an MFMA operand (register-order workspace layout)
-  const int i_row = 16 * wave + l16;
-  float srow[16];
+  // rows i = 16t + l16 of the state entering the chunk, for the four 16-dim
+  // tiles t, at the k-slots of an MFMA operand (register-order workspace layout)
+  float srow[4][16];
   {
     const float *st = p.prev + ((size_t)seq * p.n_chunk + c) * kStateElems;
-    const int x = 4 * (i_row >> 4) + (i_row & 3), lo = 16 * ((i_row & 15) >> 2);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 4; ++t) {
+      const int i = 16 * t + l16;
+      const int x = 4 * (i >> 4) + (i & 3), lo = 16 * ((i & 15) >> 2);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * kb + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-        srow[8 * kb + e] = st[(j >> 4) * 1024 + x * 64 + lo + (j & 15)];
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * kb + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+          srow[t][8 * kb + e] = st[(j >> 4) * 1024 + x * 64 + lo + (j & 15)];
+        }
+    }
   }
   Rows<Io> x;
   load_chunk<Io, false, true>(sq, c, 0, wave, lane, x);
@@ -1323,77 +1340,99 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int r = 0; r < 4; ++r) x.q[r] = one;
   op4<Op> qs[4], ks[4];
-  prep_local<Io, Op, true, 1>(sm, x, wave, lane, 0, qs, ks, true);
+  prep_local<Io, Op, true, -1>(sm, x, wave, lane, 0, qs, ks, true);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(brow[r]);
   lds_sync();
-  prep_chunk<Io, Op, true, 1>(sm, qs, ks, wave, lane, 0);
+  prep_chunk<Io, Op, true, -1>(sm, qs, ks, wave, lane, 0);
   lds_sync();
 
-  // P tiles of query block `wave` (zero above the diagonal, so every tile is finite)
+  // P^T tiles of sub-block a: rows sigma = 16b + 4 g4 + r, column tau = 16a + l16
+  // (zero for b > a and, on the diagonal tile, for sigma >= tau), packed in
+  // pairs as B operands over sigma in [32 kb, 32 kb + 32)
+  op8<Op> pf[2];
+  {
+    f4 tile[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (b <= wave) {
+    for (int b = 0; b < 4; ++b) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (b <= a) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        acc = mma(frag_row<Op>(&sm.vv[(16 * wave + l16) * LDT + 32 * kb + 4 * g4]),
-                  frag_row<Op>(&bs[(16 * b + l16) * LD + 32 * kb + 4 * g4]), acc);
+        for (int kb = 0; kb < 2; ++kb) {
+          const op8<Op> fb = frag_row<Op>(&bs[(16 * b + l16) * LD + 32 * kb + 4 * g4]);
+          const op8<Op> fa = frag_row<Op>(&sm.vv[(16 * a + l16) * OpT<Op>::LDT + 32 * kb + 4 * g4]);
+          if constexpr (sizeof(T) == 2 && sizeof(Op) == 4)  // 16-bit inputs are exact in fp16:
+            acc = mma(__builtin_convertvector(fb, h8), __builtin_convertvector(fa, h8), acc);  // same sums
+          else
+            acc = mma(fb, fa, acc);
+        }
+      }
+      if (b == a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sl = 4 * g4 + r;  // sigma within the sub-block; tau within it is l16
+          if (sl == l16) self_score[16 * a + l16] = acc[r];
+          if (sl >= l16) acc[r] = 0.f;
+          dtile[a][sl * 16 + l16] = acc[r];
+        }
+      }
+      tile[b] = acc;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tau = 16 * wave + 4 * g4 + r, sigma = 16 * b + l16;
-      ps[tau * LD + sigma] = (Op)((b < wave || (b == wave && sigma < tau)) ? acc[r] : 0.f);
-      if (b == wave && sigma == tau) self_score[tau] = acc[r];
-    }
+    for (int kb = 0; kb < 2; ++kb) pf[kb] = cat(to4<Op>(tile[2 * kb]), to4<Op>(tile[2 * kb + 1]));
   }
   lds_sync();
-  // every wave has read the score keys: the tile now takes kop itself
+  // every wave has read the score keys: the tile now takes kop itself (this
+  // barrier also publishes the self scores and diagonal tiles)
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(x.k[r]);
   lds_sync();
 
-  float es = 1.f;  // 2^E_start(a) for dim i_row
+  const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
+  const int tau = 16 * a + l16;
+  const uint32_t cell = sm.rowoff[0][tau];
+  const bool live = c * kChunk + tau < p.n_tok;
+  const float self = self_score[tau];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int t = 0; t < 4; ++t) {
+    const int i_row = 16 * t + l16;  // this lane's operand row
+    float es = 1.f;                  // 2^E_start(a) for dim i_row
+    for (int a2 = 0; a2 < a; ++a2) es *= sm.tot[a2 * kHead + i_row];
     f4 acc = {0.f, 0.f, 0.f, 0.f}, accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {  // state entering the chunk
       op8<Op> sf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sf[e] = (Op)(srow[8 * kb + e] * es);
-      acc = mma(sf, frag_row<Op>(&sm.vv[(16 * a + l16) * LDT + 32 * kb + 4 * g4]), acc);
+      for (int e = 0; e < 8; ++e) sf[e] = (Op)(srow[t][8 * kb + e] * es);
+      acc = mma(sf, frag_row<Op>(&sm.vv[tau * OpT<Op>::LDT + 32 * kb + 4 * g4]), acc);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {  // earlier sub-blocks
       if (2 * kb >= a) break;
       const float f0 = block_factor(sm, a, 2 * kb, i_row);
       const float f1 = 2 * kb + 1 < a ? block_factor(sm, a, 2 * kb + 1, i_row) : 0.f;
-      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * wave, lane);
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) xk[e] = (Op)((float)xk[e] * (e < 4 ? f0 : f1));
-      acc = mma(xk, frag_row<Op>(&ps[(16 * a + l16) * LD + 32 * kb + 4 * g4]), acc);
+      acc = mma(xk, pf[kb], acc);
     }
-    const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
     if (!exact) {  // own sub-block, referenced at its midpoint
       const int kb = a >> 1;
       const float h = (float)sm.hv[a * kHead + i_row];
-      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * wave, lane);
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) xk[e] = (Op)(((e < 4) == ((a & 1) == 0)) ? (float)xk[e] * h : 0.f);
-      accd = mma(xk, frag_row<Op>(&ps[(16 * a + l16) * LD + 32 * kb + 4 * g4]), accd);
+      accd = mma(xk, pf[kb], accd);
     }
-    const int tau = 16 * a + l16;
-    const int d0 = 16 * wave + 4 * g4;
+    const int d0 = 16 * t + 4 * g4;  // dims of this lane's results
     f4 o;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float f1 = (float)sm.qs[tau * LD + d0 + r];
       o[r] = f1 * (acc[r] + (float)sm.hv[a * kHead + d0 + r] * accd[r]);
     }
-    const bool live = c * kChunk + tau < p.n_tok;
     if (exact && live) {  // exact fp32 sum over the earlier tokens of the own sub-block
       constexpr uint32_t elt = sizeof(T);
 #pragma unroll
@@ -1401,24 +1440,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int i = d0 + r;
         if (i >= p.dk) continue;
         float ex = 0.f;
-        float run = key_elem<Io>(sq.g, sm.rowoff[0][tau] * sq.kpitch + i * elt) * kLog2e;
+        float run = key_elem<Io>(sq.g, cell * sq.kpitch + i * elt) * kLog2e;
         for (int s2 = tau - 1; s2 >= 16 * a; --s2) {
-          const uint32_t cell = sm.rowoff[0][s2];
+          const uint32_t cs = sm.rowoff[0][s2];
           // 2^(E_tau - E_s2): the log2 gates of tokens s2+1 .. tau
-          ex += (float)ps[tau * LD + s2] * key_elem<Io>(sq.k, cell * sq.kpitch + i * elt) * fast_exp2(run);
-          run += key_elem<Io>(sq.g, cell * sq.kpitch + i * elt) * kLog2e;
+          ex += dtile[a][(s2 - 16 * a) * 16 + l16] * key_elem<Io>(sq.k, cs * sq.kpitch + i * elt) * fast_exp2(run);
+          run += key_elem<Io>(sq.g, cs * sq.kpitch + i * elt) * kLog2e;
         }
         o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
       }
     }
     f4 full;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) full[r] = o[r] + self_score[tau] * (float)bs[tau * LD + d0 + r];
-    const uint32_t cell = sm.rowoff[0][tau];
+    for (int r = 0; r < 4; ++r) full[r] = o[r] + self * (float)bs[tau * LD + d0 + r];
     buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
     if (cell != kNoRow && d0 < p.dk)
       *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = o;
-    es *= sm.tot[a * kHead + i_row];
   }
 }
 
