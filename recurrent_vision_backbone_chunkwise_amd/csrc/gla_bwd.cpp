@@ -197,11 +197,13 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
   b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = d_k; b.d_v = d_v; b.stream = stream;
   if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
-  b.kop = q; b.aop = v; b.bop = dout; b.g = lag; b.out = dk; b.off = dk_off; b.prev = r.prev;  // 5. dk
+  // 5. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
+  b.kop = q; b.aop = v; b.bop = dout; b.g = lag; b.out = dk; b.off = dk_off; b.prev = r.prev;
+  b.pair = dq_off; b.kx = k;
   b.direction = direction ^ 1;
   if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
   // 6. dlog_gate
-  if ((rc = launched(gtr::launch_dgate(q, k, dq_off, dk_off, ds_final, sfin, reinterpret_cast<float *>(ws + lay.totals),
+  if ((rc = launched(gtr::launch_dgate(dk_off, ds_final, sfin, reinterpret_cast<float *>(ws + lay.totals),
                                        dlog_gate, (int)bh, grid_h, grid_w, d_k, d_v, n_chunk, direction,
                                        dtype, stream))) != GTR_OK)
     return rc;

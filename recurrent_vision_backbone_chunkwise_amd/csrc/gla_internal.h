@@ -54,7 +54,10 @@ struct LaunchArgs {
 struct BwdArgs {
   const void *kop, *aop, *bop, *g;  // [bh][grid][d_k], [bh][grid][d_v] twice, [bh][grid][d_k]
   void *out;                        // [bh][grid][d_k]
-  float *off;                       // [bh][grid][d_k] fp32: out without its self term (sigma = tau)
+  float *off;                       // [bh][grid][d_k] fp32: out without its self term (sigma = tau), or
+                                    // with `pair` set, the gate-gradient term kop * pair - kx * that
+  const float *pair;                // nullable [bh][grid][d_k] fp32: the other pass's `off` (dq)
+  const void *kx;                   // with `pair`: [bh][grid][d_k] keys k
   const float *prev;                // [bh][n_chunk][4096] register order
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
   hipStream_t stream;
@@ -90,12 +93,13 @@ int launch_gla_bwd_dqk(const BwdArgs &a);
 // g_lag at the grid cell of scan position t = log_gate of position t+1 (0 at the last position).
 int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, int d_k, int direction,
                     int dtype, hipStream_t stream);
-// dlog_gate_t = sum_{u >= t} (q_u dq_u - k_u dk_u) + rowsum(ds_final * s_final) along `direction`,
-// with dq, dk the fp32 results of the backward chunk kernel without their (cancelling) self
-// terms; totals: [bh][n_chunk][64] fp32 scratch.  ds_final / s_final may be null.
-int launch_dgate(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
-                 const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w, int d_k,
-                 int d_v, int n_chunk, int direction, int dtype, hipStream_t stream);
+// dlog_gate_t = sum_{u >= t} x_u + rowsum(ds_final * s_final) along `direction`, with
+// x = q dq - k dk per position and dim (fp32, dq and dk without their cancelling self terms, as
+// the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32 scratch.
+// ds_final / s_final may be null.
+int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
+                 int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
+                 hipStream_t stream);
 // ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][d_k][d_v].
 int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
                int direction, int dtype, hipStream_t stream);

@@ -573,7 +573,14 @@ __device__ __forceinline__ void prep_chunk(Smem<Op, NQ> &sm, const op4<Op> *qs, 
   }
 }
 
-// One element of a q/k/log_gate row, as float.
+// One element of a q/k/log_gate row, as float: by address (elem) or through a
+// buffer resource (key_elem).
+template <class Io> __device__ __forceinline__ float elem(const typename Io::T *p) {
+  if constexpr (sizeof(typename Io::T) == 4)
+    return Io::from_bits(__float_as_uint(*reinterpret_cast<const float *>(p)));
+  else
+    return Io::from_bits(*reinterpret_cast<const uint16_t *>(p));
+}
 template <class Io> __device__ __forceinline__ float key_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (sizeof(typename Io::T) == 4)
     return Io::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
@@ -1288,13 +1295,18 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
 // in fp32 (its score tile goes through LDS for that).  `off` receives out
 // without its self term (sigma = tau) in fp32: the gate gradient sums
 // q dq - k dk, where the self terms of dq and dk are equal and cancel, so
-// leaving them out keeps their rounding out of it.  With the scores in
+// leaving them out keeps their rounding out of it.  kX (the dk pass, kop = q):
+// `off` receives instead the gate-gradient term q dq - k dk of each position
+// and dim, with dq from `pair` (the dq pass's `off`) and k from `kx`, so the
+// gate kernels read one array instead of four.  With the scores in
 // registers the kernel needs 77 KB of LDS with fp32 operands: two workgroups
 // per CU.  For 16-bit I/O the scores' operands a and b are inputs, exact in
 // fp16, so those tiles run as fp16 MFMAs (exact products, fp32 sums): the
 // same results for an eighth of the instructions.
-template <class Io, typename Op>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off) {
+template <class Io, typename Op, bool kX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off,
+                                                                                           const float *pair,
+                                                                                           const void *kx) {
   using T = typename Io::T;
   constexpr int LD = OpT<Op>::LD;
   __shared__ Smem<Op, -1> sm;
@@ -1348,6 +1360,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   prep_chunk<Io, Op, true, -1>(sm, qs, ks, wave, lane, 0);
   lds_sync();
 
+  const int tau = 16 * a + l16;
+  const uint32_t cell = sm.rowoff[0][tau];
+  // kX: dq and k at this lane's position and result dims, for all four tiles;
+  // issued now (clamped to valid rows and dims, results past them are not
+  // stored) so that they arrive while the MFMAs run
+  f4 xdq[4], xkk[4];
+  if constexpr (kX) {
+    const size_t row = ((size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell)) * p.dk;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d = min(16 * t + 4 * g4, p.dk - 4);
+      xdq[t] = *reinterpret_cast<const f4 *>(pair + row + d);
+      const T *kp = static_cast<const T *>(kx) + row + d;
+      xkk[t] = f4{elem<Io>(kp), elem<Io>(kp + 1), elem<Io>(kp + 2), elem<Io>(kp + 3)};
+    }
+  }
+
   // P^T tiles of sub-block a: rows sigma = 16b + 4 g4 + r, column tau = 16a + l16
   // (zero for b > a and, on the diagonal tile, for sigma >= tau), packed in
   // pairs as B operands over sigma in [32 kb, 32 kb + 32)
@@ -1391,8 +1420,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   lds_sync();
 
   const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
-  const int tau = 16 * a + l16;
-  const uint32_t cell = sm.rowoff[0][tau];
   const bool live = c * kChunk + tau < p.n_tok;
   const float self = self_score[tau];
 #pragma unroll
@@ -1450,12 +1477,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
       }
     }
-    f4 full;
+    f4 full, w = o;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) full[r] = o[r] + self * (float)bs[tau * LD + d0 + r];
+    for (int r = 0; r < 4; ++r) {
+      const float kop = (float)bs[tau * LD + d0 + r];
+      full[r] = o[r] + self * kop;
+      if constexpr (kX) w[r] = kop * xdq[t][r] - xkk[t][r] * o[r];
+    }
     buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
     if (cell != kNoRow && d0 < p.dk)
-      *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = o;
+      *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = w;
   }
 }
 
@@ -1489,49 +1520,34 @@ __global__ __launch_bounds__(kThreads) void gla_gate_lag(const T *g, T *lag, int
   *dst = v;
 }
 
-template <class Io> __device__ __forceinline__ float elem(const typename Io::T *p) {
-  if constexpr (sizeof(typename Io::T) == 4)
-    return Io::from_bits(__float_as_uint(*reinterpret_cast<const float *>(p)));
-  else
-    return Io::from_bits(*reinterpret_cast<const uint16_t *>(p));
-}
 
-// x_t = q_t dq_t - k_t dk_t (dq and dk without their self terms, fp32) for the
-// 64 tokens of one chunk: thread (r, i) of 256 takes tokens 16r .. 16r+15 of
-// dim i, so each wave reads whole rows; tokens past the end give 0.  The 64
-// loads are unconditional (a masked position reads the sequence's first
-// element), so no branch holds one back until the previous one has returned.
-template <class Io>
-__device__ __forceinline__ void dgate_terms(const typename Io::T *q, const typename Io::T *k, const float *dq,
-                                            const float *dk, size_t base, int c, int r, int i, int n_tok,
-                                            int gh, int gw, int dir, float rcp_gh, int d_k, float *x) {
-  float qv[16], kv[16], dqv[16], dkv[16];
+// x_t (the gate-gradient term q_t dq_t - k_t dk_t, fp32) for the 64 tokens of
+// one chunk: thread (r, i) of 256 takes tokens 16r .. 16r+15 of dim i, so each
+// wave reads whole rows; tokens past the end give 0.  The 16 loads are
+// unconditional (a masked position reads the sequence's first element), so no
+// branch holds one back until the previous one has returned.
+__device__ __forceinline__ void dgate_terms(const float *xs, size_t base, int c, int r, int i, int n_tok, int gh,
+                                            int gw, int dir, float rcp_gh, int d_k, float *x) {
+  float v[16];
   bool ok[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int t = c * kChunk + 16 * r + u;
     ok[u] = t < n_tok && i < d_k;
-    const size_t at = ok[u] ? base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i : base;
-    qv[u] = elem<Io>(q + at);
-    kv[u] = elem<Io>(k + at);
-    dqv[u] = dq[at];
-    dkv[u] = dk[at];
+    v[u] = xs[ok[u] ? base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i : base];
   }
 #pragma unroll
-  for (int u = 0; u < 16; ++u) x[u] = ok[u] ? qv[u] * dqv[u] - kv[u] * dkv[u] : 0.f;
+  for (int u = 0; u < 16; ++u) x[u] = ok[u] ? v[u] : 0.f;
 }
 
 // Chunk totals of x per dim: one workgroup per (sequence, chunk).
-template <class Io>
-__global__ __launch_bounds__(kThreads) void gla_dgate_totals(const typename Io::T *q, const typename Io::T *k,
-                                                             const float *dq, const float *dk, float *totals,
-                                                             int n_tok, int gh, int gw, int dir, float rcp_gh,
-                                                             int d_k, int n_chunk) {
+__global__ __launch_bounds__(kThreads) void gla_dgate_totals(const float *xs, float *totals, int n_tok, int gh,
+                                                             int gw, int dir, float rcp_gh, int d_k, int n_chunk) {
   __shared__ float part[4][kHead];
   const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk;
   const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
   float x[16];
-  dgate_terms<Io>(q, k, dq, dk, (size_t)seq * n_tok * d_k, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
+  dgate_terms(xs, (size_t)seq * n_tok * d_k, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
   float sum = 0.f;
 #pragma unroll
   for (int u = 0; u < 16; ++u) sum += x[u];
@@ -1543,9 +1559,8 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_totals(const typename Io::
 // dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then the
 // reverse running sum inside the chunk, quarter by quarter.
 template <class Io>
-__global__ __launch_bounds__(kThreads) void gla_dgate_apply(const typename Io::T *q, const typename Io::T *k,
-                                                            const float *dq, const float *dk,
-                                                            const float *ds_final, const float *s_final,
+__global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, const float *ds_final,
+                                                            const float *s_final,
                                                             const float *totals, typename Io::T *dg, int n_tok,
                                                             int gh, int gw, int dir, float rcp_gh, int d_k,
                                                             int d_v, int n_chunk) {
@@ -1554,7 +1569,7 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const typename Io::T
   const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
   const size_t base = (size_t)seq * n_tok * d_k;
   float x[16];
-  dgate_terms<Io>(q, k, dq, dk, base, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
+  dgate_terms(xs, base, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
   float sum = 0.f;
 #pragma unroll
   for (int u = 0; u < 16; ++u) sum += x[u];
@@ -1670,7 +1685,12 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
-  launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off);
+  if (a.pair)
+    launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, true>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
+           a.pair, a.kx);
+  else
+    launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, false>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
+           a.pair, a.kx);
   return (int)hipGetLastError();
 }
 
@@ -1705,19 +1725,17 @@ int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, 
 
 namespace {
 template <class Io>
-int launch_dgate_typed(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
-                       const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w,
-                       int d_k, int d_v, int n_chunk, int direction, hipStream_t stream) {
+int launch_dgate_typed(const float *xs, const float *ds_final, const float *s_final, float *totals, void *dg,
+                       int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction,
+                       hipStream_t stream) {
   using T = typename Io::T;
   const int n_tok = grid_h * grid_w;
   const float rcp = 1.0f / (float)grid_h;
-  const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k);
-  const float *dqq = dq, *dkk = dk;
   const dim3 grid((unsigned)(bh * n_chunk));
   ProfileScope scope(kKernelBwdDgate, stream);
-  hipLaunchKernelGGL(gla_dgate_totals<Io>, grid, dim3(kThreads), 0, stream, qq, kk, dqq, dkk, totals, n_tok, grid_h,
-                     grid_w, direction, rcp, d_k, n_chunk);
-  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(kThreads), 0, stream, qq, kk, dqq, dkk, ds_final, s_final, totals,
+  hipLaunchKernelGGL(gla_dgate_totals, grid, dim3(kThreads), 0, stream, xs, totals, n_tok, grid_h, grid_w,
+                     direction, rcp, d_k, n_chunk);
+  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(kThreads), 0, stream, xs, ds_final, s_final, totals,
                      static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk);
   return (int)hipGetLastError();
 }
@@ -1733,13 +1751,13 @@ int launch_ds0_typed(const void *g, const float *g0, float *ds0, int bh, int gri
 }
 }  // namespace
 
-int launch_dgate(const void *q, const void *k, const float *dq, const float *dk, const float *ds_final,
-                 const float *s_final, float *totals, void *dg, int bh, int grid_h, int grid_w, int d_k,
-                 int d_v, int n_chunk, int direction, int dtype, hipStream_t stream) {
+int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
+                 int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
+                 hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_dgate_typed<IoF32>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
-    case 1: return launch_dgate_typed<IoF16>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
-    case 2: return launch_dgate_typed<IoBF16>(q, k, dq, dk, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 0: return launch_dgate_typed<IoF32>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 1: return launch_dgate_typed<IoF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 2: return launch_dgate_typed<IoBF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }
