@@ -93,6 +93,16 @@ def test_workload_shapes(widx):
     note(f"errors {check(q, k, v, g, w.directions[0], w.dtype, w.name, seed=37)}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_long_sequence(dtype):
+    """144 chunks: both state scans run 143 or 144 steps; with s0 and dL/dS_final."""
+    q, k, v, g = gla_inputs.make_inputs(1, 1, 96, 96, 64, 64, dtype, "light", seed=39)
+    s0 = torch.randn(1, 1, 64, 64, generator=torch.Generator().manual_seed(40)) * 0.5
+    dsf = torch.randn(1, 1, 64, 64, generator=torch.Generator().manual_seed(41))
+    for d in (0, 2):
+        note(f"errors {check(q, k, v, g, d, dtype, '96x96', s0=s0, dsf=dsf, seed=42 + d)}")
+
+
 def test_unsupported_width_and_empty_calls():
     q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 1, 4, 4, 128, 64, "f16", "light", seed=38))
     with pytest.raises(gla.GlaError) as ex:

@@ -257,6 +257,21 @@ def test_maximum_grid():
     assert float(err) < 1e-4, float(err)
 
 
+@pytest.mark.parametrize("grid", [(80, 81), (150, 128), (200, 200)], ids=lambda g: f"{g[0]}x{g[1]}")
+def test_long_boundary_scans(grid):
+    """One-chunk segments on long sequences (102, 300 and 625 chunks): boundary scans of
+    hundreds of steps, with s0 and s_final, in fp32."""
+    gh, gw = grid
+    q, k, v, g = gla_inputs.make_inputs(1, 2, gh, gw, 64, 64, "f32", "light", seed=gh + gw)
+    s0 = torch.randn(1, 2, 64, 64, generator=torch.Generator().manual_seed(gh)) * 0.5
+    for d in (0, 3):
+        note(f"long scan {gh}x{gw} dir={d}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1, path=2)
+        ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, "f32")["ok"]
+        assert parity_errors(sf.double().cpu().numpy(), sref, "f32")["ok"]
+
+
 def test_split_sequence_equals_whole():
     """Top rows then bottom rows with the state carried equals one L->R call."""
     B, H, gh, gw, r = 1, 2, 40, 40, 17
