@@ -1084,10 +1084,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg =
       dacc[r] = 1.f;
     }
     constexpr int kBatch = 4;
+    // every earlier segment's flag at once (at most 256 of them, one per
+    // thread), then the aggregates in batches
+    static_assert(kMaxFusedSegments <= kThreads, "one thread per earlier segment's flag");
+    if (tid < seg) wait_flag(p.sync, p.flags + sbase + tid, want);
+    __syncthreads();  // the flags seen by one wave hold for the whole workgroup
     for (int i = seg - 1; i >= 0;) {
       const int nb = min(kBatch, i + 1);
-      if (tid < nb) wait_flag(p.sync, p.flags + sbase + i - tid, want);
-      __syncthreads();  // the flags seen by one wave hold for the whole workgroup
       float av[kBatch][16], dv[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
