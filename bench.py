@@ -16,6 +16,8 @@ replay stream.  Prints one JSON line.
                more than 512 MB is touched between two uses of one copy (no
                input is still in the 256 MB Infinity Cache when read again);
                value is the warm figure above
+  long_sequence  the default run (1,600 tokens) also times the 16,384-token
+               round the same way: the metric is quoted at both lengths
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
                     help="run the workload with these head dims instead of 64 x 64")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-sequence", action="store_true",
+                    help="skip the 16,384-token round the default run also reports")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--profile-steps", type=int, default=50)
@@ -109,15 +113,70 @@ def main():
         hip_build.build()
     if not torch.cuda.is_available():
         raise RuntimeError("no GPU visible")
-    dev = torch.device("cuda:0")
     w = gla_inputs.workload(args.workload)
     if args.head_dims and tuple(args.head_dims) != (w.d_k, w.d_v):
         dk, dv = args.head_dims
         w = dataclasses.replace(w, d_k=dk, d_v=dv, name=f"{w.name}_dk{dk}_dv{dv}")
-    cps = args.chunks_per_segment
     path = {"auto": 0, "fused": 1, "split": 2}[args.path]
-    plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, cps, path, w.d_k, w.d_v)
+    m = measure_gla(args, w, path, args.chunks_per_segment, args.steps, with_cold=True)
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, m["cpu_inputs"], args.cpu_seconds)
+
+    # The metric is quoted at 1.6K and at 16K tokens: the default run also times the
+    # 16,384-token round (workload 5) the same way and reports it beside the main figure.
+    long_seq = None
+    if args.workload == 2 and not args.head_dims and path == 0 and not args.no_long_sequence:
+        w5 = gla_inputs.workload(5)
+        m5 = measure_gla(args, w5, 0, 0, min(args.steps, 100), with_cold=False)
+        long_seq = {"workload": w5.name, "value": round(m5["value"], 1), "unit": "tokens/s",
+                    "ms_per_step": round(m5["ms_per_step"], 6), "steps": min(args.steps, 100),
+                    "tokens_per_step": m5["tokens_per_step"],
+                    "roofline": {k: m5["roofline"][k] for k in ("bound", "kernel", "achieved", "peak",
+                                                                  "unit", "frac", "traffic")}}
+
+    plan = m["plan"]
+    line = {
+        "metric": "GLA fwd tokens/sec (B*H*N), one MI355X",
+        "value": round(m["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "n_tok": w.n_tok,
+            "d_k": w.d_k, "d_v": w.d_v, "io_dtype": w.dtype, "gate": w.gate,
+            "directions": [gla_inputs.DIR_NAMES[d] for d in w.directions],
+            "tokens_per_step": m["tokens_per_step"], "chunks_per_segment": plan["seg_len"],
+            "segments_per_sequence": plan["n_seg"], "kernels": "fused" if plan["fused"] else "split",
+            "timing": "eager" if args.eager else "hip graph replay", "wall_ms": round(m["wall_ms"], 3),
+            "accumulate": "f32",
+        },
+        "roofline": m["roofline"],
+        "cpu_baseline": cpu,
+        "cold": m["cold"],
+        "long_sequence": long_seq,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def measure_gla(args, w, path, cps, steps, with_cold):
+    """Times `steps` replays of the workload's round (one HIP graph, HIP events on its stream),
+    then the per-kernel durations of eager launches, and derives the dominant kernel's roofline."""
+    import torch
+
+    import gla_inputs
+    import recurrent_vision_backbone_chunkwise_amd as gla
+
+    dev = torch.device("cuda:0")
+    plan = gla.gtr_gla_plan(w.B, w.H, w.grid_h, w.grid_w, cps, path, w.d_k, w.d_v)
     cpu_inputs = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
     inputs = [[x.to(dev) for x in ins] for ins in cpu_inputs]
     outs = [torch.empty_like(ins[2]) for ins in inputs]
@@ -151,7 +210,7 @@ def main():
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         start.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             if graph is not None:
                 graph.replay()
             else:
@@ -159,11 +218,12 @@ def main():
         stop.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    ev_ms = start.elapsed_time(stop)
-    ms_per_step = ev_ms / args.steps
+    ms_per_step = start.elapsed_time(stop) / steps
     value = tokens_per_step / (ms_per_step * 1e-3)
 
-    cold = cold_round(args, w, inputs, outs, cps, path, stream, tokens_per_step, graph is not None)
+    cold = None
+    if with_cold:
+        cold = cold_round(args, w, inputs, outs, cps, path, stream, tokens_per_step, graph is not None)
 
     # per-kernel durations: HIP events around every launch, eager, same stream
     gla.gtr_gla_profile_begin()
@@ -198,38 +258,12 @@ def main():
                     for n, v in kern.items()},
         "source": digest,
     }
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, cpu_inputs, args.cpu_seconds)
-
-    line = {
-        "metric": "GLA fwd tokens/sec (B*H*N), one MI355X",
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "f16",
-        "data": "synthetic",
-        "config": {
-            "workload": w.name, "B": w.B, "H": w.H, "grid": [w.grid_h, w.grid_w], "n_tok": w.n_tok,
-            "d_k": w.d_k, "d_v": w.d_v, "io_dtype": w.dtype, "gate": w.gate,
-            "directions": [gla_inputs.DIR_NAMES[d] for d in w.directions],
-            "tokens_per_step": tokens_per_step, "chunks_per_segment": seg_len,
-            "segments_per_sequence": n_seg, "kernels": "fused" if plan["fused"] else "split",
-            "timing": "eager" if args.eager else "hip graph replay", "wall_ms": round(wall_ms, 3),
-            "accumulate": "f32",
-        },
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "cold": cold,
-    }
-    print(json.dumps(line), flush=True)
+    result = {"value": value, "ms_per_step": ms_per_step, "wall_ms": wall_ms, "cold": cold,
+              "roofline": roofline, "plan": plan, "tokens_per_step": tokens_per_step,
+              "cpu_inputs": cpu_inputs}
+    del graph, inputs, outs
+    torch.cuda.synchronize()
+    return result
 
 
 COLD_BYTES = 512 << 20  # twice the 256 MB Infinity Cache

@@ -49,3 +49,16 @@ def test_json_line_fields():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == d["unit"]
     assert isinstance(cb["sample"], str) and cb["sample"]
+    assert d["long_sequence"] is None  # only the default workload also reports the 16K round
+
+
+@pytest.mark.gpu
+def test_default_run_also_reports_the_long_sequence():
+    r = run("--steps", "5", "--warmup", "1", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][0])
+    assert d["config"]["workload"] == "grid40x40_f16_b1h6_4dir" and d["cpu_baseline"] is None
+    ls = d["long_sequence"]
+    assert ls["workload"] == "grid128x128_f16_b1h16_4dir" and ls["value"] > 0
+    assert ls["roofline"]["kernel"] in ("gla_seg_out", "gla_seg_state", "gla_fused")
+    assert 0 < ls["roofline"]["frac"] < 1
