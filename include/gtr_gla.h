@@ -53,7 +53,11 @@
  *     while `stream` is being captured into a graph (GTR_ERR_CAPTURE): make
  *     one call of the largest shape before capturing.  Calls on one stream
  *     are ordered by that stream; calls on different streams use different
- *     workspaces.
+ *     workspaces.  A graph captured from a stream uses that stream's
+ *     workspace, so replay it only where a call on that stream could run:
+ *     not beside another call on that stream or another replay of a graph
+ *     captured from it.  A workspace that grows keeps its old buffers until
+ *     gtr_gla_release_workspaces(), so graphs captured earlier stay valid.
  *   - Every argument is validated on the host before the first HIP call;
  *     a call that returns an error has launched nothing.  Outside stream
  *     capture each pointer is also checked to be device memory of the
@@ -217,7 +221,10 @@ const char *gtr_gla_last_error(void);
 /* Library version, major*10000 + minor*100 + patch. */
 int gtr_gla_version(void);
 
-/* Frees every cached workspace (synchronises each device that has one). */
+/* Frees every cached workspace of this library, forward, backward and Spatial
+ * SwiGLU, including the buffers that grown workspaces replaced.  It first
+ * synchronises each device that has one.  Graphs captured before this call
+ * must not be replayed after it. */
 void gtr_gla_release_workspaces(void);
 
 /*

@@ -29,7 +29,8 @@
  * Ownership and errors as in gtr_gla.h: device pointers owned by the caller,
  * 16-byte aligned; out must not overlap an input; the library owns a
  * per-(device, stream) workspace (u and h) that is grown outside stream
- * capture only (GTR_ERR_CAPTURE otherwise: run the shape once eagerly first);
+ * capture only (GTR_ERR_CAPTURE otherwise: run the shape once eagerly first)
+ * and freed by gtr_gla_release_workspaces();
  * errors are negative GTR_ERR_* codes with a message from gtr_gla_last_error().
  * Sizes: C and F multiples of 8 from 8 to 65536, 0 <= B*grid_h*grid_w <= 2^24.
  * A call with no tokens returns GTR_OK and touches nothing.

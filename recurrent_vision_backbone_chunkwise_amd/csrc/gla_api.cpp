@@ -14,7 +14,9 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
+#include <vector>
 
 #include "gla_internal.h"
 
@@ -230,8 +232,18 @@ struct Workspace {
   size_t cap_seqs = 0, cap_flags = 0;
 };
 
+// Guards the workspaces, the other cached buffers and the retired list.
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::map<std::tuple<int, int, hipStream_t>, std::pair<void *, size_t>> g_bufs;  // (owner, device, stream)
+// Buffers replaced by larger ones, with their devices.  A graph captured
+// earlier may still refer to them, so they are freed only by
+// gtr_gla_release_workspaces.
+std::vector<std::pair<int, void *>> g_retired;
+
+void retire(int device, void *p) {
+  if (p) g_retired.push_back({device, p});
+}
 
 int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, size_t flags,
                   void **data, int **sync, int **flag_words) {
@@ -257,10 +269,10 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
                 "workspace must grow (%zu -> %zu bytes, %zu -> %zu sequences, %zu -> %zu flags) "
                 "while the stream is being captured; make one call of this shape before capturing",
                 ws.data_bytes, bytes, ws.cap_seqs, seqs, ws.cap_flags, flags);
-  // Kernels queued earlier on this stream may still use the old buffers.
-  if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
+  // Kernels queued earlier, and graphs captured earlier, may still use the
+  // old buffers: they are retired, not freed.
   if (ws.data_bytes < bytes) {
-    if (ws.data) (void)hipFree(ws.data);
+    retire(device, ws.data);
     ws.data = nullptr;
     ws.data_bytes = 0;
     const size_t want = bytes + bytes / 4;  // headroom for slightly larger calls
@@ -272,7 +284,7 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
     ws.data_bytes = want;
   }
   if (!sync_ok) {
-    if (ws.sync) (void)hipFree(ws.sync);
+    retire(device, ws.sync);
     ws.sync = nullptr;
     const size_t cs = std::max(ws.cap_seqs, seqs + seqs / 4), cf = std::max(ws.cap_flags, flags + flags / 4);
     ws.cap_seqs = ws.cap_flags = 0;
@@ -335,11 +347,30 @@ bool stream_capturing(hipStream_t stream) {
   return cs != hipStreamCaptureStatusNone;
 }
 
+int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const char *what, void **out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto &buf = g_bufs[std::make_tuple(owner, device, stream)];
+  if (buf.second < bytes) {
+    if (stream_capturing(stream))
+      return set_error(GTR_ERR_CAPTURE,
+                       "%s workspace must grow (%zu -> %zu bytes) while the stream is being captured; "
+                       "make one call of this shape before capturing",
+                       what, buf.second, bytes);
+    retire(device, buf.first);
+    buf = {nullptr, 0};
+    void *p = nullptr;
+    const size_t want = bytes + bytes / 4;  // headroom for slightly larger calls
+    if (hipMalloc(&p, want) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(GTR_ERR_ALLOC, "hipMalloc of %zu %s workspace bytes failed", want, what);
+    }
+    buf = {p, want};
+  }
+  *out = buf.first;
+  return GTR_OK;
+}
+
 }  // namespace gtr
-
-extern "C" {
-
-}  // extern "C"
 
 namespace {
 
@@ -558,16 +589,32 @@ int gtr_gla_stream_status(hipStream_t stream) {
 
 void gtr_gla_release_workspaces(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
+  std::vector<std::pair<int, void *>> all = g_retired;
   for (auto &kv : g_ws) {
-    int cur = 0;
-    if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
-      (void)hipDeviceSynchronize();
-      if (kv.second.data) (void)hipFree(kv.second.data);
-      if (kv.second.sync) (void)hipFree(kv.second.sync);
-      (void)hipSetDevice(cur);
-    }
+    if (kv.second.data) all.push_back({kv.first.first, kv.second.data});
+    if (kv.second.sync) all.push_back({kv.first.first, kv.second.sync});
   }
+  for (auto &kv : g_bufs)
+    if (kv.second.first) all.push_back({std::get<1>(kv.first), kv.second.first});
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) (void)hipGetLastError();
+  int synced = -1;
+  std::sort(all.begin(), all.end());
+  for (auto &dp : all) {
+    if (dp.first != synced) {  // once per device, before its first free
+      if (hipSetDevice(dp.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        continue;
+      }
+      synced = dp.first;
+    }
+    (void)hipFree(dp.second);
+  }
+  (void)hipSetDevice(cur);
+  (void)hipGetLastError();
   g_ws.clear();
+  g_bufs.clear();
+  g_retired.clear();
 }
 
 }  // extern "C"

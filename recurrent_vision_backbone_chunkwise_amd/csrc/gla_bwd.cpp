@@ -16,9 +16,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "gla_internal.h"
 #include "gtr_gla.h"
@@ -51,31 +48,6 @@ Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int 
   l.dk_off = l.dq_off + round256((size_t)bh * n_tok * d_k * sizeof(float));
   l.total = l.dk_off + round256((size_t)bh * n_tok * d_k * sizeof(float));
   return l;
-}
-
-std::mutex g_mu;
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
-
-int workspace(int device, hipStream_t stream, size_t bytes, char **out) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  auto &ws = g_ws[{device, stream}];
-  if (ws.second < bytes) {
-    if (gtr::stream_capturing(stream))
-      return set_error(GTR_ERR_CAPTURE,
-                       "backward workspace must grow (%zu -> %zu bytes) while the stream is being "
-                       "captured; make one call of this shape before capturing", ws.second, bytes);
-    if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
-    if (ws.first) (void)hipFree(ws.first);
-    ws = {nullptr, 0};
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      return set_error(GTR_ERR_ALLOC, "hipMalloc of %zu backward workspace bytes failed", bytes);
-    }
-    ws = {p, bytes};
-  }
-  *out = static_cast<char *>(ws.first);
-  return GTR_OK;
 }
 
 int launched(int err) {
@@ -155,9 +127,10 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
 
   const int n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
   const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v, elt);
-  char *ws = nullptr;
-  int rc = workspace(device, stream, lay.total, &ws);
+  void *wsp = nullptr;
+  int rc = gtr::stream_buffer(gtr::kBufBackward, device, stream, lay.total, "backward", &wsp);
   if (rc != GTR_OK) return rc;
+  char *ws = static_cast<char *>(wsp);
   auto scan_area = [&](size_t off, gtr::LaunchArgs &a) {
     float *f = reinterpret_cast<float *>(ws + off);
     const size_t st = (size_t)bh * n_chunk * gtr::kStateElems;

@@ -88,6 +88,14 @@ int check_device_pointer(const void *p, size_t bytes, int device, const char *na
 bool pointer_checks_off();
 bool stream_capturing(hipStream_t stream);
 
+// A device buffer of at least `bytes`, cached per (owner, device, stream)
+// (defined in gla_api.cpp).  A buffer that a larger call replaces is kept,
+// not freed, until gtr_gla_release_workspaces(): a graph captured on that
+// stream may still refer to it.  Growing is refused while `stream` is being
+// captured (GTR_ERR_CAPTURE); a failed allocation gives GTR_ERR_ALLOC.
+enum BufferOwner { kBufBackward = 1, kBufSwiglu = 2 };
+int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const char *what, void **out);
+
 // Backward-pass launchers (hipError_t values).
 int launch_gla_bwd_dqk(const BwdArgs &a);
 // g_lag at the grid cell of scan position t = log_gate of position t+1 (0 at the last position).

@@ -19,7 +19,6 @@
 
 #include <map>
 #include <mutex>
-#include <utility>
 
 #include "gla_internal.h"
 #include "gla_profile.h"
@@ -226,33 +225,8 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-std::mutex g_mu;  // guards the workspaces and the rocBLAS handles (one per device)
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+std::mutex g_mu;  // guards the rocBLAS handles (one per device)
 std::map<int, rocblas_handle> g_blas;
-
-int workspace(int device, hipStream_t stream, size_t bytes, void **out) {
-  auto &ws = g_ws[{device, stream}];
-  if (ws.second >= bytes) {
-    *out = ws.first;
-    return GTR_OK;
-  }
-  if (stream_capturing(stream))
-    return set_error(GTR_ERR_CAPTURE,
-                     "workspace must grow (%zu -> %zu bytes) while the stream is being captured; "
-                     "make one call of this shape before capturing",
-                     ws.second, bytes);
-  if (hipStreamSynchronize(stream) != hipSuccess) (void)hipGetLastError();
-  if (ws.first) (void)hipFree(ws.first);
-  ws = {nullptr, 0};
-  void *p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return set_error(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", bytes);
-  }
-  ws = {p, bytes};
-  *out = p;
-  return GTR_OK;
-}
 
 int blas_handle(int device, rocblas_handle *h) {
   auto it = g_blas.find(device);
@@ -332,7 +306,7 @@ int gtr_swiglu_fwd(const void *x, const void *w_in, const void *conv_w, const vo
 
   std::lock_guard<std::mutex> lock(g_mu);
   void *ws = nullptr;
-  rc = workspace(device, stream, sz.u_bytes + sz.h_bytes, &ws);
+  rc = stream_buffer(kBufSwiglu, device, stream, sz.u_bytes + sz.h_bytes, "Spatial SwiGLU", &ws);
   if (rc != GTR_OK) return rc;
   rocblas_handle blas = nullptr;
   rc = blas_handle(device, &blas);

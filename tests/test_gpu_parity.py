@@ -391,6 +391,45 @@ def test_non_default_stream_and_graph_replay():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_graph_replays_after_workspace_growth(path):
+    """A graph keeps the workspace it was captured with: a larger eager call on the same
+    stream grows the workspace into new buffers, and the graph's still hold its data."""
+    p = PATHS[path]
+    small = [x.to(DEV) for x in gla_inputs.make_inputs(1, 6, 24, 24, 64, 64, "f16", "light", seed=21)]
+    big = [x.to(DEV) for x in gla_inputs.make_inputs(4, 8, 40, 40, 64, 64, "f16", "light", seed=22)]
+    out = torch.empty_like(small[2])
+    cap = torch.cuda.Stream()
+    note(f"graph after growth path={path}")
+    with torch.cuda.stream(cap):
+        gla.gtr_gla_fwd_ex(*small, out, 1, chunks_per_segment=1, path=p, stream=cap)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        gla.gtr_gla_fwd_ex(*small, out, 1, chunks_per_segment=1, path=p, stream=cap)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} before growth"
+        # more segments and sequences than the capture: the workspace grows
+        big_out = torch.empty_like(big[2])
+        with torch.cuda.stream(cap):
+            gla.gtr_gla_fwd_ex(*big, big_out, 1, chunks_per_segment=1, path=p, stream=cap)
+        torch.cuda.synchronize()
+        big = [torch.cat([x, x[:1]]) for x in big]  # one more batch row next time round
+    out.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager), "replay after growth"
+    del graph
+    gla.gtr_gla_release_workspaces()
+    y = gla.gla_forward(*small, 1, chunks_per_segment=1, path=p, stream=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(y, eager), "call after release"
+
+
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # the one launch is refused
 def test_capture_refuses_workspace_growth():
     q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 2, 30, 31, 64, 64, "f16", "light",
