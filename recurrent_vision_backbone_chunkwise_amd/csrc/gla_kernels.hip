@@ -888,9 +888,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NK == 
   }
 }
 
-// (Its output tile brings LDS to 63.6 KB at 16-bit I/O: two workgroups per CU.)
+// (Its output tile brings LDS to 63.6 KB at 16-bit I/O, two workgroups per CU;
+// with fp32 operands to 118 KB, one.)
+template <typename Op> constexpr int kOutOccupancy = sizeof(Op) == 4 ? 1 : 2;
 template <class Io, typename Op, int NK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_seg_out(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    kOutOccupancy<Op>, kOutOccupancy<Op>))) void gla_seg_out(Params p) {
   __shared__ Smem<Op, 1> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = blockIdx.x / p.n_seg;
@@ -1001,6 +1004,10 @@ __device__ __forceinline__ int wait_flag(int *sync, const int *f, int want) {
   }
 }
 
+// Workgroups per CU the LDS allows: fp32 operands take 100-137 KB, one;
+// 16-bit ones 54 KB for one-chunk segments, three, and up to 73 KB, two.
+template <typename Op, int kSeg> constexpr int kFusedOccupancy = sizeof(Op) == 4 ? 1 : (kSeg == 1 ? 3 : 2);
+
 // One launch, one walk.  A workgroup takes a segment (at most kSeg chunks) in
 // start order and:
 //   1. walks it from a zero state, keeping each chunk's outputs in registers
@@ -1013,7 +1020,8 @@ __device__ __forceinline__ int wait_flag(int *sync, const int *f, int want) {
 //      decay from the segment start to the chunk, and stores the outputs.
 // Inputs are read from HBM once.
 template <class Io, typename Op, int kSeg>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSeg == 1 ? 3 : 2, kSeg == 1 ? 3 : 2))) void gla_fused(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    kFusedOccupancy<Op, kSeg>, kFusedOccupancy<Op, kSeg>))) void gla_fused(Params p) {
   __shared__ Smem<Op, kSeg> sm;
   __shared__ int s_ticket, s_epoch;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1206,17 +1214,26 @@ int launch_typed(const LaunchArgs &a) {
   p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
   p.flags = a.flags; p.sync = a.sync;
   const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
+  // fp32 operands on 16-bit I/O serve only the backward's state passes: no
+  // output or one-launch kernels are built for them
+  constexpr bool kStatesOnly = sizeof(typename Io::T) == 2 && sizeof(Op) == 4;
+  if constexpr (kStatesOnly) {
+    if (a.fused || a.outputs_only || !a.states_only) return (int)hipErrorInvalidValue;
+  }
   if (a.fused) {
-    if constexpr (NK != 1) return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
-    if (a.seg_len <= 1)
-      launch(kKernelFused, gla_fused<Io, Op, 1>, n_blocks, a.stream, p);
-    else if (a.seg_len == 2)
-      launch(kKernelFused, gla_fused<Io, Op, 2>, n_blocks, a.stream, p);
-    else if (a.seg_len == 3)
-      launch(kKernelFused, gla_fused<Io, Op, 3>, n_blocks, a.stream, p);
-    else
-      return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
-    return (int)hipGetLastError();
+    if constexpr (NK != 1 || kStatesOnly) {
+      return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
+    } else {
+      if (a.seg_len <= 1)
+        launch(kKernelFused, gla_fused<Io, Op, 1>, n_blocks, a.stream, p);
+      else if (a.seg_len == 2)
+        launch(kKernelFused, gla_fused<Io, Op, 2>, n_blocks, a.stream, p);
+      else if (a.seg_len == 3)
+        launch(kKernelFused, gla_fused<Io, Op, 3>, n_blocks, a.stream, p);
+      else
+        return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
+      return (int)hipGetLastError();
+    }
   }
   const bool need_scan =
       a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr || a.states_only || a.want_prev;
@@ -1234,7 +1251,7 @@ int launch_typed(const LaunchArgs &a) {
     launch(kKernelSegScan, gla_seg_scan<NK>, (unsigned)((threads + kThreads - 1) / kThreads), a.stream, p);
   }
   if (a.states_only) return (int)hipGetLastError();
-  launch(kKernelSegOut, gla_seg_out<Io, Op, NK>, n_blocks, a.stream, p);
+  if constexpr (!kStatesOnly) launch(kKernelSegOut, gla_seg_out<Io, Op, NK>, n_blocks, a.stream, p);
   return (int)hipGetLastError();
 }
 
