@@ -65,6 +65,10 @@
  *     stream is being captured that query is skipped, so capture a call only
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
+ *   - Two environment variables serve tests and measurement only:
+ *     GTR_GLA_SKIP_POINTER_CHECKS=1 skips the device-pointer queries, and
+ *     GTR_GLA_TEST_FAIL_ALLOC=1 makes every workspace allocation fail
+ *     (GTR_ERR_ALLOC), which leaves the caches as they were.
  *
  * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
  * case; the one-launch path takes d_k <= 64); 0 <= grid_h*grid_w <= 2^23 and

@@ -245,6 +245,17 @@ void retire(int device, void *p) {
   if (p) g_retired.push_back({device, p});
 }
 
+// hipMalloc for the workspaces.  GTR_GLA_TEST_FAIL_ALLOC=1 makes it fail, so
+// that tests can reach the allocation-failure paths.
+hipError_t workspace_malloc(void **p, size_t bytes) {
+  const char *s = std::getenv("GTR_GLA_TEST_FAIL_ALLOC");
+  if (s && s[0] == '1') {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  return hipMalloc(p, bytes);
+}
+
 int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, size_t flags,
                   void **data, int **sync, int **flag_words) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -271,38 +282,37 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
                 ws.data_bytes, bytes, ws.cap_seqs, seqs, ws.cap_flags, flags);
   // Kernels queued earlier, and graphs captured earlier, may still use the
   // old buffers: they are retired, not freed.
+  // A failed allocation leaves the cached buffers as they were.
   if (ws.data_bytes < bytes) {
-    retire(device, ws.data);
-    ws.data = nullptr;
-    ws.data_bytes = 0;
     const size_t want = bytes + bytes / 4;  // headroom for slightly larger calls
-    if (hipMalloc(&ws.data, want) != hipSuccess) {
+    void *p = nullptr;
+    if (workspace_malloc(&p, want) != hipSuccess) {
       (void)hipGetLastError();
-      ws.data = nullptr;
       return fail(GTR_ERR_ALLOC, "hipMalloc of %zu workspace bytes failed", want);
     }
+    retire(device, ws.data);
+    ws.data = p;
     ws.data_bytes = want;
   }
   if (!sync_ok) {
-    retire(device, ws.sync);
-    ws.sync = nullptr;
-    const size_t cs = std::max(ws.cap_seqs, seqs + seqs / 4), cf = std::max(ws.cap_flags, flags + flags / 4);
-    ws.cap_seqs = ws.cap_flags = 0;
-    const size_t words = gtr::kSyncHeader + cs * gtr::kCtlStride + cf;
-    if (hipMalloc(&ws.sync, words * sizeof(int)) != hipSuccess) {
+    const size_t seq_cap = std::max(ws.cap_seqs, seqs + seqs / 4);
+    const size_t flag_cap = std::max(ws.cap_flags, flags + flags / 4);
+    const size_t words = gtr::kSyncHeader + seq_cap * gtr::kCtlStride + flag_cap;
+    void *p = nullptr;
+    if (workspace_malloc(&p, words * sizeof(int)) != hipSuccess) {
       (void)hipGetLastError();
-      ws.sync = nullptr;
       return fail(GTR_ERR_ALLOC, "hipMalloc of %zu sync words failed", words);
     }
     // synchronous clear, so that kernels on any stream see zeros
-    if (hipMemset(ws.sync, 0, words * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipMemset(p, 0, words * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
       (void)hipGetLastError();
-      (void)hipFree(ws.sync);
-      ws.sync = nullptr;
+      (void)hipFree(p);
       return fail(GTR_ERR_ALLOC, "clearing %zu sync words failed", words);
     }
-    ws.cap_seqs = cs;
-    ws.cap_flags = cf;
+    retire(device, ws.sync);
+    ws.sync = static_cast<int *>(p);
+    ws.cap_seqs = seq_cap;
+    ws.cap_flags = flag_cap;
   }
   hand_out();
   return GTR_OK;
@@ -356,14 +366,13 @@ int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const
                        "%s workspace must grow (%zu -> %zu bytes) while the stream is being captured; "
                        "make one call of this shape before capturing",
                        what, buf.second, bytes);
-    retire(device, buf.first);
-    buf = {nullptr, 0};
     void *p = nullptr;
     const size_t want = bytes + bytes / 4;  // headroom for slightly larger calls
-    if (hipMalloc(&p, want) != hipSuccess) {
+    if (workspace_malloc(&p, want) != hipSuccess) {
       (void)hipGetLastError();
       return set_error(GTR_ERR_ALLOC, "hipMalloc of %zu %s workspace bytes failed", want, what);
     }
+    retire(device, buf.first);
     buf = {p, want};
   }
   *out = buf.first;

@@ -123,3 +123,26 @@ def test_repeat_calls_are_bitwise_equal():
         again = gla.gla_backward(q, k, v, g, dout, 2)
         for a, b in zip(first, again):
             assert torch.equal(a, b)
+
+
+def test_workspace_allocation_failure(monkeypatch):
+    """A failed backward-workspace allocation returns GTR_ERR_ALLOC and runs nothing; the next
+    call allocates and matches the oracle."""
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 9, 17, 64, 64, "f16", "light", seed=43)
+    dout = gla_inputs.make_output_grad(v.shape, "f16", seed=44)
+    dev = [t.to(DEV) for t in (q, k, v, g, dout)]
+    s = torch.cuda.Stream()  # no workspace yet
+    outs = [torch.full_like(t, float("nan")) for t in (dev[0], dev[1], dev[2], dev[3])]
+    note("bwd allocation failure")
+    monkeypatch.setenv("GTR_GLA_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(gla.GlaError) as ex:
+        gla.gtr_gla_bwd(*dev, *outs, 1, stream=s)
+    torch.cuda.synchronize()
+    assert ex.value.code == -7 and all(torch.isnan(o).all() for o in outs)
+    monkeypatch.delenv("GTR_GLA_TEST_FAIL_ALLOC")
+    gla.gtr_gla_bwd(*dev, *outs, 1, stream=s)
+    torch.cuda.synchronize()
+    ref = oracle.gla_backward(q, k, v, g, dout, 1)
+    for name, y, o in zip(NAMES, outs, ref):
+        e = parity_errors(y.double().cpu().numpy(), o, "f16")
+        assert e["ok"] or (e["rounding_floor"] > e["tol"] and e["err_excess"] <= e["tol"]), (name, e)

@@ -430,6 +430,46 @@ def test_graph_replays_after_workspace_growth(path):
     assert torch.equal(y, eager), "call after release"
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_workspace_allocation_failure(path, monkeypatch):
+    """GTR_GLA_TEST_FAIL_ALLOC=1 makes every workspace allocation fail: the call returns
+    GTR_ERR_ALLOC and runs nothing, and the stream's cached workspace stays usable."""
+    p = PATHS[path]
+    small = gla_inputs.make_inputs(1, 2, 20, 21, 64, 64, "f16", "light", seed=41)
+    big = [x.to(DEV) for x in gla_inputs.make_inputs(2, 4, 30, 31, 64, 64, "f16", "light", seed=42)]
+    ref = oracle.gla_forward(*small, 2)
+    small = [x.to(DEV) for x in small]
+    s = torch.cuda.Stream()  # no workspace yet
+    note(f"allocation failure path={path}")
+
+    def run(ins, out):
+        gla.gtr_gla_fwd_ex(*ins, out, 2, chunks_per_segment=1, path=p, stream=s)
+        torch.cuda.synchronize()
+
+    out = torch.full_like(small[2], float("nan"))
+    monkeypatch.setenv("GTR_GLA_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(gla.GlaError) as ex:
+        run(small, out)
+    assert ex.value.code == -7 and "hipMalloc" in str(ex.value)
+    assert torch.isnan(out).all(), "a refused call ran"
+    monkeypatch.delenv("GTR_GLA_TEST_FAIL_ALLOC")
+    run(small, out)
+    assert parity_errors(out.double().cpu().numpy(), ref, "f16")["ok"]
+    first = out.clone()
+    # growing fails, and the workspace the stream has keeps serving calls that fit it
+    monkeypatch.setenv("GTR_GLA_TEST_FAIL_ALLOC", "1")
+    big_out = torch.full_like(big[2], float("nan"))
+    with pytest.raises(gla.GlaError) as ex:
+        run(big, big_out)
+    assert ex.value.code == -7 and torch.isnan(big_out).all()
+    out.fill_(float("nan"))
+    run(small, out)
+    assert torch.equal(out, first)
+    monkeypatch.delenv("GTR_GLA_TEST_FAIL_ALLOC")
+    run(big, big_out)
+    assert not torch.isnan(big_out).any()
+
+
 @pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # the one launch is refused
 def test_capture_refuses_workspace_growth():
     q, k, v, g = (x.to(DEV) for x in gla_inputs.make_inputs(1, 2, 30, 31, 64, 64, "f16", "light",

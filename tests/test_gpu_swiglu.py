@@ -110,3 +110,23 @@ def test_host_pointer_is_refused():
     rc = gla.lib().gtr_swiglu_fwd(hp, ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
                                   ins[4].data_ptr(), out.data_ptr(), 1, 4, 4, 16, 32, 1, None)
     assert rc == -6 and "x=" in gla.gtr_gla_last_error()
+
+
+def test_workspace_allocation_failure(monkeypatch):
+    """A failed workspace allocation returns GTR_ERR_ALLOC and runs nothing; the next call
+    allocates and matches the oracle."""
+    ins = gla_inputs.make_swiglu_inputs(1, 6, 7, 32, 48, "f16", seed=15)
+    dev = [t.to(DEV) for t in ins]
+    out = torch.full_like(dev[0], float("nan"))
+    s = torch.cuda.Stream()  # no workspace yet
+    note("swiglu allocation failure")
+    monkeypatch.setenv("GTR_GLA_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(gla.GlaError) as ex:
+        gla.gtr_swiglu_fwd(*dev, out, stream=s)
+    torch.cuda.synchronize()
+    assert ex.value.code == -7 and torch.isnan(out).all()
+    monkeypatch.delenv("GTR_GLA_TEST_FAIL_ALLOC")
+    gla.gtr_swiglu_fwd(*dev, out, stream=s)
+    torch.cuda.synchronize()
+    e = parity_errors(out.double().cpu().numpy(), swiglu.spatial_swiglu(*ins), "f16", SWIGLU_TOLERANCE)
+    assert e["ok"], e
