@@ -5,6 +5,7 @@ Run ``python -m recurrent_vision_backbone_chunkwise_amd.build`` or call
 """
 from __future__ import annotations
 
+import concurrent.futures
 import hashlib
 import os
 import shutil
@@ -46,24 +47,28 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _compile(hipcc: str, src: str, extra_flags: list[str], verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc, *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
+           "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{msg}")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+        if msg.strip():
+            print(msg, flush=True)
+    return obj
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
-               "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "'-packed-fp32-ops' is not a recognized feature"
-        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"compiling {src} failed:\n{msg}")
-        if msg.strip() and verbose:
-            print(msg)
-        objs.append(obj)
+    # the sources compile independently, so in parallel (each is one hipcc process)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda src: _compile(hipcc, src, extra_flags or [], verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lrocblas", "-o", tmp]
     if verbose:
