@@ -248,12 +248,12 @@ int gtr_gla_stream_status(hipStream_t stream);
  * capture is bracketed by two HIP events recorded on the call's stream.
  * gtr_gla_profile_end() waits for those events and fills, for kernel ids
  * 0..max_kernels-1, the summed elapsed milliseconds and the launch counts
- * (either array may be NULL).  Returns the number of kernel ids (11), or
+ * (either array may be NULL).  Returns the number of kernel ids (10), or
  * GTR_ERR_LAUNCH if an event could not be read.  Kernel ids: 0 gla_seg_state
  * (segment state contributions), 1 gla_seg_scan (boundary-state scan),
  * 2 gla_seg_out (outputs), 3 gla_fused (the one-kernel path),
  * 4 swiglu_gemm_in, 5 swiglu_mix, 6 swiglu_gemm_out (Spatial SwiGLU),
- * 7 gla_bwd_dqk, 8 gla_bwd_lag, 9 gla_bwd_dgate, 10 gla_bwd_ds0 (backward);
+ * 7 gla_bwd_dqk, 8 gla_bwd_dgate, 9 gla_bwd_ds0 (backward);
  * gtr_gla_kernel_name() returns those names.  The events are taken by the
  * dispatch itself, so they measure kernel execution, not launch overhead.
  */

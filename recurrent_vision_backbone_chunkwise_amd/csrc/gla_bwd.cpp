@@ -4,14 +4,15 @@
 // Gradients of S_t = diag(alpha_t) S_{t-1} + k_t^T v_t, o_t = q_t S_t (the
 // recurrence of the x-techcon article on GTR, section 架构 / Architecture):
 //   1. the states entering every 64-token chunk (forward state and scan kernels);
-//   2. the gates lagged by one scan position;
-//   3. dv, and the state gradients G entering every chunk of the reversed scan:
+//   2. dv, and the state gradients G entering every chunk of the reversed scan:
 //      a forward pass along the reversed direction with queries k, keys q,
-//      values dout, the lagged gates and dS_final as its initial state;
-//   4. dq and 5. dk with the backward chunk kernel;
-//   6. dlog_gate = reverse running sum of q dq - k dk (+ rowsum(dS_final S_final)), from
+//      values dout and dS_final as its initial state, in which each position
+//      takes the gate of the position before it along that scan (the kernels
+//      read it in place);
+//   3. dq and 4. dk with the backward chunk kernel;
+//   5. dlog_gate = reverse running sum of q dq - k dk (+ rowsum(dS_final S_final)), from
 //      dq and dk without their self terms, which cancel in it;
-//   7. ds0 = diag(alpha_0) G_0.
+//   6. ds0 = diag(alpha_0) G_0.
 
 #include <hip/hip_runtime.h>
 
@@ -32,16 +33,15 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {  // byte offsets into the workspace
-  size_t fwd, rev, lag, sfin, g0, totals, dq_off, dk_off, total;
+  size_t fwd, rev, sfin, g0, totals, dq_off, dk_off, total;
 };
 
-Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int elt) {
+Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v) {
   Layout l{};
   const size_t scan = round256(gtr::workspace_bytes((size_t)bh, (size_t)n_chunk, 1));
   l.fwd = 0;
   l.rev = l.fwd + scan;
-  l.lag = l.rev + scan;
-  l.sfin = l.lag + round256((size_t)bh * n_tok * d_k * elt);
+  l.sfin = l.rev + scan;
   l.g0 = l.sfin + round256((size_t)bh * d_k * d_v * sizeof(float));
   l.totals = l.g0 + round256((size_t)bh * d_k * d_v * sizeof(float));
   l.dq_off = l.totals + round256((size_t)bh * n_chunk * gtr::kHead * sizeof(float));
@@ -126,7 +126,7 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     return launched(gtr::launch_state_copy(ds_final, ds0, bh * d_k * d_v, stream));
 
   const int n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v, elt);
+  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v);
   void *wsp = nullptr;
   int rc = gtr::stream_buffer(gtr::kBufBackward, device, stream, lay.total, "backward", &wsp);
   if (rc != GTR_OK) return rc;
@@ -140,7 +140,6 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   };
   float *sfin = ds_final ? reinterpret_cast<float *>(ws + lay.sfin) : nullptr;
   float *g0 = ds0 ? reinterpret_cast<float *>(ws + lay.g0) : nullptr;
-  void *lag = ws + lay.lag;
 
   gtr::LaunchArgs f{};  // 1. states entering each chunk
   f.q = q; f.k = k; f.v = v; f.g = log_gate; f.out = nullptr;
@@ -151,12 +150,8 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   f.fp32_operands = true;  // the boundary states feed sums whose terms cancel (dlog_gate)
   scan_area(lay.fwd, f);
   if ((rc = launched(gtr::launch_gla(f))) != GTR_OK) return rc;
-  // 2. lagged gates
-  if ((rc = launched(gtr::launch_gate_lag(log_gate, lag, (int)bh, grid_h, grid_w, d_k, direction, dtype,
-                                          stream))) != GTR_OK)
-    return rc;
-  gtr::LaunchArgs r = f;  // 3. the state gradients along the reversed scan, then dv from them
-  r.q = k; r.k = q; r.v = dout; r.g = lag; r.out = dv;
+  gtr::LaunchArgs r = f;  // 2. the state gradients along the reversed scan, then dv from them
+  r.q = k; r.k = q; r.v = dout; r.out = dv; r.lag_gates = true;
   r.direction = direction ^ 1;
   r.s0 = ds_final; r.s_final = g0;
   scan_area(lay.rev, r);
@@ -164,23 +159,23 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands
   o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
   if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
-  gtr::BwdArgs b{};  // 4. dq
+  gtr::BwdArgs b{};  // 3. dq
   float *dq_off = reinterpret_cast<float *>(ws + lay.dq_off), *dk_off = reinterpret_cast<float *>(ws + lay.dk_off);
   b.kop = k; b.aop = dout; b.bop = v; b.g = log_gate; b.out = dq; b.off = dq_off; b.prev = f.prev;
   b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
   b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = d_k; b.d_v = d_v; b.stream = stream;
   if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
-  // 5. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
-  b.kop = q; b.aop = v; b.bop = dout; b.g = lag; b.out = dk; b.off = dk_off; b.prev = r.prev;
+  // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
+  b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
   b.pair = dq_off; b.kx = k;
   b.direction = direction ^ 1;
   if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
-  // 6. dlog_gate
+  // 5. dlog_gate
   if ((rc = launched(gtr::launch_dgate(dk_off, ds_final, sfin, reinterpret_cast<float *>(ws + lay.totals),
                                        dlog_gate, (int)bh, grid_h, grid_w, d_k, d_v, n_chunk, direction,
                                        dtype, stream))) != GTR_OK)
     return rc;
-  if (ds0)  // 7. ds0
+  if (ds0)  // 6. ds0
     return launched(gtr::launch_ds0(log_gate, g0, ds0, (int)bh, grid_h, grid_w, d_k, d_v, direction, dtype,
                                     stream));
   return GTR_OK;

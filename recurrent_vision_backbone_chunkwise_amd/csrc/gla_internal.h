@@ -42,6 +42,7 @@ struct LaunchArgs {
   bool want_prev;    // split path: write prev for every segment even where the outputs need no scan
   bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass; d_k <= 64, split path)
   bool outputs_only;   // split path: only the output kernel, entering each segment with prev as given
+  bool lag_gates;      // scan position t takes the gate of position t-1, none at t = 0 (backward)
   hipStream_t stream;
 };
 
@@ -60,6 +61,7 @@ struct BwdArgs {
   const void *kx;                   // with `pair`: [bh][grid][d_k] keys k
   const float *prev;                // [bh][n_chunk][4096] register order
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
+  bool lag_gates;                   // as in LaunchArgs
   hipStream_t stream;
 };
 
@@ -98,9 +100,6 @@ int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const
 
 // Backward-pass launchers (hipError_t values).
 int launch_gla_bwd_dqk(const BwdArgs &a);
-// g_lag at the grid cell of scan position t = log_gate of position t+1 (0 at the last position).
-int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, int d_k, int direction,
-                    int dtype, hipStream_t stream);
 // dlog_gate_t = sum_{u >= t} x_u + rowsum(ds_final * s_final) along `direction`, with
 // x = q dq - k dk per position and dim (fp32, dq and dk without their cancelling self terms, as
 // the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32 scratch.

@@ -92,7 +92,11 @@ __device__ __forceinline__ f4 exp2v(f4 x) {
 
 // ---------------------------------------------------------------- element I/O
 // Each thread moves 4 consecutive elements of a token row per access.
+// kLagGates: position t of the scan takes the gate of position t-1 (none at
+// t = 0); Lagged<> sets it.  Plain: the element format without that flag.
 struct IoF32 {
+  static constexpr bool kLagGates = false;
+  using Plain = IoF32;
   using T = float;
   using Raw = u4;  // 16 bytes
   __device__ static f4 to_f4(Raw r) { return __builtin_bit_cast(f4, r); }
@@ -102,6 +106,8 @@ struct IoF32 {
 };
 
 struct IoF16 {
+  static constexpr bool kLagGates = false;
+  using Plain = IoF16;
   using T = _Float16;
   using Raw = u2;  // 8 bytes
   __device__ static h4 to_h4(Raw r) { return __builtin_bit_cast(h4, r); }
@@ -112,6 +118,8 @@ struct IoF16 {
 };
 
 struct IoBF16 {
+  static constexpr bool kLagGates = false;
+  using Plain = IoBF16;
   using T = uint16_t;  // raw bfloat16 bits
   using Raw = u2;
   __device__ static f4 to_f4(Raw r) {
@@ -127,6 +135,14 @@ struct IoBF16 {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   }
   __device__ static Raw pack(f4 v) { return u2{rne(v.x) | (rne(v.y) << 16), rne(v.z) | (rne(v.w) << 16)}; }
+};
+
+// An element format whose gates are read one scan position late (the
+// backward pass's reversed scan, where the state gradient at t decays by the
+// gate of the position after t in the forward order).
+template <class B> struct Lagged : B {
+  static constexpr bool kLagGates = true;
+  using Plain = B;
 };
 
 // ------------------------------------------------------------ MFMA operands
@@ -204,7 +220,7 @@ __device__ __forceinline__ f8 frag_tr(const float *tile, int r0, int c0, int lan
   return f;
 }
 
-template <typename Op, class Io> struct ToOp;
+template <typename Op, class Io> struct ToOp : ToOp<Op, typename Io::Plain> {};
 template <> struct ToOp<_Float16, IoF16> {
   __device__ static h4 cvt(u2 r) { return IoF16::to_h4(r); }
 };
@@ -289,10 +305,18 @@ __device__ __forceinline__ uint32_t token_cell(const Seq &sq, int t) {
   return (uint32_t)(row * sq.gw + col);
 }
 
-// Grid cells of scan positions t0 .. t0+3 (kNoRow past the end).  Consecutive
-// scan positions step by one grid cell along the scan, so only the first needs
-// a division.
-__device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell) {
+// Grid cell whose log_gate row holds the gate of scan position t (t < n_tok):
+// t's own, or with lagged gates the one before it (kNoRow at t = 0: no decay).
+template <class Io> __device__ __forceinline__ uint32_t gate_cell(const Seq &sq, int t) {
+  if constexpr (!Io::kLagGates) return token_cell(sq, t);
+  return t > 0 ? token_cell(sq, t - 1) : kNoRow;
+}
+
+// Grid cells of scan positions t0 .. t0+3 (kNoRow past the end) and, with
+// kBefore, of t0 - 1 (kNoRow before the start).  Consecutive scan positions
+// step by one grid cell along the scan, so only the first needs a division.
+template <bool kBefore>
+__device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell, uint32_t &before) {
   const bool rev = sq.dir & 1;
   const int p0 = rev ? sq.n_tok - 1 - t0 : t0;
   if (!(sq.dir & 2)) {
@@ -301,10 +325,24 @@ __device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell) {
       const int p = rev ? p0 - r : p0 + r;
       cell[r] = t0 + r < sq.n_tok ? (uint32_t)p : kNoRow;
     }
+    if constexpr (kBefore) before = t0 > 0 && t0 <= sq.n_tok ? (uint32_t)(rev ? p0 + 1 : p0 - 1) : kNoRow;
     return;
   }
   int row, col;
   col_major_pos(p0, sq.gh, sq.rcp_gh, row, col);
+  if constexpr (kBefore) {  // one step back along the scan
+    int br = row, bc = col;
+    if (rev) {
+      if (++br == sq.gh) {
+        br = 0;
+        ++bc;
+      }
+    } else if (--br < 0) {
+      br = sq.gh - 1;
+      --bc;
+    }
+    before = t0 > 0 && t0 <= sq.n_tok ? (uint32_t)(br * sq.gw + bc) : kNoRow;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     cell[r] = t0 + r < sq.n_tok ? (uint32_t)(row * sq.gw + col) : kNoRow;
@@ -425,6 +463,7 @@ __device__ __forceinline__ int state_i(int x, int lane) { return 16 * (x >> 2) +
 template <class Io> struct Rows {
   typename Io::Raw q[4], k[4], v[4], g[4];
   uint32_t off[4];  // grid cells (kNoRow past the end)
+  uint32_t before;  // lagged gates: grid cell of the position before the first (kNoRow at the start)
 };
 
 template <class Io>
@@ -444,17 +483,21 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // kFirst: the chunk's first key block, which also finds the tokens' grid
-// cells and loads v; later key blocks reuse the cells.
+// cells and loads v; later key blocks reuse the cells.  With lagged gates each
+// position's gate row is that of the position before it along the scan.
 template <class Io, bool kOut, bool kFirst>
 __device__ __forceinline__ void load_chunk(const Seq &sq, int c, int kb, int wave, int lane, Rows<Io> &x) {
   const int dq = lane & 15;
-  if constexpr (kFirst) cells4(sq, c * kChunk + 16 * wave + 4 * (lane >> 4), x.off);
+  if constexpr (kFirst) cells4<Io::kLagGates>(sq, c * kChunk + 16 * wave + 4 * (lane >> 4), x.off, x.before);
   const uint32_t kc = key_col<Io>(sq, kHead * kb + 4 * dq);
   const uint32_t vc = val_col<Io>(sq, 4 * dq);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t o = cell_at(x.off[r], sq.kpitch, kc);
-    x.g[r] = buf_load<Io>(sq.g, o);
+    uint32_t gcell = x.off[r];
+    if constexpr (Io::kLagGates)
+      if (gcell != kNoRow) gcell = r == 0 ? x.before : x.off[r - 1];
+    x.g[r] = buf_load<Io>(sq.g, cell_at(gcell, sq.kpitch, kc));
     x.k[r] = buf_load<Io>(sq.k, o);
     if constexpr (kFirst) x.v[r] = buf_load<Io>(sq.v, cell_at(x.off[r], sq.vpitch, vc));
     if constexpr (kOut) x.q[r] = buf_load<Io>(sq.q, o);
@@ -611,7 +654,7 @@ __device__ f4 exact_diag(const Seq &sq, int c, int a, int kb, int lane) {
     float run = 0.f;
     float e_sig[4] = {0.f, 0.f, 0.f, 0.f};
     for (int u = 0; u <= l16; ++u) {
-      run += key_elem<Io>(sq.g, token_cell(sq, t0 + u) * sq.kpitch + i * elt) * kLog2e;
+      run += key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, t0 + u), sq.kpitch, i * elt)) * kLog2e;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (u == 4 * g + r) e_sig[r] = run;
@@ -1221,7 +1264,7 @@ int launch_typed(const LaunchArgs &a) {
     if (a.fused || a.outputs_only || !a.states_only) return (int)hipErrorInvalidValue;
   }
   if (a.fused) {
-    if constexpr (NK != 1 || kStatesOnly) {
+    if constexpr (NK != 1 || kStatesOnly || Io::kLagGates) {
       return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
     } else {
       if (a.seg_len <= 1)
@@ -1487,12 +1530,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int i = d0 + r;
         if (i >= p.dk) continue;
         float ex = 0.f;
-        float run = key_elem<Io>(sq.g, cell * sq.kpitch + i * elt) * kLog2e;
+        float run = key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + tau), sq.kpitch, i * elt)) * kLog2e;
         for (int s2 = tau - 1; s2 >= 16 * a; --s2) {
           const uint32_t cs = sm.rowoff[0][s2];
           // 2^(E_tau - E_s2): the log2 gates of tokens s2+1 .. tau
           ex += dtile[a][(s2 - 16 * a) * 16 + l16] * key_elem<Io>(sq.k, cs * sq.kpitch + i * elt) * fast_exp2(run);
-          run += key_elem<Io>(sq.g, cs * sq.kpitch + i * elt) * kLog2e;
+          run += key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + s2), sq.kpitch, i * elt)) * kLog2e;
         }
         o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
       }
@@ -1517,27 +1560,6 @@ __device__ __forceinline__ uint32_t scan_cell(int t, int n_tok, int gh, int gw, 
   int row, col;
   col_major_pos(p, gh, rcp_gh, row, col);
   return (uint32_t)(row * gw + col);
-}
-
-// One thread per (sequence, scan position, 4 dims).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gla_gate_lag(const T *g, T *lag, int n_tok, int gh, int gw,
-                                                         int dir, float rcp_gh, int dk, long long n) {
-  const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (gid >= n) return;
-  const int groups = dk / 4;
-  const long long per_seq = (long long)n_tok * groups;
-  const long long seq = gid / per_seq;
-  const int rem = (int)(gid - seq * per_seq);
-  const int t = rem / groups, j = 4 * (rem - (rem / groups) * groups);
-  const size_t base = (size_t)seq * n_tok * dk;
-  // four elements moved as one vector (8 or 16 bytes; j and dk are multiples of 4)
-  using V = typename std::conditional<sizeof(T) == 4, u4, u2>::type;
-  V *dst = reinterpret_cast<V *>(lag + base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * dk + j);
-  V v = {};
-  if (t + 1 < n_tok)
-    v = *reinterpret_cast<const V *>(g + base + (size_t)scan_cell(t + 1, n_tok, gh, gw, dir, rcp_gh) * dk + j);
-  *dst = v;
 }
 
 
@@ -1661,6 +1683,17 @@ int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t 
 
 int launch_gla(const LaunchArgs &a) {
   const bool two = a.nk == 2;
+  if (a.lag_gates) {  // the backward pass's reversed scan: one key block, three launches
+    if (two || a.fused) return (int)hipErrorInvalidValue;
+    switch (a.dtype) {
+      case 0: return launch_typed<Lagged<IoF32>, float, 1>(a);
+      case 1: return a.fp32_operands ? launch_typed<Lagged<IoF16>, float, 1>(a)
+                                     : launch_typed<Lagged<IoF16>, _Float16, 1>(a);
+      case 2: return a.fp32_operands ? launch_typed<Lagged<IoBF16>, float, 1>(a)
+                                     : launch_typed<Lagged<IoBF16>, _Float16, 1>(a);
+      default: return (int)hipErrorInvalidValue;
+    }
+  }
   if (a.fp32_operands && !two && !a.fused) {
     switch (a.dtype) {
       case 1: return launch_typed<IoF16, float, 1>(a);
@@ -1705,12 +1738,16 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
-  if (a.pair)
-    launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, true>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
-           a.pair, a.kx);
-  else
+  // the dk pass (which forms the gate-gradient term from `pair`) runs along
+  // the reversed scan with lagged gates; the dq pass along the forward scan
+  if (a.pair && a.lag_gates)
+    launch(kKernelBwdDqk, gla_bwd_dqk<Lagged<Io>, Op, true>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out,
+           a.off, a.pair, a.kx);
+  else if (!a.pair && !a.lag_gates)
     launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, false>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
            a.pair, a.kx);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 
@@ -1726,21 +1763,6 @@ int launch_gla_bwd_dqk(const BwdArgs &a) {
     case 2: return launch_bwd_typed<IoBF16, float>(a);
     default: return (int)hipErrorInvalidValue;
   }
-}
-
-int launch_gate_lag(const void *g, void *g_lag, int bh, int grid_h, int grid_w, int d_k, int direction,
-                    int dtype, hipStream_t stream) {
-  const int n_tok = grid_h * grid_w;
-  const long long n = (long long)bh * n_tok * (d_k / 4);
-  const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
-  const float rcp = 1.0f / (float)grid_h;
-  if (dtype == 0)
-    launch(kKernelBwdLag, gla_gate_lag<float>, blocks, stream, static_cast<const float *>(g),
-           static_cast<float *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
-  else
-    launch(kKernelBwdLag, gla_gate_lag<uint16_t>, blocks, stream, static_cast<const uint16_t *>(g),
-           static_cast<uint16_t *>(g_lag), n_tok, grid_h, grid_w, direction, rcp, d_k, n);
-  return (int)hipGetLastError();
 }
 
 namespace {

@@ -26,7 +26,7 @@ std::vector<Mark> g_marks;
 
 const char *kNames[kNumKernels] = {"gla_seg_state",  "gla_seg_scan",  "gla_seg_out",    "gla_fused",
                                    "swiglu_gemm_in", "swiglu_mix",    "swiglu_gemm_out", "gla_bwd_dqk",
-                                   "gla_bwd_lag",    "gla_bwd_dgate", "gla_bwd_ds0"};
+                                   "gla_bwd_dgate",  "gla_bwd_ds0"};
 
 }  // namespace
 

@@ -14,10 +14,9 @@ enum KernelId : int {
   kKernelSwigluMix = 5,  // depthwise 3x3 + SiLU gate
   kKernelSwigluOut = 6,  // output projection (library GEMM)
   kKernelBwdDqk = 7,     // backward chunk kernel (dq, dk)
-  kKernelBwdLag = 8,     // gates lagged by one scan position
-  kKernelBwdDgate = 9,   // gate gradient (chunk totals, then running sums)
-  kKernelBwdDs0 = 10,    // gradient of the initial state
-  kNumKernels = 11
+  kKernelBwdDgate = 8,   // gate gradient (chunk totals, then running sums)
+  kKernelBwdDs0 = 9,     // gradient of the initial state
+  kNumKernels = 10
 };
 
 // While profiling is on and `stream` is not being captured, creates a pair of

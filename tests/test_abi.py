@@ -239,7 +239,7 @@ def test_backward_valid_call_without_gpu_reports_no_device():
 def test_kernel_names_match_the_header():
     """gtr_gla_kernel_name() gives the ids gtr_gla.h documents for gtr_gla_profile_end()."""
     names = ["gla_seg_state", "gla_seg_scan", "gla_seg_out", "gla_fused", "swiglu_gemm_in",
-             "swiglu_mix", "swiglu_gemm_out", "gla_bwd_dqk", "gla_bwd_lag", "gla_bwd_dgate",
+             "swiglu_mix", "swiglu_gemm_out", "gla_bwd_dqk", "gla_bwd_dgate",
              "gla_bwd_ds0"]
     L = gla.lib()
     assert [L.gtr_gla_kernel_name(i).decode() for i in range(len(names))] == names
