@@ -69,31 +69,6 @@ struct Shape {
 constexpr int kAutoFusedChunks = 32;
 constexpr long long kAutoFusedMinGroups = 256;
 
-// Segment length of the three-launch path.  Each CU walks its workgroups'
-// chunks, two workgroups already saturate it and one alone runs about 1.35x
-// slower per chunk (measured on MI355X), so the cost of a length s is the chunk
-// load of the busiest CU in the output kernel, half that for the state kernel
-// (which moves 3/5 of the bytes and skips the last segment), plus the
-// boundary scan, which grows with the segment count.
-long long split_segment_length(long long bh, int n_chunk) {
-  constexpr long long kCUs = 256;
-  auto load = [&](long long groups, long long s) {
-    const long long waves = (groups + kCUs - 1) / kCUs;
-    return (double)(waves * s) * (waves <= 1 ? 1.35 : 1.0);
-  };
-  long long best = 1;
-  double best_cost = 1e300;
-  for (long long s = 1; s <= 32 && s <= n_chunk; ++s) {
-    const long long n_seg = (n_chunk + s - 1) / s;
-    const double cost = load(bh * n_seg, s) + 0.5 * load(bh * (n_seg - 1), s) + 0.06 * (double)n_seg;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = s;
-    }
-  }
-  return best;
-}
-
 // `bh` counts the sequences the kernels walk (B*H*value blocks); `nk` the key
 // blocks, which only the three-launch path handles beyond one.
 void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
@@ -111,7 +86,7 @@ void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, S
     if (len <= 0) len = gtr::kMaxFusedChunks;
     len = std::min<long long>(len, gtr::kMaxFusedChunks);
   } else if (len <= 0) {
-    len = split_segment_length(bh, n_chunk);
+    len = gtr::split_segment_length(bh, n_chunk);
   }
   if (len > n_chunk) len = n_chunk;
   sh->seg_len = (int)len;
@@ -329,6 +304,31 @@ bool skip_pointer_checks() {
 }  // namespace
 
 namespace gtr {
+
+// Segment length of the three-launch path.  Each CU walks its workgroups'
+// chunks, two workgroups already saturate it and one alone runs about 1.35x
+// slower per chunk (measured on MI355X), so the cost of a length s is the chunk
+// load of the busiest CU in the output kernel, half that for the state kernel
+// (which moves 3/5 of the bytes and skips the last segment), plus the
+// boundary scan, which grows with the segment count.
+long long split_segment_length(long long bh, int n_chunk) {
+  constexpr long long kCUs = 256;
+  auto load = [&](long long groups, long long s) {
+    const long long waves = (groups + kCUs - 1) / kCUs;
+    return (double)(waves * s) * (waves <= 1 ? 1.35 : 1.0);
+  };
+  long long best = 1;
+  double best_cost = 1e300;
+  for (long long s = 1; s <= 32 && s <= n_chunk; ++s) {
+    const long long n_seg = (n_chunk + s - 1) / s;
+    const double cost = load(bh * n_seg, s) + 0.5 * load(bh * (n_seg - 1), s) + 0.06 * (double)n_seg;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
 
 int set_error(int code, const char *fmt, ...) {
   char buf[512];

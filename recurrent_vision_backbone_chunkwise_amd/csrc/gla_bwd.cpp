@@ -158,6 +158,10 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   if ((rc = launched(gtr::launch_gla(r))) != GTR_OK) return rc;
   gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands
   o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
+  // segments of the forward path's length, each entering with the state of its first chunk
+  o.prev_per_chunk = true;
+  o.seg_len = (int)gtr::split_segment_length(bh, n_chunk);
+  o.n_seg = (n_chunk + o.seg_len - 1) / o.seg_len;
   if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
   gtr::BwdArgs b{};  // 3. dq
   float *dq_off = reinterpret_cast<float *>(ws + lay.dq_off), *dk_off = reinterpret_cast<float *>(ws + lay.dk_off);

@@ -43,6 +43,8 @@ struct LaunchArgs {
   bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass; d_k <= 64, split path)
   bool outputs_only;   // split path: only the output kernel, entering each segment with prev as given
   bool lag_gates;      // scan position t takes the gate of position t-1, none at t = 0 (backward)
+  bool prev_per_chunk; // outputs_only: prev holds the state entering every chunk ([seq][n_chunk]);
+                       // each segment enters with the entry of its first chunk
   hipStream_t stream;
 };
 
@@ -110,6 +112,10 @@ int launch_dgate(const float *x, const float *ds_final, const float *s_final, fl
 // ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][d_k][d_v].
 int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
                int direction, int dtype, hipStream_t stream);
+
+// Chunks per segment of the three-launch path for `seqs` sequences of
+// n_chunk chunks (defined in gla_api.cpp).
+long long split_segment_length(long long seqs, int n_chunk);
 
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);

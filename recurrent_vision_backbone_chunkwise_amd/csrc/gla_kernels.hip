@@ -403,6 +403,7 @@ struct Params {
   int n_chunk, seg_len, n_seg, n_seg_grid;
   float *agg, *agg_dec;    // [seq][n_seg][key block][4096] state contribution, [..][64] decay per key dim
   const float *prev;       // [seq][n_seg][key block][4096] register order (separate-launch path)
+  int prev_seq, prev_step;  // prev entries per sequence, and between consecutive segments
   const float *s0;         // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;          // user final state, row-major, nullable
   int *sync;               // fused path: header, per-sequence control lines (kSync* words)
@@ -946,7 +947,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   // the first chunk's are in flight together.
   f4 S[NK][4];
   {
-    const float *src = p.prev ? p.prev + ws_block<NK>(p, seq, seg, 0) * kStateElems : nullptr;
+    const size_t entry = ((size_t)seq * p.prev_seq + (size_t)seg * p.prev_step) * NK;
+    const float *src = p.prev ? p.prev + entry * kStateElems : nullptr;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(src), (short)0, p.prev ? NK * kStateElems * (int)sizeof(float) : 0, 0x00020000);
 #pragma unroll
@@ -1256,6 +1258,8 @@ int launch_typed(const LaunchArgs &a) {
   p.n_chunk = a.n_chunk; p.seg_len = a.seg_len; p.n_seg = a.n_seg; p.n_seg_grid = a.n_seg;
   p.agg = a.agg; p.agg_dec = a.agg_dec; p.s0 = a.s0; p.s_final = a.s_final;
   p.flags = a.flags; p.sync = a.sync;
+  p.prev_seq = a.n_seg;
+  p.prev_step = 1;
   const unsigned n_blocks = (unsigned)(a.bh * a.n_seg);
   // fp32 operands on 16-bit I/O serve only the backward's state passes: no
   // output or one-launch kernels are built for them
@@ -1282,6 +1286,10 @@ int launch_typed(const LaunchArgs &a) {
       a.n_seg > 1 || a.s0 != nullptr || a.s_final != nullptr || a.states_only || a.want_prev;
   if (a.outputs_only) {
     p.prev = a.prev;
+    if (a.prev_per_chunk) {
+      p.prev_seq = a.n_chunk;
+      p.prev_step = a.seg_len;
+    }
   } else if (need_scan) {
     const int n_state_seg = a.s_final ? a.n_seg : a.n_seg - 1;
     if (n_state_seg > 0) {
