@@ -168,7 +168,6 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   b.kop = k; b.aop = dout; b.bop = v; b.g = log_gate; b.out = dq; b.off = dq_off; b.prev = f.prev;
   b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
   b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = d_k; b.d_v = d_v; b.stream = stream;
-  b.chunks_per_group = o.seg_len;
   if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
   // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
   b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;

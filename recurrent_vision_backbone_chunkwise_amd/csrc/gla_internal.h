@@ -63,7 +63,6 @@ struct BwdArgs {
   const void *kx;                   // with `pair`: [bh][grid][d_k] keys k
   const float *prev;                // [bh][n_chunk][4096] register order
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
-  int chunks_per_group;             // chunks each workgroup takes in turn (<= 0: one)
   bool lag_gates;                   // as in LaunchArgs
   hipStream_t stream;
 };

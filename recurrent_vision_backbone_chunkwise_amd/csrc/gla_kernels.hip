@@ -1349,9 +1349,7 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
   return (float)sm.cv[idx * kHead + i];
 }
 
-// One workgroup per run of p.seg_len chunks (p.n_seg runs per sequence), taken
-// one after another; for 16-bit I/O the next chunk's rows are loaded while the
-// current one computes.  The forward chunk preparation runs with the query
+// One workgroup per chunk.  The forward chunk preparation runs with the query
 // set to one, which leaves in LDS exactly the factors needed here:
 //   qs = 2^(E_tau - E_start(a))       (per token and dim, <= 1)
 //   ks = kop 2^(E_end(b) - E_sigma)   (keys referenced to their sub-block end)
@@ -1388,192 +1386,178 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ float dtile[4][16 * 16];                          // diagonal P^T [sigma][tau] of each sub-block
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int seq = blockIdx.x / p.n_seg, grp = blockIdx.x - seq * p.n_seg;
-  const int c_begin = grp * p.seg_len, c_end = min(c_begin + p.seg_len, p.n_chunk);
+  const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
   const int a = wave;  // this wave's token sub-block
   const Seq sq = seq_of<Io>(p, seq);  // k: kop, v: a, g: gates, o: b (read only)
   const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<T *>(out) + (size_t)seq * p.n_tok * p.dk, (short)0,
       (int)((uint32_t)p.n_tok * (uint32_t)p.dk * sizeof(T)), 0x00020000);
-  // the next chunk's rows wait in registers for 16-bit I/O (fp32 rows would
-  // not fit beside the rest)
-  constexpr bool kPrefetch = sizeof(T) == 2;
+
+  // rows i = 16t + l16 of the state entering the chunk, for the four 16-dim
+  // tiles t, at the k-slots of an MFMA operand (register-order workspace layout)
+  float srow[4][16];
+  {
+    const float *st = p.prev + ((size_t)seq * p.n_chunk + c) * kStateElems;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 16 * t + l16;
+      const int x = 4 * (i >> 4) + (i & 3), lo = 16 * ((i & 15) >> 2);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * kb + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+          srow[t][8 * kb + e] = st[(j >> 4) * 1024 + x * 64 + lo + (j & 15)];
+        }
+    }
+  }
   Rows<Io> x;
+  load_chunk<Io, false, true>(sq, c, 0, wave, lane, x);
   typename Io::Raw brow[4];
-  auto load_rows = [&](int c) {
-    load_chunk<Io, false, true>(sq, c, 0, wave, lane, x);
+  {
     const uint32_t vc = val_col<Io>(sq, 4 * l16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) brow[r] = buf_load<Io>(sq.o, cell_at(x.off[r], sq.vpitch, vc));
-  };
-  if constexpr (kPrefetch) load_rows(c_begin);
+  }
+  const typename Io::Raw one = Io::pack(f4{1.f, 1.f, 1.f, 1.f});
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x.q[r] = one;
+  op4<Op> qs[4], ks[4];
+  prep_local<Io, Op, true, -1>(sm, x, wave, lane, 0, qs, ks, true);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(brow[r]);
+  lds_sync();
+  prep_chunk<Io, Op, true, -1>(sm, qs, ks, wave, lane, 0);
+  lds_sync();
 
-  for (int c = c_begin; c < c_end; ++c) {
-    if (c > c_begin) lds_sync();  // the previous chunk's outputs have read LDS
-    // rows i = 16t + l16 of the state entering the chunk, for the four 16-dim
-    // tiles t, at the k-slots of an MFMA operand (register-order workspace layout)
-    float srow[4][16];
-    {
-      const float *st = p.prev + ((size_t)seq * p.n_chunk + c) * kStateElems;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int i = 16 * t + l16;
-        const int x = 4 * (i >> 4) + (i & 3), lo = 16 * ((i & 15) >> 2);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 32 * kb + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-            srow[t][8 * kb + e] = st[(j >> 4) * 1024 + x * 64 + lo + (j & 15)];
-          }
-      }
-    }
-    if constexpr (!kPrefetch) load_rows(c);
-    const typename Io::Raw one = Io::pack(f4{1.f, 1.f, 1.f, 1.f});
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x.q[r] = one;
-    op4<Op> qs[4], ks[4];
-    prep_local<Io, Op, true, -1>(sm, x, wave, lane, 0, qs, ks, true);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(brow[r]);
-    typename Io::Raw kcur[4];  // kop rows, written to LDS once the scores are formed
-#pragma unroll
-    for (int r = 0; r < 4; ++r) kcur[r] = x.k[r];
-    if constexpr (kPrefetch)
-      if (c + 1 < c_end) load_rows(c + 1);
-    lds_sync();
-    prep_chunk<Io, Op, true, -1>(sm, qs, ks, wave, lane, 0);
-    lds_sync();
-
-    const int tau = 16 * a + l16;
-    const uint32_t cell = sm.rowoff[0][tau];
-    // kX: dq and k at this lane's position and result dims, for all four tiles;
-    // issued now (clamped to valid rows and dims, results past them are not
-    // stored) so that they arrive while the MFMAs run
-    f4 xdq[4], xkk[4];
-    if constexpr (kX) {
-      const size_t row = ((size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell)) * p.dk;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int d = min(16 * t + 4 * g4, p.dk - 4);
-        xdq[t] = *reinterpret_cast<const f4 *>(pair + row + d);
-        const T *kp = static_cast<const T *>(kx) + row + d;
-        xkk[t] = f4{elem<Io>(kp), elem<Io>(kp + 1), elem<Io>(kp + 2), elem<Io>(kp + 3)};
-      }
-    }
-
-    // P^T tiles of sub-block a: rows sigma = 16b + 4 g4 + r, column tau = 16a + l16
-    // (zero for b > a and, on the diagonal tile, for sigma >= tau), packed in
-    // pairs as B operands over sigma in [32 kb, 32 kb + 32)
-    op8<Op> pf[2];
-    {
-      f4 tile[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (b <= a) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const op8<Op> fb = frag_row<Op>(&bs[(16 * b + l16) * LD + 32 * kb + 4 * g4]);
-            const op8<Op> fa = frag_row<Op>(&sm.vv[(16 * a + l16) * OpT<Op>::LDT + 32 * kb + 4 * g4]);
-            if constexpr (sizeof(T) == 2 && sizeof(Op) == 4)  // 16-bit inputs are exact in fp16:
-              acc = mma(__builtin_convertvector(fb, h8), __builtin_convertvector(fa, h8), acc);  // same sums
-            else
-              acc = mma(fb, fa, acc);
-          }
-        }
-        if (b == a) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sl = 4 * g4 + r;  // sigma within the sub-block; tau within it is l16
-            if (sl == l16) self_score[16 * a + l16] = acc[r];
-            if (sl >= l16) acc[r] = 0.f;
-            dtile[a][sl * 16 + l16] = acc[r];
-          }
-        }
-        tile[b] = acc;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) pf[kb] = cat(to4<Op>(tile[2 * kb]), to4<Op>(tile[2 * kb + 1]));
-    }
-    lds_sync();
-    // every wave has read the score keys: the tile now takes kop itself (this
-    // barrier also publishes the self scores and diagonal tiles)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(kcur[r]);
-    lds_sync();
-
-    const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
-    const bool live = c * kChunk + tau < p.n_tok;
-    const float self = self_score[tau];
+  const int tau = 16 * a + l16;
+  const uint32_t cell = sm.rowoff[0][tau];
+  // kX: dq and k at this lane's position and result dims, for all four tiles;
+  // issued now (clamped to valid rows and dims, results past them are not
+  // stored) so that they arrive while the MFMAs run
+  f4 xdq[4], xkk[4];
+  if constexpr (kX) {
+    const size_t row = ((size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell)) * p.dk;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int i_row = 16 * t + l16;  // this lane's operand row
-      float es = 1.f;                  // 2^E_start(a) for dim i_row
-      for (int a2 = 0; a2 < a; ++a2) es *= sm.tot[a2 * kHead + i_row];
-      f4 acc = {0.f, 0.f, 0.f, 0.f}, accd = {0.f, 0.f, 0.f, 0.f};
+      const int d = min(16 * t + 4 * g4, p.dk - 4);
+      xdq[t] = *reinterpret_cast<const f4 *>(pair + row + d);
+      const T *kp = static_cast<const T *>(kx) + row + d;
+      xkk[t] = f4{elem<Io>(kp), elem<Io>(kp + 1), elem<Io>(kp + 2), elem<Io>(kp + 3)};
+    }
+  }
+
+  // P^T tiles of sub-block a: rows sigma = 16b + 4 g4 + r, column tau = 16a + l16
+  // (zero for b > a and, on the diagonal tile, for sigma >= tau), packed in
+  // pairs as B operands over sigma in [32 kb, 32 kb + 32)
+  op8<Op> pf[2];
+  {
+    f4 tile[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {  // state entering the chunk
-        op8<Op> sf;
+    for (int b = 0; b < 4; ++b) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (b <= a) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sf[e] = (Op)(srow[t][8 * kb + e] * es);
-        acc = mma(sf, frag_row<Op>(&sm.vv[tau * OpT<Op>::LDT + 32 * kb + 4 * g4]), acc);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {  // earlier sub-blocks
-        if (2 * kb >= a) break;
-        const float f0 = block_factor(sm, a, 2 * kb, i_row);
-        const float f1 = 2 * kb + 1 < a ? block_factor(sm, a, 2 * kb + 1, i_row) : 0.f;
-        op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xk[e] = (Op)((float)xk[e] * (e < 4 ? f0 : f1));
-        acc = mma(xk, pf[kb], acc);
-      }
-      if (!exact) {  // own sub-block, referenced at its midpoint
-        const int kb = a >> 1;
-        const float h = (float)sm.hv[a * kHead + i_row];
-        op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xk[e] = (Op)(((e < 4) == ((a & 1) == 0)) ? (float)xk[e] * h : 0.f);
-        accd = mma(xk, pf[kb], accd);
-      }
-      const int d0 = 16 * t + 4 * g4;  // dims of this lane's results
-      f4 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f1 = (float)sm.qs[tau * LD + d0 + r];
-        o[r] = f1 * (acc[r] + (float)sm.hv[a * kHead + d0 + r] * accd[r]);
-      }
-      if (exact && live) {  // exact fp32 sum over the earlier tokens of the own sub-block
-        constexpr uint32_t elt = sizeof(T);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = d0 + r;
-          if (i >= p.dk) continue;
-          float ex = 0.f;
-          float run = key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + tau), sq.kpitch, i * elt)) * kLog2e;
-          for (int s2 = tau - 1; s2 >= 16 * a; --s2) {
-            const uint32_t cs = sm.rowoff[0][s2];
-            // 2^(E_tau - E_s2): the log2 gates of tokens s2+1 .. tau
-            ex += dtile[a][(s2 - 16 * a) * 16 + l16] * key_elem<Io>(sq.k, cs * sq.kpitch + i * elt) * fast_exp2(run);
-            run += key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + s2), sq.kpitch, i * elt)) * kLog2e;
-          }
-          o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
+        for (int kb = 0; kb < 2; ++kb) {
+          const op8<Op> fb = frag_row<Op>(&bs[(16 * b + l16) * LD + 32 * kb + 4 * g4]);
+          const op8<Op> fa = frag_row<Op>(&sm.vv[(16 * a + l16) * OpT<Op>::LDT + 32 * kb + 4 * g4]);
+          if constexpr (sizeof(T) == 2 && sizeof(Op) == 4)  // 16-bit inputs are exact in fp16:
+            acc = mma(__builtin_convertvector(fb, h8), __builtin_convertvector(fa, h8), acc);  // same sums
+          else
+            acc = mma(fb, fa, acc);
         }
       }
-      f4 full, w = o;
+      if (b == a) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sl = 4 * g4 + r;  // sigma within the sub-block; tau within it is l16
+          if (sl == l16) self_score[16 * a + l16] = acc[r];
+          if (sl >= l16) acc[r] = 0.f;
+          dtile[a][sl * 16 + l16] = acc[r];
+        }
+      }
+      tile[b] = acc;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pf[kb] = cat(to4<Op>(tile[2 * kb]), to4<Op>(tile[2 * kb + 1]));
+  }
+  lds_sync();
+  // every wave has read the score keys: the tile now takes kop itself (this
+  // barrier also publishes the self scores and diagonal tiles)
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<op4<Op> *>(&bs[(16 * wave + 4 * g4 + r) * LD + 4 * l16]) = ToOp<Op, Io>::cvt(x.k[r]);
+  lds_sync();
+
+  const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
+  const bool live = c * kChunk + tau < p.n_tok;
+  const float self = self_score[tau];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i_row = 16 * t + l16;  // this lane's operand row
+    float es = 1.f;                  // 2^E_start(a) for dim i_row
+    for (int a2 = 0; a2 < a; ++a2) es *= sm.tot[a2 * kHead + i_row];
+    f4 acc = {0.f, 0.f, 0.f, 0.f}, accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {  // state entering the chunk
+      op8<Op> sf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sf[e] = (Op)(srow[t][8 * kb + e] * es);
+      acc = mma(sf, frag_row<Op>(&sm.vv[tau * OpT<Op>::LDT + 32 * kb + 4 * g4]), acc);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {  // earlier sub-blocks
+      if (2 * kb >= a) break;
+      const float f0 = block_factor(sm, a, 2 * kb, i_row);
+      const float f1 = 2 * kb + 1 < a ? block_factor(sm, a, 2 * kb + 1, i_row) : 0.f;
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xk[e] = (Op)((float)xk[e] * (e < 4 ? f0 : f1));
+      acc = mma(xk, pf[kb], acc);
+    }
+    if (!exact) {  // own sub-block, referenced at its midpoint
+      const int kb = a >> 1;
+      const float h = (float)sm.hv[a * kHead + i_row];
+      op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xk[e] = (Op)(((e < 4) == ((a & 1) == 0)) ? (float)xk[e] * h : 0.f);
+      accd = mma(xk, pf[kb], accd);
+    }
+    const int d0 = 16 * t + 4 * g4;  // dims of this lane's results
+    f4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f1 = (float)sm.qs[tau * LD + d0 + r];
+      o[r] = f1 * (acc[r] + (float)sm.hv[a * kHead + d0 + r] * accd[r]);
+    }
+    if (exact && live) {  // exact fp32 sum over the earlier tokens of the own sub-block
+      constexpr uint32_t elt = sizeof(T);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float kop = (float)bs[tau * LD + d0 + r];
-        full[r] = o[r] + self * kop;
-        if constexpr (kX) w[r] = kop * xdq[t][r] - xkk[t][r] * o[r];
+        const int i = d0 + r;
+        if (i >= p.dk) continue;
+        float ex = 0.f;
+        float run = key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + tau), sq.kpitch, i * elt)) * kLog2e;
+        for (int s2 = tau - 1; s2 >= 16 * a; --s2) {
+          const uint32_t cs = sm.rowoff[0][s2];
+          // 2^(E_tau - E_s2): the log2 gates of tokens s2+1 .. tau
+          ex += dtile[a][(s2 - 16 * a) * 16 + l16] * key_elem<Io>(sq.k, cs * sq.kpitch + i * elt) * fast_exp2(run);
+          run += key_elem<Io>(sq.g, cell_at(gate_cell<Io>(sq, c * kChunk + s2), sq.kpitch, i * elt)) * kLog2e;
+        }
+        o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
       }
-      buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
-      if (cell != kNoRow && d0 < p.dk)
-        *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = w;
     }
+    f4 full, w = o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float kop = (float)bs[tau * LD + d0 + r];
+      full[r] = o[r] + self * kop;
+      if constexpr (kX) w[r] = kop * xdq[t][r] - xkk[t][r] * o[r];
+    }
+    buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
+    if (cell != kNoRow && d0 < p.dk)
+      *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = w;
   }
 }
 
@@ -1762,15 +1746,14 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
-  p.seg_len = a.chunks_per_group > 0 ? a.chunks_per_group : 1;
-  p.n_seg = (a.n_chunk + p.seg_len - 1) / p.seg_len;
-  const unsigned blocks = (unsigned)(a.bh * p.n_seg);
   // the dk pass (which forms the gate-gradient term from `pair`) runs along
   // the reversed scan with lagged gates; the dq pass along the forward scan
   if (a.pair && a.lag_gates)
-    launch(kKernelBwdDqk, gla_bwd_dqk<Lagged<Io>, Op, true>, blocks, a.stream, p, a.out, a.off, a.pair, a.kx);
+    launch(kKernelBwdDqk, gla_bwd_dqk<Lagged<Io>, Op, true>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out,
+           a.off, a.pair, a.kx);
   else if (!a.pair && !a.lag_gates)
-    launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, false>, blocks, a.stream, p, a.out, a.off, a.pair, a.kx);
+    launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, false>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
+           a.pair, a.kx);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

@@ -93,16 +93,6 @@ def test_workload_shapes(widx):
     note(f"errors {check(q, k, v, g, w.directions[0], w.dtype, w.name, seed=37)}")
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_chunk_runs_with_a_ragged_last_run(dtype):
-    """128x128 with two heads: each chunk-kernel workgroup takes a run of 3 chunks in turn,
-    loading the next chunk's rows early; 256 chunks leave a last run of one."""
-    assert gla.gtr_gla_plan(1, 2, 128, 128, path=2)["seg_len"] == 3
-    q, k, v, g = gla_inputs.make_inputs(1, 2, 128, 128, 64, 64, dtype, "light", seed=45)
-    for d in (1, 2):
-        note(f"errors {check(q, k, v, g, d, dtype, '128x128 runs of 3', seed=46 + d)}")
-
-
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_long_sequence(dtype):
     """144 chunks: both state scans run 143 or 144 steps; with s0 and dL/dS_final."""
