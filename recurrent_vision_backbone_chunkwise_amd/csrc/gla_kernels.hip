@@ -1493,6 +1493,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool exact = !__all(sm.tot[a * kHead + lane] >= OpT<Op>::kDiagMin);
   const bool live = c * kChunk + tau < p.n_tok;
   const float self = self_score[tau];
+  // the P^T pair holding the own sub-block (a is uniform across the wave, so
+  // this is a select, not an indexed register access in the loop below)
+  const op8<Op> pown = a >= 2 ? pf[1] : pf[0];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int i_row = 16 * t + l16;  // this lane's operand row
@@ -1516,13 +1519,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int e = 0; e < 8; ++e) xk[e] = (Op)((float)xk[e] * (e < 4 ? f0 : f1));
       acc = mma(xk, pf[kb], acc);
     }
-    if (!exact) {  // own sub-block, referenced at its midpoint
+    if (!exact) {  // own sub-block (pair a / 2), referenced at its midpoint
       const int kb = a >> 1;
       const float h = (float)sm.hv[a * kHead + i_row];
       op8<Op> xk = frag_tr_ld(sm.ks, LD, 32 * kb, 16 * t, lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) xk[e] = (Op)(((e < 4) == ((a & 1) == 0)) ? (float)xk[e] * h : 0.f);
-      accd = mma(xk, pf[kb], accd);
+      accd = mma(xk, pown, accd);
     }
     const int d0 = 16 * t + 4 * g4;  // dims of this lane's results
     f4 o;

@@ -93,6 +93,14 @@ def test_workload_shapes(widx):
     note(f"errors {check(q, k, v, g, w.directions[0], w.dtype, w.name, seed=37)}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_16k_tokens(dtype):
+    """128x128, two heads, 16-bit I/O: 256 chunks along the forward and the reversed scan."""
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 128, 128, 64, 64, dtype, "light", seed=45)
+    for d in (1, 2):
+        note(f"errors {check(q, k, v, g, d, dtype, '128x128', seed=46 + d)}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_long_sequence(dtype):
     """144 chunks: both state scans run 143 or 144 steps; with s0 and dL/dS_final."""
