@@ -211,6 +211,27 @@ def test_final_state_from_zero(grid, path):
 
 
 @pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_non_finite_inputs_stay_in_their_sequence(dtype, path):
+    """Values outside the domain (NaN, infinities, a positive log-gate) in one head give an
+    unspecified result for that head only: the call succeeds, the stream stays healthy, and
+    the other heads match the oracle."""
+    q, k, v, g = gla_inputs.make_inputs(1, 3, 13, 11, 64, 64, dtype, "light", seed=51)
+    ref = oracle.gla_forward(q[:, :2], k[:, :2], v[:, :2], g[:, :2], 3)
+    q[0, 2, 1, 2, 5] = float("nan")
+    k[0, 2, 4, 4, 0] = float("inf")
+    v[0, 2, 7, 1, 9] = float("-inf")
+    g[0, 2, 3, 3, 3] = float("nan")
+    g[0, 2, 9, 0, :] = 5.0  # alpha > 1
+    g[0, 2, 10, 10, 7] = float("-inf")
+    note(f"non-finite inputs dtype={dtype} path={path}")
+    y = gpu_run(q, k, v, g, 3, path=PATHS[path], chunks_per_segment=1)
+    gla.gtr_gla_stream_status()
+    e = parity_errors(y[:, :2].double().cpu().numpy(), ref, dtype)
+    assert e["ok"], e
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
 def test_empty_calls(path):
     """No tokens: out is empty and the final state is s0 (or zero); no sequences: nothing happens."""
     s0 = torch.randn(2, 3, 64, 64, generator=torch.Generator().manual_seed(14)).to(DEV)
