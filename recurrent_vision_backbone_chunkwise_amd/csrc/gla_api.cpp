@@ -232,14 +232,16 @@ hipError_t workspace_malloc(void **p, size_t bytes) {
 }
 
 int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, size_t flags,
-                  void **data, int **sync, int **flag_words) {
+                  void **data, int **sync, long long **flag_words) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace &ws = g_ws[{device, stream}];
   const bool sync_ok = (seqs == 0 && flags == 0) || (ws.cap_seqs >= seqs && ws.cap_flags >= flags);
   auto hand_out = [&] {
     *data = ws.data;
     *sync = ws.sync;
-    *flag_words = ws.sync ? ws.sync + gtr::kSyncHeader + ws.cap_seqs * gtr::kCtlStride : nullptr;
+    // 64-bit flags after the control lines (an even word offset: 8-byte aligned)
+    *flag_words = ws.sync ? reinterpret_cast<long long *>(ws.sync + gtr::kSyncHeader + ws.cap_seqs * gtr::kCtlStride)
+                          : nullptr;
   };
   if (ws.data_bytes >= bytes && sync_ok) {
     hand_out();
@@ -272,7 +274,7 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
   if (!sync_ok) {
     const size_t seq_cap = std::max(ws.cap_seqs, seqs + seqs / 4);
     const size_t flag_cap = std::max(ws.cap_flags, flags + flags / 4);
-    const size_t words = gtr::kSyncHeader + seq_cap * gtr::kCtlStride + flag_cap;
+    const size_t words = gtr::kSyncHeader + seq_cap * gtr::kCtlStride + 2 * flag_cap;
     void *p = nullptr;
     if (workspace_malloc(&p, words * sizeof(int)) != hipSuccess) {
       (void)hipGetLastError();
@@ -489,7 +491,8 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   const bool need_ws = sh.fused || sh.n_seg > 1 || s0 || s_final;
   if (need_ws) {
     void *ws = nullptr;
-    int *sync = nullptr, *flags = nullptr;
+    int *sync = nullptr;
+    long long *flags = nullptr;
     rc = get_workspace(device, stream, gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk),
                        sh.fused ? sh.seqs : 0, sh.fused ? sh.seqs * sh.n_seg : 0, &ws, &sync, &flags);
     if (rc != GTR_OK) return rc;

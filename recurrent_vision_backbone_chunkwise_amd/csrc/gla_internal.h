@@ -34,7 +34,7 @@ struct LaunchArgs {
   float *agg_dec;    // [seq][n_seg][nk][64]   segment decay factor per key dim
   float *prev;       // [seq][n_seg][nk][4096] state entering each segment
   int *sync;         // fused path: header + per-sequence control lines (zeroed at allocation)
-  int *flags;        // [bh][n_seg] fused path: aggregate-published flags, after the control lines
+  long long *flags;  // [bh][n_seg] fused path: aggregate-published flags (64-bit epochs), after the control lines
   const float *s0;   // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;    // user final state, row-major [B*H][d_k][d_v], nullable
   bool fused;        // one launch (gla_fused) instead of three
@@ -68,7 +68,8 @@ struct BwdArgs {
 };
 
 constexpr int kSyncHeader = 32;  // fused-path header words (epoch, sequences done, error)
-constexpr int kSyncEpochWord = 0, kSyncSeqDoneWord = 1, kSyncErrorWord = 2;
+// The epoch is a 64-bit count in words 0 and 1, so it never wraps.
+constexpr int kSyncEpochWord = 0, kSyncSeqDoneWord = 2, kSyncErrorWord = 3;
 constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (ticket, done)
 
 // Float workspace bytes for (sequences, n_seg, key blocks): agg, prev and agg_dec.
@@ -79,7 +80,7 @@ inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
 // one flag per segment.  They live in their own zero-initialised allocation;
 // flags only ever hold epoch numbers, so a flag can never be confused with
 // left-over data.
-inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (kCtlStride + n_seg); }
+inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (kCtlStride + 2 * n_seg); }
 
 // Host helpers shared by the entry points (defined in gla_api.cpp): record an
 // error message for gtr_gla_last_error() and return `code`; clear it; check a

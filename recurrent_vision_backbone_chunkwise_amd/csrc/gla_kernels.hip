@@ -407,12 +407,13 @@ struct Params {
   const float *s0;         // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;          // user final state, row-major, nullable
   int *sync;               // fused path: header, per-sequence control lines (kSync* words)
-  int *flags;              // [bh][n_seg] fused path: segment aggregate published
+  long long *flags;        // [bh][n_seg] fused path: segment aggregate published (epoch + 1)
 };
 
 // Fused-path synchronisation words.  Header: the epoch (number of completed
-// fused calls on this workspace), the count of sequences finished in the
-// current call, and an error word (-1 after a wait gave up).  Per sequence: its
+// fused calls on this workspace, 64-bit so that it never wraps), the count of
+// sequences finished in the current call, and an error word (-1 after a wait
+// gave up).  Per sequence: its
 // ticket and done counters.  After every call all words other than the epoch
 // and the flags are back at 0 (or -1); flags hold epochs, all below the next
 // call's epoch + 1, whatever shape wrote them.
@@ -1036,10 +1037,10 @@ __device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcn
 
 // Bounded wait until a flag reaches at least `want`; returns the value seen
 // and records a timeout in the error word.
-__device__ __forceinline__ int wait_flag(int *sync, const int *f, int want) {
+__device__ __forceinline__ long long wait_flag(int *sync, const long long *f, long long want) {
   int spins = 0;
   for (;;) {
-    const int v = __hip_atomic_load(const_cast<int *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const long long v = __hip_atomic_load(const_cast<long long *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v >= want) return v;
     __builtin_amdgcn_s_sleep(2);
     if (++spins > kSpinLimit) {
@@ -1068,7 +1069,8 @@ template <class Io, typename Op, int kSeg>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     kFusedOccupancy<Op, kSeg>, kFusedOccupancy<Op, kSeg>))) void gla_fused(Params p) {
   __shared__ Smem<Op, kSeg> sm;
-  __shared__ int s_ticket, s_epoch;
+  __shared__ int s_ticket;
+  __shared__ long long s_epoch;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   // The sequence is fixed by the block index; the segment is the order in which
@@ -1078,12 +1080,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   int *ctl = p.sync + kSyncHeader + (size_t)bh * kCtlStride;
   if (tid == 0) {
     s_ticket = __hip_atomic_fetch_add(ctl + kCtlTicket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = __hip_atomic_load(p.sync + kSyncEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_epoch = __hip_atomic_load(reinterpret_cast<long long *>(p.sync + kSyncEpoch), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   // flag value of this call: the epoch (calls completed on this workspace) + 1;
   // earlier calls left at most the epoch
-  const int seg = s_ticket, want = s_epoch + 1;
+  const int seg = s_ticket;
+  const long long want = s_epoch + 1;
   const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
   const size_t sbase = (size_t)bh * p.n_seg;
   const Seq sq = seq_of<Io>(p, bh);
@@ -1232,7 +1236,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       if (__hip_atomic_fetch_add(p.sync + kSyncSeqDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
           p.bh_count - 1) {
         __hip_atomic_store(p.sync + kSyncSeqDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.sync + kSyncEpoch, s_epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(reinterpret_cast<long long *>(p.sync + kSyncEpoch), s_epoch + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
