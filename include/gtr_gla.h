@@ -228,7 +228,9 @@ int gtr_gla_version(void);
 /* Frees every cached workspace of this library, forward, backward and Spatial
  * SwiGLU, including the buffers that grown workspaces replaced.  It first
  * synchronises each device that has one.  Graphs captured before this call
- * must not be replayed after it. */
+ * must not be replayed after it, and no other call of this library may run on
+ * another host thread while it does (the calls themselves are thread-safe
+ * among each other). */
 void gtr_gla_release_workspaces(void);
 
 /*
