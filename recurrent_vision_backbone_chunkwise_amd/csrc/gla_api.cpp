@@ -493,14 +493,16 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
     void *ws = nullptr;
     int *sync = nullptr;
     long long *flags = nullptr;
-    rc = get_workspace(device, stream, gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk),
-                       sh.fused ? sh.seqs : 0, sh.fused ? sh.seqs * sh.n_seg : 0, &ws, &sync, &flags);
+    const size_t bytes = sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg)
+                                  : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk);
+    rc = get_workspace(device, stream, bytes, sh.fused ? sh.seqs : 0, sh.fused ? sh.seqs * sh.n_seg : 0, &ws,
+                       &sync, &flags);
     if (rc != GTR_OK) return rc;
     float *f = static_cast<float *>(ws);
     const size_t st = (size_t)sh.seqs * sh.n_seg * sh.nk * gtr::kStateElems;
     a.agg = f;
-    a.prev = f + st;
-    a.agg_dec = f + 2 * st;
+    a.prev = sh.fused ? nullptr : f + st;  // the one-launch path keeps no entering states
+    a.agg_dec = f + (sh.fused ? 1 : 2) * st;
     a.sync = sync;
     a.flags = flags;
   }
@@ -545,7 +547,7 @@ size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, in
       GTR_OK)
     return 0;
   if (sh.empty) return 0;
-  return gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk) +
+  return (sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg) : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk)) +
          (sh.fused ? gtr::sync_words(sh.seqs, sh.n_seg) * sizeof(int) : 0);
 }
 

@@ -76,6 +76,11 @@ constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (tick
 inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
   return seqs * n_seg * nk * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
+// Float workspace bytes of the one-launch path: aggregates and decays only (it
+// keeps no entering states), and none for a single segment (nothing to pass on).
+inline size_t fused_workspace_bytes(size_t seqs, size_t n_seg) {
+  return n_seg > 1 ? seqs * n_seg * ((size_t)kStateElems + kHead) * sizeof(float) : 0;
+}
 // Synchronisation words for the fused path: a control line per sequence, then
 // one flag per segment.  They live in their own zero-initialised allocation;
 // flags only ever hold epoch numbers, so a flag can never be confused with

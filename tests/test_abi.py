@@ -48,9 +48,11 @@ def test_version_and_sizes():
     split = gla.GTR_PATH_SPLIT
     fused = gla.GTR_PATH_FUSED
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
-    # one-launch path: a 32-word header, a 32-word control line per sequence, a 64-bit flag per segment
+    # one-launch path: aggregates and decays (no entering states), then a 32-word header, a 32-word
+    # control line per sequence and a 64-bit flag per segment; a single segment needs no aggregates
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
-        6 * 25 * (2 * 4096 + 64) * 4 + (32 + 6 * (32 + 2 * 25)) * 4
+        6 * 25 * (4096 + 64) * 4 + (32 + 6 * (32 + 2 * 25)) * 4
+    assert gla.gtr_gla_workspace_bytes(1, 6, 8, 8, 64, 64, 1, 1, fused) == (32 + 6 * (32 + 2)) * 4
     # head dims: value columns in 64-wide blocks are sequences of their own, key blocks share one
     per = (2 * 4096 + 64) * 4
     assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 1, split) == 6 * 25 * per
