@@ -278,6 +278,29 @@ def test_maximum_grid():
     assert float(err) < 1e-4, float(err)
 
 
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_maximum_sequence_count(path):
+    """B*H = 2^20 sequences (1024 x 1024) of a 1x3 grid: a grid of 2^20 workgroups, and on the
+    one-launch path a control line per sequence; sampled sequences are checked against the oracle."""
+    B = H = 1024
+    gen = torch.Generator(device=DEV).manual_seed(17)
+    shape = (B, H, 1, 3, 64)
+    q = torch.randn(shape, generator=gen, device=DEV).half()
+    k = (torch.randn(shape, generator=gen, device=DEV) / 8).half()
+    v = torch.randn(shape, generator=gen, device=DEV).half()
+    g = (torch.nn.functional.logsigmoid(torch.randn(shape, generator=gen, device=DEV)) / 16).half()
+    assert gla.gtr_gla_plan(B, H, 1, 3, path=PATHS.get(path, 0))["fused"] == (path == "auto")
+    note(f"2^20 sequences path={path}")
+    y = gpu_run(q, k, v, g, 1, path=PATHS.get(path, 0))
+    gla.gtr_gla_stream_status()
+    rows = torch.tensor([0, 1, 511, 777, 1023])
+    part = [t[rows][:, rows].cpu() for t in (q, k, v, g)]  # 25 sequences spread over B and H
+    ref = oracle.gla_forward(*part, 1)
+    e = parity_errors(y[rows][:, rows].double().cpu().numpy(), ref, "f16")
+    assert e["ok"], e
+    assert bool(torch.isfinite(y).all())
+
+
 @pytest.mark.parametrize("grid", [(80, 81), (150, 128), (200, 200)], ids=lambda g: f"{g[0]}x{g[1]}")
 def test_long_boundary_scans(grid):
     """One-chunk segments on long sequences (102, 300 and 625 chunks): boundary scans of
