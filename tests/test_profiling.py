@@ -1,0 +1,66 @@
+"""The rocprofv3 summary tooling (recurrent_vision_backbone_chunkwise_amd.profiling) on synthetic
+rocprofv3 CSV files (CPU)."""
+import csv
+import json
+import subprocess
+import sys
+
+from recurrent_vision_backbone_chunkwise_amd import profiling
+from recurrent_vision_backbone_chunkwise_amd.build import ROOT, source_digest
+
+MANGLED = "_ZN3gtr12_GLOBAL__N_111gla_seg_outINS0_5IoF16EDF16_Li1EEEvNS0_6ParamsE"
+
+
+def write_counters(directory, counter, rows):
+    directory.mkdir(parents=True, exist_ok=True)
+    with open(directory / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for dispatch, name, value in rows:
+            w.writerow([dispatch, name, counter, value])
+
+
+def test_kernel_stats_and_summary(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"])
+        w.writerow([MANGLED, 4, 20000, 5000, 80.0, 4000, 6000])
+        w.writerow(["__amd_rocclr_copyBuffer", 2, 5000, 2500, 20.0, 2000, 3000])
+    rows = profiling.kernel_stats(str(d))
+    assert rows[0] == {"kernel": "gla_seg_out", "calls": 4, "avg_us": 5.0, "min_us": 4.0, "max_us": 6.0,
+                       "total_us": 20.0, "percent": 80.0}
+    out = tmp_path / "summary.txt"
+    cmd = f"rocprofv3 --kernel-trace --stats -- python3 {ROOT}/bench.py"
+    subprocess.run([sys.executable, "-m", "recurrent_vision_backbone_chunkwise_amd.profiling", "stats", str(d),
+                    "--command", cmd, "--title", "t", "--out", str(out)], check=True, capture_output=True,
+                   cwd=ROOT)
+    text = out.read_text()
+    assert "$REPO/bench.py" in text and ROOT + "/" not in text
+    assert f"# kernel sources: {source_digest()}" in text
+    assert text.index("gla_seg_out") < text.index("__amd_rocclr_copyBuffer")  # sorted by total time
+
+
+def test_traffic_scaled_by_the_copy(tmp_path):
+    # kernel: 2 dispatches of 3 and 5 KiB (two rows each for the first) fetched, 1 KiB written;
+    # the copy of 1 MiB reads 2048 KiB on FETCH_SIZE (scale 2) and 1024 KiB on WRITE_SIZE (scale 1)
+    write_counters(tmp_path / "f", "FETCH_SIZE", [(1, MANGLED, 1), (1, MANGLED, 2), (2, MANGLED, 5)])
+    write_counters(tmp_path / "w", "WRITE_SIZE", [(1, MANGLED, 1), (2, MANGLED, 1)])
+    write_counters(tmp_path / "cf", "FETCH_SIZE", [(1, "copy_kernel", 2048), (2, "small", 3)])
+    write_counters(tmp_path / "cw", "WRITE_SIZE", [(1, "copy_kernel", 1024)])
+    table = tmp_path / "traffic.json"
+    table.write_text(json.dumps([{"kernel": "gla_seg_out", "workload": "wl", "source": "old"},
+                                 {"kernel": "gla_seg_out", "workload": "other", "source": "keep"}]))
+    subprocess.run([sys.executable, "-m", "recurrent_vision_backbone_chunkwise_amd.profiling", "traffic",
+                    "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"),
+                    "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"),
+                    "--copy-bytes", str(1 << 20), "--workload", "wl", "--commands", "c", "--table", str(table)],
+                   check=True, capture_output=True, cwd=ROOT)
+    rows = json.loads(table.read_text())
+    assert [r["source"] for r in rows if r["workload"] == "other"] == ["keep"]
+    (row,) = [r for r in rows if r["workload"] == "wl"]
+    assert row["fetch_bytes_per_launch"] == 4 * 1024 / 2  # mean of 3 and 5 KiB, halved
+    assert row["write_bytes_per_launch"] == 1024
+    assert row["hbm_bytes_per_launch"] == 3072
+    assert row["source"] == source_digest() and row["copy_scale"]["fetch"] == 2.0
