@@ -20,6 +20,9 @@ import csv
 import glob
 import json
 import os
+import re
+import shutil
+import subprocess
 
 from .build import ROOT, source_digest
 
@@ -33,6 +36,76 @@ def short_name(mangled: str) -> str:
     return mangled if len(mangled) <= 60 else mangled[:57] + "..."
 
 
+# Library kernels whose instantiations a summary tells apart by their template arguments.
+LIBRARY_KERNELS = KERNELS + ("gla_bwd_dqk", "gla_dgate_totals", "gla_dgate_apply", "gla_ds0",
+                             "gla_state_copy", "swiglu_mix")
+
+
+def demangle(name: str) -> str:
+    """An Itanium-mangled name demangled with c++filt when it is installed and can (older ones
+    cannot read _Float16, DF16_); otherwise as given."""
+    if not name.startswith("_Z") or shutil.which("c++filt") is None:
+        return name
+    r = subprocess.run(["c++filt", name], capture_output=True, text=True)
+    out = r.stdout.strip() if r.returncode == 0 else ""
+    return out or name
+
+
+_MANGLED_ARGS = re.compile(
+    r"(?:NS0_6LaggedINS0_\d+(?P<lagged>IoF32|IoF16|IoBF16)EEE|NS0_\d+(?P<io>IoF32|IoF16|IoBF16)E)?"
+    r"(?P<types>(?:DF16_|f|t)*)(?:L(?P<kind>[ib])(?P<value>\d+)E)?E")
+_MANGLED_TYPES = {"DF16_": "_Float16", "f": "float", "t": "unsigned short"}
+
+
+def _mangled_args(name: str, kernel: str) -> str:
+    """Template arguments of one of this library's kernels read from its mangled name: the few
+    forms they take (an element format, possibly Lagged<>, then float/_Float16 types, then one
+    integer or boolean).  Empty for any other form."""
+    at = name.find(f"{len(kernel)}{kernel}I")
+    if at < 0:
+        return ""
+    m = _MANGLED_ARGS.match(name, at + len(str(len(kernel))) + len(kernel) + 1)
+    if not m:
+        return ""
+    args = []
+    if m.group("lagged"):
+        args.append(f"Lagged<{m.group('lagged')}>")
+    elif m.group("io"):
+        args.append(m.group("io"))
+    args += [_MANGLED_TYPES[t] for t in re.findall(r"DF16_|f|t", m.group("types"))]
+    if m.group("kind") == "i":
+        args.append(m.group("value"))
+    elif m.group("kind") == "b":
+        args.append("true" if m.group("value") == "1" else "false")
+    return ", ".join(args)
+
+
+def display_name(name: str) -> str:
+    """A library kernel's name with its template arguments, from a (de)mangled name such as
+    ``void gtr::(anonymous namespace)::gla_bwd_dqk<gtr::(anonymous namespace)::Lagged<...>, float,
+    true>(...)``; other kernels as short_name gives them."""
+    name = demangle(name)
+    if name.startswith("_Z"):
+        for k in LIBRARY_KERNELS:
+            if f"{len(k)}{k}" in name:
+                args = _mangled_args(name, k)
+                return f"{k}<{args}>" if args else k
+    for k in LIBRARY_KERNELS:
+        at = name.find(k + "<")
+        if at < 0:
+            if k + "(" in name or name == k:
+                return k
+            continue
+        depth, i = 0, at + len(k)
+        for j in range(i, len(name)):
+            depth += {"<": 1, ">": -1}.get(name[j], 0)
+            if depth == 0:
+                args = name[i + 1:j].replace("gtr::(anonymous namespace)::", "")
+                return f"{k}<{args}>"
+        break
+    return short_name(name)
+
+
 def _csvs(directory: str, suffix: str) -> list[str]:
     return sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
 
@@ -43,7 +116,7 @@ def kernel_stats(directory: str) -> list[dict]:
         with open(path) as f:
             for r in csv.DictReader(f):
                 rows.append({
-                    "kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                    "kernel": display_name(r["Name"]), "calls": int(r["Calls"]),
                     "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
                     "max_us": float(r["MaxNs"]) / 1e3, "total_us": float(r["TotalDurationNs"]) / 1e3,
                     "percent": float(r["Percentage"]),

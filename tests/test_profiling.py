@@ -29,7 +29,7 @@ def test_kernel_stats_and_summary(tmp_path):
         w.writerow([MANGLED, 4, 20000, 5000, 80.0, 4000, 6000])
         w.writerow(["__amd_rocclr_copyBuffer", 2, 5000, 2500, 20.0, 2000, 3000])
     rows = profiling.kernel_stats(str(d))
-    assert rows[0] == {"kernel": "gla_seg_out", "calls": 4, "avg_us": 5.0, "min_us": 4.0, "max_us": 6.0,
+    assert rows[0] == {"kernel": "gla_seg_out<IoF16, _Float16, 1>", "calls": 4, "avg_us": 5.0, "min_us": 4.0, "max_us": 6.0,
                        "total_us": 20.0, "percent": 80.0}
     out = tmp_path / "summary.txt"
     cmd = f"rocprofv3 --kernel-trace --stats -- python3 {ROOT}/bench.py"
@@ -40,6 +40,22 @@ def test_kernel_stats_and_summary(tmp_path):
     assert "$REPO/bench.py" in text and ROOT + "/" not in text
     assert f"# kernel sources: {source_digest()}" in text
     assert text.index("gla_seg_out") < text.index("__amd_rocclr_copyBuffer")  # sorted by total time
+
+
+def test_display_names_keep_template_arguments():
+    name = ("void gtr::(anonymous namespace)::gla_bwd_dqk<gtr::(anonymous namespace)::Lagged<gtr::(anonymous "
+            "namespace)::IoF16>, float, true>(gtr::(anonymous namespace)::Params, void*, float*, float const*, "
+            "void const*)")
+    assert profiling.display_name(name) == "gla_bwd_dqk<Lagged<IoF16>, float, true>"
+    assert profiling.display_name("gla_seg_out") == "gla_seg_out"
+    assert profiling.display_name("gtr::(anonymous namespace)::gla_dgate_totals(float const*, int)") == \
+        "gla_dgate_totals"
+    assert profiling.display_name(MANGLED) == "gla_seg_out<IoF16, _Float16, 1>"
+    assert profiling.display_name("_ZN3gtr12_GLOBAL__N_110swiglu_mixIDF16_DF16_EEvPKT0_PKT_S7_PS5_iiiiii") == \
+        "swiglu_mix<_Float16, _Float16>"
+    assert profiling.display_name(
+        "_ZN3gtr12_GLOBAL__N_111gla_bwd_dqkINS0_6LaggedINS0_5IoF32EEEfLb1EEEvNS0_6ParamsEPvPfPKfPKv") == \
+        "gla_bwd_dqk<Lagged<IoF32>, float, true>"
 
 
 def test_traffic_scaled_by_the_copy(tmp_path):
