@@ -65,10 +65,12 @@
  *     stream is being captured that query is skipped, so capture a call only
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
- *   - Two environment variables serve tests and measurement only:
- *     GTR_GLA_SKIP_POINTER_CHECKS=1 skips the device-pointer queries, and
+ *   - Three environment variables serve tests and measurement only:
+ *     GTR_GLA_SKIP_POINTER_CHECKS=1 skips the device-pointer queries,
  *     GTR_GLA_TEST_FAIL_ALLOC=1 makes every workspace allocation fail
- *     (GTR_ERR_ALLOC), which leaves the caches as they were.
+ *     (GTR_ERR_ALLOC), which leaves the caches as they were, and
+ *     GTR_GLA_FOLD_BLOCK=n (1..32) sets how many segments the one-launch path
+ *     groups into a fold block (results change only by rounding).
  *
  * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
  * case; the one-launch path takes d_k <= 64); 0 <= grid_h*grid_w <= 2^23 and
@@ -115,8 +117,8 @@ extern "C" {
 
 /* launch structure (entry points _ex, _check, _workspace_bytes, _plan) */
 #define GTR_PATH_AUTO 0   /* chosen by the library from the shape */
-#define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, flag-ordered combine, outputs;
-                             at most 768 chunks (49152 tokens) per sequence */
+#define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, a fixed-order fold within blocks of
+                             segments and a chain between blocks, outputs; d_k <= 64 */
 #define GTR_PATH_SPLIT 2  /* three kernels: segment aggregates, boundary scan, outputs */
 
 /* return codes: 0 on success, negative on error */
@@ -167,8 +169,9 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
  *   path     GTR_PATH_AUTO, GTR_PATH_FUSED or GTR_PATH_SPLIT.
  * Any segment length and path give the same result up to rounding; the same
  * shape, segment length and path give bitwise the same result on every call.
- * GTR_PATH_FUSED with more than 256 segments per sequence is refused
- * (GTR_ERR_INVALID_ARG): each segment folds every earlier one.
+ * GTR_PATH_FUSED keeps a 16,640-byte slot per segment of a sequence and
+ * refuses (GTR_ERR_INVALID_ARG) shapes whose slots exceed 2^31 bytes per
+ * sequence (more than 129055 segments).
  * The initial state makes a long scan splittable: running the two halves of
  * a sequence with the first half's s_final as the second half's s0 equals one
  * call on the whole sequence.
@@ -189,9 +192,22 @@ int gtr_gla_check(const void *q, const void *k, const void *v, const void *log_g
                   int direction, int dtype, const float *s0, float *s_final,
                   int chunks_per_segment, int path);
 
-/* Workspace bytes a call of this shape uses (0 on invalid arguments). */
+/*
+ * Device memory the library keeps for a call of this shape, in bytes: the
+ * per-(device, stream) workspace of boundary states and synchronisation
+ * words that gtr_gla_fwd (and the typed entry points) would use.  The state
+ * itself does not grow with the token count, but intermediate working memory
+ * of the scan still does (x-techcon article on GTR, section 架构 /
+ * Architecture, on memory beyond the fixed-size state).  Arguments as for
+ * gtr_gla_fwd.  Returns 0 on invalid arguments and for calls that need no
+ * workspace.  Host-only: touches no device.
+ */
 size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
-                               int dtype, int chunks_per_segment, int path);
+                               int dtype);
+
+/* The same for a call of gtr_gla_fwd_ex with this segment length and path. */
+size_t gtr_gla_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                                  int dtype, int chunks_per_segment, int path);
 
 /* The plan the library uses for a shape: chunks per segment, segments per
  * sequence, and 1 if one fused kernel runs (0: three kernels).  The kernels

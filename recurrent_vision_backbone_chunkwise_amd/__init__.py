@@ -31,7 +31,8 @@ DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
 
 # Every symbol include/gtr_gla.h and include/gtr_swiglu.h declare.
 EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
-           "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes", "gtr_gla_plan",
+           "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes",
+           "gtr_gla_workspace_bytes_ex", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
            "gtr_gla_profile_begin", "gtr_gla_profile_end", "gtr_gla_kernel_name",
            "gtr_gla_stream_status", "gtr_gla_bwd", "gtr_swiglu_fwd", "gtr_swiglu_workspace_bytes")
@@ -68,8 +69,10 @@ def lib() -> ctypes.CDLL:
     for name in ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
                  "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version", "gtr_gla_plan"):
         getattr(L, name).restype = ctypes.c_int
-    L.gtr_gla_workspace_bytes.argtypes = [i] * 9
+    L.gtr_gla_workspace_bytes.argtypes = [i] * 7
     L.gtr_gla_workspace_bytes.restype = ctypes.c_size_t
+    L.gtr_gla_workspace_bytes_ex.argtypes = [i] * 9
+    L.gtr_gla_workspace_bytes_ex.restype = ctypes.c_size_t
     L.gtr_gla_last_error.argtypes = []
     L.gtr_gla_last_error.restype = ctypes.c_char_p
     L.gtr_gla_release_workspaces.argtypes = []
@@ -106,10 +109,14 @@ def gtr_gla_version() -> int:
     return lib().gtr_gla_version()
 
 
-def gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYPE_F16,
-                            chunks_per_segment=0, path=GTR_PATH_AUTO) -> int:
-    return lib().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, dtype, chunks_per_segment,
-                                         path)
+def gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYPE_F16) -> int:
+    return lib().gtr_gla_workspace_bytes(B, H, grid_h, grid_w, d_k, d_v, dtype)
+
+
+def gtr_gla_workspace_bytes_ex(B, H, grid_h, grid_w, d_k=64, d_v=64, dtype=GTR_DTYPE_F16,
+                               chunks_per_segment=0, path=GTR_PATH_AUTO) -> int:
+    return lib().gtr_gla_workspace_bytes_ex(B, H, grid_h, grid_w, d_k, d_v, dtype,
+                                            chunks_per_segment, path)
 
 
 def gtr_gla_plan(B, H, grid_h, grid_w, chunks_per_segment=0, path=GTR_PATH_AUTO, d_k=64,

@@ -53,34 +53,44 @@ struct Shape {
   long long seqs;  // sequences the kernels walk: B*H*nvb
   int n_chunk, seg_len, n_seg;
   bool fused;
-  bool empty;  // B*H == 0 or no tokens: nothing to compute
+  int fold_block;  // one-launch path: segments per fold block
+  bool empty;      // B*H == 0 or no tokens: nothing to compute
 };
 
-// Chunks per segment and launch structure for a shape.
+// Launch structure and segment length for a shape.
 //  * split: the length split_segment_length picks; the boundary scan runs in
 //    its own kernel.
 //  * fused: segments of at most kMaxFusedChunks chunks (each chunk's outputs
-//    wait in registers for the state entering the segment); every segment
-//    reads the aggregates of all earlier segments of its sequence.
+//    wait in registers for the state entering the segment), grouped in blocks
+//    of kFoldBlock segments.  Measured on MI355X (3-chunk segments, fp16, four
+//    directions): blocks of 4, 8, 16 and 32 took 342, 338, 383 and 433 us per
+//    128x128 B1 H16 round; folds cost more than the chain between blocks.
 // Automatic choice (measured on MI355X): the fused launch wins for short
-// sequences (at most kAutoFusedChunks chunks, so each segment folds few
-// predecessors) when there are enough of them to fill the chip with
-// 3-chunk segments; otherwise three launches.
+// sequences (at most kAutoFusedChunks chunks) when there are enough of them
+// to fill the chip with 3-chunk segments (40x40 B8 H6: 125 us per round
+// against 145 us split); otherwise three launches (40x40 B1 H6: 60 against
+// 73 us; 64x64 B1 H16: 59 against 64 us; 128x128 B1 H16: 281 against 338 us).
+constexpr int kFoldBlock = 8;
 constexpr int kAutoFusedChunks = 32;
 constexpr long long kAutoFusedMinGroups = 256;
+constexpr int kAssumedXcds = 8;  // MI355X; used where no device is queried
+
+bool auto_fused(long long seqs, int nk, int n_chunk) {
+  const long long groups = seqs * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
+  return nk == 1 && n_chunk <= kAutoFusedChunks && groups >= kAutoFusedMinGroups;
+}
 
 // `bh` counts the sequences the kernels walk (B*H*value blocks); `nk` the key
 // blocks, which only the three-launch path handles beyond one.
 void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
+  sh->fold_block = 0;
   if (bh == 0 || n_chunk == 0) {
     sh->fused = false;
     sh->seg_len = sh->n_seg = 0;
     return;
   }
-  const long long fused_groups = bh * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
   sh->fused = path == GTR_PATH_FUSED ||
-              (path == GTR_PATH_AUTO && nk == 1 && n_chunk <= kAutoFusedChunks &&
-               fused_groups >= kAutoFusedMinGroups && chunks_per_segment <= gtr::kMaxFusedChunks);
+              (path == GTR_PATH_AUTO && chunks_per_segment <= gtr::kMaxFusedChunks && auto_fused(bh, nk, n_chunk));
   long long len = chunks_per_segment;
   if (sh->fused) {
     if (len <= 0) len = gtr::kMaxFusedChunks;
@@ -91,6 +101,15 @@ void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, S
   if (len > n_chunk) len = n_chunk;
   sh->seg_len = (int)len;
   sh->n_seg = (int)((n_chunk + len - 1) / len);
+  if (sh->fused) {
+    sh->fold_block = std::min(sh->n_seg, kFoldBlock);
+    // measurement aid: GTR_GLA_FOLD_BLOCK=n sets the fold block size (1..32)
+    static const int forced = [] {
+      const char *e = std::getenv("GTR_GLA_FOLD_BLOCK");
+      return e ? std::atoi(e) : 0;
+    }();
+    if (forced >= 1 && forced <= gtr::kMaxFoldBlock) sh->fold_block = std::min(forced, sh->n_seg);
+  }
 }
 
 // Shape, direction and dtype checks; fills `shape`.
@@ -130,11 +149,12 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
   plan(shape->seqs, shape->nk, shape->n_chunk, path, chunks_per_segment, shape);
   if (shape->seqs * shape->n_seg * shape->nk > 0x7fffffffLL)
     return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", shape->seqs * shape->n_seg);
-  if (shape->fused && shape->n_seg > gtr::kMaxFusedSegments)
+  // a sequence's payload slots are addressed with 32-bit byte offsets
+  if (shape->fused && (long long)shape->n_seg * gtr::kSlotFloats * (long long)sizeof(float) >= (1LL << 31))
     return fail(GTR_ERR_INVALID_ARG,
-                "one-launch path: %d segments exceed %d (at most %d chunks per sequence); use "
-                "GTR_PATH_SPLIT or GTR_PATH_AUTO",
-                shape->n_seg, gtr::kMaxFusedSegments, gtr::kMaxFusedSegments * gtr::kMaxFusedChunks);
+                "one-launch path: %d segments of %d chunks exceed its per-sequence workspace; use longer "
+                "segments, GTR_PATH_SPLIT or GTR_PATH_AUTO",
+                shape->n_seg, shape->seg_len);
   return GTR_OK;
 }
 
@@ -196,15 +216,15 @@ int check_device_range(const void *p, size_t bytes, int device, const char *name
   return GTR_OK;
 }
 
-// Fused-path synchronisation words live at positions fixed by the allocation's
-// capacities, never by a call's shape: [header][cap_seqs control lines]
-// [cap_flags flags].  Control lines return to zero after every call and flags
-// only hold epochs, so any shape can follow any other on the same workspace.
+// Fused-path synchronisation words live at positions that do not depend on a
+// call's shape: [header][per-XCD work words][cap_flags flags].  The header and
+// work words return to zero (the epoch aside) after every call and flags only
+// hold epochs, so any shape can follow any other on the same workspace.
 struct Workspace {
   void *data = nullptr;  // float32 aggregates and boundary states
   size_t data_bytes = 0;
   int *sync = nullptr;   // zero-initialised
-  size_t cap_seqs = 0, cap_flags = 0;
+  size_t cap_flags = 0;
 };
 
 // Guards the workspaces, the other cached buffers and the retired list.
@@ -231,17 +251,17 @@ hipError_t workspace_malloc(void **p, size_t bytes) {
   return hipMalloc(p, bytes);
 }
 
-int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, size_t flags,
+// `need_sync`: the call uses the synchronisation words, with `flags` flags.
+int get_workspace(int device, hipStream_t stream, size_t bytes, bool need_sync, size_t flags,
                   void **data, int **sync, long long **flag_words) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace &ws = g_ws[{device, stream}];
-  const bool sync_ok = (seqs == 0 && flags == 0) || (ws.cap_seqs >= seqs && ws.cap_flags >= flags);
+  const bool sync_ok = !need_sync || (ws.sync && ws.cap_flags >= flags);
   auto hand_out = [&] {
     *data = ws.data;
     *sync = ws.sync;
-    // 64-bit flags after the control lines (an even word offset: 8-byte aligned)
-    *flag_words = ws.sync ? reinterpret_cast<long long *>(ws.sync + gtr::kSyncHeader + ws.cap_seqs * gtr::kCtlStride)
-                          : nullptr;
+    // 64-bit flags after the work words (an even word offset: 8-byte aligned)
+    *flag_words = ws.sync ? reinterpret_cast<long long *>(ws.sync + gtr::kSyncFlagWord) : nullptr;
   };
   if (ws.data_bytes >= bytes && sync_ok) {
     hand_out();
@@ -254,9 +274,9 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
   }
   if (cs != hipStreamCaptureStatusNone)
     return fail(GTR_ERR_CAPTURE,
-                "workspace must grow (%zu -> %zu bytes, %zu -> %zu sequences, %zu -> %zu flags) "
+                "workspace must grow (%zu -> %zu bytes, %zu -> %zu flags) "
                 "while the stream is being captured; make one call of this shape before capturing",
-                ws.data_bytes, bytes, ws.cap_seqs, seqs, ws.cap_flags, flags);
+                ws.data_bytes, bytes, ws.cap_flags, flags);
   // Kernels queued earlier, and graphs captured earlier, may still use the
   // old buffers: they are retired, not freed.
   // A failed allocation leaves the cached buffers as they were.
@@ -272,9 +292,8 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
     ws.data_bytes = want;
   }
   if (!sync_ok) {
-    const size_t seq_cap = std::max(ws.cap_seqs, seqs + seqs / 4);
     const size_t flag_cap = std::max(ws.cap_flags, flags + flags / 4);
-    const size_t words = gtr::kSyncHeader + seq_cap * gtr::kCtlStride + 2 * flag_cap;
+    const size_t words = gtr::sync_words(flag_cap);
     void *p = nullptr;
     if (workspace_malloc(&p, words * sizeof(int)) != hipSuccess) {
       (void)hipGetLastError();
@@ -288,11 +307,32 @@ int get_workspace(int device, hipStream_t stream, size_t bytes, size_t seqs, siz
     }
     retire(device, ws.sync);
     ws.sync = static_cast<int *>(p);
-    ws.cap_seqs = seq_cap;
     ws.cap_flags = flag_cap;
   }
   hand_out();
   return GTR_OK;
+}
+
+// CU and XCD counts of a device, queried once (MI355X: 256 and 8).  They size
+// the one-launch path's persistent grid and its sequence batches.
+struct DeviceShape {
+  int cus = 256, xcds = kAssumedXcds;
+};
+constexpr long long kMaxBatch = 16;  // sequences an XCD claims at a time
+
+const DeviceShape &device_shape(int device) {
+  static std::mutex m;
+  static std::map<int, DeviceShape> cache;
+  std::lock_guard<std::mutex> lock(m);
+  auto it = cache.find(device);
+  if (it != cache.end()) return it->second;
+  DeviceShape d;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && v > 0) d.cus = v;
+  else (void)hipGetLastError();
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, device) == hipSuccess && v > 0) d.xcds = v;
+  else (void)hipGetLastError();
+  return cache.emplace(device, d).first->second;
 }
 
 bool skip_pointer_checks() {
@@ -495,16 +535,24 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
     long long *flags = nullptr;
     const size_t bytes = sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg)
                                   : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk);
-    rc = get_workspace(device, stream, bytes, sh.fused ? sh.seqs : 0, sh.fused ? sh.seqs * sh.n_seg : 0, &ws,
-                       &sync, &flags);
+    rc = get_workspace(device, stream, bytes, sh.fused, sh.fused ? sh.seqs * sh.n_seg : 0, &ws, &sync, &flags);
     if (rc != GTR_OK) return rc;
     float *f = static_cast<float *>(ws);
     const size_t st = (size_t)sh.seqs * sh.n_seg * sh.nk * gtr::kStateElems;
     a.agg = f;
     a.prev = sh.fused ? nullptr : f + st;  // the one-launch path keeps no entering states
-    a.agg_dec = f + (sh.fused ? 1 : 2) * st;
+    a.agg_dec = sh.fused ? nullptr : f + 2 * st;  // (its decays sit in each segment's payload slot)
     a.sync = sync;
     a.flags = flags;
+  }
+  if (sh.fused) {
+    const DeviceShape &ds = device_shape(device);
+    const int occupancy = dtype == GTR_DTYPE_F32 ? 1 : (sh.seg_len == 1 ? 3 : 2);
+    a.fold_block = sh.fold_block;
+    a.xcds = ds.xcds;
+    a.batch = (int)std::min<long long>(kMaxBatch, (sh.seqs + ds.xcds - 1) / ds.xcds);
+    const long long per_xcd = (long long)a.batch * sh.n_seg;
+    a.grid = (int)std::max<long long>(1, std::min<long long>((long long)occupancy * ds.cus, per_xcd * ds.xcds));
   }
   const int err = gtr::launch_gla(a);
   if (err != (int)hipSuccess)
@@ -540,15 +588,19 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
                      GTR_DTYPE_BF16, stream);
 }
 
-size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dtype,
-                               int chunks_per_segment, int path) {
+size_t gtr_gla_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dtype,
+                                  int chunks_per_segment, int path) {
   Shape sh;
   if (validate_shape(B, H, grid_h, grid_w, d_k, d_v, 0, dtype, chunks_per_segment, path, &sh) !=
       GTR_OK)
     return 0;
   if (sh.empty) return 0;
   return (sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg) : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk)) +
-         (sh.fused ? gtr::sync_words(sh.seqs, sh.n_seg) * sizeof(int) : 0);
+         (sh.fused ? gtr::sync_words((size_t)(sh.seqs * sh.n_seg)) * sizeof(int) : 0);
+}
+
+size_t gtr_gla_workspace_bytes(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int dtype) {
+  return gtr_gla_workspace_bytes_ex(B, H, grid_h, grid_w, d_k, d_v, dtype, 0, GTR_PATH_AUTO);
 }
 
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,

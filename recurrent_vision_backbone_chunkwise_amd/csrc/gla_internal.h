@@ -11,10 +11,10 @@ constexpr int kChunk = 64;   // tokens per chunk (the pages' operator uses 64)
 constexpr int kHead = 64;    // width of a key or value block (d_k, d_v <= 2 blocks)
 constexpr int kStateElems = kHead * kHead;
 constexpr int kMaxFusedChunks = 3;  // chunks per segment of the one-launch path (outputs held in registers)
-// Segments per sequence of the one-launch path.  Every segment folds the
-// aggregates of all earlier ones in a fixed order (so results do not depend on
-// timing), which costs O(segments^2) cache reads per sequence.
-constexpr int kMaxFusedSegments = 256;
+// One-launch path: segments are grouped in blocks of at most this many; each
+// segment folds the aggregates of the earlier segments of its block.
+constexpr int kMaxFoldBlock = 32;
+constexpr int kSlotFloats = kStateElems + kHead;  // one segment's payload: a state and 64 decays
 
 struct LaunchArgs {
   const void *q, *k, *v, *g;
@@ -33,8 +33,12 @@ struct LaunchArgs {
   float *agg;        // [seq][n_seg][nk][4096] segment state contributions
   float *agg_dec;    // [seq][n_seg][nk][64]   segment decay factor per key dim
   float *prev;       // [seq][n_seg][nk][4096] state entering each segment
-  int *sync;         // fused path: header + per-sequence control lines (zeroed at allocation)
-  long long *flags;  // [bh][n_seg] fused path: aggregate-published flags (64-bit epochs), after the control lines
+  int *sync;         // fused path: header + per-XCD work words (zeroed at allocation)
+  long long *flags;  // [bh][n_seg] fused path: payload-published flags (64-bit epochs), after the work words
+  int fold_block;    // fused path: segments per fold block
+  int batch;         // fused path: sequences an XCD claims at a time
+  int grid;          // fused path: persistent workgroups
+  int xcds;          // fused path: XCDs of the device (their L2s are not coherent with each other)
   const float *s0;   // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;    // user final state, row-major [B*H][d_k][d_v], nullable
   bool fused;        // one launch (gla_fused) instead of three
@@ -67,25 +71,31 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
-constexpr int kSyncHeader = 32;  // fused-path header words (epoch, sequences done, error)
-// The epoch is a 64-bit count in words 0 and 1, so it never wraps.
-constexpr int kSyncEpochWord = 0, kSyncSeqDoneWord = 2, kSyncErrorWord = 3;
-constexpr int kCtlStride = 32;   // one 128-byte control line per sequence (ticket, done)
+// Synchronisation words of the one-launch path (32-bit words of one zeroed
+// allocation): a header (64-bit epoch in words 0-1, error word, count of
+// workgroups that found no work left, next batch to hand out, mask of XCDs
+// that have begun their starting batch), one 64-bit work
+// word per XCD on its own 128-byte line (XCC_ID has 4 bits: 16 lines), then
+// one 64-bit flag per segment.  Their positions do not depend on the shape.
+constexpr int kSyncHeader = 32;
+constexpr int kSyncEpochWord = 0, kSyncErrorWord = 3, kSyncExitedWord = 4, kSyncNextBatchWord = 5,
+              kSyncStartedWord = 6;
+constexpr int kXcdSlots = 16;
+constexpr int kSlotStride = 32;
+constexpr int kSyncSlotWord = kSyncHeader;
+constexpr int kSyncFlagWord = kSyncHeader + kXcdSlots * kSlotStride;
 
 // Float workspace bytes for (sequences, n_seg, key blocks): agg, prev and agg_dec.
 inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
   return seqs * n_seg * nk * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
-// Float workspace bytes of the one-launch path: aggregates and decays only (it
-// keeps no entering states), and none for a single segment (nothing to pass on).
+// Float workspace bytes of the one-launch path: one payload slot per segment
+// (aggregate or block prefix, and decays), none for a single segment.
 inline size_t fused_workspace_bytes(size_t seqs, size_t n_seg) {
-  return n_seg > 1 ? seqs * n_seg * ((size_t)kStateElems + kHead) * sizeof(float) : 0;
+  return n_seg > 1 ? seqs * n_seg * (size_t)kSlotFloats * sizeof(float) : 0;
 }
-// Synchronisation words for the fused path: a control line per sequence, then
-// one flag per segment.  They live in their own zero-initialised allocation;
-// flags only ever hold epoch numbers, so a flag can never be confused with
-// left-over data.
-inline size_t sync_words(size_t bh, size_t n_seg) { return kSyncHeader + bh * (kCtlStride + 2 * n_seg); }
+// Synchronisation words for `n_flags` segment flags.
+inline size_t sync_words(size_t n_flags) { return kSyncFlagWord + 2 * n_flags; }
 
 // Host helpers shared by the entry points (defined in gla_api.cpp): record an
 // error message for gtr_gla_last_error() and return `code`; clear it; check a

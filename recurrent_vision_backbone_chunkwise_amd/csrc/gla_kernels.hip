@@ -406,19 +406,12 @@ struct Params {
   int prev_seq, prev_step;  // prev entries per sequence, and between consecutive segments
   const float *s0;         // user initial state, row-major [B*H][d_k][d_v], nullable
   float *s_final;          // user final state, row-major, nullable
-  int *sync;               // fused path: header, per-sequence control lines (kSync* words)
-  long long *flags;        // [bh][n_seg] fused path: segment aggregate published (epoch + 1)
+  int *sync;               // fused path: header and per-XCD work words (kSync* words)
+  long long *flags;        // [bh][n_seg] fused path: segment payload published (epoch + 1)
+  int fold_block;          // fused path: segments per fold block
+  int batch, n_batch;      // fused path: sequences per batch an XCD takes, and batches
+  int n_pre;               // fused path: batches 0 .. n_pre-1 start out assigned to XCDs 0 .. n_pre-1
 };
-
-// Fused-path synchronisation words.  Header: the epoch (number of completed
-// fused calls on this workspace, 64-bit so that it never wraps), the count of
-// sequences finished in the current call, and an error word (-1 after a wait
-// gave up).  Per sequence: its
-// ticket and done counters.  After every call all words other than the epoch
-// and the flags are back at 0 (or -1); flags hold epochs, all below the next
-// call's epoch + 1, whatever shape wrote them.
-enum : int { kSyncEpoch = kSyncEpochWord, kSyncSeqDone = kSyncSeqDoneWord, kSyncError = kSyncErrorWord };
-enum : int { kCtlTicket = 0, kCtlDone = 1 };
 
 template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int seq) {
   using T = typename Io::T;
@@ -1015,230 +1008,415 @@ __global__ __launch_bounds__(kThreads) void gla_seg_scan(Params p) {
   if (p.s_final && user >= 0) p.s_final[user] = s;
 }
 
-// Publication between workgroups, which may sit on different XCDs whose L2
-// caches are not kept coherent with each other.  Every word that crosses
-// workgroups (aggregate, decay, flag) is written and read with agent-scope
-// atomic accesses, which the compiler emits as device-scope (sc1) stores and
-// loads: a store completes only once it is visible at device scope, and a
-// load never returns a copy that is stale at that scope.  The producer waits
-// for its payload stores to complete (vmcnt), the workgroup synchronises, and
-// then one thread stores the flag; the consumer issues its payload loads only
-// after it has read the flag.  No cache-wide writeback or invalidation is
-// needed, as it would be for plain stores and loads behind release/acquire
-// fences.
-__device__ __forceinline__ void store_shared(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ------------------------------------------------------------ one-launch path
+//
+// The caller's fp32 state of sequence `bh` (s0 or s_final, row-major
+// [B*H][d_k][d_v]) as a buffer resource, and the byte offset of this thread's
+// element (row i, column 16 wave + lane%16 of the value block), or -1 (out of
+// range: reads 0, stores dropped) past d_k or d_v.  The head dims pass through
+// an empty asm statement, so these offsets are formed where they are used, not
+// hoisted out of the workgroup's loop and held (spilled) across every segment.
+struct UserState {
+  __amdgpu_buffer_rsrc_t r;
+  int dk, dv, j;
+};
+__device__ __forceinline__ UserState user_state(const Params &p, const float *base, int bh, int wave, int lane) {
+  int dk = p.dk, dv = p.dv;
+  asm volatile("" : "+s"(dk), "+s"(dv));
+  const int bhh = bh / p.nvb, j = kHead * (bh - bhh * p.nvb) + 16 * wave + (lane & 15);
+  return UserState{__builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base) + (size_t)bhh * dk * dv, (short)0,
+                                                     dk * dv * (int)sizeof(float), 0x00020000),
+                   dk, dv, j};
 }
-__device__ __forceinline__ float load_shared(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int user_state_off(const UserState &u, int i) {
+  return (i < u.dk && u.j < u.dv) ? (i * u.dv + u.j) * (int)sizeof(float) : -1;
 }
+
+//
+// Exchange between workgroups.  All segments of a sequence are processed on
+// one XCD (take_work), so the aggregates, block prefixes and flags that pass
+// between them go through that XCD's L2 and never cross the fabric: the
+// producer writes a payload with plain stores, waits until they have completed
+// (they are then in L2), synchronises the workgroup, and one thread stores the
+// segment's flag; consumers poll the flag and read payloads with non-temporal
+// loads, which do not hit in the CU's L1 and are served by L2.  Measured on
+// MI355X: no stale read in 256000 reads within an XCD.  Plain loads there hit
+// stale L1 lines, and across XCDs the L2s are not coherent with each other:
+// that is why a sequence never spans two XCDs.  Flags only ever hold epochs
+// and grow from call to call, so a stale copy can never pass for a fresh one.
+constexpr int kNonTemporal = 2;  // buffer-access cache policy: nt
+
+// XCC_ID (hardware register 20, bits 3:0): the XCD this wave runs on.  Waves
+// with equal ids share one L2.
+__device__ __forceinline__ int xcc_slot() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcdSlots - 1));
+}
+
+// A sequence's segment flags as a buffer resource (8 bytes per segment).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flag_rsrc(const Params &p, int bh) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.flags + (size_t)bh * p.n_seg, (short)0, p.n_seg * 8, 0x00020000);
+}
+__device__ __forceinline__ long long read_flag(__amdgpu_buffer_rsrc_t f, int s) {
+  return __builtin_bit_cast(long long, __builtin_amdgcn_raw_buffer_load_b64(f, s * 8, 0, kNonTemporal));
+}
+
+// Bounded wait until segment s's flag reaches `want`.  A wait that gives up
+// records -1 in the error word and returns false.
+__device__ __forceinline__ bool wait_flag(int *sync, __amdgpu_buffer_rsrc_t f, int s, long long want) {
+  for (int spins = 0; read_flag(f, s) < want; ++spins) {
+    if (spins > kSpinLimit) {
+      __hip_atomic_store(sync + kSyncErrorWord, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
 // Waits until this wave's stores have completed.
 __device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Bounded wait until a flag reaches at least `want`; returns the value seen
-// and records a timeout in the error word.
-__device__ __forceinline__ long long wait_flag(int *sync, const long long *f, long long want) {
-  int spins = 0;
-  for (;;) {
-    const long long v = __hip_atomic_load(const_cast<long long *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v >= want) return v;
-    __builtin_amdgcn_s_sleep(2);
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(sync + kSyncError, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return v;
+// Work of one XCD.  Sequences are handed out in batches of p.batch.  XCD x
+// starts with batch x (x < p.n_pre); later batches come from a counter shared
+// by all XCDs.  The workgroups of an XCD take tickets t = 0, 1, ... of its
+// current batch, ticket t being segment t / k of the batch's sequence t % k
+// (k sequences in the batch).  Tickets follow scan order within each sequence,
+// so every segment a workgroup waits for holds a smaller ticket, taken by a
+// running workgroup of the same XCD (which is why a workgroup may leave while
+// another one of its XCD still has work: no ticket waits on a later one).  The XCD's 64-bit work word holds
+// (tag << 32) + next ticket, the tag being 0 (the starting batch, or none),
+// batch + 1, kStolen or kBatchDone.  The workgroup whose ticket is the first
+// past the end of its batch takes the next batch and keeps its ticket 0;
+// workgroups past it wait until it has.  When the counter runs out, that
+// workgroup takes over the starting batch of an XCD whose work word no
+// workgroup has touched yet (changing it to kStolen, so that XCD's workgroups
+// take no ticket of it), which covers an XCD that never runs a workgroup of
+// this launch.
+constexpr unsigned kBatchDone = 0xffffffffu, kStolen = 0xfffffffeu;
+__device__ __forceinline__ unsigned long long *work_word(const Params &p, int slot) {
+  return reinterpret_cast<unsigned long long *>(p.sync + kSyncSlotWord + slot * kSlotStride);
+}
+// Takes the next ticket of the XCD's batch: the returned word, read by take_work.
+__device__ __forceinline__ unsigned long long work_add(const Params &p, int slot) {
+  return __hip_atomic_fetch_add(work_word(p, slot), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Turns the word a work_add returned into a segment: writes the sequence and
+// segment to out[0], out[1] (out[0] = -1: no work left).
+__device__ void take_work(const Params &p, int slot, unsigned long long v, int *out) {
+  unsigned long long *word = work_word(p, slot);
+  auto start = [&](int b) {  // this workgroup starts batch b with ticket 0
+    __hip_atomic_store(word, ((unsigned long long)b + 1ull) << 32 | 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    out[0] = b * p.batch;
+    out[1] = 0;
+  };
+  for (int spins = 0;; v = work_add(p, slot)) {
+    const unsigned tag = (unsigned)(v >> 32), t = (unsigned)v;
+    if (tag == kBatchDone) {
+      out[0] = -1;
+      return;
+    }
+    const int b = tag == 0 ? (slot < p.n_pre ? slot : -1) : (tag == kStolen ? -1 : (int)tag - 1);
+    const int first = b * p.batch, k = b < 0 ? 0 : min(p.batch, p.bh_count - first);
+    const unsigned n_in = (unsigned)k * (unsigned)p.n_seg;
+    if (t < n_in) {
+      if (tag == 0 && t == 0)  // this XCD has begun its starting batch
+        __hip_atomic_fetch_or(p.sync + kSyncStartedWord, 1 << slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      out[0] = first + (int)(t % (unsigned)k);
+      out[1] = (int)(t / (unsigned)k);
+      return;
+    }
+    if (t == n_in) {  // the next batch for this XCD (none beyond the starting ones: no counter)
+      const int nb = p.n_pre >= p.n_batch ? p.n_batch
+                                          : p.n_pre + __hip_atomic_fetch_add(p.sync + kSyncNextBatchWord, 1,
+                                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (nb < p.n_batch) {
+        start(nb);
+        return;
+      }
+      // none left: a starting batch that its XCD has not begun (the started
+      // mask only saves compare-exchanges; the exchange itself decides)
+      const unsigned started =
+          (unsigned)__hip_atomic_load(p.sync + kSyncStartedWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int y = 0; y < p.n_pre; ++y) {
+        unsigned long long zero = 0;
+        if (y != slot && !(started >> y & 1u) &&
+            __hip_atomic_compare_exchange_strong(work_word(p, y), &zero, (unsigned long long)kStolen << 32,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          start(y);
+          return;
+        }
+      }
+      __hip_atomic_store(word, (unsigned long long)kBatchDone << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      out[0] = -1;
+      return;
+    }
+    // Another workgroup of this XCD is taking the next batch.  With no batch
+    // beyond the starting ones, it can only take over a starting batch that
+    // another XCD never began, and works through that alone: leave now.
+    if (p.n_pre >= p.n_batch) {
+      out[0] = -1;
+      return;
+    }
+    while ((unsigned)(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == tag) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(p.sync + kSyncErrorWord, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        out[0] = -1;
+        return;
+      }
     }
   }
+}
+
+// A sequence's payload slots: per segment, a 64x64 fp32 state (the segment's
+// aggregate, or for a block's last segment the block prefix) in f4 register
+// order, then the segment's 64 decays.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const Params &p, int bh) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.agg + (size_t)bh * p.n_seg * kSlotFloats, (short)0,
+                                           p.n_seg * kSlotFloats * (int)sizeof(float), 0x00020000);
+}
+// Byte offsets: f4 `it` of thread (wave, lane) of segment s's state (rows
+// 16 it + 4(lane/16) + 0..3, column 16 wave + lane%16), and decay `row`.
+__device__ __forceinline__ int slot_state_off(int s, int wave, int it, int lane) {
+  return (s * kSlotFloats + ((wave * 4 + it) * 64 + lane) * 4) * (int)sizeof(float);
+}
+__device__ __forceinline__ int slot_decay_off(int s, int row) {
+  return (s * kSlotFloats + kStateElems + row) * (int)sizeof(float);
+}
+__device__ __forceinline__ f4 slot_load(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
+__device__ __forceinline__ void slot_store(__amdgpu_buffer_rsrc_t r, int off, f4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+}
+
+// Writes state X (and, kDecay, the decays `dec` held by wave 0, lanes < 16)
+// to segment s's slot, then raises its flag.  Every thread of the workgroup
+// calls it.
+template <bool kDecay>
+__device__ __forceinline__ void publish(const Params &p, __amdgpu_buffer_rsrc_t r, int bh, int s, int tid,
+                                        const f4 *X, f4 dec, long long want) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) slot_store(r, slot_state_off(s, wave, it, lane), X[it]);
+  if (kDecay && wave == 0 && lane < 16) slot_store(r, slot_decay_off(s, 4 * lane), dec);
+  stores_complete();  // this wave's payload is in L2 ...
+  __syncthreads();    // ... for every wave ...
+  if (tid == 0)       // ... before the flag is raised
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, want), flag_rsrc(p, bh), s * 8, 0, 0);
 }
 
 // Workgroups per CU the LDS allows: fp32 operands take 100-137 KB, one;
 // 16-bit ones 54 KB for one-chunk segments, three, and up to 73 KB, two.
 template <typename Op, int kSeg> constexpr int kFusedOccupancy = sizeof(Op) == 4 ? 1 : (kSeg == 1 ? 3 : 2);
 
-// One launch, one walk.  A workgroup takes a segment (at most kSeg chunks) in
-// start order and:
+// One launch.  A persistent grid; each workgroup repeatedly takes a segment
+// (at most kSeg chunks) of a sequence of its XCD and:
 //   1. walks it from a zero state, keeping each chunk's outputs in registers
 //      (intra-segment part: scores plus the state carried inside the segment)
 //      and ending with the segment's own aggregate A and decay D;
-//   2. publishes (A, D) for the segments after it;
-//   3. combines s0 and the aggregates of the segments before it into S_prev,
-//      the state entering the segment;
-//   4. adds each chunk's share of S_prev, (q 2^E * Dcum) S_prev with Dcum the
+//   2. publishes (A, D) for the later segments of its block (segments are
+//      grouped in blocks of p.fold_block);
+//   3. forms S_prev, the state entering the segment, by folding in a fixed
+//      order the aggregates of the earlier segments of its block and the
+//      entering term: the prefix published by the previous block's last
+//      segment, or s0 in the first block;
+//   4. if it is a block's last segment, publishes that block's prefix
+//      D S_prev + A; the sequence's last segment writes it as s_final;
+//   5. adds each chunk's share of S_prev, (q 2^E * Dcum) S_prev with Dcum the
 //      decay from the segment start to the chunk, and stores the outputs.
-// Inputs are read from HBM once.
+// Inputs are read from HBM once.  The fold order depends only on the shape,
+// so a call gives bitwise the same result however its workgroups run.
 template <class Io, typename Op, int kSeg>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     kFusedOccupancy<Op, kSeg>, kFusedOccupancy<Op, kSeg>))) void gla_fused(Params p) {
   __shared__ Smem<Op, kSeg> sm;
-  __shared__ int s_ticket;
+  __shared__ int s_work[2];
+  __shared__ int s_fail;
   __shared__ long long s_epoch;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  // The sequence is fixed by the block index; the segment is the order in which
-  // this sequence's workgroups start (a per-sequence ticket), so every segment a
-  // workgroup waits for belongs to a workgroup that is already running.
-  const int bh = blockIdx.x % p.bh_count;
-  int *ctl = p.sync + kSyncHeader + (size_t)bh * kCtlStride;
+  const int slot = xcc_slot();
   if (tid == 0) {
-    s_ticket = __hip_atomic_fetch_add(ctl + kCtlTicket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_epoch = __hip_atomic_load(reinterpret_cast<long long *>(p.sync + kSyncEpoch), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+    // flag value of this call: the epoch (calls completed on this workspace) + 1;
+    // earlier calls left at most the epoch.  Read together with the first ticket.
+    const long long e = __hip_atomic_load(reinterpret_cast<long long *>(p.sync + kSyncEpochWord), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long v = work_add(p, slot);
+    s_epoch = e;
+    take_work(p, slot, v, s_work);
   }
   __syncthreads();
-  // flag value of this call: the epoch (calls completed on this workspace) + 1;
-  // earlier calls left at most the epoch
-  const int seg = s_ticket;
-  const long long want = s_epoch + 1;
-  const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
-  const size_t sbase = (size_t)bh * p.n_seg;
-  const Seq sq = seq_of<Io>(p, bh);
+  // uniform: scalar registers
+  const long long want = (long long)(((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane((int)(s_epoch >> 32)) << 32) |
+                                     (unsigned)__builtin_amdgcn_readfirstlane((int)s_epoch)) + 1;
+  const int G = p.fold_block;
+  // the current segment (uniform across the workgroup: scalar registers, so the
+  // buffer resources built from them stay scalar), and its first chunk's rows
+  int bh = __builtin_amdgcn_readfirstlane(s_work[0]), seg = __builtin_amdgcn_readfirstlane(s_work[1]);
+  while (bh >= 0) {
+    if (tid == 0) s_fail = 0;
+    __syncthreads();  // s_work has been read by every thread before it is rewritten below
+    // the next ticket's work-word increment, issued now so that it returns during the walk
+    unsigned long long next_word = 0;
+    if (tid == kThreads - 1) next_word = work_add(p, slot);
+    const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
+    const Seq sq = seq_of<Io>(p, bh);
+    const __amdgpu_buffer_rsrc_t slots = slot_rsrc(p, bh);
 
-  // 1. the segment from a zero state
-  f4 keep[kSeg][4];
-  f4 L[4] = {};
-  f4 sdec = {1.f, 1.f, 1.f, 1.f};
-  {
+    // 1. the segment from a zero state
     Rows<Io> x;
     load_chunk<Io, true, true>(sq, c0, 0, wave, lane, x);
+    f4 keep[kSeg][4];
+    f4 L[4] = {};
+    f4 sdec = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int j = 0; j < kSeg; ++j)
       if (c0 + j < c1)
-        chunk<Io, Op, kKeep, 1>(sq, sm, x, c0 + j, c1, wave, lane, j, &L, &sdec, keep[j], nullptr,
-                                nullptr, false);
-  }
-  // decay across the whole segment, read in step 5; tot is not read after a
-  // chunk's last barrier, so wave 0 may overwrite it while others finish
-  float *segdec = sm.tot;
-  if (wave == 0 && lane < 16) *reinterpret_cast<f4 *>(&segdec[4 * lane]) = sdec;
+        chunk<Io, Op, kKeep, 1>(sq, sm, x, c0 + j, c1, wave, lane, j, &L, &sdec, keep[j], nullptr, nullptr,
+                                false);
+    // decay across the whole segment; tot is not read after a chunk's last
+    // barrier, so wave 0 may overwrite it while others finish
+    float *segdec = sm.tot;
+    if (wave == 0 && lane < 16) *reinterpret_cast<f4 *>(&segdec[4 * lane]) = sdec;
+    lds_sync();  // segdec visible; qs (the fold's scratch below) no longer read
 
-  // 2. publish the aggregate (the last segment has no successor), row-major [i][j]
-  if (seg + 1 < p.n_seg) {
-    float *dst = p.agg + (sbase + seg) * kStateElems + 16 * wave + l16;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) store_shared(dst + state_i(x, lane) * kHead, L[x >> 2][x & 3]);
-    if (wave == 0 && lane < 16) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) store_shared(&p.agg_dec[(sbase + seg) * kHead + 4 * lane + d], sdec[d]);
-    }
-    stores_complete();  // this wave's payload is visible at device scope ...
-    __syncthreads();    // ... for every wave ...
-    if (tid == 0)       // ... before the flag is raised
-      __hip_atomic_store(p.flags + sbase + seg, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+    // 2. the aggregate, for the later segments of this block
+    const int blk0 = seg - seg % G;          // first segment of this block
+    const bool blk_last = seg % G == G - 1;  // publishes the block prefix instead
+    const bool has_next = seg + 1 < p.n_seg;
+    if (has_next && !blk_last) publish<true>(p, slots, bh, seg, tid, L, sdec, want);
 
-  // 3. S_prev: the aggregates of all earlier segments, folded backwards from
-  //    the nearest, each with the decay of the segments between, plus the
-  //    decayed s0.  The order is fixed, so the result does not depend on which
-  //    workgroups finished first.  Wave w combines rows [16w, 16w+16), lane l
-  //    column l, so every load reads one contiguous 256-byte row; the result
-  //    goes through LDS (qs and ks, idle now) into the register layout.
-  const bool have_prev = seg > 0 || p.s0 != nullptr;
-  f4 S[4] = {};
-  if (have_prev) {
-    float X[16], dacc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      X[r] = 0.f;
-      dacc[r] = 1.f;
-    }
-    constexpr int kBatch = 4;
-    // every earlier segment's flag at once (at most 256 of them, one per
-    // thread), then the aggregates in batches
-    static_assert(kMaxFusedSegments <= kThreads, "one thread per earlier segment's flag");
-    if (tid < seg) wait_flag(p.sync, p.flags + sbase + tid, want);
-    __syncthreads();  // the flags seen by one wave hold for the whole workgroup
-    for (int i = seg - 1; i >= 0;) {
-      const int nb = min(kBatch, i + 1);
-      float av[kBatch][16], dv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-          const float *src = p.agg + (sbase + i - u) * kStateElems + 16 * wave * kHead + lane;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) av[u][r] = load_shared(src + r * kHead);
-          dv[u] = load_shared(p.agg_dec + (sbase + i - u) * kHead + 16 * wave + l16);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < nb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            X[r] += dacc[r] * av[u][r];
-            dacc[r] *= __shfl(dv[u], r);  // decay of row 16w+r across segment i-u
-          }
-        }
-      }
-      i -= nb;
-    }
-    if (p.s0) {
-      bool col_ok;
-      const float *s0 = p.s0 + user_state_row0(p, bh, lane, col_ok);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)  // row 16w + r: uniform across the wave
-        if (col_ok && 16 * wave + r < p.dk) X[r] += dacc[r] * s0[(size_t)(16 * wave + r) * p.dv];
-    }
-    float *xs = reinterpret_cast<float *>(sm.qs);
-    constexpr int kLdX = 68;
-    static_assert(sizeof(sm.qs) + sizeof(sm.ks) >= kChunk * kLdX * sizeof(float),
-                  "xs must fit in qs and ks, which are adjacent");
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xs[(16 * wave + r) * kLdX + lane] = X[r];
-    __syncthreads();  // also makes segdec visible to every wave
-#pragma unroll
-    for (int x = 0; x < 16; ++x) S[x >> 2][x & 3] = xs[state_i(x, lane) * kLdX + 16 * wave + l16];
-  }
-
-  // 3b. the final state after the last segment: D S_prev + A
-  if (p.s_final && seg + 1 == p.n_seg) {
-    if (!have_prev) __syncthreads();  // segdec visible
-    f4 after[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      after[it] = L[it];
-      if (have_prev) after[it] += *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
-    }
-    store_user_state(p, p.s_final, bh, 0, wave, lane, after);
-  }
-
-  // 4. add each chunk's share of S_prev and store
-  const uint32_t col = val_col<Io>(sq, 16 * wave + 4 * g);
-  constexpr int LD = OpT<Op>::LD;
-#pragma unroll
-  for (int j = 0; j < kSeg; ++j) {
-    if (c0 + j >= c1) break;
+    // 3. S_prev: first the aggregates of this block's earlier segments ...
+    const int n_a = seg - blk0;
+    const bool has_p = blk0 > 0;  // ... then the prefix of the previous block, or s0
+    const bool have_prev = seg > 0 || p.s0 != nullptr;
+    const __amdgpu_buffer_rsrc_t fl = flag_rsrc(p, bh);
+    if (have_prev && tid < n_a && !wait_flag(p.sync, fl, blk0 + tid, want)) s_fail = 1;
+    __syncthreads();  // every awaited aggregate is visible
+    f4 S[4] = {};
     if (have_prev) {
-      op8<Op> sf[2];
+      // Horner's rule over the block's earlier segments, oldest first:
+      // X <- D_u X + A_u, and prod = product of their decays, for the entering
+      // term.  Each round trip brings kBatch aggregates and their decays; the
+      // decays (one per thread) go through LDS to the rows each thread holds.
+      constexpr int kBatch = kFusedOccupancy<Op, kSeg> > 2 ? 2 : 4;  // aggregates per round trip
+      float *dlds = reinterpret_cast<float *>(sm.qs);                 // [2][kBatch][64], alternating
+      f4 prod[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]);
-        const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]);
-        sf[kb] = cat(to4<Op>(S[2 * kb] * d0), to4<Op>(S[2 * kb + 1] * d1));
+      for (int it = 0; it < 4; ++it) prod[it] = f4{1.f, 1.f, 1.f, 1.f};
+      for (int u0 = 0, half = 0; u0 < n_a; u0 += kBatch, half ^= 1) {
+        f4 a[kBatch][4];
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v)
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            a[v][it] = slot_load(slots, slot_state_off(blk0 + min(u0 + v, n_a - 1), wave, it, lane));
+        if (tid < kBatch * kHead)
+          dlds[half * kBatch * kHead + tid] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         slots, slot_decay_off(blk0 + min(u0 + tid / kHead, n_a - 1), tid % kHead), 0, kNonTemporal));
+        lds_sync();
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v)
+          if (u0 + v < n_a)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+              const f4 d = *reinterpret_cast<const f4 *>(&dlds[(half * kBatch + v) * kHead + 16 * it + 4 * g]);
+              S[it] = d * S[it] + a[v][it];
+              prod[it] *= d;
+            }
+      }
+      if (has_p) {  // the chain between blocks: this wait is its only step per block
+        if (tid == 0 && !wait_flag(p.sync, fl, blk0 - 1, want)) s_fail = 1;
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 4; ++it) S[it] += prod[it] * slot_load(slots, slot_state_off(blk0 - 1, wave, it, lane));
+      } else if (p.s0) {
+        const UserState u = user_state(p, p.s0, bh, wave, lane);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          f4 e;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            e[r] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(u.r, user_state_off(u, 16 * it + 4 * g + r), 0, 0));
+          S[it] += prod[it] * e;
+        }
+      }
+      if (s_fail) {  // a wait gave up: poison this segment and everything after it
+#pragma unroll
+        for (int it = 0; it < 4; ++it) S[it] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      }
+    }
+
+    // 4. the state after the segment: the next block's entering term, or s_final
+    if (blk_last && has_next) {
+      f4 after[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) after[it] = L[it] + *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
+      publish<false>(p, slots, bh, seg, tid, after, sdec, want);
+    }
+    if (p.s_final && !has_next) {
+      const UserState u = user_state(p, p.s_final, bh, wave, lane);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const f4 after = L[it] + *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(after[r]), u.r, user_state_off(u, 16 * it + 4 * g + r),
+                                                0, 0);
+      }
+    }
+
+    // 5. add each chunk's share of S_prev and store
+    const uint32_t col = val_col<Io>(sq, 16 * wave + 4 * g);
+    constexpr int LD = OpT<Op>::LD;
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+      if (c0 + j >= c1) break;
+      if (have_prev) {
+        op8<Op> sf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]);
+          const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]);
+          sf[kb] = cat(to4<Op>(S[2 * kb] * d0), to4<Op>(S[2 * kb + 1] * d1));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
+        buf_store<Io>(sq.o, cell_at(sm.rowoff[j][16 * tt + l16], sq.vpitch, col), Io::pack(keep[j][tt]));
     }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      buf_store<Io>(sq.o, cell_at(sm.rowoff[j][16 * tt + l16], sq.vpitch, col), Io::pack(keep[j][tt]));
+    // the next ticket (its work-word increment returned long ago; taking the
+    // next batch, when this one has run out, waits here, off the fold's path)
+    if (tid == kThreads - 1) take_work(p, slot, next_word, s_work);
+    __syncthreads();  // the next ticket is visible; the LDS tiles are free for the next walk
+    bh = __builtin_amdgcn_readfirstlane(s_work[0]);
+    seg = __builtin_amdgcn_readfirstlane(s_work[1]);
   }
 
-  // 5. a sequence's last workgroup resets its ticket and done counters; the
-  //    last sequence to finish resets the sequence count and advances the
-  //    epoch, so the next call on this workspace (ordered after this kernel by
-  //    the stream) starts clean.
+  // Every workgroup counts itself out once it has found no work left; the last
+  // one resets the work words and the batch counter and advances the epoch, so
+  // the next call on this workspace (ordered after this kernel by the stream)
+  // starts clean.  Each workgroup's last access to the work words returned a
+  // value before it counts itself out, so none is still in flight.
   if (tid == 0) {
-    if (__hip_atomic_fetch_add(ctl + kCtlDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.n_seg - 1) {
-      __hip_atomic_store(ctl + kCtlTicket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctl + kCtlDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__hip_atomic_fetch_add(p.sync + kSyncSeqDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          p.bh_count - 1) {
-        __hip_atomic_store(p.sync + kSyncSeqDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(reinterpret_cast<long long *>(p.sync + kSyncEpoch), s_epoch + 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+    if (__hip_atomic_fetch_add(p.sync + kSyncExitedWord, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        (int)gridDim.x - 1) {
+      for (int x = 0; x < kXcdSlots; ++x)
+        __hip_atomic_store(reinterpret_cast<unsigned long long *>(p.sync + kSyncSlotWord + x * kSlotStride), 0ull,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.sync + kSyncNextBatchWord, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.sync + kSyncStartedWord, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.sync + kSyncExitedWord, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<long long *>(p.sync + kSyncEpochWord), s_epoch + 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1276,12 +1454,17 @@ int launch_typed(const LaunchArgs &a) {
     if constexpr (NK != 1 || kStatesOnly || Io::kLagGates) {
       return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
     } else {
+      p.fold_block = a.fold_block;
+      p.batch = a.batch;
+      p.n_batch = (a.bh + a.batch - 1) / a.batch;
+      p.n_pre = min(p.n_batch, min(a.xcds, kXcdSlots));
+      const unsigned grid = (unsigned)a.grid;
       if (a.seg_len <= 1)
-        launch(kKernelFused, gla_fused<Io, Op, 1>, n_blocks, a.stream, p);
+        launch(kKernelFused, gla_fused<Io, Op, 1>, grid, a.stream, p);
       else if (a.seg_len == 2)
-        launch(kKernelFused, gla_fused<Io, Op, 2>, n_blocks, a.stream, p);
+        launch(kKernelFused, gla_fused<Io, Op, 2>, grid, a.stream, p);
       else if (a.seg_len == 3)
-        launch(kKernelFused, gla_fused<Io, Op, 3>, n_blocks, a.stream, p);
+        launch(kKernelFused, gla_fused<Io, Op, 3>, grid, a.stream, p);
       else
         return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
       return (int)hipGetLastError();

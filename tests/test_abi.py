@@ -47,20 +47,43 @@ def test_version_and_sizes():
     assert gla.gtr_gla_version() == 10000
     split = gla.GTR_PATH_SPLIT
     fused = gla.GTR_PATH_FUSED
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
-    # one-launch path: aggregates and decays (no entering states), then a 32-word header, a 32-word
-    # control line per sequence and a 64-bit flag per segment; a single segment needs no aggregates
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
-        6 * 25 * (4096 + 64) * 4 + (32 + 6 * (32 + 2 * 25)) * 4
-    assert gla.gtr_gla_workspace_bytes(1, 6, 8, 8, 64, 64, 1, 1, fused) == (32 + 6 * (32 + 2)) * 4
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 64, 64, 1, 1, split) == 6 * 25 * (2 * 4096 + 64) * 4
+    # one-launch path: a payload slot per segment (state and decays; no entering states), then a
+    # 32-word header, a 128-byte work line for each of 16 XCD ids and a 64-bit flag per segment;
+    # a single segment needs no payload
+    sync = lambda flags: (32 + 16 * 32 + 2 * flags) * 4
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 64, 64, 1, 1, fused) == \
+        6 * 25 * (4096 + 64) * 4 + sync(6 * 25)
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 8, 8, 64, 64, 1, 1, fused) == sync(6)
     # head dims: value columns in 64-wide blocks are sequences of their own, key blocks share one
     per = (2 * 4096 + 64) * 4
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 32, 64, 1, 1, split) == 6 * 25 * per
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 128, 1, 1, split) == 12 * 25 * per
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 128, 64, 1, 1, split) == 6 * 25 * 2 * per
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 132, 64, 1, 0, 0) == 0
-    assert gla.gtr_gla_workspace_bytes(0, 6, 40, 40, 64, 64, 1, 0, 0) == 0
-    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 1, 0, 3) == 0
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 32, 64, 1, 1, split) == 6 * 25 * per
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 64, 128, 1, 1, split) == 12 * 25 * per
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 128, 64, 1, 1, split) == 6 * 25 * 2 * per
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 132, 64, 1, 0, 0) == 0
+    assert gla.gtr_gla_workspace_bytes_ex(0, 6, 40, 40, 64, 64, 1, 0, 0) == 0
+    assert gla.gtr_gla_workspace_bytes_ex(1, 6, 40, 40, 64, 64, 1, 0, 3) == 0
+    # the seven-argument form is the library's own choice of path and segment length
+    for shape in [(1, 6, 40, 40, 64, 64, 1), (8, 6, 40, 40, 64, 64, 1), (1, 16, 128, 128, 64, 64, 1),
+                  (1, 2, 40, 40, 64, 64, 0), (1, 16, 64, 64, 64, 64, 2), (1, 4, 33, 17, 128, 96, 1)]:
+        assert gla.gtr_gla_workspace_bytes(*shape) == gla.gtr_gla_workspace_bytes_ex(*shape, 0, 0) > 0
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 132, 64, 1) == 0
+    assert gla.gtr_gla_workspace_bytes(1, 6, 40, 40, 64, 64, 3) == 0
+
+
+def test_workspace_bytes_signatures_through_ctypes():
+    """The boundary's sizing call takes (B, H, grid_h, grid_w, d_k, d_v, dtype); the _ex form adds
+    the segment length and path of gtr_gla_fwd_ex."""
+    import ctypes
+    L = ctypes.CDLL(gla.LIB_PATH)
+    f7, f9 = L.gtr_gla_workspace_bytes, L.gtr_gla_workspace_bytes_ex
+    f7.argtypes, f7.restype = [ctypes.c_int] * 7, ctypes.c_size_t
+    f9.argtypes, f9.restype = [ctypes.c_int] * 9, ctypes.c_size_t
+    assert f7(1, 6, 40, 40, 64, 64, 1) == f9(1, 6, 40, 40, 64, 64, 1, 0, 0) > 0
+    assert f7(1, 16, 128, 128, 64, 64, 1) == f9(1, 16, 128, 128, 64, 64, 1, 0, 0) > 0
+    assert f9(1, 6, 40, 40, 64, 64, 1, 1, 2) == 6 * 25 * (2 * 4096 + 64) * 4
+    assert f7(-1, 6, 40, 40, 64, 64, 1) == 0
+
 
 
 def test_plans():
@@ -88,10 +111,12 @@ def test_plans():
     pl = gla.gtr_gla_plan(1, 1, 1, 1, chunks_per_segment=9)
     assert pl["seg_len"] == 1 and pl["n_seg"] == 1
     assert gla.gtr_gla_plan(1, 1, 0, 1) == {"seg_len": 0, "n_seg": 0, "fused": False}  # no tokens
-    # the one-launch path folds every earlier segment: at most 256 of 3 chunks
-    assert gla.gtr_gla_plan(1, 1, 768, 64, path=gla.GTR_PATH_FUSED)["n_seg"] == 256
+    # the one-launch path takes any length; only its per-sequence payload slots (16,640 bytes per
+    # segment, 32-bit byte offsets) bound the segment count
+    assert gla.gtr_gla_plan(1, 1, 769, 64, path=gla.GTR_PATH_FUSED)["n_seg"] == 257
+    assert gla.gtr_gla_plan(1, 1, 2048, 4096, path=gla.GTR_PATH_FUSED)["n_seg"] == 43691
     with pytest.raises(gla.GlaError):
-        gla.gtr_gla_plan(1, 1, 769, 64, path=gla.GTR_PATH_FUSED)
+        gla.gtr_gla_plan(1, 1, 2048, 4096, chunks_per_segment=1, path=gla.GTR_PATH_FUSED)
     assert gla.gtr_gla_plan(1, 1, 769, 64, chunks_per_segment=3)["fused"] is False
     with pytest.raises(gla.GlaError):
         gla.gtr_gla_plan(1, 1, -1, 1)

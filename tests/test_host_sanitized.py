@@ -48,7 +48,7 @@ int main(void) {
   expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 4, 4, 128, 64, 0, 1, NULL, NULL, 0, GTR_PATH_FUSED, 0),
          GTR_ERR_UNSUPPORTED, "fused d_k 128");
   expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 4, 4, 64, 64, 0, 1, NULL, NULL, 0, 7, 0), GTR_ERR_INVALID_ARG, "path");
-  expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 200, 200, 64, 64, 0, 1, NULL, NULL, 1, GTR_PATH_FUSED, 0),
+  expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 2048, 4096, 64, 64, 0, 1, NULL, NULL, 1, GTR_PATH_FUSED, 0),
          GTR_ERR_INVALID_ARG, "fused segments");
   /* empty calls: nothing to do, no device needed */
   expect(gtr_gla_fwd(NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 4, 64, 64, 0, 1, 0), GTR_OK, "B = 0");
@@ -74,7 +74,8 @@ int main(void) {
           const int rc = gtr_gla_plan(1, bh, side, side + 3, dims[di], dims[5 - di], 0, path, &seg, &n_seg, &fused);
           if (rc != GTR_OK && rc != GTR_ERR_UNSUPPORTED && rc != GTR_ERR_INVALID_ARG) expect(rc, GTR_OK, "plan");
           if (rc == GTR_OK && (seg < 1 || n_seg < 1)) expect(seg, 1, "plan seg");
-          (void)gtr_gla_workspace_bytes(1, bh, side, side + 3, dims[di], dims[5 - di], di % 3, 0, path);
+          (void)gtr_gla_workspace_bytes_ex(1, bh, side, side + 3, dims[di], dims[5 - di], di % 3, 0, path);
+          (void)gtr_gla_workspace_bytes(1, bh, side, side + 3, dims[di], dims[5 - di], di % 3);
           (void)gtr_swiglu_workspace_bytes(bh, side, side, 8 * (di + 1), 64, di % 3);
         }
   /* profiler and workspaces with nothing recorded */
