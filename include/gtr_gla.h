@@ -135,6 +135,7 @@ extern "C" {
 #define GTR_ERR_CAPTURE (-8)      /* workspace would have to grow during stream capture */
 #define GTR_ERR_LAUNCH (-9)       /* a kernel launch failed */
 #define GTR_ERR_TIMEOUT (-10)     /* a one-launch-path wait between workgroups gave up (see gtr_gla_stream_status) */
+#define GTR_ERR_SCRATCH (-11)     /* gtr_gla_fwd_static: the shape needs more working memory than its fixed array */
 
 /*
  * Generic entry point: dtype selects the element type (GTR_DTYPE_*).
@@ -145,6 +146,26 @@ extern "C" {
 int gtr_gla_fwd(const void *q, const void *k, const void *v, const void *log_gate,
                 void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
                 int direction, int dtype, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): gtr_gla_fwd with the
+ * same arguments and results, computed by the three-launch path, whose only
+ * working memory (the boundary states) comes from a fixed array in the
+ * library's device code: GTR_GLA_STATIC_SCRATCH_BYTES per device, held from
+ * the library's load until the process ends.  It calls no hipMalloc or hipFree
+ * and nothing that allocates.  The segment length is the library's choice,
+ * lengthened up to 32 chunks if the states would not fit; a shape that still
+ * does not fit returns GTR_ERR_SCRATCH with a message (e.g. one 2^23-token
+ * sequence; any number of sequences of at most 32 chunks always fits).  Every
+ * call on a device shares that device's array: calls that overlap on one
+ * device (other streams or threads, graph replays) race and give undefined
+ * outputs.  Each call writes every word it reads, so no clearing is needed.
+ */
+#define GTR_GLA_STATIC_SCRATCH_BYTES (32u << 20)
+int gtr_gla_fwd_static(const void *q, const void *k, const void *v, const void *log_gate,
+                       void *out, int B, int H, int grid_h, int grid_w, int d_k, int d_v,
+                       int direction, int dtype, hipStream_t stream);
 
 /* Typed entry points with the plain argument list; the element type is in the name. */
 int gtr_gla_fwd_f32(const void *q, const void *k, const void *v, const void *log_gate,

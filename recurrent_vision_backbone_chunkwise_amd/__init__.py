@@ -24,13 +24,13 @@ GTR_PATH_AUTO, GTR_PATH_FUSED, GTR_PATH_SPLIT = 0, 1, 2
 ERRORS = {
     0: "GTR_OK", -1: "GTR_ERR_INVALID_ARG", -2: "GTR_ERR_UNSUPPORTED", -3: "GTR_ERR_ALIGNMENT",
     -4: "GTR_ERR_ALIAS", -5: "GTR_ERR_NO_DEVICE", -6: "GTR_ERR_POINTER", -7: "GTR_ERR_ALLOC",
-    -8: "GTR_ERR_CAPTURE", -9: "GTR_ERR_LAUNCH", -10: "GTR_ERR_TIMEOUT",
+    -8: "GTR_ERR_CAPTURE", -9: "GTR_ERR_LAUNCH", -10: "GTR_ERR_TIMEOUT", -11: "GTR_ERR_SCRATCH",
 }
 DTYPE_CODES = {torch.float32: GTR_DTYPE_F32, torch.float16: GTR_DTYPE_F16,
                torch.bfloat16: GTR_DTYPE_BF16}
 
 # Every symbol include/gtr_gla.h and include/gtr_swiglu.h declare.
-EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
+EXPORTS = ("gtr_gla_fwd", "gtr_gla_fwd_static", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
            "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_workspace_bytes",
            "gtr_gla_workspace_bytes_ex", "gtr_gla_plan",
            "gtr_gla_last_error", "gtr_gla_version", "gtr_gla_release_workspaces",
@@ -60,13 +60,14 @@ def lib() -> ctypes.CDLL:
     fp = ctypes.c_void_p
     sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i]
     L.gtr_gla_fwd.argtypes = sig + [i, st]
+    L.gtr_gla_fwd_static.argtypes = sig + [i, st]
     for name in ("gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16"):
         getattr(L, name).argtypes = sig + [st]
     L.gtr_gla_fwd_ex.argtypes = sig + [i, fp, fp, i, i, st]
     L.gtr_gla_check.argtypes = sig + [i, fp, fp, i, i]
     ip = ctypes.POINTER(ctypes.c_int)
     L.gtr_gla_plan.argtypes = [i] * 8 + [ip, ip, ip]
-    for name in ("gtr_gla_fwd", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
+    for name in ("gtr_gla_fwd", "gtr_gla_fwd_static", "gtr_gla_fwd_f32", "gtr_gla_fwd_f16", "gtr_gla_fwd_bf16",
                  "gtr_gla_fwd_ex", "gtr_gla_check", "gtr_gla_version", "gtr_gla_plan"):
         getattr(L, name).restype = ctypes.c_int
     L.gtr_gla_workspace_bytes.argtypes = [i] * 7
@@ -197,6 +198,14 @@ def gtr_gla_fwd(q, k, v, log_gate, out, direction: int, stream=None) -> None:
     _check(lib().gtr_gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(),
                              out.data_ptr(), B, H, gh, gw, dk, dv, int(direction),
                              DTYPE_CODES[q.dtype], _stream_handle(stream)))
+
+
+def gtr_gla_fwd_static(q, k, v, log_gate, out, direction: int, stream=None) -> None:
+    """gtr_gla_fwd with its working memory in the library's fixed device array (no allocation)."""
+    B, H, gh, gw, dk, dv = _shapes(q, k, v, log_gate, out)
+    _check(lib().gtr_gla_fwd_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(),
+                                    out.data_ptr(), B, H, gh, gw, dk, dv, int(direction),
+                                    DTYPE_CODES[q.dtype], _stream_handle(stream)))
 
 
 def gtr_gla_fwd_ex(q, k, v, log_gate, out, direction: int, s0=None, s_final=None,

@@ -560,6 +560,68 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   return GTR_OK;
 }
 
+int gtr_gla_fwd_static(const void *q, const void *k, const void *v, const void *log_gate, void *out, int B,
+                       int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
+                       hipStream_t stream) {
+  Shape sh;
+  int device = 0;
+  int rc = check_call(q, k, v, log_gate, out, B, H, grid_h, grid_w, d_k, d_v, direction, dtype, nullptr,
+                      nullptr, 0, GTR_PATH_SPLIT, &sh, &device, stream, true);
+  if (rc != GTR_OK || sh.empty) return rc;
+  // Three launches, whose boundary states (the only working memory) must fit
+  // the fixed array: the planner's segment length, or the shortest longer one
+  // (up to 32 chunks) that fits; a single segment per sequence needs none.
+  auto ws_bytes = [&](long long n_seg) {
+    return n_seg > 1 ? gtr::workspace_bytes((size_t)sh.seqs, (size_t)n_seg, (size_t)sh.nk) : (size_t)0;
+  };
+  long long seg_len = sh.seg_len, n_seg = sh.n_seg;
+  while (ws_bytes(n_seg) > gtr::kStaticScratchBytes && seg_len < std::min<long long>(32, sh.n_chunk)) {
+    ++seg_len;
+    n_seg = (sh.n_chunk + seg_len - 1) / seg_len;
+  }
+  if (ws_bytes(n_seg) > gtr::kStaticScratchBytes)
+    return fail(GTR_ERR_SCRATCH,
+                "gtr_gla_fwd_static: %lld sequences of %d chunks need %zu bytes of boundary states even with "
+                "%lld-chunk segments; its fixed array holds %zu (use gtr_gla_fwd)",
+                sh.seqs, sh.n_chunk, ws_bytes(n_seg), seg_len, gtr::kStaticScratchBytes);
+  gtr::LaunchArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = log_gate;
+  a.out = out;
+  a.bh = (int)sh.seqs;
+  a.d_k = d_k;
+  a.d_v = d_v;
+  a.nk = sh.nk;
+  a.nvb = sh.nvb;
+  a.grid_h = grid_h;
+  a.grid_w = grid_w;
+  a.n_tok = (int)sh.n_tok;
+  a.direction = direction;
+  a.dtype = dtype;
+  a.n_chunk = sh.n_chunk;
+  a.seg_len = (int)seg_len;
+  a.n_seg = (int)n_seg;
+  a.stream = stream;
+  if (n_seg > 1) {
+    void *ptr = nullptr;
+    const int e = gtr::static_scratch(device, &ptr);
+    if (e != (int)hipSuccess)
+      return fail(GTR_ERR_LAUNCH, "gtr_gla_fwd_static: the fixed array's device address: %s",
+                  hipGetErrorString((hipError_t)e));
+    float *f = static_cast<float *>(ptr);
+    const size_t st = (size_t)sh.seqs * n_seg * sh.nk * gtr::kStateElems;
+    a.agg = f;
+    a.prev = f + st;
+    a.agg_dec = f + 2 * st;
+  }
+  const int err = gtr::launch_gla(a);
+  if (err != (int)hipSuccess)
+    return fail(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  return GTR_OK;
+}
+
 int gtr_gla_fwd(const void *q, const void *k, const void *v, const void *log_gate, void *out, int B,
                 int H, int grid_h, int grid_w, int d_k, int d_v, int direction, int dtype,
                 hipStream_t stream) {

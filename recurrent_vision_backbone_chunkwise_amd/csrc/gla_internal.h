@@ -136,6 +136,12 @@ long long split_segment_length(long long seqs, int n_chunk);
 // Enqueues the kernels for one call.  Returns a hipError_t value.
 int launch_gla(const LaunchArgs &a);
 
+// Size of the fixed device array gtr_gla_fwd_static takes its working memory
+// from (GTR_GLA_STATIC_SCRATCH_BYTES), and that array's address on `device`,
+// which must be the current device (queried once per device; hipError_t value).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+int static_scratch(int device, void **ptr);
+
 // s_final[i] = s0 ? s0[i] : 0 for i < n (a call with no tokens).  Returns a hipError_t value.
 int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t stream);
 

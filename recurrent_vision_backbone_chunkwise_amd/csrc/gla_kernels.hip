@@ -56,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "gla_internal.h"
@@ -1878,6 +1880,30 @@ int launch_state_copy(const float *s0, float *s_final, long long n, hipStream_t 
   hipLaunchKernelGGL(gla_state_copy, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                      stream, s0, s_final, n);
   return (int)hipGetLastError();
+}
+
+// Working memory of gtr_gla_fwd_static: a fixed array in this library's device
+// code, one copy per device, held until the process ends.  Host code must not
+// use the name `scratch` as an address (on the host it is only a stand-in for
+// the symbol): static_scratch() gives each device's own address.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratchBytes];
+
+int static_scratch(int device, void **ptr) {
+  static std::mutex m;
+  static std::map<int, void *> addr;
+  std::lock_guard<std::mutex> lock(m);
+  auto it = addr.find(device);
+  if (it == addr.end()) {
+    void *p = nullptr;  // queried with `device` current (the caller's current device)
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+    }
+    it = addr.emplace(device, p).first;
+  }
+  *ptr = it->second;
+  return (int)hipSuccess;
 }
 
 int launch_gla(const LaunchArgs &a) {
