@@ -60,6 +60,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "gla_index.h"
 #include "gla_internal.h"
 #include "gla_profile.h"
 
@@ -251,25 +252,7 @@ template <typename Op> __device__ __forceinline__ op4<Op> to4(f4 x) {
 __device__ __forceinline__ int tile_a(int s) { return s >= 6 ? 3 : (s >= 3 ? 2 : (s >= 1 ? 1 : 0)); }
 __device__ __forceinline__ int tile_slot(int a, int b) { return (a * (a + 1)) / 2 + b; }
 
-// ----------------------------------------------------------- scan direction
-// Grid index of scan position t (see gtr_gla.h for the four orders).  The
-// column-major orders divide by grid_h with a float reciprocal and one exact
-// correction step (t < 2^23, so float(t) is exact and the estimate is off by
-// at most one).
-__device__ __forceinline__ void col_major_pos(int p, int gh, float rcp_gh, int &row, int &col) {
-  col = (int)((float)p * rcp_gh);
-  row = p - col * gh;
-  if (row < 0) {
-    --col;
-    row += gh;
-  } else if (row >= gh) {
-    ++col;
-    row -= gh;
-  }
-}
-
 constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer range: loads give 0, stores drop
-constexpr uint32_t kNoRow = 0xffffffffu;  // grid cell of a scan position past the end
 
 // One sequence's tensors as buffer resources: byte offsets are 32-bit and
 // uniform bases live in scalar registers.  A sequence is one (batch, head) and
@@ -298,66 +281,11 @@ template <class Io> __device__ __forceinline__ uint32_t val_col(const Seq &sq, i
   return j < sq.dv ? (uint32_t)j * (uint32_t)sizeof(typename Io::T) : kOob;
 }
 
-// Grid cell of scan position t (t < n_tok).
-__device__ __forceinline__ uint32_t token_cell(const Seq &sq, int t) {
-  const int p = (sq.dir & 1) ? sq.n_tok - 1 - t : t;
-  if (!(sq.dir & 2)) return (uint32_t)p;
-  int row, col;
-  col_major_pos(p, sq.gh, sq.rcp_gh, row, col);
-  return (uint32_t)(row * sq.gw + col);
-}
-
 // Grid cell whose log_gate row holds the gate of scan position t (t < n_tok):
 // t's own, or with lagged gates the one before it (kNoRow at t = 0: no decay).
 template <class Io> __device__ __forceinline__ uint32_t gate_cell(const Seq &sq, int t) {
   if constexpr (!Io::kLagGates) return token_cell(sq, t);
   return t > 0 ? token_cell(sq, t - 1) : kNoRow;
-}
-
-// Grid cells of scan positions t0 .. t0+3 (kNoRow past the end) and, with
-// kBefore, of t0 - 1 (kNoRow before the start).  Consecutive scan positions
-// step by one grid cell along the scan, so only the first needs a division.
-template <bool kBefore>
-__device__ __forceinline__ void cells4(const Seq &sq, int t0, uint32_t *cell, uint32_t &before) {
-  const bool rev = sq.dir & 1;
-  const int p0 = rev ? sq.n_tok - 1 - t0 : t0;
-  if (!(sq.dir & 2)) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = rev ? p0 - r : p0 + r;
-      cell[r] = t0 + r < sq.n_tok ? (uint32_t)p : kNoRow;
-    }
-    if constexpr (kBefore) before = t0 > 0 && t0 <= sq.n_tok ? (uint32_t)(rev ? p0 + 1 : p0 - 1) : kNoRow;
-    return;
-  }
-  int row, col;
-  col_major_pos(p0, sq.gh, sq.rcp_gh, row, col);
-  if constexpr (kBefore) {  // one step back along the scan
-    int br = row, bc = col;
-    if (rev) {
-      if (++br == sq.gh) {
-        br = 0;
-        ++bc;
-      }
-    } else if (--br < 0) {
-      br = sq.gh - 1;
-      --bc;
-    }
-    before = t0 > 0 && t0 <= sq.n_tok ? (uint32_t)(br * sq.gw + bc) : kNoRow;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    cell[r] = t0 + r < sq.n_tok ? (uint32_t)(row * sq.gw + col) : kNoRow;
-    if (rev) {
-      if (--row < 0) {
-        row = sq.gh - 1;
-        --col;
-      }
-    } else if (++row == sq.gh) {
-      row = 0;
-      ++col;
-    }
-  }
 }
 
 // -------------------------------------------------------------- shared memory
@@ -720,6 +648,41 @@ __device__ __forceinline__ void scores(const Seq &sq, Smem<Op, NQ> &sm, int c, i
   }
 }
 
+// Largest of a wave's 64 values of v (unsigned), in every lane: across the
+// four 16-lane rows with two row swaps, then within each row with DPP
+// rotations by 8, 4, 2 and 1 lanes.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)s16[0], (uint32_t)s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((uint32_t)s32[0], (uint32_t)s32[1]);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));  // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));  // row_ror:1
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// A state slice S (this wave's 16 columns, 16 values per lane) becomes an fp16
+// MFMA operand through an exact power of two 2^k chosen from its largest
+// magnitude m, so that m 2^k lies in [2^14, 2^15): nothing overflows fp16's
+// 65504, and small states keep fp16's full precision instead of falling into
+// its subnormal range.  Returns 2^k and sets unscale = 2^-k, by which the
+// fp32 product is multiplied back (exactly).  A zero, infinite or NaN slice
+// keeps k = 0.
+__device__ __forceinline__ float state_scale(const f4 *S, float &unscale) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = max(m, __float_as_uint(S[it][r]) & 0x7fffffffu);
+  m = wave_max(m);
+  int k = 0;
+  if (m != 0 && m < 0x7f800000u) k = min(126, max(-126, 14 - ((int)(m >> 23) - 127)));
+  unscale = __uint_as_float((uint32_t)(127 - k) << 23);
+  return __uint_as_float((uint32_t)(127 + k) << 23);
+}
+
 // How a walk treats each chunk.
 enum : int {
   kAgg = 0,    // state only: no queries, no outputs
@@ -736,14 +699,24 @@ __device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int la
                                         const op8<Op> *vf, const f4 *S, typename OpT<Op>::Bits *ot,
                                         f4 *keep) {
   constexpr int LD = OpT<Op>::LD;
+  constexpr bool kScaled = sizeof(Op) == 2;  // 16-bit operands: the state goes through state_scale
   const int g = lane >> 4, l16 = lane & 15;
   op8<Op> sf[2];
+  float unscale = 1.f;
+  const float scale = kScaled ? state_scale(S, unscale) : 1.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) sf[kb] = cat(to4<Op>(S[2 * kb]), to4<Op>(S[2 * kb + 1]));
+  for (int kb = 0; kb < 2; ++kb) sf[kb] = cat(to4<Op>(S[2 * kb] * scale), to4<Op>(S[2 * kb + 1] * scale));
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kAcc) acc = keep[tt];
+    if constexpr (kScaled) {  // the state term on its own accumulator, scaled back, then the scores
+      f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        st = mma(sf[kb], frag_row<Op>(&sm.qh[slot][(16 * tt + l16) * LD + 32 * kb + 4 * g]), st);
+      acc += st * unscale;
+    }
 #pragma unroll
     for (int kb = 0; kb <= (tt >> 1); ++kb) {
       const op4<Op> lo = *reinterpret_cast<const op4<Op> *>(&sm.pt[tile_slot(tt, 2 * kb) * 256 + lane * 4]);
@@ -752,9 +725,11 @@ __device__ __forceinline__ void outputs(const Smem<Op, NQ> &sm, int wave, int la
         hi = *reinterpret_cast<const op4<Op> *>(&sm.pt[tile_slot(tt, 2 * kb + 1) * 256 + lane * 4]);
       acc = mma(vf[kb], cat(lo, hi), acc);
     }
+    if constexpr (!kScaled) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      acc = mma(sf[kb], frag_row<Op>(&sm.qh[slot][(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
+      for (int kb = 0; kb < 2; ++kb)
+        acc = mma(sf[kb], frag_row<Op>(&sm.qh[slot][(16 * tt + l16) * LD + 32 * kb + 4 * g]), acc);
+    }
     if constexpr (kMode == kStore && kFinal)
       *reinterpret_cast<typename Io::Raw *>(&ot[(16 * tt + l16) * OpT<Op>::LDO + 16 * wave + 4 * g]) =
           Io::pack(acc);
@@ -1371,9 +1346,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       }
     }
 
-    // 5. add each chunk's share of S_prev and store
+    // 5. add each chunk's share of S_prev and store (16-bit operands: S_prev
+    // scaled as in outputs(); the decays Dcum <= 1 only shrink it further)
     const uint32_t col = val_col<Io>(sq, 16 * wave + 4 * g);
     constexpr int LD = OpT<Op>::LD;
+    constexpr bool kScaled = sizeof(Op) == 2;
+    float unscale = 1.f;
+    const float scale = kScaled && have_prev ? state_scale(S, unscale) : 1.f;
 #pragma unroll
     for (int j = 0; j < kSeg; ++j) {
       if (c0 + j >= c1) break;
@@ -1381,15 +1360,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         op8<Op> sf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]);
-          const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]);
+          const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]) * scale;
+          const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]) * scale;
           sf[kb] = cat(to4<Op>(S[2 * kb] * d0), to4<Op>(S[2 * kb + 1] * d1));
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt) {
+          f4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            keep[j][tt] = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), keep[j][tt]);
+            st = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), st);
+          keep[j][tt] += st * unscale;
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
