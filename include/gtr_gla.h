@@ -84,10 +84,11 @@
  *   - q and k times at most 2^8, on the within-chunk diagonal score tiles
  *     (|q|, |k| < 256 always suffices there);
  *   - each within-chunk score, which is at most |q_t|*|k_s| (Euclidean norms
- *     of a query and an earlier key of the same chunk);
- *   - each entry of the state entering a chunk.
- * Beyond these the output is unspecified (typically inf or NaN).  fp32 I/O
- * uses fp32 operands throughout and has none of these limits.
+ *     of a query and an earlier key of the same chunk).
+ * Beyond these the output is unspecified (typically inf or NaN).  The state,
+ * kept in fp32, is not limited by this: it becomes an operand only after an
+ * exact power of two brings its largest entry near 2^14.  fp32 I/O uses fp32
+ * operands throughout and has none of these limits.
  *
  * Empty calls: with B*H == 0 or no tokens there is nothing to compute and
  * tensor pointers may be NULL; the call returns GTR_OK without touching the

@@ -45,9 +45,12 @@ def test_json_line_fields():
     rl = d["roofline"]
     assert rl["bound"] in ("hbm", "mfma", "alu") and rl["unit"] in ("GB/s", "TFLOP/s")
     assert 0 < rl["achieved"] and rl["frac"] == pytest.approx(rl["achieved"] / rl["peak"], rel=1e-3)
-    assert "traffic" in rl
+    assert "traffic" in rl and rl["kernel_frac"] == rl["frac"]
+    # the whole call, launch gaps included, cannot beat its dominant kernel
+    assert 0 < rl["call_frac"] <= 1.25 * rl["kernel_frac"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == d["unit"]
+    assert cb["host_cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
     assert d["long_sequence"] is None  # only the default workload also reports the 16K round
 
@@ -61,4 +64,4 @@ def test_default_run_also_reports_the_long_sequence():
     ls = d["long_sequence"]
     assert ls["workload"] == "grid128x128_f16_b1h16_4dir" and ls["value"] > 0
     assert ls["roofline"]["kernel"] in ("gla_seg_out", "gla_seg_state", "gla_fused")
-    assert 0 < ls["roofline"]["frac"] < 1
+    assert 0 < ls["roofline"]["frac"] < 1 and 0 < ls["roofline"]["call_frac"] <= 1.25 * ls["roofline"]["frac"]

@@ -131,6 +131,26 @@ def test_unit_gate_long_sequence():
     check(q, k, v, g, 1, "f16", "ones 128x128")
 
 
+@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_state_beyond_the_fp16_range(dtype, path):
+    """alpha = 1 with keys near 2 and values near 4 (positive means): every state entry grows by
+    about 8 per token and passes 65504 halfway through 16,384 tokens, while queries near 1/256
+    keep the outputs in range.  The state reaches the fp16 MFMA operands through an exact power
+    of two, so it neither overflows there nor loses precision when small."""
+    gen = torch.Generator().manual_seed(77)
+    shape = (1, 2, 128, 128, 64)
+    q = (torch.randn(shape, generator=gen) / 256).to(gla_inputs.TORCH_DTYPES[dtype])
+    k = (2 + 0.1 * torch.randn(shape, generator=gen)).to(gla_inputs.TORCH_DTYPES[dtype])
+    v = (4 + 0.1 * torch.randn(shape, generator=gen)).to(gla_inputs.TORCH_DTYPES[dtype])
+    g = torch.zeros(shape, dtype=gla_inputs.TORCH_DTYPES[dtype])
+    for d in (0, 3):
+        e = check(q, k, v, g, d, dtype, f"state beyond fp16 range ({path})", path=PATHS[path])
+        assert np.isfinite(e["err_raw"])
+    s_end = oracle.gla_forward(q, k, v, g, 0, want_state=True)[1]
+    assert np.abs(s_end).max() > 1e5  # the state did leave the fp16 range
+
+
 # ---- head dims: 64-wide key blocks walked together, value blocks as sequences of their own,
 #      narrower heads masked --------------------------------------------------------------
 
