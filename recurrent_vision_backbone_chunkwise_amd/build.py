@@ -29,14 +29,46 @@ HIP_FLAGS = [
 SOURCES = ["gla_kernels.hip", "gla_api.cpp", "gla_bwd.cpp", "gla_profile.cpp", "swiglu.hip"]
 
 
+def code_tokens(text: str) -> str:
+    """C/C++ source without its comments, with every run of whitespace as one space (string and
+    character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c.isspace():
+            j = i
+            while j < n and text[j].isspace():
+                j += 1
+            out.append(" ")
+            i = j
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest() -> str:
-    """Short digest of the kernel and host sources: ties measurements to the code they measured."""
+    """Short digest of the kernel and host sources: ties measurements to the code they measured.
+    Comments and layout do not count, so editing them leaves measurements attached."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
                 h.update(name.encode())
-                h.update(f.read())
+                h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,7 +10,14 @@
         HBM-side bytes per launch of each kernel from ``--pmc FETCH_SIZE`` and
         ``--pmc WRITE_SIZE`` runs (KiB per dispatch), each scaled by what the
         same counter reads, per byte, for a plain device copy of N bytes; the
-        result is stored with a digest of the kernel sources.
+        result is stored with a digest of the kernel sources;
+
+    python -m recurrent_vision_backbone_chunkwise_amd.profiling counters --pmc DIR [DIR ...] \
+        --trace DIR --workload NAME --commands "..." [--alg KERNEL=BYTES ...] [--out F]
+        per-kernel hardware counters from ``--pmc`` runs (one directory per pass) as a
+        short text table: MFMA utilisation and rate, time the waves spend waiting, L2
+        hit rate, and the bytes L2 read and wrote past itself, sized from its request
+        counts by size class, beside each kernel's algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -142,6 +149,122 @@ def counter_per_dispatch(directory: str, counter: str) -> dict[str, float]:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def counter_rows(directories: list[str]) -> dict[str, dict[str, tuple[float, float]]]:
+    """For every kernel and counter in the ``--pmc`` runs under `directories`: the means over
+    dispatches of the counter's sum and of its largest value over its per-dispatch rows (the rows
+    are per shader engine or cache instance)."""
+    acc = collections.defaultdict(lambda: [0.0, float("-inf")])
+    names = {}
+    for directory in directories:
+        for path in _csvs(directory, "counter_collection.csv"):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (path, r["Dispatch_Id"], r["Counter_Name"])
+                    v = float(r["Counter_Value"])
+                    acc[key][0] += v
+                    acc[key][1] = max(acc[key][1], v)
+                    names[key] = short_name(r["Kernel_Name"])
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for key, (total, peak) in acc.items():
+        per[names[key]][key[2]].append((total, peak))
+    return {k: {c: (sum(t for t, _ in v) / len(v), sum(m for _, m in v) / len(v)) for c, v in cs.items()}
+            for k, cs in per.items()}
+
+
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9  # MI355X peak engine clock
+MFMA_PEAK = {"F16": 2.5e15, "BF16": 2.5e15, "F32": 157.3e12}  # dense flop/s per operand type
+
+
+def derived_counters(c: dict[str, tuple[float, float]], avg_us: float | None, alg: float | None) -> dict:
+    """Per-launch figures from one kernel's counter means (see counter_rows)."""
+    def get(name, which=0):
+        return c[name][which] if name in c else None
+
+    out = {}
+    busy = get("SQ_VALU_MFMA_BUSY_CYCLES")
+    if busy is not None and avg_us:
+        out["mfma_busy_pct"] = 100.0 * busy / (avg_us * 1e-6 * CLOCK_HZ * SIMDS)
+    mops = {t: get("SQ_INSTS_VALU_MFMA_MOPS_" + t) for t in MFMA_PEAK}
+    if any(m is not None for m in mops.values()):
+        # one MOP is 512 flops
+        flops = 512.0 * sum(m for m in mops.values() if m is not None)
+        out["mfma_gflop"] = flops / 1e9
+        if avg_us:
+            out["mfma_tflops"] = flops / (avg_us * 1e-6) / 1e12
+            peak_s = sum(512.0 * m / MFMA_PEAK[t] for t, m in mops.items() if m is not None)
+            out["mfma_peak_pct"] = 100.0 * peak_s / (avg_us * 1e-6)
+    wait, active = get("SQ_WAIT_INST_ANY"), get("SQ_BUSY_CYCLES")
+    if wait is not None and get("SQ_WAVE_CYCLES"):
+        out["wave_wait_pct"] = 100.0 * wait / get("SQ_WAVE_CYCLES")
+    lds, conflict = get("SQ_INSTS_LDS"), get("SQ_LDS_BANK_CONFLICT")
+    if lds and conflict is not None:
+        out["lds_conflict_per_inst"] = conflict / lds
+    hit, miss = get("TCC_HIT_sum"), get("TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        out["l2_hit_pct"] = 100.0 * hit / (hit + miss)
+    r32, r64, r128 = get("TCC_EA0_RDREQ_32B_sum"), get("TCC_EA0_RDREQ_64B_sum"), get("TCC_EA0_RDREQ_128B_sum")
+    if r32 is not None and r64 is not None and r128 is not None:
+        out["read_bytes"] = 32.0 * r32 + 64.0 * r64 + 128.0 * r128
+    wr, wr64 = get("TCC_EA0_WRREQ_sum"), get("TCC_EA0_WRREQ_64B_sum")
+    if wr is not None and wr64 is not None:
+        out["write_bytes"] = 64.0 * wr64 + 32.0 * (wr - wr64)
+    if alg and "read_bytes" in out and "write_bytes" in out:
+        out["moved_over_alg"] = (out["read_bytes"] + out["write_bytes"]) / alg
+    if avg_us and "read_bytes" in out and "write_bytes" in out:
+        out["moved_gbs"] = (out["read_bytes"] + out["write_bytes"]) / (avg_us * 1e-6) / 1e9
+    return out
+
+
+def cmd_counters(a) -> None:
+    rows = counter_rows(a.pmc)
+    durations = {short_name(r["kernel"]): r["avg_us"] for r in kernel_stats(a.trace)} if a.trace else {}
+    alg = {}
+    for item in a.alg or []:
+        k, v = item.split("=")
+        alg[k] = float(v)
+    cols = [("avg us", "avg_us", "{:8.2f}"), ("MFMA busy %", "mfma_busy_pct", "{:11.2f}"),
+            ("MFMA TF/s", "mfma_tflops", "{:9.1f}"), ("% MFMA peak", "mfma_peak_pct", "{:11.2f}"), ("wait %", "wave_wait_pct", "{:6.1f}"),
+            ("LDS cf/inst", "lds_conflict_per_inst", "{:11.2f}"),
+            ("L2 hit %", "l2_hit_pct", "{:8.1f}"), ("read MB", "read_bytes", "{:8.2f}"),
+            ("write MB", "write_bytes", "{:8.2f}"), ("alg MB", "alg_bytes", "{:8.2f}"),
+            ("moved/alg", "moved_over_alg", "{:9.3f}"), ("moved GB/s", "moved_gbs", "{:10.0f}")]
+    mb = {"read_bytes", "write_bytes", "alg_bytes"}
+    lines = [f"# rocprofv3 hardware counters ({a.workload})",
+             "# commands ($REPO is the repository root):"]
+    lines += [f"#   {portable_command(c)}" for c in a.commands]
+    lines += [f"# kernel sources: {source_digest()}",
+              "# per launch, means over dispatches; avg us from the kernel trace; MFMA busy % = "
+              f"SQ_VALU_MFMA_BUSY_CYCLES over avg us x {CLOCK_HZ / 1e9:g} GHz x {SIMDS} SIMDs; MFMA TF/s = 512 "
+              "flops per SQ_INSTS_VALU_MFMA_MOPS_* over avg us; % MFMA peak against the dense peak of each "
+              "operand type (fp16 2.5 PFLOP/s, fp32 157.3 TFLOP/s); wait % = SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES; LDS cf/inst = "
+              "SQ_LDS_BANK_CONFLICT cycles per SQ_INSTS_LDS; L2 hit % = TCC_HIT over "
+              "TCC_HIT + TCC_MISS; read MB = 32/64/128 x TCC_EA0_RDREQ_{32B,64B,128B}; write MB = "
+              "64 x TCC_EA0_WRREQ_64B + 32 x the other TCC_EA0_WRREQ; moved = read + write", "",
+              f"{'kernel':16s}" + "".join(f" {h:>{len(fmt.format(0))}s}" for h, _, fmt in cols)]
+    for k in sorted(rows):
+        if k not in KERNELS and not a.all:
+            continue
+        d = derived_counters(rows[k], durations.get(k), alg.get(k))
+        d["avg_us"] = durations.get(k)
+        d["alg_bytes"] = alg.get(k)
+        cells = []
+        for h, key, fmt in cols:
+            v = d.get(key)
+            width = len(fmt.format(0))
+            cells.append(" " + ("-".rjust(width) if v is None else fmt.format(v / 1e6 if key in mb else v)))
+        lines.append(f"{k:16s}" + "".join(cells))
+    lines += ["", "# raw counters, means per dispatch"]
+    for k in sorted(rows):
+        if k in KERNELS or a.all:
+            lines.append(f"{k}: " + ", ".join(f"{c} {v[0]:.0f}" for c, v in sorted(rows[k].items())))
+    text = "\n".join(lines) + "\n"
+    print(text, end="")
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+
+
 def portable_command(command: str) -> str:
     """The command with this checkout's absolute root written as $REPO."""
     return command.replace(os.path.abspath(ROOT) + "/", "$REPO/")
@@ -212,8 +335,16 @@ def main() -> None:
     t.add_argument("--workload", required=True)
     t.add_argument("--commands", required=True)
     t.add_argument("--table", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--trace")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--commands", nargs="+", required=True)
+    c.add_argument("--alg", nargs="*")
+    c.add_argument("--out")
+    c.add_argument("--all", action="store_true", help="also list kernels that are not this library's")
     a = ap.parse_args()
-    (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

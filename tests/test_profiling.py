@@ -80,3 +80,52 @@ def test_traffic_scaled_by_the_copy(tmp_path):
     assert row["write_bytes_per_launch"] == 1024
     assert row["hbm_bytes_per_launch"] == 3072
     assert row["source"] == source_digest() and row["copy_scale"]["fetch"] == 2.0
+
+
+def write_multi(directory, rows):
+    directory.mkdir(parents=True, exist_ok=True)
+    with open(directory / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for row in rows:
+            w.writerow(row)
+
+
+def test_counter_table(tmp_path):
+    # one dispatch: MFMA busy over 2 rows, GUI active per instance (largest taken), hits and
+    # misses, read requests by size and writes by size
+    write_multi(tmp_path / "p1", [(1, MANGLED, "SQ_VALU_MFMA_BUSY_CYCLES", 600), (1, MANGLED, "SQ_VALU_MFMA_BUSY_CYCLES", 424),
+                                  (1, MANGLED, "GRBM_GUI_ACTIVE", 10), (1, MANGLED, "GRBM_GUI_ACTIVE", 4),
+                                  (1, MANGLED, "SQ_INSTS_VALU_MFMA_MOPS_F16", 1000),
+                                  (1, MANGLED, "SQ_WAIT_INST_ANY", 30), (1, MANGLED, "SQ_WAVE_CYCLES", 120),
+                                  (1, MANGLED, "SQ_INSTS_LDS", 8), (1, MANGLED, "SQ_LDS_BANK_CONFLICT", 2)])
+    write_multi(tmp_path / "p2", [(1, MANGLED, "TCC_HIT_sum", 3), (1, MANGLED, "TCC_MISS_sum", 1),
+                                  (1, MANGLED, "TCC_EA0_RDREQ_sum", 10), (1, MANGLED, "TCC_EA0_RDREQ_DRAM_sum", 5)])
+    write_multi(tmp_path / "p3", [(1, MANGLED, "TCC_EA0_RDREQ_32B_sum", 2), (1, MANGLED, "TCC_EA0_RDREQ_64B_sum", 3),
+                                  (1, MANGLED, "TCC_EA0_RDREQ_128B_sum", 5),
+                                  (1, MANGLED, "TCC_EA0_WRREQ_sum", 4), (1, MANGLED, "TCC_EA0_WRREQ_64B_sum", 3)])
+    rows = profiling.counter_rows([str(tmp_path / p) for p in ("p1", "p2", "p3")])
+    d = profiling.derived_counters(rows["gla_seg_out"], avg_us=2.0, alg=900.0)
+    assert d["mfma_busy_pct"] == 100.0 * 1024 / (2e-6 * profiling.CLOCK_HZ * profiling.SIMDS)
+    assert d["mfma_gflop"] == 512 * 1000 / 1e9 and d["mfma_tflops"] == 512 * 1000 / 2e-6 / 1e12
+    assert abs(d["mfma_peak_pct"] - 100.0 * 512 * 1000 / 2.5e15 / 2e-6) < 1e-12
+    assert d["lds_conflict_per_inst"] == 0.25
+    assert d["wave_wait_pct"] == 25.0 and d["l2_hit_pct"] == 75.0
+    assert d["read_bytes"] == 32 * 2 + 64 * 3 + 128 * 5 and d["write_bytes"] == 64 * 3 + 32 * 1
+    assert d["moved_over_alg"] == (896 + 224) / 900.0
+    out = tmp_path / "c.txt"
+    subprocess.run([sys.executable, "-m", "recurrent_vision_backbone_chunkwise_amd.profiling", "counters",
+                    "--pmc", str(tmp_path / "p1"), str(tmp_path / "p2"), str(tmp_path / "p3"), "--workload", "wl",
+                    "--commands", f"rocprofv3 --pmc X -- python3 {ROOT}/bench.py", "--alg", "gla_seg_out=900",
+                    "--out", str(out)], check=True, capture_output=True, cwd=ROOT)
+    text = out.read_text()
+    assert "$REPO/bench.py" in text and "gla_seg_out" in text and source_digest() in text
+
+
+def test_digest_ignores_comments_and_layout():
+    from recurrent_vision_backbone_chunkwise_amd.build import code_tokens
+    a = 'int a = 1; // note\n/* block\n comment */ const char *s = "x // y /* z */";\nchar q = \'"\';   int b;\n'
+    b = 'int a = 1;\nconst char *s = "x // y /* z */"; char q = \'"\'; int b; // other note\n'
+    assert code_tokens(a) == code_tokens(b)
+    assert code_tokens(a) != code_tokens(b.replace("int b", "int c"))
+    assert '"x // y /* z */"' in code_tokens(a)
