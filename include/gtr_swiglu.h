@@ -23,8 +23,10 @@
  *   w_out   : [F][C]
  * Arithmetic: the projections are library GEMMs (rocBLAS) with fp32
  * accumulation; u is kept in fp16 for fp16 I/O and in fp32 otherwise; h is
- * rounded to the I/O dtype before the output projection; out is rounded to the
- * I/O dtype.
+ * rounded to the I/O dtype before the output projection, except for bf16 I/O,
+ * where h is fp16 and W_out is converted to fp16 for the projection (so |h|
+ * and |W_out| must stay below 65504; W_out loses bits only below 2^-17),
+ * whose fp32 result is then rounded; out is rounded to the I/O dtype.
  *
  * Ownership and errors as in gtr_gla.h: device pointers owned by the caller,
  * 16-byte aligned; out must not overlap an input; the library owns a

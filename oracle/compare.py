@@ -30,13 +30,13 @@ def ulp(x, dtype: str) -> np.ndarray:
     return np.exp2(e - mant)
 
 
-# Spatial SwiGLU block: the same gates, except bfloat16, whose hidden activations
-# are rounded to bfloat16 before the output projection (the projection's
-# operands share the I/O type).  That second rounding alone leaves about 0.8e-2
-# of rms after the output's own half-ulp is removed (two roundings of 2^-9
-# each, the first passed through W_o with about unit gain, measured on the
-# block's workloads in an fp64 simulation); the bound is twice that.
-SWIGLU_TOLERANCE = {"f32": 1e-4, "f16": 1e-2, "bf16": 2e-2}
+# Spatial SwiGLU block: the same gates.  For bfloat16 I/O the hidden
+# activations reach the output projection as fp16, not bfloat16.  A bfloat16
+# rounding there (relative error up to 2^-8, passed through W_o at about unit
+# gain) would alone leave about 0.8e-2 of rms after the output's own half-ulp
+# is removed (fp64 simulation on the block's workloads); fp16 rounds 8 times
+# finer (2^-11).
+SWIGLU_TOLERANCE = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}
 
 
 def parity_errors(y, o, dtype: str, tolerance: dict | None = None) -> dict:

@@ -5,8 +5,11 @@
 // patches exchange information) runs as three steps on the caller's stream:
 //   1. u = x W_in           rocBLAS GEMM, fp32 accumulation; u stored in fp16
 //                           for fp16 I/O, else in fp32
-//   2. h = SiLU(u_g) * (DWConv3x3(u_v) + b)   swiglu_mix below, h in the I/O type
-//   3. out = h W_out        rocBLAS GEMM, fp32 accumulation
+//   2. h = SiLU(u_g) * (DWConv3x3(u_v) + b)   swiglu_mix below, h in the I/O
+//                           type, except fp16 for bf16 I/O
+//   3. out = h W_out        rocBLAS GEMM, fp32 accumulation; for bf16 I/O on
+//                           fp16 operands (W_out converted first) into fp32,
+//                           then rounded to bf16
 // The projections are plain dense GEMMs, the library's job; the step between
 // them is bandwidth-bound elementwise work with a 3 x 3 neighbourhood, done by
 // one kernel that stages each tile's value columns (with a one-token halo) in
@@ -17,6 +20,7 @@
 #include <rocblas/rocblas.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 
@@ -69,11 +73,11 @@ constexpr int kHaloY = kTileY + 2, kHaloX = kTileX + 2;    // 10 x 18 positions
 
 __device__ __forceinline__ f4 load4(const f4 *p) { return *p; }
 
-template <typename T, typename U>
+template <typename T, typename U, typename H>
 __global__ __launch_bounds__(kMixThreads) void swiglu_mix(const U *__restrict__ u,
                                                           const T *__restrict__ conv_w,
                                                           const T *__restrict__ conv_b,
-                                                          T *__restrict__ h, int grid_h, int grid_w,
+                                                          H *__restrict__ h, int grid_h, int grid_w,
                                                           int F, int slices, int tiles_x, int tiles_y) {
   __shared__ f4 val[kHaloY * kHaloX * kGroups];  // 46 KB
   const int tid = threadIdx.x;
@@ -157,11 +161,11 @@ __global__ __launch_bounds__(kMixThreads) void swiglu_mix(const U *__restrict__ 
   }
 }
 
-template <typename T, typename U>
+template <typename T, typename U, typename H>
 int launch_mix(const void *u_ws, const void *conv_w, const void *conv_b, void *h, int B, int grid_h,
                int grid_w, int F, hipStream_t stream) {
   const U *u = static_cast<const U *>(u_ws);
-  auto kernel = swiglu_mix<T, U>;
+  auto kernel = swiglu_mix<T, U, H>;
   const int slices = (F + kSlice - 1) / kSlice;
   const int tiles_x = (grid_w + kTileX - 1) / kTileX, tiles_y = (grid_h + kTileY - 1) / kTileY;
   const dim3 grid((unsigned)((long long)B * tiles_y * tiles_x * slices));  // < 2^31 (checked on the host)
@@ -169,11 +173,36 @@ int launch_mix(const void *u_ws, const void *conv_w, const void *conv_b, void *h
   if (profile_events(kKernelSwigluMix, stream, &t0, &t1))
     hipExtLaunchKernelGGL(kernel, grid, dim3(kMixThreads), 0, stream, t0, t1, 0, u,
                           static_cast<const T *>(conv_w), static_cast<const T *>(conv_b),
-                          static_cast<T *>(h), grid_h, grid_w, F, slices, tiles_x, tiles_y);
+                          static_cast<H *>(h), grid_h, grid_w, F, slices, tiles_x, tiles_y);
   else
     hipLaunchKernelGGL(kernel, grid, dim3(kMixThreads), 0, stream, u, static_cast<const T *>(conv_w),
-                       static_cast<const T *>(conv_b), static_cast<T *>(h), grid_h, grid_w, F, slices,
+                       static_cast<const T *>(conv_b), static_cast<H *>(h), grid_h, grid_w, F, slices,
                        tiles_x, tiles_y);
+  return (int)hipGetLastError();
+}
+
+// Elementwise format changes around the bf16 output projection, four
+// elements per thread (n is a multiple of 8): bf16 -> fp16 (exact for
+// magnitudes from 2^-17 to 65504) and fp32 -> bf16 (round to nearest even).
+constexpr int kConvThreads = 256;
+__global__ __launch_bounds__(kConvThreads) void bf16_to_f16(const uint16_t *__restrict__ src,
+                                                             _Float16 *__restrict__ dst, long long n4) {
+  for (long long i = blockIdx.x * (long long)kConvThreads + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * kConvThreads)
+    store4(dst + 4 * i, load4(src + 4 * i));
+}
+__global__ __launch_bounds__(kConvThreads) void f32_to_bf16(const float *__restrict__ src,
+                                                             uint16_t *__restrict__ dst, long long n4) {
+  for (long long i = blockIdx.x * (long long)kConvThreads + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * kConvThreads)
+    store4(dst + 4 * i, load4(src + 4 * i));
+}
+template <typename K, typename S, typename D>
+int launch_convert(K kernel, const S *src, D *dst, long long n, hipStream_t stream) {
+  const long long n4 = n / 4;
+  const unsigned blocks = (unsigned)std::min<long long>(4096, (n4 + kConvThreads - 1) / kConvThreads);
+  if (blocks == 0) return (int)hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kConvThreads), 0, stream, src, dst, n4);
   return (int)hipGetLastError();
 }
 
@@ -186,6 +215,9 @@ int elem_bytes(int dtype) { return dtype == GTR_DTYPE_F32 ? 4 : 2; }
 // u keeps the I/O precision for fp16 (one more fp16 rounding, well inside the
 // fp16 tolerance) and fp32 otherwise (bf16 has no precision to spare).
 int u_bytes_per_elem(int dtype) { return dtype == GTR_DTYPE_F16 ? 2 : 4; }
+// h is fp16 for bf16 I/O: a bf16 h would add a rounding of 2^-9 that the
+// output projection passes on at about unit gain.
+int h_bytes_per_elem(int dtype) { return dtype == GTR_DTYPE_F32 ? 4 : 2; }
 
 rocblas_datatype blas_type(int dtype) {
   return dtype == GTR_DTYPE_F32 ? rocblas_datatype_f32_r
@@ -195,6 +227,7 @@ rocblas_datatype blas_type(int dtype) {
 struct Sizes {
   long long tokens;
   size_t u_bytes, h_bytes;  // workspace parts, each rounded up to 256 bytes
+  size_t out32_bytes;       // bf16 I/O: the fp32 output and fp16 W_out, in u's part once u is read
 };
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -216,7 +249,12 @@ int validate(int B, int grid_h, int grid_w, int C, int F, int dtype, Sizes *sz) 
                      kTileX);
   sz->tokens = tokens;
   sz->u_bytes = round256((size_t)tokens * 2 * F * u_bytes_per_elem(dtype));
-  sz->h_bytes = round256((size_t)tokens * F * elem_bytes(dtype));
+  sz->h_bytes = round256((size_t)tokens * F * h_bytes_per_elem(dtype));
+  sz->out32_bytes = 0;
+  if (dtype == GTR_DTYPE_BF16) {
+    sz->out32_bytes = round256((size_t)tokens * C * sizeof(float));
+    sz->u_bytes = std::max(sz->u_bytes, sz->out32_bytes + round256((size_t)F * C * sizeof(_Float16)));
+  }
   return GTR_OK;
 }
 
@@ -325,17 +363,33 @@ int gtr_swiglu_fwd(const void *x, const void *w_in, const void *conv_w, const vo
   if (rc != GTR_OK) return rc;
   int err;
   switch (dtype) {
-    case GTR_DTYPE_F32: err = launch_mix<float, float>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
-    case GTR_DTYPE_F16: err = launch_mix<_Float16, _Float16>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
-    default: err = launch_mix<uint16_t, float>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
+    case GTR_DTYPE_F32: err = launch_mix<float, float, float>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
+    case GTR_DTYPE_F16: err = launch_mix<_Float16, _Float16, _Float16>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
+    default: err = launch_mix<uint16_t, float, _Float16>(u, conv_w, conv_b, h, B, grid_h, grid_w, F, stream); break;
   }
   if (err != (int)hipSuccess)
     return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  if (dtype != GTR_DTYPE_BF16) {
+    ProfileScope scope(kKernelSwigluOut, stream);
+    return gemm(blas, M, C, F, h, t, w_out, t, out, t, "output projection");
+  }
+  // bf16: fp16 operands (h as the mix wrote it, W_out converted) into an fp32
+  // product, rounded once to bf16; u has been read, so its part holds both
+  float *out32 = static_cast<float *>(u);
+  _Float16 *w16 = reinterpret_cast<_Float16 *>(static_cast<char *>(u) + sz.out32_bytes);
   {
     ProfileScope scope(kKernelSwigluOut, stream);
-    rc = gemm(blas, M, C, F, h, t, w_out, t, out, t, "output projection");
+    err = launch_convert(bf16_to_f16, static_cast<const uint16_t *>(w_out), w16, (long long)F * C, stream);
+    if (err != (int)hipSuccess)
+      return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+    rc = gemm(blas, M, C, F, h, rocblas_datatype_f16_r, w16, rocblas_datatype_f16_r, out32,
+              rocblas_datatype_f32_r, "output projection");
+    if (rc != GTR_OK) return rc;
+    err = launch_convert(f32_to_bf16, out32, static_cast<uint16_t *>(out), (long long)sz.tokens * C, stream);
   }
-  return rc;
+  if (err != (int)hipSuccess)
+    return set_error(GTR_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)err));
+  return GTR_OK;
 }
 
 }  // extern "C"

@@ -321,19 +321,36 @@ def test_maximum_sequence_count(path):
     assert bool(torch.isfinite(y).all())
 
 
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("grid", [(80, 81), (150, 128), (200, 200)], ids=lambda g: f"{g[0]}x{g[1]}")
-def test_long_boundary_scans(grid):
+def test_long_boundary_scans(grid, path):
     """One-chunk segments on long sequences (102, 300 and 625 chunks): boundary scans of
-    hundreds of steps, with s0 and s_final, in fp32."""
+    hundreds of steps, with s0 and s_final, in fp32.  On the one-launch path the segments form
+    13 to 79 fold blocks of 8, and the state passes from block to block."""
     gh, gw = grid
     q, k, v, g = gla_inputs.make_inputs(1, 2, gh, gw, 64, 64, "f32", "light", seed=gh + gw)
     s0 = torch.randn(1, 2, 64, 64, generator=torch.Generator().manual_seed(gh)) * 0.5
     for d in (0, 3):
-        note(f"long scan {gh}x{gw} dir={d}")
-        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1, path=2)
+        note(f"long scan {gh}x{gw} dir={d} path={path}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=1,
+                        path=PATHS[path])
         ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
         assert parity_errors(y.double().cpu().numpy(), ref, "f32")["ok"]
         assert parity_errors(sf.double().cpu().numpy(), sref, "f32")["ok"]
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3])
+def test_long_sequence_state_16bit_one_launch(seg):
+    """The one-launch path at 16-bit I/O over 12,800 tokens (200 chunks: 67 to 200 segments,
+    9 to 25 fold blocks) with s0 and s_final."""
+    q, k, v, g = gla_inputs.make_inputs(1, 3, 100, 128, 64, 64, "f16", "light", seed=40 + seg)
+    s0 = torch.randn(1, 3, 64, 64, generator=torch.Generator().manual_seed(seg)) * 0.5
+    for d in (1, 2):
+        note(f"one-launch state 100x128 seg={seg} dir={d}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg, path=1)
+        ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, "f16")["ok"]
+        assert parity_errors(sf.double().cpu().numpy(), sref, "f16")["ok"]
 
 
 def test_split_sequence_equals_whole():

@@ -1,9 +1,8 @@
 """Spatial SwiGLU block through the C ABI vs the fp64 oracle (needs an MI355X).
 
 Gate: max|y - o| / rms(o) <= 1e-4 for fp32 and <= 1e-2 for fp16; bf16 is gated
-on the excess over the output's half-ulp, <= 2e-2, because its hidden
-activations are rounded to bf16 before the output projection (see
-oracle/compare.py for the derivation).
+on the excess over the output's half-ulp, <= 1e-2 (its hidden activations reach
+the output projection as fp16; oracle/compare.py gives the arithmetic).
 """
 import sys
 
@@ -52,6 +51,16 @@ def test_small_shapes(shape, dtype, bias):
     B, gh, gw, C, F = shape
     ins = gla_inputs.make_swiglu_inputs(B, gh, gw, C, F, dtype, seed=sum(shape), bias=bias)
     check(ins, dtype, "small")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_other_dtypes_at_workload_width(dtype):
+    """The 40x40 workload's widths (C 384, F 1024) in bf16 and fp32: bf16 takes the fp16
+    output projection and must meet the same 1e-2 as fp16."""
+    w = gla_inputs.swiglu_workload(1)
+    ins = gla_inputs.make_swiglu_inputs(w.B, w.grid_h, w.grid_w, w.C, w.F, dtype, seed=w.seed + 1)
+    e = check(ins, dtype, f"{w.name} as {dtype}")
+    note(f"  err_raw={e['err_raw']:.3g} err_excess={e['err_excess']:.3g}")
 
 
 @pytest.mark.parametrize("idx", [1, 2])
