@@ -73,7 +73,7 @@
  *     groups into a fold block (results change only by rounding).
  *
  * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
- * case; the one-launch path takes d_k <= 64); 0 <= grid_h*grid_w <= 2^23 and
+ * case); 0 <= grid_h*grid_w <= 2^23 and
  * grid_h*grid_w*max(d_k, d_v)*element bytes <= 2^31; 0 <= B*H <= 2^20.
  * Pointers must be 16-byte aligned.
  *
@@ -119,14 +119,13 @@ extern "C" {
 /* launch structure (entry points _ex, _check, _workspace_bytes, _plan) */
 #define GTR_PATH_AUTO 0   /* chosen by the library from the shape */
 #define GTR_PATH_FUSED 1  /* one kernel: segment aggregates, a fixed-order fold within blocks of
-                             segments and a chain between blocks, outputs; d_k <= 64 */
+                             segments and a chain between blocks, outputs */
 #define GTR_PATH_SPLIT 2  /* three kernels: segment aggregates, boundary scan, outputs */
 
 /* return codes: 0 on success, negative on error */
 #define GTR_OK 0
 #define GTR_ERR_INVALID_ARG (-1)  /* null pointer, negative or too large size, bad direction/dtype/path */
-#define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v above 128 or not a multiple of 4;
-                                     d_k > 64 on GTR_PATH_FUSED */
+#define GTR_ERR_UNSUPPORTED (-2)  /* d_k or d_v above 128 or not a multiple of 4 */
 #define GTR_ERR_ALIGNMENT (-3)    /* a pointer is not 16-byte aligned */
 #define GTR_ERR_ALIAS (-4)        /* out (or s_final) overlaps an input */
 #define GTR_ERR_NO_DEVICE (-5)    /* no usable HIP device */
@@ -191,9 +190,10 @@ int gtr_gla_fwd_bf16(const void *q, const void *k, const void *v, const void *lo
  *   path     GTR_PATH_AUTO, GTR_PATH_FUSED or GTR_PATH_SPLIT.
  * Any segment length and path give the same result up to rounding; the same
  * shape, segment length and path give bitwise the same result on every call.
- * GTR_PATH_FUSED keeps a 16,640-byte slot per segment of a sequence and
- * refuses (GTR_ERR_INVALID_ARG) shapes whose slots exceed 2^31 bytes per
- * sequence (more than 129055 segments).
+ * GTR_PATH_FUSED keeps a 16,640-byte slot per segment and 64-wide key block
+ * of a sequence and refuses (GTR_ERR_INVALID_ARG) shapes whose slots exceed
+ * 2^31 bytes per sequence (more than 129055 segments at d_k <= 64, 64527
+ * above); with d_k > 64 and fp32 I/O its segments hold at most 2 chunks.
  * The initial state makes a long scan splittable: running the two halves of
  * a sequence with the first half's s_final as the second half's s0 equals one
  * call on the whole sequence.
@@ -234,6 +234,8 @@ size_t gtr_gla_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d_k,
 /* The plan the library uses for a shape: chunks per segment, segments per
  * sequence, and 1 if one fused kernel runs (0: three kernels).  The kernels
  * walk B*H*ceil(d_v/64) sequences, one per 64-wide block of value columns.
+ * The plan is that of 16-bit I/O (fp32 I/O differs only on the one-launch
+ * path with d_k > 64, whose segments hold at most 2 chunks).
  * Any output pointer may be NULL.  Returns 0 or an argument error. */
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,
                  int path, int *seg_len, int *n_seg, int *fused);

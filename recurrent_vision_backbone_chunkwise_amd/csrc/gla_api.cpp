@@ -82,7 +82,7 @@ bool auto_fused(long long seqs, int nk, int n_chunk) {
 
 // `bh` counts the sequences the kernels walk (B*H*value blocks); `nk` the key
 // blocks, which only the three-launch path handles beyond one.
-void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, Shape *sh) {
+void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, int dtype, Shape *sh) {
   sh->fold_block = 0;
   if (bh == 0 || n_chunk == 0) {
     sh->fused = false;
@@ -93,8 +93,11 @@ void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, S
               (path == GTR_PATH_AUTO && chunks_per_segment <= gtr::kMaxFusedChunks && auto_fused(bh, nk, n_chunk));
   long long len = chunks_per_segment;
   if (sh->fused) {
-    if (len <= 0) len = gtr::kMaxFusedChunks;
-    len = std::min<long long>(len, gtr::kMaxFusedChunks);
+    // each kept chunk holds a query tile per key block in LDS: with fp32
+    // operands and two key blocks, two chunks fill it
+    const int max_len = nk == 2 && dtype == GTR_DTYPE_F32 ? 2 : gtr::kMaxFusedChunks;
+    if (len <= 0) len = max_len;
+    len = std::min<long long>(len, max_len);
   } else if (len <= 0) {
     len = gtr::split_segment_length(bh, n_chunk);
   }
@@ -144,13 +147,12 @@ int validate_shape(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int d
   shape->seqs = bh * shape->nvb;
   shape->empty = bh == 0 || n_tok == 0;
   shape->n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  if (path == GTR_PATH_FUSED && shape->nk > 1)
-    return fail(GTR_ERR_UNSUPPORTED, "one-launch path: d_k=%d, at most 64", d_k);
-  plan(shape->seqs, shape->nk, shape->n_chunk, path, chunks_per_segment, shape);
+  plan(shape->seqs, shape->nk, shape->n_chunk, path, chunks_per_segment, dtype, shape);
   if (shape->seqs * shape->n_seg * shape->nk > 0x7fffffffLL)
     return fail(GTR_ERR_INVALID_ARG, "too many segments (%lld)", shape->seqs * shape->n_seg);
   // a sequence's payload slots are addressed with 32-bit byte offsets
-  if (shape->fused && (long long)shape->n_seg * gtr::kSlotFloats * (long long)sizeof(float) >= (1LL << 31))
+  if (shape->fused &&
+      (long long)shape->n_seg * shape->nk * gtr::kSlotFloats * (long long)sizeof(float) >= (1LL << 31))
     return fail(GTR_ERR_INVALID_ARG,
                 "one-launch path: %d segments of %d chunks exceed its per-sequence workspace; use longer "
                 "segments, GTR_PATH_SPLIT or GTR_PATH_AUTO",
@@ -533,7 +535,7 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
     void *ws = nullptr;
     int *sync = nullptr;
     long long *flags = nullptr;
-    const size_t bytes = sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg)
+    const size_t bytes = sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg, sh.nk)
                                   : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk);
     rc = get_workspace(device, stream, bytes, sh.fused, sh.fused ? sh.seqs * sh.n_seg : 0, &ws, &sync, &flags);
     if (rc != GTR_OK) return rc;
@@ -547,7 +549,7 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   }
   if (sh.fused) {
     const DeviceShape &ds = device_shape(device);
-    const int occupancy = dtype == GTR_DTYPE_F32 ? 1 : (sh.seg_len == 1 ? 3 : 2);
+    const int occupancy = dtype == GTR_DTYPE_F32 || sh.nk == 2 ? 1 : (sh.seg_len == 1 ? 3 : 2);
     a.fold_block = sh.fold_block;
     a.xcds = ds.xcds;
     a.batch = (int)std::min<long long>(kMaxBatch, (sh.seqs + ds.xcds - 1) / ds.xcds);
@@ -657,7 +659,8 @@ size_t gtr_gla_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d_k,
       GTR_OK)
     return 0;
   if (sh.empty) return 0;
-  return (sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg) : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk)) +
+  return (sh.fused ? gtr::fused_workspace_bytes(sh.seqs, sh.n_seg, sh.nk)
+                   : gtr::workspace_bytes(sh.seqs, sh.n_seg, sh.nk)) +
          (sh.fused ? gtr::sync_words((size_t)(sh.seqs * sh.n_seg)) * sizeof(int) : 0);
 }
 

@@ -90,9 +90,10 @@ inline size_t workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
   return seqs * n_seg * nk * (2 * (size_t)kStateElems + kHead) * sizeof(float);
 }
 // Float workspace bytes of the one-launch path: one payload slot per segment
-// (aggregate or block prefix, and decays), none for a single segment.
-inline size_t fused_workspace_bytes(size_t seqs, size_t n_seg) {
-  return n_seg > 1 ? seqs * n_seg * (size_t)kSlotFloats * sizeof(float) : 0;
+// and key block (aggregate or block prefix, and decays), none for a single
+// segment.
+inline size_t fused_workspace_bytes(size_t seqs, size_t n_seg, size_t nk) {
+  return n_seg > 1 ? seqs * n_seg * nk * (size_t)kSlotFloats * sizeof(float) : 0;
 }
 // Synchronisation words for `n_flags` segment flags.
 inline size_t sync_words(size_t n_flags) { return kSyncFlagWord + 2 * n_flags; }

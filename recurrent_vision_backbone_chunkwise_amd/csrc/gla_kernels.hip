@@ -790,7 +790,6 @@ template <class Io, typename Op, int kMode, int NK, int NQ>
 __device__ __forceinline__ void chunk(const Seq &sq, Smem<Op, NQ> &sm, Rows<Io> &x, int c, int c_end,
                                       int wave, int lane, int slot, f4 (*S)[4], f4 *seg_dec, f4 *keep,
                                       typename OpT<Op>::Bits *ot, uint32_t *pend, bool have_pend) {
-  static_assert(kMode != kKeep || NK == 1, "outputs kept across a segment use one key block");
   constexpr bool kOut = kMode != kAgg;
   op8<Op> vf[2];
   f4 part[4];  // outputs summed over the key blocks so far
@@ -814,7 +813,10 @@ __device__ __forceinline__ void chunk(const Seq &sq, Smem<Op, NQ> &sm, Rows<Io> 
         for (int r = 0; r < 4; ++r) pend[r] = cur[r];
       }
     }
-    prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, slot);
+    // kept outputs need each key block's query tile and decays until the
+    // segment's entering state is known: LDS slots slot * NK + kb
+    const int qslot = kMode == kKeep ? slot * NK + kb : slot;
+    prep_chunk<Io, Op, kOut>(sm, qs, ks, wave, lane, qslot);
     if (first) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) vf[b] = frag_tr(sm.vv, 32 * b, 16 * wave, lane);
@@ -822,7 +824,7 @@ __device__ __forceinline__ void chunk(const Seq &sq, Smem<Op, NQ> &sm, Rows<Io> 
     if (kMode != kStore && wave == 0 && lane < 16) {
       f4 t[4];
       sub_block_products(sm, lane, t);
-      if constexpr (kMode == kKeep) *reinterpret_cast<f4 *>(&sm.dcum[slot][4 * lane]) = seg_dec[kb];
+      if constexpr (kMode == kKeep) *reinterpret_cast<f4 *>(&sm.dcum[qslot][4 * lane]) = seg_dec[kb];
       seg_dec[kb] *= t[0] * t[1] * t[2] * t[3];
     }
     lds_sync();
@@ -831,13 +833,13 @@ __device__ __forceinline__ void chunk(const Seq &sq, Smem<Op, NQ> &sm, Rows<Io> 
       lds_sync();
       f4 *acc = kMode == kKeep ? keep : part;
       if (kb == 0 && kb + 1 == NK)
-        outputs<Io, Op, kMode, false, true>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+        outputs<Io, Op, kMode, false, true>(sm, wave, lane, qslot, vf, S[kb], ot, acc);
       else if (kb == 0)
-        outputs<Io, Op, kMode, false, false>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+        outputs<Io, Op, kMode, false, false>(sm, wave, lane, qslot, vf, S[kb], ot, acc);
       else if (kb + 1 == NK)
-        outputs<Io, Op, kMode, true, true>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+        outputs<Io, Op, kMode, true, true>(sm, wave, lane, qslot, vf, S[kb], ot, acc);
       else
-        outputs<Io, Op, kMode, true, false>(sm, wave, lane, slot, vf, S[kb], ot, acc);
+        outputs<Io, Op, kMode, true, false>(sm, wave, lane, qslot, vf, S[kb], ot, acc);
     }
     carry_state<Op>(sm, lane, vf, S[kb]);
   }
@@ -1149,14 +1151,15 @@ __device__ void take_work(const Params &p, int slot, unsigned long long v, int *
   }
 }
 
-// A sequence's payload slots: per segment, a 64x64 fp32 state (the segment's
-// aggregate, or for a block's last segment the block prefix) in f4 register
-// order, then the segment's 64 decays.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const Params &p, int bh) {
-  return __builtin_amdgcn_make_buffer_rsrc(p.agg + (size_t)bh * p.n_seg * kSlotFloats, (short)0,
-                                           p.n_seg * kSlotFloats * (int)sizeof(float), 0x00020000);
+// A sequence's payload slots: per segment and key block (slot s * NK + kb), a
+// 64x64 fp32 state (the segment's aggregate, or for a block's last segment
+// the block prefix) in f4 register order, then the segment's 64 decays of
+// that key block.
+template <int NK> __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const Params &p, int bh) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.agg + (size_t)bh * p.n_seg * NK * kSlotFloats, (short)0,
+                                           p.n_seg * NK * kSlotFloats * (int)sizeof(float), 0x00020000);
 }
-// Byte offsets: f4 `it` of thread (wave, lane) of segment s's state (rows
+// Byte offsets: f4 `it` of thread (wave, lane) of slot s's state (rows
 // 16 it + 4(lane/16) + 0..3, column 16 wave + lane%16), and decay `row`.
 __device__ __forceinline__ int slot_state_off(int s, int wave, int it, int lane) {
   return (s * kSlotFloats + ((wave * 4 + it) * 64 + lane) * 4) * (int)sizeof(float);
@@ -1171,16 +1174,19 @@ __device__ __forceinline__ void slot_store(__amdgpu_buffer_rsrc_t r, int off, f4
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
 }
 
-// Writes state X (and, kDecay, the decays `dec` held by wave 0, lanes < 16)
-// to segment s's slot, then raises its flag.  Every thread of the workgroup
-// calls it.
-template <bool kDecay>
+// Writes the NK key blocks of state X (and, kDecay, their decays dec[kb]
+// held by wave 0, lanes < 16) to segment s's slots, then raises its flag.
+// Every thread of the workgroup calls it.
+template <bool kDecay, int NK>
 __device__ __forceinline__ void publish(const Params &p, __amdgpu_buffer_rsrc_t r, int bh, int s, int tid,
-                                        const f4 *X, f4 dec, long long want) {
+                                        const f4 (*X)[4], const f4 *dec, long long want) {
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) slot_store(r, slot_state_off(s, wave, it, lane), X[it]);
-  if (kDecay && wave == 0 && lane < 16) slot_store(r, slot_decay_off(s, 4 * lane), dec);
+  for (int kb = 0; kb < NK; ++kb) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) slot_store(r, slot_state_off(s * NK + kb, wave, it, lane), X[kb][it]);
+    if (kDecay && wave == 0 && lane < 16) slot_store(r, slot_decay_off(s * NK + kb, 4 * lane), dec[kb]);
+  }
   stores_complete();  // this wave's payload is in L2 ...
   __syncthreads();    // ... for every wave ...
   if (tid == 0)       // ... before the flag is raised
@@ -1188,8 +1194,10 @@ __device__ __forceinline__ void publish(const Params &p, __amdgpu_buffer_rsrc_t 
 }
 
 // Workgroups per CU the LDS allows: fp32 operands take 100-137 KB, one;
-// 16-bit ones 54 KB for one-chunk segments, three, and up to 73 KB, two.
-template <typename Op, int kSeg> constexpr int kFusedOccupancy = sizeof(Op) == 4 ? 1 : (kSeg == 1 ? 3 : 2);
+// 16-bit ones 54 KB for one-chunk segments, three, and up to 73 KB, two; two
+// key blocks (a query tile per key block and kept chunk) 64-98 KB, one.
+template <typename Op, int kSeg, int NK>
+constexpr int kFusedOccupancy = sizeof(Op) == 4 || NK == 2 ? 1 : (kSeg == 1 ? 3 : 2);
 
 // One launch.  A persistent grid; each workgroup repeatedly takes a segment
 // (at most kSeg chunks) of a sequence of its XCD and:
@@ -1208,10 +1216,10 @@ template <typename Op, int kSeg> constexpr int kFusedOccupancy = sizeof(Op) == 4
 //      decay from the segment start to the chunk, and stores the outputs.
 // Inputs are read from HBM once.  The fold order depends only on the shape,
 // so a call gives bitwise the same result however its workgroups run.
-template <class Io, typename Op, int kSeg>
+template <class Io, typename Op, int kSeg, int NK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    kFusedOccupancy<Op, kSeg>, kFusedOccupancy<Op, kSeg>))) void gla_fused(Params p) {
-  __shared__ Smem<Op, kSeg> sm;
+    kFusedOccupancy<Op, kSeg, NK>, kFusedOccupancy<Op, kSeg, NK>))) void gla_fused(Params p) {
+  __shared__ Smem<Op, kSeg * NK> sm;
   __shared__ int s_work[2];
   __shared__ int s_fail;
   __shared__ long long s_epoch;
@@ -1243,30 +1251,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if (tid == kThreads - 1) next_word = work_add(p, slot);
     const int c0 = seg * p.seg_len, c1 = min(c0 + p.seg_len, p.n_chunk);
     const Seq sq = seq_of<Io>(p, bh);
-    const __amdgpu_buffer_rsrc_t slots = slot_rsrc(p, bh);
+    const __amdgpu_buffer_rsrc_t slots = slot_rsrc<NK>(p, bh);
 
     // 1. the segment from a zero state
     Rows<Io> x;
     load_chunk<Io, true, true>(sq, c0, 0, wave, lane, x);
     f4 keep[kSeg][4];
-    f4 L[4] = {};
-    f4 sdec = {1.f, 1.f, 1.f, 1.f};
+    f4 L[NK][4] = {};
+    f4 sdec[NK];
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) sdec[kb] = f4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int j = 0; j < kSeg; ++j)
       if (c0 + j < c1)
-        chunk<Io, Op, kKeep, 1>(sq, sm, x, c0 + j, c1, wave, lane, j, &L, &sdec, keep[j], nullptr, nullptr,
-                                false);
-    // decay across the whole segment; tot is not read after a chunk's last
-    // barrier, so wave 0 may overwrite it while others finish
+        chunk<Io, Op, kKeep, NK>(sq, sm, x, c0 + j, c1, wave, lane, j, L, sdec, keep[j], nullptr, nullptr,
+                                 false);
+    // decay across the whole segment (key dim 64 kb + i at kb * 64 + i); tot
+    // is not read after a chunk's last barrier, so wave 0 may overwrite it
+    // while others finish
     float *segdec = sm.tot;
-    if (wave == 0 && lane < 16) *reinterpret_cast<f4 *>(&segdec[4 * lane]) = sdec;
+    static_assert(sizeof(sm.tot) >= NK * kHead * sizeof(float), "segment decays fit in tot");
+    if (wave == 0 && lane < 16)
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) *reinterpret_cast<f4 *>(&segdec[kb * kHead + 4 * lane]) = sdec[kb];
     lds_sync();  // segdec visible; qs (the fold's scratch below) no longer read
 
     // 2. the aggregate, for the later segments of this block
     const int blk0 = seg - seg % G;          // first segment of this block
     const bool blk_last = seg % G == G - 1;  // publishes the block prefix instead
     const bool has_next = seg + 1 < p.n_seg;
-    if (has_next && !blk_last) publish<true>(p, slots, bh, seg, tid, L, sdec, want);
+    if (has_next && !blk_last) publish<true, NK>(p, slots, bh, seg, tid, L, sdec, want);
 
     // 3. S_prev: first the aggregates of this block's earlier segments ...
     const int n_a = seg - blk0;
@@ -1275,79 +1289,108 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const __amdgpu_buffer_rsrc_t fl = flag_rsrc(p, bh);
     if (have_prev && tid < n_a && !wait_flag(p.sync, fl, blk0 + tid, want)) s_fail = 1;
     __syncthreads();  // every awaited aggregate is visible
-    f4 S[4] = {};
+    f4 S[NK][4] = {};
     if (have_prev) {
       // Horner's rule over the block's earlier segments, oldest first:
-      // X <- D_u X + A_u, and prod = product of their decays, for the entering
-      // term.  Each round trip brings kBatch aggregates and their decays; the
-      // decays (one per thread) go through LDS to the rows each thread holds.
-      constexpr int kBatch = kFusedOccupancy<Op, kSeg> > 2 ? 2 : 4;  // aggregates per round trip
-      float *dlds = reinterpret_cast<float *>(sm.qs);                 // [2][kBatch][64], alternating
-      f4 prod[4];
+      // X <- D_u X + A_u (per key block), and prod = product of their decays,
+      // for the entering term.  Each round trip brings kBatch aggregates and
+      // their decays; the decays (one per thread) go through LDS to the rows
+      // each thread holds.
+      constexpr int kBatch = NK == 2 || kFusedOccupancy<Op, kSeg, NK> > 2 ? 2 : 4;  // aggregates per round trip
+      constexpr int kDecays = NK * kHead;                                            // decays per aggregate
+      static_assert(kBatch * kDecays <= kThreads, "one decay per thread");
+      float *dlds = reinterpret_cast<float *>(sm.qs);  // [2][kBatch][NK * 64], alternating
+      static_assert(sizeof(sm.qs) >= 2 * kBatch * kDecays * sizeof(float), "decays fit in the query tile");
+      f4 prod[NK][4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) prod[it] = f4{1.f, 1.f, 1.f, 1.f};
+      for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) prod[kb][it] = f4{1.f, 1.f, 1.f, 1.f};
       for (int u0 = 0, half = 0; u0 < n_a; u0 += kBatch, half ^= 1) {
-        f4 a[kBatch][4];
+        f4 a[kBatch][NK][4];
 #pragma unroll
         for (int v = 0; v < kBatch; ++v)
 #pragma unroll
-          for (int it = 0; it < 4; ++it)
-            a[v][it] = slot_load(slots, slot_state_off(blk0 + min(u0 + v, n_a - 1), wave, it, lane));
-        if (tid < kBatch * kHead)
-          dlds[half * kBatch * kHead + tid] = __builtin_bit_cast(
+          for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+              a[v][kb][it] =
+                  slot_load(slots, slot_state_off((blk0 + min(u0 + v, n_a - 1)) * NK + kb, wave, it, lane));
+        if (tid < kBatch * kDecays) {
+          const int v = tid / kDecays, kb = tid % kDecays / kHead, row = tid % kHead;
+          dlds[half * kBatch * kDecays + tid] = __builtin_bit_cast(
               float, __builtin_amdgcn_raw_buffer_load_b32(
-                         slots, slot_decay_off(blk0 + min(u0 + tid / kHead, n_a - 1), tid % kHead), 0, kNonTemporal));
+                         slots, slot_decay_off((blk0 + min(u0 + v, n_a - 1)) * NK + kb, row), 0, kNonTemporal));
+        }
         lds_sync();
 #pragma unroll
         for (int v = 0; v < kBatch; ++v)
           if (u0 + v < n_a)
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-              const f4 d = *reinterpret_cast<const f4 *>(&dlds[(half * kBatch + v) * kHead + 16 * it + 4 * g]);
-              S[it] = d * S[it] + a[v][it];
-              prod[it] *= d;
-            }
+            for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+              for (int it = 0; it < 4; ++it) {
+                const f4 d = *reinterpret_cast<const f4 *>(
+                    &dlds[(half * kBatch + v) * kDecays + kb * kHead + 16 * it + 4 * g]);
+                S[kb][it] = d * S[kb][it] + a[v][kb][it];
+                prod[kb][it] *= d;
+              }
       }
       if (has_p) {  // the chain between blocks: this wait is its only step per block
         if (tid == 0 && !wait_flag(p.sync, fl, blk0 - 1, want)) s_fail = 1;
         __syncthreads();
 #pragma unroll
-        for (int it = 0; it < 4; ++it) S[it] += prod[it] * slot_load(slots, slot_state_off(blk0 - 1, wave, it, lane));
+        for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            S[kb][it] += prod[kb][it] * slot_load(slots, slot_state_off((blk0 - 1) * NK + kb, wave, it, lane));
       } else if (p.s0) {
         const UserState u = user_state(p, p.s0, bh, wave, lane);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          f4 e;
+        for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            e[r] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(u.r, user_state_off(u, 16 * it + 4 * g + r), 0, 0));
-          S[it] += prod[it] * e;
-        }
+          for (int it = 0; it < 4; ++it) {
+            f4 e;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              e[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   u.r, user_state_off(u, kHead * kb + 16 * it + 4 * g + r), 0, 0));
+            S[kb][it] += prod[kb][it] * e;
+          }
       }
       if (s_fail) {  // a wait gave up: poison this segment and everything after it
 #pragma unroll
-        for (int it = 0; it < 4; ++it) S[it] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            S[kb][it] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       }
     }
 
     // 4. the state after the segment: the next block's entering term, or s_final
     if (blk_last && has_next) {
-      f4 after[4];
+      f4 after[NK][4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) after[it] = L[it] + *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
-      publish<false>(p, slots, bh, seg, tid, after, sdec, want);
+      for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          after[kb][it] =
+              L[kb][it] + *reinterpret_cast<const f4 *>(&segdec[kb * kHead + 16 * it + 4 * g]) * S[kb][it];
+      publish<false, NK>(p, slots, bh, seg, tid, after, sdec, want);
     }
     if (p.s_final && !has_next) {
       const UserState u = user_state(p, p.s_final, bh, wave, lane);
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const f4 after = L[it] + *reinterpret_cast<const f4 *>(&segdec[16 * it + 4 * g]) * S[it];
+      for (int kb = 0; kb < NK; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(after[r]), u.r, user_state_off(u, 16 * it + 4 * g + r),
-                                                0, 0);
-      }
+        for (int it = 0; it < 4; ++it) {
+          const f4 after =
+              L[kb][it] + *reinterpret_cast<const f4 *>(&segdec[kb * kHead + 16 * it + 4 * g]) * S[kb][it];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(after[r]), u.r,
+                                                  user_state_off(u, kHead * kb + 16 * it + 4 * g + r), 0, 0);
+        }
     }
 
     // 5. add each chunk's share of S_prev and store (16-bit operands: S_prev
@@ -1355,26 +1398,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const uint32_t col = val_col<Io>(sq, 16 * wave + 4 * g);
     constexpr int LD = OpT<Op>::LD;
     constexpr bool kScaled = sizeof(Op) == 2;
-    float unscale = 1.f;
-    const float scale = kScaled && have_prev ? state_scale(S, unscale) : 1.f;
+    float unscale[NK], scale[NK];
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+      unscale[kb] = 1.f;
+      scale[kb] = kScaled && have_prev ? state_scale(S[kb], unscale[kb]) : 1.f;
+    }
 #pragma unroll
     for (int j = 0; j < kSeg; ++j) {
       if (c0 + j >= c1) break;
       if (have_prev) {
-        op8<Op> sf[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 4 * g]) * scale;
-          const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[j][32 * kb + 16 + 4 * g]) * scale;
-          sf[kb] = cat(to4<Op>(S[2 * kb] * d0), to4<Op>(S[2 * kb + 1] * d1));
-        }
+        for (int kb = 0; kb < NK; ++kb) {  // each key block's share, scaled on its own
+          const int qslot = j * NK + kb;
+          op8<Op> sf[2];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          f4 st = {0.f, 0.f, 0.f, 0.f};
+          for (int h = 0; h < 2; ++h) {
+            const f4 d0 = *reinterpret_cast<const f4 *>(&sm.dcum[qslot][32 * h + 4 * g]) * scale[kb];
+            const f4 d1 = *reinterpret_cast<const f4 *>(&sm.dcum[qslot][32 * h + 16 + 4 * g]) * scale[kb];
+            sf[h] = cat(to4<Op>(S[kb][2 * h] * d0), to4<Op>(S[kb][2 * h + 1] * d1));
+          }
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            st = mma(sf[kb], frag_row<Op>(&sm.qh[j][(16 * tt + l16) * LD + 32 * kb + 4 * g]), st);
-          keep[j][tt] += st * unscale;
+          for (int tt = 0; tt < 4; ++tt) {
+            f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              st = mma(sf[h], frag_row<Op>(&sm.qh[qslot][(16 * tt + l16) * LD + 32 * h + 4 * g]), st);
+            keep[j][tt] += st * unscale[kb];
+          }
         }
       }
 #pragma unroll
@@ -1439,22 +1490,29 @@ int launch_typed(const LaunchArgs &a) {
     if (a.fused || a.outputs_only || !a.states_only) return (int)hipErrorInvalidValue;
   }
   if (a.fused) {
-    if constexpr (NK != 1 || kStatesOnly || Io::kLagGates) {
-      return (int)hipErrorInvalidValue;  // the planner keeps d_k > 64 off this path
+    if constexpr (kStatesOnly || Io::kLagGates) {
+      return (int)hipErrorInvalidValue;
     } else {
       p.fold_block = a.fold_block;
       p.batch = a.batch;
       p.n_batch = (a.bh + a.batch - 1) / a.batch;
       p.n_pre = min(p.n_batch, min(a.xcds, kXcdSlots));
       const unsigned grid = (unsigned)a.grid;
+      // fp32 operands with two key blocks keep at most two chunks (three
+      // would need 184 KB of LDS); the planner caps the segment length
+      constexpr int kMaxSeg = sizeof(Op) == 4 && NK == 2 ? 2 : kMaxFusedChunks;
       if (a.seg_len <= 1)
-        launch(kKernelFused, gla_fused<Io, Op, 1>, grid, a.stream, p);
+        launch(kKernelFused, gla_fused<Io, Op, 1, NK>, grid, a.stream, p);
       else if (a.seg_len == 2)
-        launch(kKernelFused, gla_fused<Io, Op, 2>, grid, a.stream, p);
-      else if (a.seg_len == 3)
-        launch(kKernelFused, gla_fused<Io, Op, 3>, grid, a.stream, p);
-      else
-        return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
+        launch(kKernelFused, gla_fused<Io, Op, 2, NK>, grid, a.stream, p);
+      else if constexpr (kMaxSeg >= 3) {
+        if (a.seg_len == 3)
+          launch(kKernelFused, gla_fused<Io, Op, 3, NK>, grid, a.stream, p);
+        else
+          return (int)hipErrorInvalidValue;  // the planner caps fused segments at kMaxFusedChunks
+      } else {
+        return (int)hipErrorInvalidValue;
+      }
       return (int)hipGetLastError();
     }
   }

@@ -163,7 +163,8 @@ HEAD_DIMS = [(32, 32), (32, 64), (64, 32), (128, 64), (64, 128), (128, 128), (32
 def test_head_dims(dims, dtype):
     dk, dv = dims
     q, k, v, g = gla_inputs.make_inputs(2, 3, 9, 17, dk, dv, dtype, "light", seed=dk * 1000 + dv)
-    runs = [(2, 1), (2, 3), (0, 0)] + ([(1, 2)] if dk <= 64 else [])  # (path, chunks per segment)
+    # (path, chunks per segment); above 64 key dims the one-launch path keeps both key blocks
+    runs = [(2, 1), (2, 3), (0, 0), (1, 2)] if dk <= 64 else [(2, 1), (1, 3), (0, 0), (1, 2)]
     for d in range(4):
         path, seg = runs[d % len(runs)]
         check(q, k, v, g, d, dtype, f"dk={dk} dv={dv}", path=path, chunks_per_segment=seg)
@@ -177,7 +178,7 @@ def test_head_dims_state(dims, dtype):
     B, H, gh, gw = 1, 2, 11, 13
     q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, dk, dv, dtype, "light", seed=dk + dv)
     s0 = torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(dk * dv)) * 0.5
-    runs = [(2, 1), (2, 4)] + ([(1, 1), (1, 3)] if dk <= 64 else [])
+    runs = [(2, 1), (2, 4), (1, 1), (1, 3)]
     for d, (path, seg) in zip(range(4), runs * 2):
         note(f"state dk={dk} dv={dv} dir={d} dtype={dtype} path={path} seg={seg}")
         y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg,
@@ -193,8 +194,25 @@ def test_head_dims_state(dims, dtype):
 def test_gate_extremes_wide_heads(gate, dtype):
     """The exact diagonal tiles of the second key block, and masked value columns."""
     q, k, v, g = gla_inputs.make_inputs(1, 2, 13, 11, 128, 96, dtype, gate, seed=21)
-    for d, seg in ((1, 1), (3, 2)):
-        check(q, k, v, g, d, dtype, f"wide gate={gate}", path=2, chunks_per_segment=seg)
+    for d, seg, path in ((1, 1, 2), (3, 2, 2), (0, 3, 1), (2, 1, 1)):
+        check(q, k, v, g, d, dtype, f"wide gate={gate}", path=path, chunks_per_segment=seg)
+
+
+@pytest.mark.parametrize("dims", [(128, 64), (96, 128)], ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_wide_keys_one_launch_long(dims, dtype):
+    """Two key blocks on the one-launch path over 4,096 tokens (22 to 64 segments, up to 8 fold
+    blocks): both blocks' aggregates, decays and prefixes pass between workgroups; with s0 and
+    s_final."""
+    dk, dv = dims
+    q, k, v, g = gla_inputs.make_inputs(1, 3, 64, 64, dk, dv, dtype, "light", seed=dk + 7 * dv)
+    s0 = torch.randn(1, 3, dk, dv, generator=torch.Generator().manual_seed(dk)) * 0.5
+    for d, seg in ((0, 3), (3, 1), (2, 2)):
+        note(f"wide keys one launch dk={dk} dv={dv} dtype={dtype} dir={d} seg={seg}")
+        y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg, path=1)
+        ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+        assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
+        assert parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")["ok"]
 
 
 # ---- initial / final state -----------------------------------------------------------------

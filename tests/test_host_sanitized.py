@@ -45,8 +45,10 @@ int main(void) {
   expect(gtr_gla_fwd(NULL, p, p, p, c + 4096, 1, 1, 4, 4, 64, 64, 0, 1, 0), GTR_ERR_INVALID_ARG, "null q");
   expect(gtr_gla_fwd(p, p, p, p, c + 4096, 1, 1, 1 << 12, 1 << 12, 64, 64, 0, 1, 0), GTR_ERR_INVALID_ARG, "2^24 tokens");
   expect(gtr_gla_fwd(p, p, p, p, c + 4096, 1 << 11, 1 << 10, 4, 4, 64, 64, 0, 1, 0), GTR_ERR_INVALID_ARG, "2^21 sequences");
-  expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 4, 4, 128, 64, 0, 1, NULL, NULL, 0, GTR_PATH_FUSED, 0),
-         GTR_ERR_UNSUPPORTED, "fused d_k 128");
+  expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 4, 4, 132, 64, 0, 1, NULL, NULL, 0, GTR_PATH_FUSED, 0),
+         GTR_ERR_UNSUPPORTED, "fused d_k 132");
+  expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 2048, 2048, 128, 64, 0, 1, NULL, NULL, 1, GTR_PATH_FUSED, 0),
+         GTR_ERR_INVALID_ARG, "fused segments of two key blocks");
   expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 4, 4, 64, 64, 0, 1, NULL, NULL, 0, 7, 0), GTR_ERR_INVALID_ARG, "path");
   expect(gtr_gla_fwd_ex(p, p, p, p, c + 4096, 1, 1, 2048, 4096, 64, 64, 0, 1, NULL, NULL, 1, GTR_PATH_FUSED, 0),
          GTR_ERR_INVALID_ARG, "fused segments");
