@@ -377,6 +377,9 @@ def bwd_main(args):
     if not torch.cuda.is_available():
         raise RuntimeError("no GPU visible")
     w = gla_inputs.workload(args.workload)
+    if args.head_dims and tuple(args.head_dims) != (w.d_k, w.d_v):
+        dk, dv = args.head_dims
+        w = dataclasses.replace(w, d_k=dk, d_v=dv, name=f"{w.name}_dk{dk}_dv{dv}")
     cpu_in = [gla_inputs.workload_inputs(w, layer) for layer in range(len(w.directions))]
     douts = [gla_inputs.make_output_grad(ins[2].shape, w.dtype, seed=9000 + i) for i, ins in enumerate(cpu_in)]
     ins = [[t.to("cuda:0") for t in x] + [d.to("cuda:0")] for x, d in zip(cpu_in, douts)]

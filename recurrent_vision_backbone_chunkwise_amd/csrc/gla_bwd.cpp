@@ -36,17 +36,19 @@ struct Layout {  // byte offsets into the workspace
   size_t fwd, rev, sfin, g0, totals, dq_off, dk_off, total;
 };
 
-Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v) {
+// nk: 64-wide key blocks; the fp32 gradient terms hold one key block at a time.
+Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int nk) {
   Layout l{};
-  const size_t scan = round256(gtr::workspace_bytes((size_t)bh, (size_t)n_chunk, 1));
+  const int kw = d_k < gtr::kHead ? d_k : gtr::kHead;
+  const size_t scan = round256(gtr::workspace_bytes((size_t)bh, (size_t)n_chunk, (size_t)nk));
   l.fwd = 0;
   l.rev = l.fwd + scan;
   l.sfin = l.rev + scan;
   l.g0 = l.sfin + round256((size_t)bh * d_k * d_v * sizeof(float));
   l.totals = l.g0 + round256((size_t)bh * d_k * d_v * sizeof(float));
   l.dq_off = l.totals + round256((size_t)bh * n_chunk * gtr::kHead * sizeof(float));
-  l.dk_off = l.dq_off + round256((size_t)bh * n_tok * d_k * sizeof(float));
-  l.total = l.dk_off + round256((size_t)bh * n_tok * d_k * sizeof(float));
+  l.dk_off = l.dq_off + round256((size_t)bh * n_tok * kw * sizeof(float));
+  l.total = l.dk_off + round256((size_t)bh * n_tok * kw * sizeof(float));
   return l;
 }
 
@@ -69,13 +71,16 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     return set_error(GTR_ERR_INVALID_ARG, "sizes must be >= 0 and head sizes > 0");
   if (direction < 0 || direction > 3) return set_error(GTR_ERR_INVALID_ARG, "direction %d not in 0..3", direction);
   if (dtype < 0 || dtype > 2) return set_error(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
-  if (d_k % 4 || d_v % 4 || d_k > gtr::kHead || d_v > gtr::kHead)
-    return set_error(GTR_ERR_UNSUPPORTED, "backward: d_k=%d d_v=%d, head dims must be multiples of 4 up to 64",
+  if (d_k % 4 || d_v % 4 || d_k > 2 * gtr::kHead || d_v > gtr::kHead)
+    return set_error(GTR_ERR_UNSUPPORTED,
+                     "backward: d_k=%d d_v=%d, head dims must be multiples of 4, d_k up to 128 and d_v up to 64",
                      d_k, d_v);
   const long long n_tok = (long long)grid_h * grid_w, bh = (long long)B * H;
   if (n_tok > (1LL << 23)) return set_error(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^23 tokens", grid_h, grid_w);
   if (bh > (1LL << 20)) return set_error(GTR_ERR_INVALID_ARG, "B*H = %lld exceeds 2^20", bh);
   const int elt = dtype == GTR_DTYPE_F32 ? 4 : 2;
+  if (n_tok * d_k * elt > (1LL << 31))
+    return set_error(GTR_ERR_INVALID_ARG, "%lld tokens of %d elements exceed 2^31 bytes per sequence", n_tok, d_k);
   const size_t kb = (size_t)bh * n_tok * d_k * elt, vb = (size_t)bh * n_tok * d_v * elt;
   const size_t sb = (size_t)bh * d_k * d_v * sizeof(float);
   const bool empty = bh == 0 || n_tok == 0;
@@ -126,14 +131,15 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     return launched(gtr::launch_state_copy(ds_final, ds0, bh * d_k * d_v, stream));
 
   const int n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v);
+  const int nk = (d_k + gtr::kHead - 1) / gtr::kHead;  // 64-wide key blocks
+  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v, nk);
   void *wsp = nullptr;
   int rc = gtr::stream_buffer(gtr::kBufBackward, device, stream, lay.total, "backward", &wsp);
   if (rc != GTR_OK) return rc;
   char *ws = static_cast<char *>(wsp);
   auto scan_area = [&](size_t off, gtr::LaunchArgs &a) {
     float *f = reinterpret_cast<float *>(ws + off);
-    const size_t st = (size_t)bh * n_chunk * gtr::kStateElems;
+    const size_t st = (size_t)bh * n_chunk * nk * gtr::kStateElems;
     a.agg = f;
     a.prev = f + st;
     a.agg_dec = f + 2 * st;
@@ -141,9 +147,10 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   float *sfin = ds_final ? reinterpret_cast<float *>(ws + lay.sfin) : nullptr;
   float *g0 = ds0 ? reinterpret_cast<float *>(ws + lay.g0) : nullptr;
 
-  gtr::LaunchArgs f{};  // 1. states entering each chunk
+  // 1. states entering each chunk, both key blocks at once: [bh][n_chunk][nk][4096]
+  gtr::LaunchArgs f{};
   f.q = q; f.k = k; f.v = v; f.g = log_gate; f.out = nullptr;
-  f.bh = (int)bh; f.d_k = d_k; f.d_v = d_v; f.nk = 1; f.nvb = 1;
+  f.bh = (int)bh; f.d_k = d_k; f.d_v = d_v; f.nk = nk; f.nvb = 1;
   f.grid_h = grid_h; f.grid_w = grid_w; f.n_tok = (int)n_tok; f.direction = direction; f.dtype = dtype;
   f.n_chunk = n_chunk; f.seg_len = 1; f.n_seg = n_chunk;
   f.s0 = s0; f.s_final = sfin; f.fused = false; f.states_only = true; f.stream = stream;
@@ -156,32 +163,45 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   r.s0 = ds_final; r.s_final = g0;
   scan_area(lay.rev, r);
   if ((rc = launched(gtr::launch_gla(r))) != GTR_OK) return rc;
-  gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands
+  gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands; it sums over both key blocks in fp32
   o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
   // segments of the forward path's length, each entering with the state of its first chunk
   o.prev_per_chunk = true;
   o.seg_len = (int)gtr::split_segment_length(bh, n_chunk);
   o.n_seg = (n_chunk + o.seg_len - 1) / o.seg_len;
   if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
-  gtr::BwdArgs b{};  // 3. dq
+
+  // 3-6 per key block: the rows of S and G, dq, dk, dlog_gate and ds0 of key
+  // dims [64 h, 64 h + 64) depend only on those dims of q, k and log_gate (the
+  // gate is diagonal), so each block runs as a slice of the key-side rows
   float *dq_off = reinterpret_cast<float *>(ws + lay.dq_off), *dk_off = reinterpret_cast<float *>(ws + lay.dk_off);
-  b.kop = k; b.aop = dout; b.bop = v; b.g = log_gate; b.out = dq; b.off = dq_off; b.prev = f.prev;
-  b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
-  b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = d_k; b.d_v = d_v; b.stream = stream;
-  if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
-  // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
-  b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
-  b.pair = dq_off; b.kx = k;
-  b.direction = direction ^ 1;
-  if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
-  // 5. dlog_gate
-  if ((rc = launched(gtr::launch_dgate(dk_off, ds_final, sfin, reinterpret_cast<float *>(ws + lay.totals),
-                                       dlog_gate, (int)bh, grid_h, grid_w, d_k, d_v, n_chunk, direction,
-                                       dtype, stream))) != GTR_OK)
-    return rc;
-  if (ds0)  // 6. ds0
-    return launched(gtr::launch_ds0(log_gate, g0, ds0, (int)bh, grid_h, grid_w, d_k, d_v, direction, dtype,
-                                    stream));
+  for (int h = 0; h < nk; ++h) {
+    const int kcol = gtr::kHead * h, kw = d_k - kcol < gtr::kHead ? d_k - kcol : gtr::kHead;
+    gtr::BwdArgs b{};  // 3. dq
+    b.kop = k; b.aop = dout; b.bop = v; b.g = log_gate; b.out = dq; b.off = dq_off; b.prev = f.prev;
+    b.prev_nk = nk; b.prev_kb = h;
+    b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
+    b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = kw; b.d_v = d_v; b.stream = stream;
+    b.kpitch = d_k; b.kcol = kcol;
+    if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
+    // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
+    b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
+    b.pair = dq_off; b.kx = k;
+    b.direction = direction ^ 1;
+    if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
+    // 5. dlog_gate
+    char *dg = static_cast<char *>(dlog_gate) + (size_t)kcol * elt;
+    const size_t srow = (size_t)kcol * d_v;  // first state row of the block
+    if ((rc = launched(gtr::launch_dgate(dk_off, ds_final ? ds_final + srow : nullptr, sfin ? sfin + srow : nullptr,
+                                         reinterpret_cast<float *>(ws + lay.totals), dg, (int)bh, grid_h,
+                                         grid_w, kw, d_v, n_chunk, direction, dtype, d_k, stream))) != GTR_OK)
+      return rc;
+    if (ds0)  // 6. ds0
+      if ((rc = launched(gtr::launch_ds0(static_cast<const char *>(log_gate) + (size_t)kcol * elt, g0 + srow,
+                                         ds0 + srow, (int)bh, grid_h, grid_w, kw, d_v, direction, dtype, d_k,
+                                         stream))) != GTR_OK)
+        return rc;
+  }
   return GTR_OK;
 }
 

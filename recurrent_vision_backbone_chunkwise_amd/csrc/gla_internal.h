@@ -44,7 +44,7 @@ struct LaunchArgs {
   bool fused;        // one launch (gla_fused) instead of three
   bool states_only;  // split path without outputs: only the states entering each segment (prev)
   bool want_prev;    // split path: write prev for every segment even where the outputs need no scan
-  bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass; d_k <= 64, split path)
+  bool fp32_operands;  // fp32 MFMA operands for 16-bit I/O too (backward pass, split path)
   bool outputs_only;   // split path: only the output kernel, entering each segment with prev as given
   bool lag_gates;      // scan position t takes the gate of position t-1, none at t = 0 (backward)
   bool prev_per_chunk; // outputs_only: prev holds the state entering every chunk ([seq][n_chunk]);
@@ -65,8 +65,11 @@ struct BwdArgs {
                                     // with `pair` set, the gate-gradient term kop * pair - kx * that
   const float *pair;                // nullable [bh][grid][d_k] fp32: the other pass's `off` (dq)
   const void *kx;                   // with `pair`: [bh][grid][d_k] keys k
-  const float *prev;                // [bh][n_chunk][4096] register order
+  const float *prev;                // [bh][n_chunk][prev_nk][4096] register order; key block prev_kb
+  int prev_nk, prev_kb;             // (prev_nk 0 counts as 1)
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
+  int kpitch, kcol;                 // d_k > 64: a slice of d_k dims from column kcol of rows of kpitch
+                                    // elements (kop, g, kx, out); kpitch 0: rows of d_k
   bool lag_gates;                   // as in LaunchArgs
   hipStream_t stream;
 };
@@ -120,15 +123,17 @@ int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const
 // Backward-pass launchers (hipError_t values).
 int launch_gla_bwd_dqk(const BwdArgs &a);
 // dlog_gate_t = sum_{u >= t} x_u + rowsum(ds_final * s_final) along `direction`, with
-// x = q dq - k dk per position and dim (fp32, dq and dk without their cancelling self terms, as
-// the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32 scratch.
-// ds_final / s_final may be null.
+// x = q dq - k dk per position and dim (fp32 [bh][grid][d_k], dq and dk without their cancelling
+// self terms, as the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32
+// scratch.  ds_final / s_final may be null.  dg rows and the states' row blocks hold kp >= d_k
+// dims; dg, ds_final and s_final point at the first of the d_k dims computed.
 int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
                  int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
-                 hipStream_t stream);
-// ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][d_k][d_v].
+                 int kp, hipStream_t stream);
+// ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][kp][d_v], for
+// d_k rows from where g, g0 and ds0 point (g rows hold kp dims).
 int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
-               int direction, int dtype, hipStream_t stream);
+               int direction, int dtype, int kp, hipStream_t stream);
 
 // Chunks per segment of the three-launch path for `seqs` sequences of
 // n_chunk chunks (defined in gla_api.cpp).

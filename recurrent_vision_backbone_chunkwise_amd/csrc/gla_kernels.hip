@@ -341,15 +341,20 @@ struct Params {
   int fold_block;          // fused path: segments per fold block
   int batch, n_batch;      // fused path: sequences per batch an XCD takes, and batches
   int n_pre;               // fused path: batches 0 .. n_pre-1 start out assigned to XCDs 0 .. n_pre-1
+  // a slice of the key dims (backward pass, d_k > 64): q/k/log_gate rows hold
+  // kpitch elements (0: dk) and the slice's dk dims start at column kcol
+  int kpitch, kcol;
+  int prev_nk, prev_kb;    // backward chunk kernel: key blocks per entry of prev, and the slice's block
 };
 
 template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int seq) {
   using T = typename Io::T;
   constexpr uint32_t elt = sizeof(T);
   const int bh = seq / p.nvb, vb = seq - bh * p.nvb;
-  const size_t kbase = (size_t)bh * p.n_tok * p.dk;
+  const int kp = p.kpitch ? p.kpitch : p.dk;
+  const size_t kbase = (size_t)bh * p.n_tok * kp + p.kcol;
   const size_t vbase = (size_t)bh * p.n_tok * p.dv + (size_t)kHead * vb;
-  const uint32_t kbytes = (uint32_t)p.n_tok * (uint32_t)p.dk * elt;
+  const uint32_t kbytes = (uint32_t)p.n_tok * (uint32_t)kp * elt - (uint32_t)p.kcol * elt;
   const uint32_t vbytes = (uint32_t)p.n_tok * (uint32_t)p.dv * elt - (uint32_t)(kHead * vb) * elt;
   auto rsrc = [](const void *ptr, size_t base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(static_cast<const T *>(ptr) + base),
@@ -357,7 +362,7 @@ template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int s
   };
   return Seq{rsrc(p.q, kbase, kbytes), rsrc(p.k, kbase, kbytes), rsrc(p.v, vbase, vbytes),
              rsrc(p.g, kbase, kbytes), rsrc(p.out, vbase, vbytes), p.n_tok, p.gh, p.gw, p.dir,
-             p.rcp_gh, (uint32_t)p.dk * elt, (uint32_t)p.dv * elt, p.dk,
+             p.rcp_gh, (uint32_t)kp * elt, (uint32_t)p.dv * elt, p.dk,
              min(kHead, p.dv - kHead * vb)};
 }
 
@@ -1623,15 +1628,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
   const int a = wave;  // this wave's token sub-block
   const Seq sq = seq_of<Io>(p, seq);  // k: kop, v: a, g: gates, o: b (read only)
+  const int kp = p.kpitch ? p.kpitch : p.dk;  // out and kx rows: kp elements, this slice from kcol
   const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<T *>(out) + (size_t)seq * p.n_tok * p.dk, (short)0,
-      (int)((uint32_t)p.n_tok * (uint32_t)p.dk * sizeof(T)), 0x00020000);
+      static_cast<T *>(out) + (size_t)seq * p.n_tok * kp + p.kcol, (short)0,
+      (int)((uint32_t)p.n_tok * (uint32_t)kp * sizeof(T) - (uint32_t)p.kcol * sizeof(T)), 0x00020000);
 
   // rows i = 16t + l16 of the state entering the chunk, for the four 16-dim
   // tiles t, at the k-slots of an MFMA operand (register-order workspace layout)
   float srow[4][16];
   {
-    const float *st = p.prev + ((size_t)seq * p.n_chunk + c) * kStateElems;
+    const float *st = p.prev + (((size_t)seq * p.n_chunk + c) * p.prev_nk + p.prev_kb) * kStateElems;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = 16 * t + l16;
@@ -1672,13 +1678,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // stored) so that they arrive while the MFMAs run
   f4 xdq[4], xkk[4];
   if constexpr (kX) {
-    const size_t row = ((size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell)) * p.dk;
+    const size_t prow = (size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int d = min(16 * t + 4 * g4, p.dk - 4);
-      xdq[t] = *reinterpret_cast<const f4 *>(pair + row + d);
-      const T *kp = static_cast<const T *>(kx) + row + d;
-      xkk[t] = f4{elem<Io>(kp), elem<Io>(kp + 1), elem<Io>(kp + 2), elem<Io>(kp + 3)};
+      xdq[t] = *reinterpret_cast<const f4 *>(pair + prow * p.dk + d);
+      const T *kr = static_cast<const T *>(kx) + prow * kp + p.kcol + d;
+      xkk[t] = f4{elem<Io>(kr), elem<Io>(kr + 1), elem<Io>(kr + 2), elem<Io>(kr + 3)};
     }
   }
 
@@ -1845,12 +1851,14 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_totals(const float *xs, fl
 
 // dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then the
 // reverse running sum inside the chunk, quarter by quarter.
+// d_k dims of xs (rows of d_k); dg rows and the states' row blocks hold kp
+// dims (dg and the state pointers start at the slice's first dim).
 template <class Io>
 __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, const float *ds_final,
                                                             const float *s_final,
                                                             const float *totals, typename Io::T *dg, int n_tok,
                                                             int gh, int gw, int dir, float rcp_gh, int d_k,
-                                                            int d_v, int n_chunk) {
+                                                            int d_v, int n_chunk, int kp) {
   __shared__ float part[4][kHead];
   const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk;
   const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
@@ -1866,8 +1874,8 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, con
   float run = 0.f;
   if (i < d_k) {
     if (r == 0 && ds_final && s_final) {  // rows of d_v floats, d_v a multiple of 4
-      const f4 *a = reinterpret_cast<const f4 *>(ds_final + ((size_t)seq * d_k + i) * d_v);
-      const f4 *b = reinterpret_cast<const f4 *>(s_final + ((size_t)seq * d_k + i) * d_v);
+      const f4 *a = reinterpret_cast<const f4 *>(ds_final + ((size_t)seq * kp + i) * d_v);
+      const f4 *b = reinterpret_cast<const f4 *>(s_final + ((size_t)seq * kp + i) * d_v);
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int j0 = 0; j0 < d_v / 4; j0 += 4) {
         f4 av[4], bv[4];
@@ -1906,7 +1914,8 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, con
   for (int u = 15; u >= 0; --u) {
     const int t = c * kChunk + 16 * r + u;
     run += x[u];
-    if (t < n_tok) dg[base + (size_t)scan_cell(t, n_tok, gh, gw, dir, rcp_gh) * d_k + i] = Io::narrow(run);
+    if (t < n_tok)
+      dg[((size_t)seq * n_tok + scan_cell(t, n_tok, gh, gw, dir, rcp_gh)) * kp + i] = Io::narrow(run);
   }
 }
 
@@ -1952,21 +1961,25 @@ int static_scratch(int device, void **ptr) {
 
 int launch_gla(const LaunchArgs &a) {
   const bool two = a.nk == 2;
-  if (a.lag_gates) {  // the backward pass's reversed scan: one key block, three launches
-    if (two || a.fused) return (int)hipErrorInvalidValue;
+  if (a.lag_gates) {  // the backward pass's reversed scan: three launches
+    if (a.fused) return (int)hipErrorInvalidValue;
     switch (a.dtype) {
-      case 0: return launch_typed<Lagged<IoF32>, float, 1>(a);
-      case 1: return a.fp32_operands ? launch_typed<Lagged<IoF16>, float, 1>(a)
-                                     : launch_typed<Lagged<IoF16>, _Float16, 1>(a);
-      case 2: return a.fp32_operands ? launch_typed<Lagged<IoBF16>, float, 1>(a)
-                                     : launch_typed<Lagged<IoBF16>, _Float16, 1>(a);
+      case 0: return two ? launch_typed<Lagged<IoF32>, float, 2>(a) : launch_typed<Lagged<IoF32>, float, 1>(a);
+      case 1:
+        if (a.fp32_operands)
+          return two ? launch_typed<Lagged<IoF16>, float, 2>(a) : launch_typed<Lagged<IoF16>, float, 1>(a);
+        return two ? launch_typed<Lagged<IoF16>, _Float16, 2>(a) : launch_typed<Lagged<IoF16>, _Float16, 1>(a);
+      case 2:
+        if (a.fp32_operands)
+          return two ? launch_typed<Lagged<IoBF16>, float, 2>(a) : launch_typed<Lagged<IoBF16>, float, 1>(a);
+        return two ? launch_typed<Lagged<IoBF16>, _Float16, 2>(a) : launch_typed<Lagged<IoBF16>, _Float16, 1>(a);
       default: return (int)hipErrorInvalidValue;
     }
   }
-  if (a.fp32_operands && !two && !a.fused) {
+  if (a.fp32_operands && !a.fused) {
     switch (a.dtype) {
-      case 1: return launch_typed<IoF16, float, 1>(a);
-      case 2: return launch_typed<IoBF16, float, 1>(a);
+      case 1: return two ? launch_typed<IoF16, float, 2>(a) : launch_typed<IoF16, float, 1>(a);
+      case 2: return two ? launch_typed<IoBF16, float, 2>(a) : launch_typed<IoBF16, float, 1>(a);
       default: break;
     }
   }
@@ -1986,17 +1999,20 @@ namespace gtr {
 namespace {
 
 // ds0 = diag(alpha_0) G_0: one thread per state element.
+// d_k dims per sequence (a slice when kp > d_k: g rows and the states' row
+// blocks hold kp dims, and the pointers start at the slice's first dim).
 template <class Io>
 __global__ __launch_bounds__(kThreads) void gla_ds0(const typename Io::T *g, const float *g0, float *ds0,
                                                     int n_tok, int gh, int gw, int dir, float rcp_gh,
-                                                    int d_k, int d_v, long long n) {
+                                                    int d_k, int d_v, long long n, int kp) {
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= n) return;
   const long long per_seq = (long long)d_k * d_v;
   const long long seq = gid / per_seq;
-  const int i = (int)((gid - seq * per_seq) / d_v);
-  const size_t at = (size_t)seq * n_tok * d_k + (size_t)scan_cell(0, n_tok, gh, gw, dir, rcp_gh) * d_k + i;
-  ds0[gid] = expf(elem<Io>(g + at)) * g0[gid];
+  const int i = (int)((gid - seq * per_seq) / d_v), j = (int)(gid - seq * per_seq - (long long)i * d_v);
+  const size_t at = ((size_t)seq * n_tok + scan_cell(0, n_tok, gh, gw, dir, rcp_gh)) * kp + i;
+  const size_t e = ((size_t)seq * kp + i) * d_v + j;
+  ds0[e] = expf(elem<Io>(g + at)) * g0[e];
 }
 
 template <class Io, typename Op>
@@ -2006,7 +2022,10 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.bh_count = a.bh; p.n_tok = a.n_tok; p.gh = a.grid_h; p.gw = a.grid_w; p.dir = a.direction;
   p.rcp_gh = 1.0f / (float)a.grid_h;
   p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
+  p.kpitch = a.kpitch; p.kcol = a.kcol;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
+  p.prev_nk = a.prev_nk > 0 ? a.prev_nk : 1;
+  p.prev_kb = a.prev_kb;
   // the dk pass (which forms the gate-gradient term from `pair`) runs along
   // the reversed scan with lagged gates; the dq pass along the forward scan
   if (a.pair && a.lag_gates)
@@ -2037,7 +2056,7 @@ int launch_gla_bwd_dqk(const BwdArgs &a) {
 namespace {
 template <class Io>
 int launch_dgate_typed(const float *xs, const float *ds_final, const float *s_final, float *totals, void *dg,
-                       int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction,
+                       int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int kp,
                        hipStream_t stream) {
   using T = typename Io::T;
   const int n_tok = grid_h * grid_w;
@@ -2047,38 +2066,38 @@ int launch_dgate_typed(const float *xs, const float *ds_final, const float *s_fi
   hipLaunchKernelGGL(gla_dgate_totals, grid, dim3(kThreads), 0, stream, xs, totals, n_tok, grid_h, grid_w,
                      direction, rcp, d_k, n_chunk);
   hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(kThreads), 0, stream, xs, ds_final, s_final, totals,
-                     static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk);
+                     static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk, kp);
   return (int)hipGetLastError();
 }
 
 template <class Io>
 int launch_ds0_typed(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k,
-                     int d_v, int direction, hipStream_t stream) {
+                     int d_v, int direction, int kp, hipStream_t stream) {
   const long long n = (long long)bh * d_k * d_v;
   launch(kKernelBwdDs0, gla_ds0<Io>, (unsigned)((n + kThreads - 1) / kThreads), stream,
          static_cast<const typename Io::T *>(g), g0, ds0, grid_h * grid_w, grid_h, grid_w, direction,
-         1.0f / (float)grid_h, d_k, d_v, n);
+         1.0f / (float)grid_h, d_k, d_v, n, kp);
   return (int)hipGetLastError();
 }
 }  // namespace
 
 int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
                  int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
-                 hipStream_t stream) {
+                 int kp, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_dgate_typed<IoF32>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
-    case 1: return launch_dgate_typed<IoF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
-    case 2: return launch_dgate_typed<IoBF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, stream);
+    case 0: return launch_dgate_typed<IoF32>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, kp, stream);
+    case 1: return launch_dgate_typed<IoF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, kp, stream);
+    case 2: return launch_dgate_typed<IoBF16>(x, ds_final, s_final, totals, dg, bh, grid_h, grid_w, d_k, d_v, n_chunk, direction, kp, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }
 
 int launch_ds0(const void *g, const float *g0, float *ds0, int bh, int grid_h, int grid_w, int d_k, int d_v,
-               int direction, int dtype, hipStream_t stream) {
+               int direction, int dtype, int kp, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_ds0_typed<IoF32>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
-    case 1: return launch_ds0_typed<IoF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
-    case 2: return launch_ds0_typed<IoBF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, stream);
+    case 0: return launch_ds0_typed<IoF32>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, kp, stream);
+    case 1: return launch_ds0_typed<IoF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, kp, stream);
+    case 2: return launch_ds0_typed<IoBF16>(g, g0, ds0, bh, grid_h, grid_w, d_k, d_v, direction, kp, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -60,8 +60,10 @@ int main(void) {
   expect(gtr_gla_check(p, c + 1024, c + 2048, c + 3072, c + 8192, 1, 1, 2, 2, 64, 64, 0, 1, NULL, NULL, 0, 0),
          GTR_ERR_NO_DEVICE, "check without device");
   /* backward and Spatial SwiGLU argument checks */
-  expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 128,
-                     64, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_k 128");
+  expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 64,
+                     128, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_v 128");
+  expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 132,
+                     64, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_k 132");
   expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, p, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 64, 64, 0, 1, 0),
          GTR_ERR_ALIAS, "bwd alias");
   expect(gtr_swiglu_fwd(p, p, p, NULL, p, c + 4096, 1, 4, 4, 12, 64, 1, 0), GTR_ERR_UNSUPPORTED, "swiglu C 12");
