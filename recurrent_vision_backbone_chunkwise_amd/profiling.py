@@ -149,10 +149,59 @@ def counter_per_dispatch(directory: str, counter: str) -> dict[str, float]:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def counter_rows(directories: list[str]) -> dict[str, dict[str, tuple[float, float]]]:
+def counter_name(mangled: str) -> str:
+    """short_name, also for the other library kernels and the rocBLAS GEMMs (Tensile's Cijk_ names
+    carry the macro tile after MT)."""
+    for k in LIBRARY_KERNELS:
+        if k in mangled:
+            return k
+    if mangled.startswith("Cijk_"):
+        tile = mangled.split("_MT")[1].split("_")[0] if "_MT" in mangled else "?"
+        return f"rocBLAS GEMM MT{tile}"
+    return short_name(mangled)
+
+
+def _roles(names_by_key: dict, alternate: dict[str, int]) -> dict:
+    """With `alternate` = {kernel: k}: that kernel's dispatches in each file take roles 0..k-1 in
+    turn (by dispatch order), and are named kernel#role."""
+    out = dict(names_by_key)
+    for name, k in alternate.items():
+        by_file = collections.defaultdict(list)
+        for key, n in names_by_key.items():
+            if n == name:
+                by_file[key[0]].append(key)
+        for keys in by_file.values():
+            for rank, key in enumerate(sorted(keys, key=lambda x: int(x[1]))):
+                out[key] = f"{name}#{rank % k}"
+    return out
+
+
+def trace_durations(directory: str, alternate: dict[str, int] | None = None) -> dict[str, float]:
+    """Mean duration (us) per kernel from a kernel trace's per-dispatch rows (with `alternate` as
+    in _roles)."""
+    starts = collections.defaultdict(list)
+    for path in _csvs(directory, "kernel_trace.csv"):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                starts[counter_name(r["Kernel_Name"])].append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in starts.items():
+        k = (alternate or {}).get(name, 1)
+        v.sort()
+        for role in range(k):
+            d = [dur for i, (_, dur) in enumerate(v) if i % k == role]
+            if d:
+                out[name if k == 1 else f"{name}#{role}"] = sum(d) / len(d) / 1e3
+    return out
+
+
+def counter_rows(directories: list[str], alternate: dict[str, int] | None = None
+                 ) -> dict[str, dict[str, tuple[float, float]]]:
     """For every kernel and counter in the ``--pmc`` runs under `directories`: the means over
     dispatches of the counter's sum and of its largest value over its per-dispatch rows (the rows
-    are per shader engine or cache instance)."""
+    are per shader engine or cache instance).  `alternate` splits a kernel by dispatch order
+    (_roles), for a kernel that serves several calls in turn."""
     acc = collections.defaultdict(lambda: [0.0, float("-inf")])
     names = {}
     for directory in directories:
@@ -163,7 +212,10 @@ def counter_rows(directories: list[str]) -> dict[str, dict[str, tuple[float, flo
                     v = float(r["Counter_Value"])
                     acc[key][0] += v
                     acc[key][1] = max(acc[key][1], v)
-                    names[key] = short_name(r["Kernel_Name"])
+                    names[key] = counter_name(r["Kernel_Name"])
+    if alternate:
+        per_dispatch = _roles({(k[0], k[1]): n for k, n in names.items()}, alternate)
+        names = {k: per_dispatch[(k[0], k[1])] for k in names}
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     for key, (total, peak) in acc.items():
         per[names[key]][key[2]].append((total, peak))
@@ -217,8 +269,12 @@ def derived_counters(c: dict[str, tuple[float, float]], avg_us: float | None, al
 
 
 def cmd_counters(a) -> None:
-    rows = counter_rows(a.pmc)
-    durations = {short_name(r["kernel"]): r["avg_us"] for r in kernel_stats(a.trace)} if a.trace else {}
+    alternate = {}
+    for item in a.alternate or []:
+        name, k = item.rsplit("=", 1)
+        alternate[name] = int(k)
+    rows = counter_rows(a.pmc, alternate)
+    durations = trace_durations(a.trace, alternate) if a.trace else {}
     alg = {}
     for item in a.alg or []:
         k, v = item.split("=")
@@ -230,10 +286,11 @@ def cmd_counters(a) -> None:
             ("write MB", "write_bytes", "{:8.2f}"), ("alg MB", "alg_bytes", "{:8.2f}"),
             ("moved/alg", "moved_over_alg", "{:9.3f}"), ("moved GB/s", "moved_gbs", "{:10.0f}")]
     mb = {"read_bytes", "write_bytes", "alg_bytes"}
+    width = max([16] + [len(k) for k in rows if k.split("#")[0] in KERNELS or a.all])
     lines = [f"# rocprofv3 hardware counters ({a.workload})",
              "# commands ($REPO is the repository root):"]
     lines += [f"#   {portable_command(c)}" for c in a.commands]
-    lines += [f"# kernel sources: {source_digest()}",
+    lines += [f"# kernel sources: {a.source or source_digest()}",
               "# per launch, means over dispatches; avg us from the kernel trace; MFMA busy % = "
               f"SQ_VALU_MFMA_BUSY_CYCLES over avg us x {CLOCK_HZ / 1e9:g} GHz x {SIMDS} SIMDs; MFMA TF/s = 512 "
               "flops per SQ_INSTS_VALU_MFMA_MOPS_* over avg us; % MFMA peak against the dense peak of each "
@@ -241,9 +298,9 @@ def cmd_counters(a) -> None:
               "SQ_LDS_BANK_CONFLICT cycles per SQ_INSTS_LDS; L2 hit % = TCC_HIT over "
               "TCC_HIT + TCC_MISS; read MB = 32/64/128 x TCC_EA0_RDREQ_{32B,64B,128B}; write MB = "
               "64 x TCC_EA0_WRREQ_64B + 32 x the other TCC_EA0_WRREQ; moved = read + write", "",
-              f"{'kernel':16s}" + "".join(f" {h:>{len(fmt.format(0))}s}" for h, _, fmt in cols)]
+              f"{'kernel':{width}s}" + "".join(f" {h:>{len(fmt.format(0))}s}" for h, _, fmt in cols)]
     for k in sorted(rows):
-        if k not in KERNELS and not a.all:
+        if k.split("#")[0] not in KERNELS and not a.all:
             continue
         d = derived_counters(rows[k], durations.get(k), alg.get(k))
         d["avg_us"] = durations.get(k)
@@ -251,12 +308,12 @@ def cmd_counters(a) -> None:
         cells = []
         for h, key, fmt in cols:
             v = d.get(key)
-            width = len(fmt.format(0))
-            cells.append(" " + ("-".rjust(width) if v is None else fmt.format(v / 1e6 if key in mb else v)))
-        lines.append(f"{k:16s}" + "".join(cells))
+            cw = len(fmt.format(0))
+            cells.append(" " + ("-".rjust(cw) if v is None else fmt.format(v / 1e6 if key in mb else v)))
+        lines.append(f"{k:{width}s}" + "".join(cells))
     lines += ["", "# raw counters, means per dispatch"]
     for k in sorted(rows):
-        if k in KERNELS or a.all:
+        if k.split("#")[0] in KERNELS or a.all:
             lines.append(f"{k}: " + ", ".join(f"{c} {v[0]:.0f}" for c, v in sorted(rows[k].items())))
     text = "\n".join(lines) + "\n"
     print(text, end="")
@@ -274,7 +331,7 @@ def cmd_stats(a) -> None:
     rows = kernel_stats(a.dir)
     lines = [f"# rocprofv3 kernel trace ({a.title})",
              f"# command ($REPO is the repository root): {portable_command(a.command)}",
-             f"# kernel sources: {source_digest()}", "",
+             f"# kernel sources: {a.source or source_digest()}", "",
              f"{'kernel':60s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'% time':>7s}"]
     for r in sorted(rows, key=lambda r: -r["total_us"]):
         lines.append(f"{r['kernel']:60s} {r['calls']:7d} {r['avg_us']:9.3f} {r['min_us']:9.3f} "
@@ -299,7 +356,7 @@ def cmd_traffic(a) -> None:
     if os.path.exists(a.table):
         with open(a.table) as f:
             table = json.load(f)
-    digest = source_digest()
+    digest = a.source or source_digest()
     table = [r for r in table if not (r.get("workload") == a.workload and r.get("kernel") in fetch)]
     for k in sorted(fetch):
         if k not in KERNELS:
@@ -343,6 +400,11 @@ def main() -> None:
     c.add_argument("--alg", nargs="*")
     c.add_argument("--out")
     c.add_argument("--all", action="store_true", help="also list kernels that are not this library's")
+    c.add_argument("--alternate", nargs="*", metavar="KERNEL=K",
+                   help="split KERNEL's dispatches into K roles taken in turn (KERNEL#0 .. #K-1)")
+    for sp in (s, t, c):
+        sp.add_argument("--source", help="digest of the sources the run measured (the `source` that "
+                        "bench.py printed); default: the sources as they are now")
     a = ap.parse_args()
     {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 

@@ -129,3 +129,13 @@ def test_digest_ignores_comments_and_layout():
     assert code_tokens(a) == code_tokens(b)
     assert code_tokens(a) != code_tokens(b.replace("int b", "int c"))
     assert '"x // y /* z */"' in code_tokens(a)
+
+
+def test_counter_roles_for_a_kernel_that_alternates(tmp_path):
+    """A library GEMM serving two projections in turn is split by dispatch order."""
+    gemm = "Cijk_Ailk_Bljk_HHS_BH_MT256x256x64_MI16x16x1"
+    write_multi(tmp_path / "p1", [(1, gemm, "SQ_INSTS_VALU_MFMA_MOPS_F16", 100), (2, gemm, "SQ_INSTS_VALU_MFMA_MOPS_F16", 40),
+                                  (3, gemm, "SQ_INSTS_VALU_MFMA_MOPS_F16", 110), (4, gemm, "SQ_INSTS_VALU_MFMA_MOPS_F16", 50)])
+    rows = profiling.counter_rows([str(tmp_path / "p1")], {"rocBLAS GEMM MT256x256x64": 2})
+    assert rows["rocBLAS GEMM MT256x256x64#0"]["SQ_INSTS_VALU_MFMA_MOPS_F16"][0] == 105
+    assert rows["rocBLAS GEMM MT256x256x64#1"]["SQ_INSTS_VALU_MFMA_MOPS_F16"][0] == 45
