@@ -246,9 +246,10 @@ int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chu
  * ds0 is not NULL.  s0 is the forward call's initial state (NULL = zero).
  * Gradients follow the recurrence of gtr_gla_fwd by the chain rule (x-techcon
  * article on GTR, section 架构 / Architecture, for the recurrence).  Head dims
- * are multiples of 4, d_k up to 128 and d_v up to 64 (GTR_ERR_UNSUPPORTED
- * otherwise; above 64 key dims, dq, dk, dlog_gate and ds0 are formed one
- * 64-wide key block at a time, since the gate is diagonal); every output
+ * are multiples of 4 up to 128 (GTR_ERR_UNSUPPORTED otherwise; above 64 key
+ * dims, dq, dk, dlog_gate and ds0 are formed one 64-wide key block at a time,
+ * since the gate is diagonal; above 64 value dims, dq and dk are summed over
+ * the 64-wide value blocks in fp32 before one rounding); every output
  * must be distinct from every input and from the others; the other rules are
  * those of gtr_gla_fwd_ex.  Asynchronous on `stream`; the library keeps a
  * separate per-(device, stream) backward workspace.  For 16-bit I/O the

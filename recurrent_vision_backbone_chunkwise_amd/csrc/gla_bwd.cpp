@@ -33,14 +33,15 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {  // byte offsets into the workspace
-  size_t fwd, rev, sfin, g0, totals, dq_off, dk_off, total;
+  size_t fwd, rev, sfin, g0, totals, dq_off, dk_off, accf, acco, total;
 };
 
-// nk: 64-wide key blocks; the fp32 gradient terms hold one key block at a time.
-Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int nk) {
+// nk: 64-wide key blocks, nvb: 64-wide value blocks; the fp32 gradient terms
+// hold one key block at a time.
+Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int nk, int nvb) {
   Layout l{};
   const int kw = d_k < gtr::kHead ? d_k : gtr::kHead;
-  const size_t scan = round256(gtr::workspace_bytes((size_t)bh, (size_t)n_chunk, (size_t)nk));
+  const size_t scan = round256(gtr::workspace_bytes((size_t)bh * nvb, (size_t)n_chunk, (size_t)nk));
   l.fwd = 0;
   l.rev = l.fwd + scan;
   l.sfin = l.rev + scan;
@@ -48,7 +49,10 @@ Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int 
   l.totals = l.g0 + round256((size_t)bh * d_k * d_v * sizeof(float));
   l.dq_off = l.totals + round256((size_t)bh * n_chunk * gtr::kHead * sizeof(float));
   l.dk_off = l.dq_off + round256((size_t)bh * n_tok * kw * sizeof(float));
-  l.total = l.dk_off + round256((size_t)bh * n_tok * kw * sizeof(float));
+  l.accf = l.dk_off + round256((size_t)bh * n_tok * kw * sizeof(float));
+  const size_t acc = nvb > 1 ? round256((size_t)bh * n_tok * kw * sizeof(float)) : 0;
+  l.acco = l.accf + acc;
+  l.total = l.acco + acc;
   return l;
 }
 
@@ -71,16 +75,16 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     return set_error(GTR_ERR_INVALID_ARG, "sizes must be >= 0 and head sizes > 0");
   if (direction < 0 || direction > 3) return set_error(GTR_ERR_INVALID_ARG, "direction %d not in 0..3", direction);
   if (dtype < 0 || dtype > 2) return set_error(GTR_ERR_INVALID_ARG, "dtype %d not in 0..2", dtype);
-  if (d_k % 4 || d_v % 4 || d_k > 2 * gtr::kHead || d_v > gtr::kHead)
-    return set_error(GTR_ERR_UNSUPPORTED,
-                     "backward: d_k=%d d_v=%d, head dims must be multiples of 4, d_k up to 128 and d_v up to 64",
+  if (d_k % 4 || d_v % 4 || d_k > 2 * gtr::kHead || d_v > 2 * gtr::kHead)
+    return set_error(GTR_ERR_UNSUPPORTED, "backward: d_k=%d d_v=%d, head dims must be multiples of 4 up to 128",
                      d_k, d_v);
   const long long n_tok = (long long)grid_h * grid_w, bh = (long long)B * H;
   if (n_tok > (1LL << 23)) return set_error(GTR_ERR_INVALID_ARG, "grid %dx%d has more than 2^23 tokens", grid_h, grid_w);
   if (bh > (1LL << 20)) return set_error(GTR_ERR_INVALID_ARG, "B*H = %lld exceeds 2^20", bh);
   const int elt = dtype == GTR_DTYPE_F32 ? 4 : 2;
-  if (n_tok * d_k * elt > (1LL << 31))
-    return set_error(GTR_ERR_INVALID_ARG, "%lld tokens of %d elements exceed 2^31 bytes per sequence", n_tok, d_k);
+  if (n_tok * (d_k > d_v ? d_k : d_v) * elt > (1LL << 31))
+    return set_error(GTR_ERR_INVALID_ARG, "%lld tokens of %d elements exceed 2^31 bytes per sequence", n_tok,
+                     d_k > d_v ? d_k : d_v);
   const size_t kb = (size_t)bh * n_tok * d_k * elt, vb = (size_t)bh * n_tok * d_v * elt;
   const size_t sb = (size_t)bh * d_k * d_v * sizeof(float);
   const bool empty = bh == 0 || n_tok == 0;
@@ -131,15 +135,16 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     return launched(gtr::launch_state_copy(ds_final, ds0, bh * d_k * d_v, stream));
 
   const int n_chunk = (int)((n_tok + gtr::kChunk - 1) / gtr::kChunk);
-  const int nk = (d_k + gtr::kHead - 1) / gtr::kHead;  // 64-wide key blocks
-  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v, nk);
+  const int nk = (d_k + gtr::kHead - 1) / gtr::kHead;   // 64-wide key blocks
+  const int nvb = (d_v + gtr::kHead - 1) / gtr::kHead;  // 64-wide value blocks
+  const Layout lay = layout(bh, n_tok, n_chunk, d_k, d_v, nk, nvb);
   void *wsp = nullptr;
   int rc = gtr::stream_buffer(gtr::kBufBackward, device, stream, lay.total, "backward", &wsp);
   if (rc != GTR_OK) return rc;
   char *ws = static_cast<char *>(wsp);
   auto scan_area = [&](size_t off, gtr::LaunchArgs &a) {
     float *f = reinterpret_cast<float *>(ws + off);
-    const size_t st = (size_t)bh * n_chunk * nk * gtr::kStateElems;
+    const size_t st = (size_t)bh * nvb * n_chunk * nk * gtr::kStateElems;
     a.agg = f;
     a.prev = f + st;
     a.agg_dec = f + 2 * st;
@@ -147,10 +152,11 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   float *sfin = ds_final ? reinterpret_cast<float *>(ws + lay.sfin) : nullptr;
   float *g0 = ds0 ? reinterpret_cast<float *>(ws + lay.g0) : nullptr;
 
-  // 1. states entering each chunk, both key blocks at once: [bh][n_chunk][nk][4096]
+  // 1. states entering each chunk, both key blocks at once and each value
+  // block as a sequence of its own: [bh][nvb][n_chunk][nk][4096]
   gtr::LaunchArgs f{};
   f.q = q; f.k = k; f.v = v; f.g = log_gate; f.out = nullptr;
-  f.bh = (int)bh; f.d_k = d_k; f.d_v = d_v; f.nk = nk; f.nvb = 1;
+  f.bh = (int)(bh * nvb); f.d_k = d_k; f.d_v = d_v; f.nk = nk; f.nvb = nvb;
   f.grid_h = grid_h; f.grid_w = grid_w; f.n_tok = (int)n_tok; f.direction = direction; f.dtype = dtype;
   f.n_chunk = n_chunk; f.seg_len = 1; f.n_seg = n_chunk;
   f.s0 = s0; f.s_final = sfin; f.fused = false; f.states_only = true; f.stream = stream;
@@ -167,14 +173,17 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
   // segments of the forward path's length, each entering with the state of its first chunk
   o.prev_per_chunk = true;
-  o.seg_len = (int)gtr::split_segment_length(bh, n_chunk);
+  o.seg_len = (int)gtr::split_segment_length(bh * nvb, n_chunk);
   o.n_seg = (n_chunk + o.seg_len - 1) / o.seg_len;
   if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
 
   // 3-6 per key block: the rows of S and G, dq, dk, dlog_gate and ds0 of key
   // dims [64 h, 64 h + 64) depend only on those dims of q, k and log_gate (the
-  // gate is diagonal), so each block runs as a slice of the key-side rows
+  // gate is diagonal), so each block runs as a slice of the key-side rows.  dq
+  // and dk sum over the value dims: with two value blocks, the first block's
+  // pass leaves fp32 sums that the second adds before rounding once.
   float *dq_off = reinterpret_cast<float *>(ws + lay.dq_off), *dk_off = reinterpret_cast<float *>(ws + lay.dk_off);
+  float *accf = reinterpret_cast<float *>(ws + lay.accf), *acco = reinterpret_cast<float *>(ws + lay.acco);
   for (int h = 0; h < nk; ++h) {
     const int kcol = gtr::kHead * h, kw = d_k - kcol < gtr::kHead ? d_k - kcol : gtr::kHead;
     gtr::BwdArgs b{};  // 3. dq
@@ -183,12 +192,22 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     b.bh = (int)bh; b.grid_h = grid_h; b.grid_w = grid_w; b.n_tok = (int)n_tok; b.direction = direction;
     b.dtype = dtype; b.n_chunk = n_chunk; b.d_k = kw; b.d_v = d_v; b.stream = stream;
     b.kpitch = d_k; b.kcol = kcol;
-    if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
+    b.nvb = nvb; b.accf = accf; b.acco = acco;
+    auto passes = [&]() {  // one launch per value block
+      for (int vb = 0; vb < nvb; ++vb) {
+        b.vb = vb;
+        b.vmode = nvb == 1 ? 0 : (vb == 0 ? 1 : 2);
+        const int rcv = launched(gtr::launch_gla_bwd_dqk(b));
+        if (rcv != GTR_OK) return rcv;
+      }
+      return (int)GTR_OK;
+    };
+    if ((rc = passes()) != GTR_OK) return rc;
     // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
     b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
     b.pair = dq_off; b.kx = k;
     b.direction = direction ^ 1;
-    if ((rc = launched(gtr::launch_gla_bwd_dqk(b))) != GTR_OK) return rc;
+    if ((rc = passes()) != GTR_OK) return rc;
     // 5. dlog_gate
     char *dg = static_cast<char *>(dlog_gate) + (size_t)kcol * elt;
     const size_t srow = (size_t)kcol * d_v;  // first state row of the block

@@ -70,6 +70,11 @@ struct BwdArgs {
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
   int kpitch, kcol;                 // d_k > 64: a slice of d_k dims from column kcol of rows of kpitch
                                     // elements (kop, g, kx, out); kpitch 0: rows of d_k
+  int nvb, vb;                      // d_v > 64: value block vb of nvb (aop, bop columns and prev
+                                    // entries [bh][nvb][n_chunk]...); nvb 0 counts as 1
+  int vmode;                        // 0: one value block; 1: first of two (sums to accf, acco, no
+                                    // out or off); 2: last (adds them, writes out and off)
+  float *accf, *acco;               // [bh][grid][d_k] fp32, with nvb = 2
   bool lag_gates;                   // as in LaunchArgs
   hipStream_t stream;
 };

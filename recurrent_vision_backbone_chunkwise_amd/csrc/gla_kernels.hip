@@ -345,6 +345,9 @@ struct Params {
   // kpitch elements (0: dk) and the slice's dk dims start at column kcol
   int kpitch, kcol;
   int prev_nk, prev_kb;    // backward chunk kernel: key blocks per entry of prev, and the slice's block
+  int vb;                  // backward chunk kernel: the value block (of nvb) a pass covers
+  int vmode;               // backward chunk kernel: kVSingle, kVFirst or kVLast (value blocks summed)
+  float *accf, *acco;      // backward chunk kernel, d_v > 64: fp32 sums over the value blocks so far
 };
 
 template <class Io> __device__ __forceinline__ Seq seq_of(const Params &p, int seq) {
@@ -1613,6 +1616,12 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
 // per CU.  For 16-bit I/O the scores' operands a and b are inputs, exact in
 // fp16, so those tiles run as fp16 MFMAs (exact products, fp32 sums): the
 // same results for an eighth of the instructions.
+// Value blocks of a backward pass over d_v > 64: the result sums over them, so
+// the first block's pass leaves its sums in fp32 (accf: with the self term,
+// acco: without) and the last adds its own and writes out and off; a single
+// block writes them directly.
+enum : int { kVSingle = 0, kVFirst = 1, kVLast = 2 };
+
 template <class Io, typename Op, bool kX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off,
                                                                                            const float *pair,
@@ -1627,7 +1636,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int g4 = lane >> 4, l16 = lane & 15;
   const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
   const int a = wave;  // this wave's token sub-block
-  const Seq sq = seq_of<Io>(p, seq);  // k: kop, v: a, g: gates, o: b (read only)
+  const Seq sq = seq_of<Io>(p, seq * p.nvb + p.vb);  // k: kop, v: a, g: gates, o: b (read only); value block vb
   const int kp = p.kpitch ? p.kpitch : p.dk;  // out and kx rows: kp elements, this slice from kcol
   const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<T *>(out) + (size_t)seq * p.n_tok * kp + p.kcol, (short)0,
@@ -1637,7 +1646,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // tiles t, at the k-slots of an MFMA operand (register-order workspace layout)
   float srow[4][16];
   {
-    const float *st = p.prev + (((size_t)seq * p.n_chunk + c) * p.prev_nk + p.prev_kb) * kStateElems;
+    const float *st =
+        p.prev + ((((size_t)seq * p.nvb + p.vb) * p.n_chunk + c) * p.prev_nk + p.prev_kb) * kStateElems;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = 16 * t + l16;
@@ -1791,16 +1801,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         o[r] = (float)sm.qs[tau * LD + i] * acc[r] + ex;
       }
     }
-    f4 full, w = o;
+    f4 full;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float kop = (float)bs[tau * LD + d0 + r];
-      full[r] = o[r] + self * kop;
-      if constexpr (kX) w[r] = kop * xdq[t][r] - xkk[t][r] * o[r];
+    for (int r = 0; r < 4; ++r) full[r] = o[r] + self * (float)bs[tau * LD + d0 + r];
+    const bool here = cell != kNoRow && d0 < p.dk;
+    const size_t at = ((size_t)seq * p.n_tok + (cell == kNoRow ? 0u : cell)) * p.dk + d0;
+    if (p.vmode == kVFirst) {  // this value block's sums, for the last block to add to
+      if (here) {
+        *reinterpret_cast<f4 *>(p.accf + at) = full;
+        *reinterpret_cast<f4 *>(p.acco + at) = o;
+      }
+      continue;
+    }
+    if (p.vmode == kVLast && here) {
+      full += *reinterpret_cast<const f4 *>(p.accf + at);
+      o += *reinterpret_cast<const f4 *>(p.acco + at);
+    }
+    f4 w = o;
+    if constexpr (kX) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (float)bs[tau * LD + d0 + r] * xdq[t][r] - xkk[t][r] * o[r];
     }
     buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
-    if (cell != kNoRow && d0 < p.dk)
-      *reinterpret_cast<f4 *>(off + ((size_t)seq * p.n_tok + cell) * p.dk + d0) = w;
+    if (here) *reinterpret_cast<f4 *>(off + at) = w;
   }
 }
 
@@ -2021,8 +2044,9 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.q = a.kop; p.k = a.kop; p.v = a.aop; p.g = a.g; p.out = const_cast<void *>(a.bop);
   p.bh_count = a.bh; p.n_tok = a.n_tok; p.gh = a.grid_h; p.gw = a.grid_w; p.dir = a.direction;
   p.rcp_gh = 1.0f / (float)a.grid_h;
-  p.dk = a.d_k; p.dv = a.d_v; p.nvb = 1;
+  p.dk = a.d_k; p.dv = a.d_v;
   p.kpitch = a.kpitch; p.kcol = a.kcol;
+  p.nvb = a.nvb > 0 ? a.nvb : 1; p.vb = a.vb; p.vmode = a.vmode; p.accf = a.accf; p.acco = a.acco;
   p.n_chunk = a.n_chunk; p.prev = a.prev;
   p.prev_nk = a.prev_nk > 0 ? a.prev_nk : 1;
   p.prev_kb = a.prev_kb;

@@ -86,11 +86,13 @@ def test_head_dims(dims, dtype):
         check(q, k, v, g, d, dtype, f"dk={dk} dv={dv}", s0=s0, dsf=dsf, seed=36 + d)
 
 
-@pytest.mark.parametrize("dims", [(128, 64), (96, 32), (68, 64), (128, 4)], ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+@pytest.mark.parametrize("dims", [(128, 64), (96, 32), (68, 64), (128, 4), (64, 128), (32, 100), (128, 128),
+                                  (100, 68)], ids=lambda d: f"dk{d[0]}_dv{d[1]}")
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_wide_keys(dims, dtype):
-    """More than 64 key dims: both key blocks' states in one pass, dv summed over them in fp32,
-    and dq, dk, dlog_gate, ds0 per key block as slices of the key-side rows."""
+def test_wide_heads(dims, dtype):
+    """Heads wider than 64: both key blocks' states in one pass, dv summed over them in fp32, and
+    dq, dk, dlog_gate, ds0 per key block as slices of the key-side rows; each value block's states
+    as a sequence of its own, and dq and dk summed over the value blocks in fp32."""
     dk, dv = dims
     q, k, v, g = gla_inputs.make_inputs(2, 2, 9, 17, dk, dv, dtype, "light", seed=dk * 3 + dv)
     gen = torch.Generator().manual_seed(dk + 5 * dv)
@@ -101,14 +103,14 @@ def test_wide_keys(dims, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_wide_keys_long(dtype):
-    """d_k = 128 over 4,096 tokens (64 chunks per scan) with extreme gates on some dims."""
-    q, k, v, g = gla_inputs.make_inputs(1, 2, 64, 64, 128, 64, dtype, "mixed_extreme", seed=52)
+def test_wide_heads_long(dtype):
+    """128 x 128 heads over 4,096 tokens (64 chunks per scan) with extreme gates on some dims."""
+    q, k, v, g = gla_inputs.make_inputs(1, 2, 64, 64, 128, 128, dtype, "mixed_extreme", seed=52)
     gen = torch.Generator().manual_seed(53)
-    s0 = torch.randn(1, 2, 128, 64, generator=gen) * 0.5
-    dsf = torch.randn(1, 2, 128, 64, generator=gen) * 0.1
+    s0 = torch.randn(1, 2, 128, 128, generator=gen) * 0.5
+    dsf = torch.randn(1, 2, 128, 128, generator=gen) * 0.1
     for d in (1, 2):
-        note(f"errors {check(q, k, v, g, d, dtype, '64x64 dk=128', s0=s0, dsf=dsf, seed=54 + d)}")
+        note(f"errors {check(q, k, v, g, d, dtype, '64x64 dk=dv=128', s0=s0, dsf=dsf, seed=54 + d)}")
 
 
 @pytest.mark.parametrize("widx", [2, 4])
@@ -137,8 +139,9 @@ def test_long_sequence(dtype):
 
 
 def test_unsupported_width_and_empty_calls():
-    q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 1, 4, 4, 64, 128, "f16", "light", seed=38))
-    with pytest.raises(gla.GlaError) as ex:  # d_v above 64
+    q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 1, 4, 4, 64, 64, "f16", "light", seed=38))
+    v = torch.zeros(1, 1, 4, 4, 132, dtype=torch.float16, device=DEV)
+    with pytest.raises(gla.GlaError) as ex:  # d_v above 128
         gla.gla_backward(q, k, v, g, torch.zeros_like(v), 0)
     assert ex.value.code == -2
     x = torch.empty(2, 3, 0, 5, 64, dtype=torch.float16, device=DEV)

@@ -61,7 +61,7 @@ int main(void) {
          GTR_ERR_NO_DEVICE, "check without device");
   /* backward and Spatial SwiGLU argument checks */
   expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 64,
-                     128, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_v 128");
+                     132, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_v 132");
   expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 132,
                      64, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_k 132");
   expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, p, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 64, 64, 0, 1, 0),
