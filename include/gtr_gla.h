@@ -252,7 +252,12 @@ int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chu
  * the 64-wide value blocks in fp32 before one rounding); every output
  * must be distinct from every input and from the others; the other rules are
  * those of gtr_gla_fwd_ex.  Asynchronous on `stream`; the library keeps a
- * separate per-(device, stream) backward workspace.  For 16-bit I/O the
+ * separate per-(device, stream) backward workspace.  The passes along the
+ * reversed scan run on a second stream of the library's, forked from `stream`
+ * with an event and joined back into it within the call, so the call is
+ * ordered on `stream` like a single kernel.  That second stream is made by the
+ * first call on a (device, stream): a stream must see one call before it is
+ * captured into a graph (GTR_ERR_CAPTURE otherwise).  For 16-bit I/O the
  * states and dq, dk come from fp32 operands; dv comes from the forward
  * kernels run along the reversed scan (keys q, values dout, states dL/dS), so
  * the value-range rules above apply to q, dout and the state gradients. */

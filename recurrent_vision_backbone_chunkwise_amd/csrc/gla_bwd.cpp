@@ -17,6 +17,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "gla_internal.h"
 #include "gtr_gla.h"
@@ -54,6 +57,39 @@ Layout layout(long long bh, long long n_tok, int n_chunk, int d_k, int d_v, int 
   l.acco = l.accf + acc;
   l.total = l.acco + acc;
   return l;
+}
+
+// A second stream per (device, caller stream) for the passes that do not
+// depend on each other (the reversed scan and dv run beside the forward
+// states and dq), with the events that fork it from the caller's stream and
+// join it back.  Default priority, non-blocking; created outside stream
+// capture only, kept until the process ends.
+struct Side {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mutex;
+std::map<std::pair<int, hipStream_t>, Side> g_sides;
+
+int side_stream(int device, hipStream_t stream, Side *out) {
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  auto it = g_sides.find({device, stream});
+  if (it == g_sides.end()) {
+    if (gtr::stream_capturing(stream))
+      return set_error(GTR_ERR_CAPTURE,
+                       "backward: make one call on this stream before capturing it (its second stream is "
+                       "created on the first call)");
+    Side sd;
+    if (hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(GTR_ERR_ALLOC, "backward: creating its second stream failed");
+    }
+    it = g_sides.emplace(std::make_pair(device, stream), sd).first;
+  }
+  *out = it->second;
+  return GTR_OK;
 }
 
 int launched(int err) {
@@ -151,6 +187,24 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   };
   float *sfin = ds_final ? reinterpret_cast<float *>(ws + lay.sfin) : nullptr;
   float *g0 = ds0 ? reinterpret_cast<float *>(ws + lay.g0) : nullptr;
+  Side side;
+  if ((rc = side_stream(device, stream, &side)) != GTR_OK) return rc;
+  // the second stream starts after everything queued on the caller's stream
+  if (hipEventRecord(side.fork, stream) != hipSuccess || hipStreamWaitEvent(side.stream, side.fork, 0) != hipSuccess)
+    return launched((int)hipGetLastError());
+  bool joined = false;
+  auto join = [&]() -> int {  // the caller's stream continues once the second one is done
+    if (joined) return GTR_OK;
+    joined = true;
+    if (hipEventRecord(side.join, side.stream) != hipSuccess || hipStreamWaitEvent(stream, side.join, 0) != hipSuccess)
+      return launched((int)hipGetLastError());
+    return GTR_OK;
+  };
+  // every return after the fork joins first, so a captured graph never ends with the fork open
+  auto fail_joined = [&](int code) {
+    (void)join();
+    return code;
+  };
 
   // 1. states entering each chunk, both key blocks at once and each value
   // block as a sequence of its own: [bh][nvb][n_chunk][nk][4096]
@@ -162,20 +216,21 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   f.s0 = s0; f.s_final = sfin; f.fused = false; f.states_only = true; f.stream = stream;
   f.fp32_operands = true;  // the boundary states feed sums whose terms cancel (dlog_gate)
   scan_area(lay.fwd, f);
-  if ((rc = launched(gtr::launch_gla(f))) != GTR_OK) return rc;
   gtr::LaunchArgs r = f;  // 2. the state gradients along the reversed scan, then dv from them
   r.q = k; r.k = q; r.v = dout; r.out = dv; r.lag_gates = true;
   r.direction = direction ^ 1;
   r.s0 = ds_final; r.s_final = g0;
+  r.stream = side.stream;  // on the second stream, beside 1 and the first dq pass
   scan_area(lay.rev, r);
-  if ((rc = launched(gtr::launch_gla(r))) != GTR_OK) return rc;
+  if ((rc = launched(gtr::launch_gla(r))) != GTR_OK) return fail_joined(rc);
   gtr::LaunchArgs o = r;  // dv alone needs no fp32 operands; it sums over both key blocks in fp32
   o.states_only = false; o.outputs_only = true; o.fp32_operands = false; o.s0 = nullptr; o.s_final = nullptr;
   // segments of the forward path's length, each entering with the state of its first chunk
   o.prev_per_chunk = true;
   o.seg_len = (int)gtr::split_segment_length(bh * nvb, n_chunk);
   o.n_seg = (n_chunk + o.seg_len - 1) / o.seg_len;
-  if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return rc;
+  if ((rc = launched(gtr::launch_gla(o))) != GTR_OK) return fail_joined(rc);
+  if ((rc = launched(gtr::launch_gla(f))) != GTR_OK) return fail_joined(rc);
 
   // 3-6 per key block: the rows of S and G, dq, dk, dlog_gate and ds0 of key
   // dims [64 h, 64 h + 64) depend only on those dims of q, k and log_gate (the
@@ -202,12 +257,13 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
       }
       return (int)GTR_OK;
     };
-    if ((rc = passes()) != GTR_OK) return rc;
+    if ((rc = passes()) != GTR_OK) return fail_joined(rc);
+    if ((rc = join()) != GTR_OK) return rc;  // dk needs the reversed scan's states
     // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
     b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
     b.pair = dq_off; b.kx = k;
     b.direction = direction ^ 1;
-    if ((rc = passes()) != GTR_OK) return rc;
+    if ((rc = passes()) != GTR_OK) return fail_joined(rc);
     // 5. dlog_gate
     char *dg = static_cast<char *>(dlog_gate) + (size_t)kcol * elt;
     const size_t srow = (size_t)kcol * d_v;  // first state row of the block

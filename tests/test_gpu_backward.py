@@ -182,3 +182,39 @@ def test_workspace_allocation_failure(monkeypatch):
     for name, y, o in zip(NAMES, outs, ref):
         e = parity_errors(y.double().cpu().numpy(), o, "f16")
         assert e["ok"] or (e["rounding_floor"] > e["tol"] and e["err_excess"] <= e["tol"]), (name, e)
+
+
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)], ids=lambda d: f"dk{d[0]}_dv{d[1]}")
+def test_graph_replays_match_eager(dims):
+    """The reversed scan and dv run on a second stream forked from the caller's and joined back:
+    captured in a HIP graph (after one eager call), every replay gives bitwise the eager result,
+    with eager work between the replays."""
+    dk_, dv_ = dims
+    q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(1, 3, 23, 29, dk_, dv_, "f16", "light", seed=61))
+    dout = gla_inputs.make_output_grad(v.shape, "f16", seed=62).to(DEV)
+    gen = torch.Generator().manual_seed(63)
+    s0 = (torch.randn(1, 3, dk_, dv_, generator=gen) * 0.5).to(DEV)
+    dsf = (torch.randn(1, 3, dk_, dv_, generator=gen) * 0.1).to(DEV)
+    outs = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+            torch.empty(1, 3, dk_, dv_, device=DEV)]
+    stream = torch.cuda.Stream()
+
+    def call():
+        gla.gtr_gla_bwd(q, k, v, g, dout, outs[0], outs[1], outs[2], outs[3], 2, s0=s0, ds_final=dsf,
+                        ds0=outs[4], stream=stream)
+
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))  # eager work between the replays, on the default stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(NAMES, outs, eager):
+            assert torch.equal(a, b), f"replay {i}: {name} differs from the eager call"
