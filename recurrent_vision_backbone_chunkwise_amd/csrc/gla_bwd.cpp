@@ -261,7 +261,7 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
     if ((rc = join()) != GTR_OK) return rc;  // dk needs the reversed scan's states
     // 4. dk, and beside it the gate-gradient term x = q dq - k dk (in dk_off)
     b.kop = q; b.aop = v; b.bop = dout; b.out = dk; b.off = dk_off; b.prev = r.prev; b.lag_gates = true;
-    b.pair = dq_off; b.kx = k;
+    b.pair = dq_off; b.kx = k; b.totals = reinterpret_cast<float *>(ws + lay.totals);
     b.direction = direction ^ 1;
     if ((rc = passes()) != GTR_OK) return fail_joined(rc);
     // 5. dlog_gate

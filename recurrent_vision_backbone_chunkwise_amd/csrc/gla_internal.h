@@ -65,6 +65,8 @@ struct BwdArgs {
                                     // with `pair` set, the gate-gradient term kop * pair - kx * that
   const float *pair;                // nullable [bh][grid][d_k] fp32: the other pass's `off` (dq)
   const void *kx;                   // with `pair`: [bh][grid][d_k] keys k
+  float *totals;                    // with `pair`: [bh][n_chunk][64] fp32, each chunk's sum of the
+                                    // gate-gradient term per dim (chunks along this pass's scan)
   const float *prev;                // [bh][n_chunk][prev_nk][4096] register order; key block prev_kb
   int prev_nk, prev_kb;             // (prev_nk 0 counts as 1)
   int bh, grid_h, grid_w, n_tok, direction, dtype, n_chunk, d_k, d_v;
@@ -129,10 +131,11 @@ int stream_buffer(int owner, int device, hipStream_t stream, size_t bytes, const
 int launch_gla_bwd_dqk(const BwdArgs &a);
 // dlog_gate_t = sum_{u >= t} x_u + rowsum(ds_final * s_final) along `direction`, with
 // x = q dq - k dk per position and dim (fp32 [bh][grid][d_k], dq and dk without their cancelling
-// self terms, as the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32
-// scratch.  ds_final / s_final may be null.  dg rows and the states' row blocks hold kp >= d_k
-// dims; dg, ds_final and s_final point at the first of the d_k dims computed.
-int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
+// self terms, as the backward chunk kernel's dk pass writes it); totals: [bh][n_chunk][64] fp32,
+// the sum of x over each chunk of the reversed scan (direction ^ 1), as the dk pass writes them.
+// ds_final / s_final may be null.  dg rows and the states' row blocks hold kp >= d_k dims; dg,
+// ds_final and s_final point at the first of the d_k dims computed.
+int launch_dgate(const float *x, const float *ds_final, const float *s_final, const float *totals, void *dg,
                  int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
                  int kp, hipStream_t stream);
 // ds0[i][j] = alpha_0[i] g0[i][j] (alpha of the first scan position), row-major [bh][kp][d_v], for

@@ -1611,7 +1611,9 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
 // leaving them out keeps their rounding out of it.  kX (the dk pass, kop = q):
 // `off` receives instead the gate-gradient term q dq - k dk of each position
 // and dim, with dq from `pair` (the dq pass's `off`) and k from `kx`, so the
-// gate kernels read one array instead of four.  With the scores in
+// gate kernel reads one array instead of four, and `tot` the chunk's sum of
+// that term per dim (this pass's chunks, along the reversed scan), which the
+// gate kernel's running sums start from.  With the scores in
 // registers the kernel needs 77 KB of LDS with fp32 operands: two workgroups
 // per CU.  For 16-bit I/O the scores' operands a and b are inputs, exact in
 // fp16, so those tiles run as fp16 MFMAs (exact products, fp32 sums): the
@@ -1622,16 +1624,27 @@ __device__ __forceinline__ float block_factor(const Smem<Op, NQ> &sm, int a, int
 // block writes them directly.
 enum : int { kVSingle = 0, kVFirst = 1, kVLast = 2 };
 
+// Sum of x over each 16-lane row of a wave, in every lane of the row (DPP
+// rotations by 8, 4, 2 and 1 lanes within the row).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+
 template <class Io, typename Op, bool kX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gla_bwd_dqk(Params p, void *out, float *off,
                                                                                            const float *pair,
-                                                                                           const void *kx) {
+                                                                                           const void *kx, float *tot) {
   using T = typename Io::T;
   constexpr int LD = OpT<Op>::LD;
   __shared__ Smem<Op, -1> sm;
   __shared__ __attribute__((aligned(16))) Op bs[kChunk * LD];  // score keys b [sigma][j], then kop [tau][i]
   __shared__ float self_score[kChunk];                         // P [tau][tau]
   __shared__ float dtile[4][16 * 16];                          // diagonal P^T [sigma][tau] of each sub-block
+  __shared__ float xsum[kX ? 4 : 1][kHead];                    // kX: each wave's sum of the term per dim
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, l16 = lane & 15;
   const int seq = blockIdx.x / p.n_chunk, c = blockIdx.x - seq * p.n_chunk;
@@ -1820,10 +1833,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     f4 w = o;
     if constexpr (kX) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (float)bs[tau * LD + d0 + r] * xdq[t][r] - xkk[t][r] * o[r];
+      for (int r = 0; r < 4; ++r) {
+        w[r] = (float)bs[tau * LD + d0 + r] * xdq[t][r] - xkk[t][r] * o[r];
+        // the wave's 16 tokens of dim d0 + r (missing tokens and dims count 0)
+        const float sr = row_sum16(here ? w[r] : 0.f);
+        if (l16 == 0) xsum[a][d0 + r] = sr;
+      }
     }
     buf_store<Io>(orsrc, cell_at(cell, sq.kpitch, key_col<Io>(sq, d0)), Io::pack(full));
     if (here) *reinterpret_cast<f4 *>(off + at) = w;
+  }
+  if constexpr (kX) {
+    if (p.vmode != kVFirst) {  // uniform: the first of two value blocks writes no term
+      lds_sync();
+      if (tid < kHead)
+        tot[((size_t)seq * p.n_chunk + c) * kHead + tid] = xsum[0][tid] + xsum[1][tid] + xsum[2][tid] + xsum[3][tid];
+    }
   }
 }
 
@@ -1856,24 +1881,11 @@ __device__ __forceinline__ void dgate_terms(const float *xs, size_t base, int c,
   for (int u = 0; u < 16; ++u) x[u] = ok[u] ? v[u] : 0.f;
 }
 
-// Chunk totals of x per dim: one workgroup per (sequence, chunk).
-__global__ __launch_bounds__(kThreads) void gla_dgate_totals(const float *xs, float *totals, int n_tok, int gh,
-                                                             int gw, int dir, float rcp_gh, int d_k, int n_chunk) {
-  __shared__ float part[4][kHead];
-  const int seq = blockIdx.x / n_chunk, c = blockIdx.x - seq * n_chunk;
-  const int r = threadIdx.x >> 6, i = threadIdx.x & 63;
-  float x[16];
-  dgate_terms(xs, (size_t)seq * n_tok * d_k, c, r, i, n_tok, gh, gw, dir, rcp_gh, d_k, x);
-  float sum = 0.f;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) sum += x[u];
-  part[r][i] = sum;
-  __syncthreads();
-  if (r == 0) totals[((size_t)seq * n_chunk + c) * kHead + i] = part[0][i] + part[1][i] + part[2][i] + part[3][i];
-}
-
-// dlog_gate: the later chunks' totals (plus rowsum(dS_final S_final)), then the
-// reverse running sum inside the chunk, quarter by quarter.
+// dlog_gate_t = sum over the positions u from t to the end of the forward
+// scan of x_u (plus rowsum(dS_final S_final)).  Read along the reversed scan
+// (`dir`), the one the dk pass's chunks follow, that is a running sum from
+// its start: the earlier chunks' totals (written by the dk pass), then the
+// sum inside the chunk, quarter by quarter.
 // d_k dims of xs (rows of d_k); dg rows and the states' row blocks hold kp
 // dims (dg and the state pointers start at the slice's first dim).
 template <class Io>
@@ -1892,7 +1904,7 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, con
 #pragma unroll
   for (int u = 0; u < 16; ++u) sum += x[u];
   part[r][i] = sum;
-  // what follows this quarter: the later quarters, the later chunks, the final-state term
+  // what precedes this quarter: the earlier quarters, the earlier chunks, the final-state term
   // (batches of independent loads: a clamped index, then a masked add)
   float run = 0.f;
   if (i < d_k) {
@@ -1916,25 +1928,25 @@ __global__ __launch_bounds__(kThreads) void gla_dgate_apply(const float *xs, con
     }
     const float *tot = totals + (size_t)seq * n_chunk * kHead + i;
     constexpr int kBatch = 8;
-    for (int c2 = n_chunk - 1 - r; c2 > c; c2 -= 4 * kBatch) {
+    for (int c2 = r; c2 < c; c2 += 4 * kBatch) {
       float tv[kBatch];
 #pragma unroll
-      for (int e = 0; e < kBatch; ++e) tv[e] = tot[(size_t)max(c2 - 4 * e, 0) * kHead];
+      for (int e = 0; e < kBatch; ++e) tv[e] = tot[(size_t)min(c2 + 4 * e, n_chunk - 1) * kHead];
 #pragma unroll
       for (int e = 0; e < kBatch; ++e)
-        if (c2 - 4 * e > c) run += tv[e];
+        if (c2 + 4 * e < c) run += tv[e];
     }
   }
   __syncthreads();
-  float later = 0.f;
-  for (int r2 = r + 1; r2 < 4; ++r2) later += part[r2][i];
+  float earlier = 0.f;
+  for (int r2 = 0; r2 < r; ++r2) earlier += part[r2][i];
   __syncthreads();
-  part[r][i] = run;  // this thread's share of the later chunks and the final-state term
+  part[r][i] = run;  // this thread's share of the earlier chunks and the final-state term
   __syncthreads();
-  run = later + part[0][i] + part[1][i] + part[2][i] + part[3][i];
+  run = earlier + part[0][i] + part[1][i] + part[2][i] + part[3][i];
   if (i >= d_k) return;
 #pragma unroll
-  for (int u = 15; u >= 0; --u) {
+  for (int u = 0; u < 16; ++u) {
     const int t = c * kChunk + 16 * r + u;
     run += x[u];
     if (t < n_tok)
@@ -2052,12 +2064,12 @@ int launch_bwd_typed(const BwdArgs &a) {
   p.prev_kb = a.prev_kb;
   // the dk pass (which forms the gate-gradient term from `pair`) runs along
   // the reversed scan with lagged gates; the dq pass along the forward scan
-  if (a.pair && a.lag_gates)
+  if (a.pair && a.lag_gates && a.totals)
     launch(kKernelBwdDqk, gla_bwd_dqk<Lagged<Io>, Op, true>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out,
-           a.off, a.pair, a.kx);
+           a.off, a.pair, a.kx, a.totals);
   else if (!a.pair && !a.lag_gates)
     launch(kKernelBwdDqk, gla_bwd_dqk<Io, Op, false>, (unsigned)(a.bh * a.n_chunk), a.stream, p, a.out, a.off,
-           a.pair, a.kx);
+           a.pair, a.kx, a.totals);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
@@ -2079,18 +2091,17 @@ int launch_gla_bwd_dqk(const BwdArgs &a) {
 
 namespace {
 template <class Io>
-int launch_dgate_typed(const float *xs, const float *ds_final, const float *s_final, float *totals, void *dg,
+int launch_dgate_typed(const float *xs, const float *ds_final, const float *s_final, const float *totals, void *dg,
                        int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int kp,
                        hipStream_t stream) {
   using T = typename Io::T;
   const int n_tok = grid_h * grid_w;
   const float rcp = 1.0f / (float)grid_h;
   const dim3 grid((unsigned)(bh * n_chunk));
-  ProfileScope scope(kKernelBwdDgate, stream);
-  hipLaunchKernelGGL(gla_dgate_totals, grid, dim3(kThreads), 0, stream, xs, totals, n_tok, grid_h, grid_w,
-                     direction, rcp, d_k, n_chunk);
-  hipLaunchKernelGGL(gla_dgate_apply<Io>, grid, dim3(kThreads), 0, stream, xs, ds_final, s_final, totals,
-                     static_cast<T *>(dg), n_tok, grid_h, grid_w, direction, rcp, d_k, d_v, n_chunk, kp);
+  // the chunk totals come from the dk pass, whose chunks follow the reversed scan
+  launch(kKernelBwdDgate, gla_dgate_apply<Io>, grid.x, stream, xs, ds_final, s_final,
+         totals, static_cast<T *>(dg), n_tok, grid_h, grid_w, direction ^ 1, rcp,
+         d_k, d_v, n_chunk, kp);
   return (int)hipGetLastError();
 }
 
@@ -2105,7 +2116,7 @@ int launch_ds0_typed(const void *g, const float *g0, float *ds0, int bh, int gri
 }
 }  // namespace
 
-int launch_dgate(const float *x, const float *ds_final, const float *s_final, float *totals, void *dg,
+int launch_dgate(const float *x, const float *ds_final, const float *s_final, const float *totals, void *dg,
                  int bh, int grid_h, int grid_w, int d_k, int d_v, int n_chunk, int direction, int dtype,
                  int kp, hipStream_t stream) {
   switch (dtype) {

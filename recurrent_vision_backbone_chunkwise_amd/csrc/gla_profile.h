@@ -14,7 +14,7 @@ enum KernelId : int {
   kKernelSwigluMix = 5,  // depthwise 3x3 + SiLU gate
   kKernelSwigluOut = 6,  // output projection (library GEMM)
   kKernelBwdDqk = 7,     // backward chunk kernel (dq, dk)
-  kKernelBwdDgate = 8,   // gate gradient (chunk totals, then running sums)
+  kKernelBwdDgate = 8,   // gate gradient (running sums from the dk pass's chunk totals)
   kKernelBwdDs0 = 9,     // gradient of the initial state
   kNumKernels = 10
 };

@@ -44,7 +44,7 @@ def short_name(mangled: str) -> str:
 
 
 # Library kernels whose instantiations a summary tells apart by their template arguments.
-LIBRARY_KERNELS = KERNELS + ("gla_bwd_dqk", "gla_dgate_totals", "gla_dgate_apply", "gla_ds0",
+LIBRARY_KERNELS = KERNELS + ("gla_bwd_dqk", "gla_dgate_apply", "gla_ds0",
                              "gla_state_copy", "swiglu_mix")
 
 

@@ -48,8 +48,8 @@ def test_display_names_keep_template_arguments():
             "void const*)")
     assert profiling.display_name(name) == "gla_bwd_dqk<Lagged<IoF16>, float, true>"
     assert profiling.display_name("gla_seg_out") == "gla_seg_out"
-    assert profiling.display_name("gtr::(anonymous namespace)::gla_dgate_totals(float const*, int)") == \
-        "gla_dgate_totals"
+    assert profiling.display_name("gtr::(anonymous namespace)::gla_state_copy(float const*, float*, long long)") == \
+        "gla_state_copy"
     assert profiling.display_name(MANGLED) == "gla_seg_out<IoF16, _Float16, 1>"
     assert profiling.display_name("_ZN3gtr12_GLOBAL__N_110swiglu_mixIDF16_DF16_EEvPKT0_PKT_S7_PS5_iiiiii") == \
         "swiglu_mix<_Float16, _Float16>"
