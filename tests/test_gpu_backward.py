@@ -49,7 +49,8 @@ def check(q, k, v, g, direction, dtype, label, s0=None, dsf=None, seed=0):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("direction", [0, 1, 2, 3])
-@pytest.mark.parametrize("grid", [(1, 1), (1, 63), (7, 9), (9, 17), (13, 11)], ids=lambda g: f"{g[0]}x{g[1]}")
+@pytest.mark.parametrize("grid", [(1, 1), (1, 63), (7, 9), (9, 17), (13, 11), (8, 8), (8, 24), (16, 16)],
+                         ids=lambda g: f"{g[0]}x{g[1]}")
 def test_small_grids(grid, direction, dtype):
     gh, gw = grid
     q, k, v, g = gla_inputs.make_inputs(2, 3, gh, gw, 64, 64, dtype, "light", seed=gh * 100 + gw + direction)
@@ -218,3 +219,4 @@ def test_graph_replays_match_eager(dims):
         torch.cuda.synchronize()
         for name, a, b in zip(NAMES, outs, eager):
             assert torch.equal(a, b), f"replay {i}: {name} differs from the eager call"
+
