@@ -295,7 +295,9 @@ int gtr_gla_stream_status(hipStream_t stream);
 /*
  * Per-kernel timing (measurement aid).  Between gtr_gla_profile_begin() and
  * gtr_gla_profile_end() every kernel the library launches outside graph
- * capture is bracketed by two HIP events recorded on the call's stream.
+ * capture is bracketed by two HIP events recorded on the stream it runs on
+ * (the call's stream, or the backward pass's second stream).  Kernels that
+ * run side by side on two streams each count their whole duration.
  * gtr_gla_profile_end() waits for those events and fills, for kernel ids
  * 0..max_kernels-1, the summed elapsed milliseconds and the launch counts
  * (either array may be NULL).  Returns the number of kernel ids (10), or
