@@ -10,9 +10,13 @@
 //      takes the gate of the position before it along that scan (the kernels
 //      read it in place);
 //   3. dq and 4. dk with the backward chunk kernel;
-//   5. dlog_gate = reverse running sum of q dq - k dk (+ rowsum(dS_final S_final)), from
-//      dq and dk without their self terms, which cancel in it;
+//   5. dlog_gate = running sum of q dq - k dk from the end of the forward scan
+//      (+ rowsum(dS_final S_final)), from dq and dk without their self terms,
+//      which cancel in it; the dk pass sums the term over each of its chunks,
+//      and the gate kernel walks the reversed scan from those totals;
 //   6. ds0 = diag(alpha_0) G_0.
+// Step 2 needs nothing from steps 1 and 3, so it runs on a second stream forked
+// from the caller's and joined back before step 4.
 
 #include <hip/hip_runtime.h>
 
