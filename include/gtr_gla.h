@@ -74,7 +74,10 @@
  *
  * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
  * case); 0 <= grid_h*grid_w <= 2^23 and
- * grid_h*grid_w*max(d_k, d_v)*element bytes <= 2^31; 0 <= B*H <= 2^20.
+ * grid_h*grid_w*max(d_k, d_v)*element bytes <= 2^31; 0 <= B*H <= 2^20; and
+ * the launch grids fit 31 bits: B*H*ceil(d_v/64)*ceil(d_k/64) times the
+ * segments per sequence (forward) or the 64-token chunks per sequence
+ * (backward) at most 2^31 - 1 (GTR_ERR_INVALID_ARG otherwise).
  * Pointers must be 16-byte aligned.
  *
  * Value range.  For fp16 and bf16 I/O the matrix operands are fp16 (products

@@ -125,6 +125,12 @@ int gtr_gla_bwd(const void *q, const void *k, const void *v, const void *log_gat
   if (n_tok * (d_k > d_v ? d_k : d_v) * elt > (1LL << 31))
     return set_error(GTR_ERR_INVALID_ARG, "%lld tokens of %d elements exceed 2^31 bytes per sequence", n_tok,
                      d_k > d_v ? d_k : d_v);
+  {  // every launch's grid (one workgroup per chunk and sequence) fits 31 bits
+    const long long chunks = (n_tok + gtr::kChunk - 1) / gtr::kChunk;
+    const long long seqs = bh * ((d_v + gtr::kHead - 1) / gtr::kHead);
+    if (seqs * chunks * ((d_k + gtr::kHead - 1) / gtr::kHead) > 0x7fffffffLL)
+      return set_error(GTR_ERR_INVALID_ARG, "backward: %lld sequences of %lld chunks are too many", seqs, chunks);
+  }
   const size_t kb = (size_t)bh * n_tok * d_k * elt, vb = (size_t)bh * n_tok * d_v * elt;
   const size_t sb = (size_t)bh * d_k * d_v * sizeof(float);
   const bool empty = bh == 0 || n_tok == 0;

@@ -248,7 +248,7 @@ def bwd_call(q=A, k=A + 0x100000, v=A + 0x200000, g=A + 0x300000, do=A + 0x40000
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=4), -1), (dict(dt=3), -1), (dict(B=-1), -1), (dict(q=None), -1), (dict(dg=None), -1),
-    (dict(do=None), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1),
+    (dict(do=None), -1), (dict(gh=1 << 12, gw=1 << 11 | 1), -1), (dict(B=1 << 10, H=1 << 10, gh=2048, gw=4096), -1),
     (dict(dkk=132), -2), (dict(dvv=132), -2), (dict(dvv=30), -2),
     (dict(dq=A + 0x500008), -3), (dict(ds0=A + 0x900004), -3),
     (dict(dq=A), -4), (dict(dv=A + 0x400000), -4), (dict(dk=A + 0x500000), -4),

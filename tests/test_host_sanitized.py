@@ -66,6 +66,8 @@ int main(void) {
                      64, 0, 1, 0), GTR_ERR_UNSUPPORTED, "bwd d_k 132");
   expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, p, c + 8192, c + 12288, c + 16384, NULL, 1, 1, 4, 4, 64, 64, 0, 1, 0),
          GTR_ERR_ALIAS, "bwd alias");
+  expect(gtr_gla_bwd(p, p, p, p, p, NULL, NULL, c + 4096, c + 8192, c + 12288, c + 16384, NULL, 1 << 10, 1 << 10, 2048,
+                     4096, 64, 64, 0, 1, 0), GTR_ERR_INVALID_ARG, "bwd too many chunks");
   expect(gtr_swiglu_fwd(p, p, p, NULL, p, c + 4096, 1, 4, 4, 12, 64, 1, 0), GTR_ERR_UNSUPPORTED, "swiglu C 12");
   expect(gtr_swiglu_fwd(NULL, NULL, NULL, NULL, NULL, NULL, 0, 4, 4, 64, 64, 1, 0), GTR_OK, "swiglu empty");
   /* planner and sizes over a sweep of shapes */
