@@ -220,3 +220,31 @@ def test_graph_replays_match_eager(dims):
         for name, a, b in zip(NAMES, outs, eager):
             assert torch.equal(a, b), f"replay {i}: {name} differs from the eager call"
 
+
+
+def test_two_streams_side_by_side():
+    """Calls on two caller streams, each with its own workspace and second stream, run side by
+    side and give bitwise the results of the same calls made one at a time."""
+    def inputs(seed, shape):
+        q, k, v, g = (t.to(DEV) for t in gla_inputs.make_inputs(*shape, 64, 64, "f16", "light", seed=seed))
+        return q, k, v, g, gla_inputs.make_output_grad(v.shape, "f16", seed=seed + 1).to(DEV)
+    a = inputs(81, (1, 4, 40, 40))
+    b = inputs(83, (2, 3, 33, 29))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(sa):
+        ref_a = gla.gla_backward(*a, 2, want_ds0=True, stream=sa)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sb):
+        ref_b = gla.gla_backward(*b, 1, want_ds0=True, stream=sb)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        note(f"two streams, repeat {rep}")
+        with torch.cuda.stream(sa):
+            got_a = gla.gla_backward(*a, 2, want_ds0=True, stream=sa)
+        with torch.cuda.stream(sb):
+            got_b = gla.gla_backward(*b, 1, want_ds0=True, stream=sb)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, got_a, ref_a):
+            assert torch.equal(x, y), f"stream a, repeat {rep}: {name}"
+        for name, x, y in zip(NAMES, got_b, ref_b):
+            assert torch.equal(x, y), f"stream b, repeat {rep}: {name}"
