@@ -65,12 +65,14 @@
  *     stream is being captured that query is skipped, so capture a call only
  *     after the same call has run eagerly.  Faults inside a kernel surface at
  *     the caller's next synchronisation.
- *   - Three environment variables serve tests and measurement only:
+ *   - Four environment variables serve tests and measurement only:
  *     GTR_GLA_SKIP_POINTER_CHECKS=1 skips the device-pointer queries,
  *     GTR_GLA_TEST_FAIL_ALLOC=1 makes every workspace allocation fail
- *     (GTR_ERR_ALLOC), which leaves the caches as they were, and
+ *     (GTR_ERR_ALLOC), which leaves the caches as they were,
  *     GTR_GLA_FOLD_BLOCK=n (1..32) sets how many segments the one-launch path
- *     groups into a fold block (results change only by rounding).
+ *     groups into a fold block, and GTR_GLA_SCAN=lanes runs boundary scans of
+ *     at most 64 steps as scans across the lanes of a wave (slower; read at
+ *     every call).  Results change only by rounding.
  *
  * Supported sizes: d_k and d_v multiples of 4 from 4 to 128 (64 is the tuned
  * case); 0 <= grid_h*grid_w <= 2^23 and

@@ -56,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -999,6 +1001,90 @@ __global__ __launch_bounds__(kThreads) void gla_seg_scan(Params p) {
   if (p.s_final && user >= 0) p.s_final[user] = s;
 }
 
+// The same recurrence for chains of at most 64 steps, as a scan across the
+// lanes of a wave.  Lane u of a group of P lanes (P the smallest power of two
+// >= the steps) holds segment u's aggregate for 16 consecutive state elements
+// (one row i, 16 columns) and its decay for that row; log2(P) rounds of
+// ds_bpermute combine each lane's block with the block before it:
+//   (D_e, A_e) then (D_l, A_l)  ->  (D_e D_l, D_l A_e + A_l),
+// after which lane u holds the state after segments 0..u from zero and the
+// product of their decays, and writes the state entering segment u + 1 (plus
+// the product times s0).  Loads and stores are 16-byte vectors; every lane of
+// a wave takes part in every round (lanes past the steps carry the identity).
+__device__ __forceinline__ float lane_from(float v, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+template <int NK>
+__global__ __launch_bounds__(kThreads) void gla_seg_scan_lanes(Params p) {
+  constexpr int kGroups = kStateElems / 16;  // element groups per state block
+  const int n_seg = p.n_seg;
+  const int steps = p.s_final ? n_seg : n_seg - 1;
+  int P = 1;
+  while (P < steps) P <<= 1;
+  const long gid = (long)blockIdx.x * kThreads + threadIdx.x;
+  const long grp = gid / P;
+  const int u = (int)(gid - grp * P), lane = threadIdx.x & 63;
+  const long seq_l = grp / (NK * kGroups);
+  const bool valid = seq_l < p.bh_count;
+  const int seq = valid ? (int)seq_l : 0;
+  const int rg = (int)(grp - seq_l * (NK * kGroups)) & (NK * kGroups - 1);
+  const int kb = rg / kGroups, e0 = 16 * (rg % kGroups);
+  const int w = e0 >> 10, x = (e0 >> 6) & 15, i = state_i(x, e0 & 63);
+  const bool have = valid && u < steps;
+  const size_t blk = ((size_t)seq * n_seg + (size_t)min(u, max(steps - 1, 0))) * NK + kb;
+  f4 A[4];
+  float D = have ? p.agg_dec[blk * kHead + i] : 1.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    A[q] = have ? *reinterpret_cast<const f4 *>(p.agg + blk * kStateElems + e0 + 4 * q) : f4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 1; k < P; k <<= 1) {
+    const int src = (lane - k) & 63;
+    const float De = lane_from(D, src);
+    f4 Ae[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Ae[q][c] = lane_from(A[q][c], src);
+    if (u >= k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) A[q] = D * Ae[q] + A[q];
+      D = De * D;
+    }
+  }
+  if (!valid) return;
+  // s0 for these 16 elements (row i of key block kb, columns 16 w .. 16 w + 15 of the value block)
+  f4 S0[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const long long ui = p.s0 ? user_state_index(p, seq, kHead * kb + i, 16 * w + 4 * q + c) : -1;
+      S0[q][c] = ui >= 0 ? p.s0[ui] : 0.f;
+    }
+  float *prev = const_cast<float *>(p.prev);
+  const size_t first = (size_t)seq * n_seg * NK + kb;  // workspace block of segment 0
+  if (u == 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<f4 *>(prev + first * kStateElems + e0 + 4 * q) = S0[q];
+  if (!have) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) A[q] = D * S0[q] + A[q];
+  if (u + 1 < n_seg) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f4 *>(prev + (first + (size_t)(u + 1) * NK) * kStateElems + e0 + 4 * q) = A[q];
+  } else if (p.s_final) {  // u = n_seg - 1: the state after the sequence
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const long long ui = user_state_index(p, seq, kHead * kb + i, 16 * w + 4 * q + c);
+        if (ui >= 0) p.s_final[ui] = A[q][c];
+      }
+  }
+}
+
 // ------------------------------------------------------------ one-launch path
 //
 // The caller's fp32 state of sequence `bh` (s0 or s_final, row-major
@@ -1469,6 +1555,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 }
 
 // Launches `kernel`, bracketed by dispatch-timestamped events while profiling.
+// GTR_GLA_SCAN=lanes (measurement and test aid, read at every launch):
+// boundary scans of at most 64 steps run across lanes (gla_seg_scan_lanes)
+// instead of one lane per element.  Measured on MI355X it is the slower of the
+// two (4.7 -> 6.3 us per scan at 40x40 B1 H6, 4.8 -> 7.5 us at 128x128 B1 H16),
+// so it is off by default.
+bool scan_across_lanes() {
+  const char *e = std::getenv("GTR_GLA_SCAN");
+  return e && e[0] == 'l';
+}
+
 template <typename K, typename... Args>
 void launch(int id, K kernel, unsigned blocks, hipStream_t stream, Args... args) {
   hipEvent_t t0, t1;
@@ -1540,8 +1636,16 @@ int launch_typed(const LaunchArgs &a) {
       launch(kKernelSegState, gla_seg_state<Io, Op, NK>, (unsigned)(a.bh * n_state_seg), a.stream, ps);
     }
     p.prev = a.prev;
-    const long threads = (long)a.bh * NK * kStateElems;
-    launch(kKernelSegScan, gla_seg_scan<NK>, (unsigned)((threads + kThreads - 1) / kThreads), a.stream, p);
+    const int steps = a.s_final ? a.n_seg : a.n_seg - 1;
+    int P = 1;
+    while (P < steps) P <<= 1;
+    const long lanes = (long)a.bh * NK * (kStateElems / 16) * P;
+    if (steps <= 64 && lanes / kThreads < (1L << 30) && scan_across_lanes()) {
+      launch(kKernelSegScan, gla_seg_scan_lanes<NK>, (unsigned)((lanes + kThreads - 1) / kThreads), a.stream, p);
+    } else {
+      const long threads = (long)a.bh * NK * kStateElems;
+      launch(kKernelSegScan, gla_seg_scan<NK>, (unsigned)((threads + kThreads - 1) / kThreads), a.stream, p);
+    }
   }
   if (a.states_only) return (int)hipGetLastError();
   if constexpr (!kStatesOnly) launch(kKernelSegOut, gla_seg_out<Io, Op, NK>, n_blocks, a.stream, p);

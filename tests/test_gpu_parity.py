@@ -634,3 +634,25 @@ def test_single_runtime_and_library_loaded():
     assert len(gla.hip_runtimes_mapped()) == 1
     with open("/proc/self/maps") as f:
         assert any("libgtr_gla.so" in ln for ln in f)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_boundary_scan_across_lanes(dtype, monkeypatch):
+    """The boundary scan as a scan across the lanes of a wave (GTR_GLA_SCAN=lanes, off by
+    default because it is slower): outputs and final states against the oracle, with and
+    without an initial state, over several segment counts, in every direction."""
+    monkeypatch.setenv("GTR_GLA_SCAN", "lanes")
+    B, H, gh, gw = 1, 3, 23, 29
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, dtype, "light", seed=91)
+    s0 = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(92)) * 0.5
+    for seg in (1, 2, 5, 11):
+        for d in range(4):
+            note(f"lane scan seg={seg} dir={d} dtype={dtype}")
+            y, sf = gpu_run(q, k, v, g, d, s0=s0.to(DEV), want_state=True, chunks_per_segment=seg,
+                            path=PATHS["split"])
+            ref, sref = oracle.gla_forward(q, k, v, g, d, s0=s0.double().numpy(), want_state=True)
+            assert parity_errors(y.double().cpu().numpy(), ref, dtype)["ok"]
+            es = parity_errors(sf.double().cpu().numpy(), sref, "f32" if dtype == "f32" else "f16")
+            assert es["ok"], es
+            y2 = gpu_run(q, k, v, g, d, chunks_per_segment=seg, path=PATHS["split"])
+            assert parity_errors(y2.double().cpu().numpy(), oracle.gla_forward(q, k, v, g, d), dtype)["ok"]
