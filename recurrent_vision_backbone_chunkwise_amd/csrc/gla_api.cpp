@@ -105,7 +105,11 @@ void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, i
   sh->seg_len = (int)len;
   sh->n_seg = (int)((n_chunk + len - 1) / len);
   if (sh->fused) {
-    sh->fold_block = std::min(sh->n_seg, kFoldBlock);
+    // blocks of at most kFoldBlock segments, balanced: 9 segments fold as 5 + 4
+    // rather than 8 + 1, which shortens the fold on the path to the last block
+    // (40x40 B8 H6: 117.7 -> 115.0 us per round)
+    const int blocks = (sh->n_seg + kFoldBlock - 1) / kFoldBlock;
+    sh->fold_block = (sh->n_seg + blocks - 1) / blocks;
     // measurement aid: GTR_GLA_FOLD_BLOCK=n sets the fold block size (1..32)
     static const int forced = [] {
       const char *e = std::getenv("GTR_GLA_FOLD_BLOCK");

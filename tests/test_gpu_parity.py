@@ -344,7 +344,7 @@ def test_maximum_sequence_count(path):
 def test_long_boundary_scans(grid, path):
     """One-chunk segments on long sequences (102, 300 and 625 chunks): boundary scans of
     hundreds of steps, with s0 and s_final, in fp32.  On the one-launch path the segments form
-    13 to 79 fold blocks of 8, and the state passes from block to block."""
+    13 to 79 fold blocks of at most 8, and the state passes from block to block."""
     gh, gw = grid
     q, k, v, g = gla_inputs.make_inputs(1, 2, gh, gw, 64, 64, "f32", "light", seed=gh + gw)
     s0 = torch.randn(1, 2, 64, 64, generator=torch.Generator().manual_seed(gh)) * 0.5
