@@ -239,8 +239,9 @@ size_t gtr_gla_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d_k,
 /* The plan the library uses for a shape: chunks per segment, segments per
  * sequence, and 1 if one fused kernel runs (0: three kernels).  The kernels
  * walk B*H*ceil(d_v/64) sequences, one per 64-wide block of value columns.
- * The plan is that of 16-bit I/O (fp32 I/O differs only on the one-launch
- * path with d_k > 64, whose segments hold at most 2 chunks).
+ * The plan is that of 16-bit I/O.  fp32 I/O can differ: its one-launch path
+ * runs one workgroup per CU instead of two, which moves the automatic choice
+ * for some shapes, and with d_k > 64 holds at most 2 chunks per segment.
  * Any output pointer may be NULL.  Returns 0 or an argument error. */
 int gtr_gla_plan(int B, int H, int grid_h, int grid_w, int d_k, int d_v, int chunks_per_segment,
                  int path, int *seg_len, int *n_seg, int *fused);

@@ -65,19 +65,42 @@ struct Shape {
 //    of kFoldBlock segments.  Measured on MI355X (3-chunk segments, fp16, four
 //    directions): blocks of 4, 8, 16 and 32 took 342, 338, 383 and 433 us per
 //    128x128 B1 H16 round; folds cost more than the chain between blocks.
-// Automatic choice (measured on MI355X): the fused launch wins for short
-// sequences (at most kAutoFusedChunks chunks) when there are enough of them
-// to fill the chip with 3-chunk segments (40x40 B8 H6: 125 us per round
-// against 145 us split); otherwise three launches (40x40 B1 H6: 60 against
-// 73 us; 64x64 B1 H16: 59 against 64 us; 128x128 B1 H16: 281 against 338 us).
+// Automatic choice, from four-direction rounds measured on MI355X (64x64
+// heads; us per round, three launches against one):
+//  * the one launch wins where a sequence has at most 48 chunks, there are
+//    at least as many sequences as XCDs, and the segments fill about one
+//    round of resident workgroups (two per CU at 16-bit I/O, one at fp32),
+//    with the shortest segments that fit best:
+//      1-chunk segments: 24x24 B4 H6 69.4 -> 56.4, 32x32 B3 H6 80.7 -> 69.0,
+//        40x40 B2 H6 80.3 -> 72.3, 40x40 B1 H8 67.6 -> 64.3;
+//      2-chunk: 48x48 B1 H16 102.7 -> 86.0 (1-chunk: 91), 40x40 B4 H6
+//        100.1 -> 85.1 (1-chunk: 90.5), 16x16 B32 H6 118 -> 82;
+//      3-chunk, allowed one more workgroup per CU: 40x40 B8 H6 145 -> 112
+//        (2-chunk: 121.5), 32x32 B16 H6 149 -> 122;
+//      fp32: 32x32 B4 H6 130 -> 110 (2-chunk), 48x48 B1 H16 182 -> 145 and
+//        40x40 B8 H6 289 -> 258 (3-chunk);
+//  * three launches win with longer sequences (64x64 B1 H12: 98 against 104;
+//    128x128 B1 H4: 125 against 183), fewer sequences than XCDs (40x40 B1
+//    H6: 61.1 against 64.7), more segments than about one round (40x40 B16
+//    H6: 187 against 194), and where a sequence would be one segment, for
+//    which they launch only their output kernel (8x8 B16 H8: 25.3 against
+//    44.1).
+// The one launch's occupancy makes the choice depend on the element type;
+// gtr_gla_plan, which takes none, reports it for 16-bit I/O.
 constexpr int kFoldBlock = 8;
-constexpr int kAutoFusedChunks = 32;
-constexpr long long kAutoFusedMinGroups = 256;
-constexpr int kAssumedXcds = 8;  // MI355X; used where no device is queried
+constexpr int kAutoFusedChunks = 48;
+constexpr int kAssumedXcds = 8;         // MI355X; used where no device is queried
+constexpr long long kAssumedCus = 256;  // MI355X; the automatic choice is made before any HIP call
 
-bool auto_fused(long long seqs, int nk, int n_chunk) {
-  const long long groups = seqs * ((n_chunk + gtr::kMaxFusedChunks - 1) / gtr::kMaxFusedChunks);
-  return nk == 1 && n_chunk <= kAutoFusedChunks && groups >= kAutoFusedMinGroups;
+// Segment length of the automatic one-launch choice, or 0 for three launches.
+int auto_fused_length(long long seqs, int nk, int n_chunk, int dtype) {
+  if (nk != 1 || n_chunk > kAutoFusedChunks || seqs < kAssumedXcds) return 0;
+  const long long round = (dtype == GTR_DTYPE_F32 ? 1 : 2) * kAssumedCus;  // resident workgroups
+  for (int len = 1; len <= gtr::kMaxFusedChunks && len < n_chunk; ++len) {  // two segments or more
+    const long long segments = seqs * ((n_chunk + len - 1) / len);
+    if (segments <= (len == gtr::kMaxFusedChunks ? round + kAssumedCus : round)) return len;
+  }
+  return 0;
 }
 
 // `bh` counts the sequences the kernels walk (B*H*value blocks); `nk` the key
@@ -89,14 +112,15 @@ void plan(long long bh, int nk, int n_chunk, int path, int chunks_per_segment, i
     sh->seg_len = sh->n_seg = 0;
     return;
   }
-  sh->fused = path == GTR_PATH_FUSED ||
-              (path == GTR_PATH_AUTO && chunks_per_segment <= gtr::kMaxFusedChunks && auto_fused(bh, nk, n_chunk));
+  const int auto_len =
+      path == GTR_PATH_AUTO && chunks_per_segment <= gtr::kMaxFusedChunks ? auto_fused_length(bh, nk, n_chunk, dtype) : 0;
+  sh->fused = path == GTR_PATH_FUSED || auto_len > 0;
   long long len = chunks_per_segment;
   if (sh->fused) {
     // each kept chunk holds a query tile per key block in LDS: with fp32
     // operands and two key blocks, two chunks fill it
     const int max_len = nk == 2 && dtype == GTR_DTYPE_F32 ? 2 : gtr::kMaxFusedChunks;
-    if (len <= 0) len = max_len;
+    if (len <= 0) len = auto_len > 0 ? auto_len : max_len;
     len = std::min<long long>(len, max_len);
   } else if (len <= 0) {
     len = gtr::split_segment_length(bh, n_chunk);
@@ -553,10 +577,16 @@ int gtr_gla_fwd_ex(const void *q, const void *k, const void *v, const void *log_
   }
   if (sh.fused) {
     const DeviceShape &ds = device_shape(device);
-    const int occupancy = dtype == GTR_DTYPE_F32 || sh.nk == 2 ? 1 : (sh.seg_len == 1 ? 3 : 2);
+    const int occupancy = dtype == GTR_DTYPE_F32 || sh.nk == 2 ? 1 : 2;  // workgroups per CU (as the kernel's bounds)
     a.fold_block = sh.fold_block;
     a.xcds = ds.xcds;
-    a.batch = (int)std::min<long long>(kMaxBatch, (sh.seqs + ds.xcds - 1) / ds.xcds);
+    // one batch per XCD where every segment fits in one round of resident
+    // workgroups (16x16 B32 H6, 2-chunk segments: 12 batches of at most 16
+    // sequences left four XCDs a second round); otherwise batches of at most
+    // kMaxBatch sequences, handed out as XCDs free up
+    const long long per_xcd_seqs = (sh.seqs + ds.xcds - 1) / ds.xcds;
+    const bool one_round = per_xcd_seqs * sh.n_seg * ds.xcds <= (long long)occupancy * ds.cus;
+    a.batch = (int)(one_round ? per_xcd_seqs : std::min<long long>(kMaxBatch, per_xcd_seqs));
     const long long per_xcd = (long long)a.batch * sh.n_seg;
     a.grid = (int)std::max<long long>(1, std::min<long long>((long long)occupancy * ds.cus, per_xcd * ds.xcds));
   }

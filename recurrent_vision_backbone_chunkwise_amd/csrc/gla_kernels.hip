@@ -1228,9 +1228,18 @@ __device__ void take_work(const Params &p, int slot, unsigned long long v, int *
       return;
     }
     // Another workgroup of this XCD is taking the next batch.  With no batch
-    // beyond the starting ones, it can only take over a starting batch that
-    // another XCD never began, and works through that alone: leave now.
-    if (p.n_pre >= p.n_batch) {
+    // beyond the starting ones, that workgroup can only take over a starting
+    // batch that another XCD has not begun.  After a batch of this XCD's own
+    // (b >= 0) it is a workgroup that has just finished a segment, and such a
+    // batch is left only where an XCD runs no workgroup of this launch: leave
+    // now rather than poll the work word beside the working ones (the taker
+    // works it alone).  Without one (an XCD with no starting batch, or whose
+    // batch was taken), it acts at launch, where a batch whose XCD has not
+    // begun yet is common: wait, and work the batch it takes with all the
+    // workgroups of this XCD.  (Leaving then left such a batch to one
+    // workgroup: 64x64 B1 H12 with 2-chunk segments took 1.2 ms per
+    // four-call round instead of 0.11 ms.)
+    if (p.n_pre >= p.n_batch && b >= 0) {
       out[0] = -1;
       return;
     }
@@ -1287,11 +1296,14 @@ __device__ __forceinline__ void publish(const Params &p, __amdgpu_buffer_rsrc_t 
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, want), flag_rsrc(p, bh), s * 8, 0, 0);
 }
 
-// Workgroups per CU the LDS allows: fp32 operands take 100-137 KB, one;
-// 16-bit ones 54 KB for one-chunk segments, three, and up to 73 KB, two; two
-// key blocks (a query tile per key block and kept chunk) 64-98 KB, one.
+// Workgroups per CU: fp32 operands take 100-137 KB of LDS, one; two key
+// blocks (a query tile per key block and kept chunk) 64-98 KB, one; 16-bit
+// ones 54-73 KB, two.  The 54 KB of one-chunk segments would let three share
+// a CU, but three leave 168 registers per lane and the fold then spills to
+// scratch (40x40 B1 H6 with one-chunk segments: 80-90 us per call with three,
+// 15 us with two).
 template <typename Op, int kSeg, int NK>
-constexpr int kFusedOccupancy = sizeof(Op) == 4 || NK == 2 ? 1 : (kSeg == 1 ? 3 : 2);
+constexpr int kFusedOccupancy = sizeof(Op) == 4 || NK == 2 ? 1 : 2;
 
 // One launch.  A persistent grid; each workgroup repeatedly takes a segment
 // (at most kSeg chunks) of a sequence of its XCD and:
@@ -1390,7 +1402,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       // for the entering term.  Each round trip brings kBatch aggregates and
       // their decays; the decays (one per thread) go through LDS to the rows
       // each thread holds.
-      constexpr int kBatch = NK == 2 || kFusedOccupancy<Op, kSeg, NK> > 2 ? 2 : 4;  // aggregates per round trip
+      // Two aggregates per round trip: four keep 32 more registers live beside
+      // the kept outputs, which spilled them at 3-chunk segments (40x40 B8 H6:
+      // 114 -> 112 us per round without the spills).
+      constexpr int kBatch = 2;
       constexpr int kDecays = NK * kHead;                                            // decays per aggregate
       static_assert(kBatch * kDecays <= kThreads, "one decay per thread");
       float *dlds = reinterpret_cast<float *>(sm.qs);  // [2][kBatch][NK * 64], alternating

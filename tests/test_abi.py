@@ -134,6 +134,38 @@ def test_plans():
     assert gla.gtr_gla_plan(1, 6, 40, 40, d_k=64, d_v=128) == gla.gtr_gla_plan(1, 12, 40, 40)
 
 
+def test_automatic_choice():
+    """The one launch for sequences of 2 to 48 chunks, at least one sequence per XCD, with the
+    shortest segments (two or more per sequence) whose count fits about one round of resident
+    workgroups (512 at 16-bit I/O; 3-chunk segments up to 768); three launches otherwise."""
+    def auto(B, H, gh, gw):
+        pl = gla.gtr_gla_plan(B, H, gh, gw)
+        return pl["seg_len"] if pl["fused"] else 0
+
+    assert auto(4, 6, 24, 24) == 1      # 24 sequences x 9 chunks: 216 one-chunk segments
+    assert auto(1, 8, 40, 40) == 1      # 8 x 25 = 200
+    assert auto(2, 16, 32, 32) == 1     # 32 x 16 = 512, the most that fit
+    assert auto(1, 16, 48, 48) == 2     # 16 x 36 = 576 one-chunk segments, 288 of two chunks
+    assert auto(32, 6, 16, 16) == 2     # 192 x 4 = 768, then 384
+    assert auto(8, 6, 40, 40) == 3      # 48 x 25: 1200, 624, then 432 of three chunks
+    assert auto(16, 6, 32, 32) == 3     # 96 x 16: 1536, 768, then 576 <= 768
+    assert auto(16, 6, 40, 40) == 0     # 96 x 25: 864 three-chunk segments, more than a round
+    assert auto(1, 6, 40, 40) == 0      # fewer sequences than XCDs
+    assert auto(1, 12, 64, 64) == 0     # 64 chunks per sequence
+    assert auto(1, 16, 56, 56) == 0     # 49 chunks
+    assert auto(16, 8, 8, 8) == 0       # one chunk: a single segment per sequence
+    assert auto(16, 8, 8, 16) == 1      # two chunks: two one-chunk segments
+    assert gla.gtr_gla_plan(8, 6, 40, 40, d_k=128)["fused"] is False  # two key blocks
+    # fp32 I/O runs the one launch at one workgroup per CU (256 resident): 24 x 16 = 384 one-chunk
+    # segments do not fit, 192 of two chunks do; the workspace follows the plan of the call's type
+    ws = gla.lib().gtr_gla_workspace_bytes_ex
+    ws.argtypes, ws.restype = [ctypes.c_int] * 9, ctypes.c_size_t
+    fused = gla.GTR_PATH_FUSED
+    assert ws(4, 6, 32, 32, 64, 64, gla.GTR_DTYPE_F32, 0, 0) == ws(4, 6, 32, 32, 64, 64, gla.GTR_DTYPE_F32, 2, fused)
+    assert ws(4, 6, 32, 32, 64, 64, gla.GTR_DTYPE_F16, 0, 0) == ws(4, 6, 32, 32, 64, 64, gla.GTR_DTYPE_F16, 1, fused)
+    assert auto(4, 6, 32, 32) == 1
+
+
 A = 0x10000  # fake, 16-byte aligned, never dereferenced
 
 

@@ -316,10 +316,11 @@ def test_maximum_grid():
     assert float(err) < 1e-4, float(err)
 
 
-@pytest.mark.parametrize("path", ["auto", "split"])
+@pytest.mark.parametrize("path", ["fused", "split"])
 def test_maximum_sequence_count(path):
     """B*H = 2^20 sequences (1024 x 1024) of a 1x3 grid: a grid of 2^20 workgroups, and on the
-    one-launch path a control line per sequence; sampled sequences are checked against the oracle."""
+    one-launch path a control line per sequence; sampled sequences are checked against the oracle.
+    (The automatic choice takes three launches here: a sequence is one segment.)"""
     B = H = 1024
     gen = torch.Generator(device=DEV).manual_seed(17)
     shape = (B, H, 1, 3, 64)
@@ -327,9 +328,10 @@ def test_maximum_sequence_count(path):
     k = (torch.randn(shape, generator=gen, device=DEV) / 8).half()
     v = torch.randn(shape, generator=gen, device=DEV).half()
     g = (torch.nn.functional.logsigmoid(torch.randn(shape, generator=gen, device=DEV)) / 16).half()
-    assert gla.gtr_gla_plan(B, H, 1, 3, path=PATHS.get(path, 0))["fused"] == (path == "auto")
+    assert gla.gtr_gla_plan(B, H, 1, 3, path=PATHS[path])["fused"] == (path == "fused")
+    assert not gla.gtr_gla_plan(B, H, 1, 3)["fused"]
     note(f"2^20 sequences path={path}")
-    y = gpu_run(q, k, v, g, 1, path=PATHS.get(path, 0))
+    y = gpu_run(q, k, v, g, 1, path=PATHS[path])
     gla.gtr_gla_stream_status()
     rows = torch.tensor([0, 1, 511, 777, 1023])
     part = [t[rows][:, rows].cpu() for t in (q, k, v, g)]  # 25 sequences spread over B and H
@@ -444,6 +446,48 @@ def test_fused_repeated_calls_are_identical():
     gla.gtr_gla_fwd_ex(q, k, v, g, out, 2, path=1)
     gla.gtr_gla_stream_status()  # no wait between workgroups gave up
     assert torch.equal(out, first)
+
+
+@pytest.mark.parametrize("shape", [(1, 12, 64, 64, 2), (1, 12, 64, 64, 1), (1, 4, 64, 64, 3), (1, 6, 40, 40, 1),
+                                   (1, 9, 40, 40, 2), (3, 1, 33, 31, 1)],
+                         ids=lambda s: "B{}H{}_{}x{}_seg{}".format(*s))
+def test_one_launch_with_fewer_batches_than_xcds(shape):
+    """The one-launch path with fewer sequence batches than XCDs: an XCD without a batch of its
+    own takes over, at launch, one whose XCD has not begun, and works it with all its workgroups.
+    Whoever works a batch, the outputs match the oracle, no wait gives up, and a second call is
+    bitwise the same."""
+    B, H, gh, gw, seg = shape
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, "f16", "light", seed=H + gh + seg)
+    ref = oracle.gla_forward(q, k, v, g, 3)
+    note(f"few batches {shape}")
+    y = gpu_run(q, k, v, g, 3, chunks_per_segment=seg, path=1)
+    gla.gtr_gla_stream_status()
+    assert parity_errors(y.double().cpu().numpy(), ref, "f16")["ok"]
+    y2 = gpu_run(q, k, v, g, 3, chunks_per_segment=seg, path=1)
+    gla.gtr_gla_stream_status()
+    assert torch.equal(y, y2)
+
+
+# (B, H, grid, dtype, the segment length the automatic choice takes for that type)
+AUTO_SHAPES = [(4, 6, (24, 24), "f16", 1), (1, 16, (48, 48), "bf16", 2), (32, 6, (16, 16), "f16", 2),
+               (16, 6, (32, 32), "f16", 3), (4, 6, (32, 32), "f32", 2), (1, 8, (40, 40), "f16", 1)]
+
+
+@pytest.mark.parametrize("case", AUTO_SHAPES, ids=lambda c: f"B{c[0]}H{c[1]}_{c[2][0]}x{c[2][1]}_{c[3]}")
+def test_automatic_one_launch_shapes(case):
+    """Shapes for which the automatic choice takes the one launch with 1-, 2- or 3-chunk segments:
+    parity with the oracle, and bitwise the same as an explicit call with that plan."""
+    B, H, (gh, gw), dtype, seg = case
+    q, k, v, g = gla_inputs.make_inputs(B, H, gh, gw, 64, 64, dtype, "light", seed=B * H + gh)
+    for direction in (0, 2):
+        note(f"auto {case} dir={direction}")
+        y = gpu_run(q, k, v, g, direction)
+        ref = oracle.gla_forward(q, k, v, g, direction)
+        e = parity_errors(y.double().cpu().numpy(), ref, dtype)
+        assert e["ok"], (case, direction, e)
+        explicit = gpu_run(q, k, v, g, direction, chunks_per_segment=seg, path=1)
+        gla.gtr_gla_stream_status()
+        assert torch.equal(y, explicit), case
 
 
 def test_paths_agree_and_repeat_on_one_workspace():
