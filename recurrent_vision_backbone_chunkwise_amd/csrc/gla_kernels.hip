@@ -1160,8 +1160,9 @@ __device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcn
 // (k sequences in the batch).  Tickets follow scan order within each sequence,
 // so every segment a workgroup waits for holds a smaller ticket, taken by a
 // running workgroup of the same XCD (which is why a workgroup may leave while
-// another one of its XCD still has work: no ticket waits on a later one).  The XCD's 64-bit work word holds
-// (tag << 32) + next ticket, the tag being 0 (the starting batch, or none),
+// another one of its XCD still has work: no ticket waits on a later one).
+// The XCD's 64-bit work word holds (tag << 32) + next ticket, the tag being
+// 0 (the starting batch, or none),
 // batch + 1, kStolen or kBatchDone.  The workgroup whose ticket is the first
 // past the end of its batch takes the next batch and keeps its ticket 0;
 // workgroups past it wait until it has.  When the counter runs out, that
@@ -1238,7 +1239,7 @@ __device__ void take_work(const Params &p, int slot, unsigned long long v, int *
     // begun yet is common: wait, and work the batch it takes with all the
     // workgroups of this XCD.  (Leaving then left such a batch to one
     // workgroup: 64x64 B1 H12 with 2-chunk segments took 1.2 ms per
-    // four-call round instead of 0.11 ms.)
+    // four-call round instead of 0.10 ms.)
     if (p.n_pre >= p.n_batch && b >= 0) {
       out[0] = -1;
       return;
