@@ -470,7 +470,8 @@ def test_one_launch_with_fewer_batches_than_xcds(shape):
 
 # (B, H, grid, dtype, the segment length the automatic choice takes for that type)
 AUTO_SHAPES = [(4, 6, (24, 24), "f16", 1), (1, 16, (48, 48), "bf16", 2), (32, 6, (16, 16), "f16", 2),
-               (16, 6, (32, 32), "f16", 3), (4, 6, (32, 32), "f32", 2), (1, 8, (40, 40), "f16", 1)]
+               (16, 6, (32, 32), "f16", 3), (4, 6, (32, 32), "f32", 2), (1, 8, (40, 40), "f16", 1),
+               (2, 8, (9, 13), "f16", 1), (16, 8, (8, 16), "bf16", 1)]  # 2 chunks, the first ragged
 
 
 @pytest.mark.parametrize("case", AUTO_SHAPES, ids=lambda c: f"B{c[0]}H{c[1]}_{c[2][0]}x{c[2][1]}_{c[3]}")
