@@ -68,6 +68,56 @@ def test_forward_random_configuration(seed):
         assert es["ok"], f"{c}: s_final {es}"
 
 
+def draw_many(seed):
+    """Like draw, with 2 to 60 sequences (B*H, twice with d_v > 64) on grids of up to 40x40, so that the
+    automatic choice takes the one launch with 1-, 2- or 3-chunk segments for many of them."""
+    r = np.random.RandomState(seed)
+    c = draw(seed)
+    c.update(B=int(r.randint(1, 7)), H=int(r.randint(2, 11)), gh=int(r.randint(4, 41)), gw=int(r.randint(4, 41)),
+             dk=64 if r.randint(3) else 4 * int(r.randint(1, 17)), dv=64 if r.randint(3) else 4 * int(r.randint(1, 33)),
+             path=int(gla.GTR_PATH_AUTO), seg=0)
+    if seed % 6 == 4:  # 24 sequences of 23 to 25 chunks: 2-chunk segments
+        c.update(B=4, H=6, gh=40, gw=int(r.randint(36, 41)), dk=64, dv=64)
+    if seed % 6 == 5:  # 48 sequences of 21 to 25 chunks: 3-chunk segments
+        c.update(B=8, H=6, gh=int(r.randint(36, 41)), gw=int(r.randint(36, 41)), dk=64, dv=64)
+    return c
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_forward_random_many_sequences(seed):
+    c = draw_many(9000 + seed)
+    plan = gla.gtr_gla_plan(c["B"], c["H"], c["gh"], c["gw"], 0, gla.GTR_PATH_AUTO, c["dk"], c["dv"])
+    note(f"forward many seed={seed} {c} plan={plan}")
+    q, k, v, g = gla_inputs.make_inputs(c["B"], c["H"], c["gh"], c["gw"], c["dk"], c["dv"], c["dtype"],
+                                        c["gate"], seed=9100 + seed)
+    s0 = None
+    if c["s0"]:
+        s0 = torch.randn(c["B"], c["H"], c["dk"], c["dv"], generator=torch.Generator().manual_seed(9200 + seed)) * 0.5
+    res = gla.gla_forward(*(t.to(DEV) for t in (q, k, v, g)), c["direction"],
+                          s0=s0.to(DEV) if s0 is not None else None, want_state=c["want_state"])
+    gla.gtr_gla_stream_status()
+    y, sf = res if c["want_state"] else (res, None)
+    ref = oracle.gla_forward(q, k, v, g, c["direction"], s0=s0.double().numpy() if s0 is not None else None,
+                             want_state=c["want_state"])
+    ref, sref = ref if c["want_state"] else (ref, None)
+    e = parity_errors(y.double().cpu().numpy(), ref, c["dtype"])
+    assert e["ok"], f"{c}: out {e}"
+    if c["want_state"]:
+        es = parity_errors(sf.double().cpu().numpy(), sref, state_tolerance_dtype(c["dtype"]))
+        assert es["ok"], f"{c}: s_final {es}"
+
+
+def test_many_sequence_draws_reach_every_automatic_plan():
+    """The draws above cover three launches and the one launch with 1-, 2- and 3-chunk segments
+    (host-side check of the plans the seeds give)."""
+    lens = set()
+    for seed in range(24):
+        c = draw_many(9000 + seed)
+        pl = gla.gtr_gla_plan(c["B"], c["H"], c["gh"], c["gw"], 0, gla.GTR_PATH_AUTO, c["dk"], c["dv"])
+        lens.add(pl["seg_len"] if pl["fused"] else 0)
+    assert {0, 1, 2, 3} <= lens, lens
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_backward_random_configuration(seed):
     c = draw(8000 + seed)
